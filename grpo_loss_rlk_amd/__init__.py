@@ -1,0 +1,185 @@
+"""rlk on MI355X: token log-probabilities, entropy and the GRPO token loss.
+
+Thin Python binding over the C ABI in include/rlk.h (librlk.so, hand-written
+HIP kernels for gfx950). This module only marshals arguments: it allocates the
+output and workspace tensors with torch on the input's device and passes raw
+pointers and the current HIP stream. Every step of the computation runs in the
+library's kernels; there is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _native
+from ._native import (DTYPE_BF16, DTYPE_F32, FLAG_BAD_PARAM, FLAG_BAD_TARGET,  # noqa: F401
+                      FLAG_BOUNDARY, FLAG_NONFINITE, FLAG_OUTSIDE, RlkError, lib)
+
+__all__ = ["logprob_from_logits", "logprob_fused_linear", "logprob_fused_linear_bwd",
+           "grpo_token_loss", "lib", "RlkError"]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns blocks aligned to at least 512 bytes
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _f32_opt(x, n, device):
+    if x is None:
+        return None
+    x = torch.as_tensor(x, dtype=torch.float32, device=device).contiguous()
+    assert x.numel() == n
+    return x
+
+
+def logprob_from_logits(logits: torch.Tensor, targets: torch.Tensor, temperature: float,
+                        top_p: float = 1.0, *, vocab: int | None = None,
+                        temperature_per_row=None, top_p_per_row=None, top_k: int = 0,
+                        want_entropy_full: bool = True, want_nucleus: bool = True) -> dict:
+    """Full and top-p truncated logprob / entropy for each row of ``logits``.
+
+    ``logits`` is [N, row_stride] fp32 or bf16 on the GPU (row-major, rows may
+    be padded: only the first ``vocab`` entries are scored). Returns a dict of
+    tensors: lp_full, lp_trunc, entropy_trunc, entropy_full, nucleus_size,
+    threshold, flags.
+    """
+    if logits.dtype == torch.float32:
+        dtype = DTYPE_F32
+    elif logits.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+    else:
+        raise TypeError(f"logits dtype {logits.dtype} is not float32 or bfloat16")
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D tensor with unit column stride")
+    N, width = logits.shape
+    V = width if vocab is None else int(vocab)
+    dev = logits.device
+    targets = targets.to(device=dev, dtype=torch.int64).contiguous()
+    f = dict(device=dev, dtype=torch.float32)
+    out = {"lp_full": torch.empty(N, **f), "lp_trunc": torch.empty(N, **f),
+           "entropy_trunc": torch.empty(N, **f),
+           "entropy_full": torch.empty(N, **f) if want_entropy_full else None,
+           "nucleus_size": torch.empty(N, device=dev, dtype=torch.int32) if want_nucleus else None,
+           "threshold": torch.empty(N, **f) if want_nucleus else None,
+           "flags": torch.empty(N, device=dev, dtype=torch.uint8)}
+    t_row = _f32_opt(temperature_per_row, N, dev)
+    p_row = _f32_opt(top_p_per_row, N, dev)
+    L = lib()
+    ws_n = L.rlk_logprob_from_logits_workspace_size(N, V, dtype)
+    ws = _workspace(ws_n, dev)
+    st = L.rlk_logprob_from_logits(
+        _ptr(logits), dtype, N, V, logits.stride(0) if N > 0 else V, _ptr(targets),
+        float(temperature), float(top_p), _ptr(t_row), _ptr(p_row), int(top_k),
+        _ptr(out["lp_full"]), _ptr(out["lp_trunc"]), _ptr(out["entropy_trunc"]),
+        _ptr(out["entropy_full"]), _ptr(out["nucleus_size"]), _ptr(out["threshold"]),
+        _ptr(out["flags"]), _ptr(ws), ws_n, _stream(dev))
+    _native.check(st, "rlk_logprob_from_logits")
+    return out
+
+
+def logprob_fused_linear(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                         temperature: float = 1.0, top_p: float = 1.0, *, top_k: int = 0,
+                         want_saved: bool = True) -> dict:
+    """Fused LM head: logprob / entropy of targets under softmax(hidden W^T / T).
+
+    ``hidden`` [N, H] and ``weight`` [V, H] are bf16 on the GPU. Returns
+    logprob, entropy, saved ([N, 4], for the backward), nucleus_size, flags.
+    """
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    N, H = hidden.shape
+    V, H2 = weight.shape
+    if H2 != H:
+        raise ValueError("hidden and weight disagree on the hidden size")
+    if hidden.stride(1) != 1 or weight.stride(1) != 1:
+        raise ValueError("hidden and weight need unit column stride")
+    dev = hidden.device
+    targets = targets.to(device=dev, dtype=torch.int64).contiguous()
+    f = dict(device=dev, dtype=torch.float32)
+    out = {"logprob": torch.empty(N, **f), "entropy": torch.empty(N, **f),
+           "saved": torch.empty(N, 4, **f) if want_saved else None,
+           "nucleus_size": torch.empty(N, device=dev, dtype=torch.int32),
+           "flags": torch.empty(N, device=dev, dtype=torch.uint8)}
+    L = lib()
+    ws_n = L.rlk_logprob_fused_linear_workspace_size(N, H, V, float(top_p))
+    ws = _workspace(ws_n, dev)
+    st = L.rlk_logprob_fused_linear(
+        _ptr(hidden), _ptr(weight), N, H, V, hidden.stride(0), weight.stride(0), _ptr(targets),
+        float(temperature), float(top_p), int(top_k), _ptr(out["logprob"]), _ptr(out["entropy"]),
+        _ptr(out["saved"]), _ptr(out["nucleus_size"]), _ptr(out["flags"]), _ptr(ws), ws_n,
+        _stream(dev))
+    _native.check(st, "rlk_logprob_fused_linear")
+    return out
+
+
+def logprob_fused_linear_bwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                             saved: torch.Tensor, grad_logprob=None, grad_entropy=None,
+                             temperature: float = 1.0, top_p: float = 1.0, *,
+                             top_k: int = 0) -> tuple[torch.Tensor, torch.Tensor]:
+    """Backward of the fused LM head: (dL/dhidden bf16 [N, H], dL/dW fp32 [V, H])."""
+    N, H = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    targets = targets.to(device=dev, dtype=torch.int64).contiguous()
+    g_lp = _f32_opt(grad_logprob, N, dev)
+    g_h = _f32_opt(grad_entropy, N, dev)
+    dh = torch.empty(N, H, device=dev, dtype=torch.bfloat16)
+    dw = torch.empty(V, H, device=dev, dtype=torch.float32)
+    L = lib()
+    ws_n = L.rlk_logprob_fused_linear_bwd_workspace_size(N, H, V, float(top_p))
+    ws = _workspace(ws_n, dev)
+    st = L.rlk_logprob_fused_linear_bwd(
+        _ptr(hidden), _ptr(weight), N, H, V, hidden.stride(0), weight.stride(0), _ptr(targets),
+        _ptr(saved.contiguous()), _ptr(g_lp), _ptr(g_h), float(temperature), float(top_p),
+        int(top_k), _ptr(dh), _ptr(dw), _ptr(ws), ws_n, _stream(dev))
+    _native.check(st, "rlk_logprob_fused_linear_bwd")
+    return dh, dw
+
+
+def grpo_token_loss(lp_new: torch.Tensor, lp_old: torch.Tensor, lp_ref, cu_seqlens,
+                    *, rewards=None, advantages=None, group_size: int = 8,
+                    tis_cap: float = 2.0, eps_low: float = 0.2, eps_high: float = 0.28,
+                    kl_coef: float = 0.01, adv_eps: float = 1e-6, std_ddof: int = 1,
+                    normalize_std: bool = True) -> dict:
+    """GRPO/DAPO token-mean loss over packed responses (``cu_seqlens`` on the host).
+
+    Returns loss (device scalar), grad (dL/dlp_new), token_loss, token_flags,
+    metrics [clip frac, TIS frac, mean k3, mean ratio], advantages.
+    """
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if torch.is_tensor(cu_seqlens)
+                                         else cu_seqlens, dtype=np.int64))
+    B = cu.size - 1
+    T = int(cu[-1]) if B >= 0 else 0
+    dev = lp_new.device
+    lp_new = lp_new.to(torch.float32).contiguous()
+    lp_old = lp_old.to(torch.float32).contiguous()
+    lp_ref = None if lp_ref is None else lp_ref.to(torch.float32).contiguous()
+    rw = _f32_opt(rewards, B, dev)
+    ad = _f32_opt(advantages, B, dev)
+    f = dict(device=dev, dtype=torch.float32)
+    out = {"loss": torch.empty((), **f), "grad": torch.empty(T, **f),
+           "token_loss": torch.empty(T, **f),
+           "token_flags": torch.empty(T, device=dev, dtype=torch.uint8),
+           "metrics": torch.empty(4, **f), "advantages": torch.empty(B, **f)}
+    prm = _native.GrpoParams(ctypes.sizeof(_native.GrpoParams), tis_cap, eps_low, eps_high,
+                             kl_coef, adv_eps, std_ddof, int(bool(normalize_std)))
+    L = lib()
+    ws_n = L.rlk_grpo_token_loss_workspace_size(T, B)
+    ws = _workspace(ws_n, dev)
+    st = L.rlk_grpo_token_loss(
+        _ptr(lp_new), _ptr(lp_old), _ptr(lp_ref), cu.ctypes.data_as(ctypes.c_void_p), B,
+        _ptr(rw), _ptr(ad), int(group_size), ctypes.byref(prm), _ptr(out["loss"]),
+        _ptr(out["grad"]), _ptr(out["token_loss"]), _ptr(out["token_flags"]), _ptr(out["metrics"]),
+        _ptr(out["advantages"]), _ptr(ws), ws_n, _stream(dev))
+    _native.check(st, "rlk_grpo_token_loss")
+    return out

@@ -1,0 +1,222 @@
+// The C ABI (include/rlk.h): host-side argument validation, workspace sizing
+// and dispatch onto the caller's stream. Nothing is launched or written when
+// validation fails.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/rlk.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+rlk_status fail(rlk_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+rlk_status ok() {
+  g_last_error[0] = '\0';
+  return RLK_OK;
+}
+
+rlk_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(RLK_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+rlk_status check_sampling(float temperature, float top_p, int32_t top_k) {
+  if (top_k != 0)
+    return fail(RLK_EUNSUPPORTED, "top_k=%d: top-k filtering is rejected, not ignored", top_k);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(RLK_EINVAL, "temperature=%g must be finite and > 0", double(temperature));
+  if (!(top_p > 0.f) || !(top_p <= 1.f))
+    return fail(RLK_EINVAL, "top_p=%g must lie in (0, 1]", double(top_p));
+  return RLK_OK;
+}
+
+rlk_status check_workspace(const void* ws, size_t have, size_t need) {
+  if (need == 0) return RLK_OK;
+  if (ws == nullptr) return fail(RLK_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, 256)) return fail(RLK_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(RLK_EWORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return RLK_OK;
+}
+
+constexpr int64_t kMaxVocab = int64_t(1) << 24;
+
+}  // namespace
+
+extern "C" {
+
+int32_t rlk_abi_version(void) { return 1; }
+
+const char* rlk_status_str(rlk_status s) {
+  switch (s) {
+    case RLK_OK: return "ok";
+    case RLK_EINVAL: return "invalid argument";
+    case RLK_EUNSUPPORTED: return "unsupported";
+    case RLK_EWORKSPACE: return "workspace too small or misaligned";
+    case RLK_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* rlk_last_error(void) { return g_last_error; }
+
+// ------------------------------------------------------------------ logits in
+size_t rlk_logprob_from_logits_workspace_size(int64_t n_rows, int64_t vocab, int32_t dtype) {
+  if (n_rows < 0) return 0;
+  return rlk::logits_rows_workspace(n_rows, vocab, dtype);
+}
+
+rlk_status rlk_logprob_from_logits(const void* logits, int32_t dtype, int64_t n_rows,
+                                   int64_t vocab, int64_t row_stride, const int64_t* targets,
+                                   float temperature, float top_p,
+                                   const float* temperature_per_row, const float* top_p_per_row,
+                                   int32_t top_k, float* lp_full, float* lp_trunc,
+                                   float* entropy_trunc, float* entropy_full,
+                                   int32_t* nucleus_size, float* threshold, uint8_t* flags,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != RLK_DTYPE_F32 && dtype != RLK_DTYPE_BF16)
+    return fail(RLK_EINVAL, "dtype=%d is not RLK_DTYPE_F32 or RLK_DTYPE_BF16", dtype);
+  rlk_status s = check_sampling(temperature, top_p, top_k);
+  if (s != RLK_OK) return s;
+  if (n_rows < 0) return fail(RLK_EINVAL, "n_rows=%lld < 0", (long long)n_rows);
+  if (vocab < 1 || vocab > kMaxVocab)
+    return fail(RLK_EINVAL, "vocab=%lld outside [1, 2^24]", (long long)vocab);
+  if (row_stride < vocab)
+    return fail(RLK_EINVAL, "row_stride=%lld < vocab=%lld", (long long)row_stride,
+                (long long)vocab);
+  if (n_rows == 0) return ok();
+  const size_t esz = dtype == RLK_DTYPE_F32 ? 4 : 2;
+  if (!logits || !targets || !lp_full || !lp_trunc || !entropy_trunc)
+    return fail(RLK_EINVAL, "logits, targets, lp_full, lp_trunc and entropy_trunc are required");
+  if (!aligned(logits, esz) || !aligned(targets, 8) || !aligned(lp_full, 4) ||
+      !aligned(lp_trunc, 4) || !aligned(entropy_trunc, 4) || !aligned(entropy_full, 4) ||
+      !aligned(nucleus_size, 4) || !aligned(threshold, 4) || !aligned(temperature_per_row, 4) ||
+      !aligned(top_p_per_row, 4))
+    return fail(RLK_EINVAL, "an array is not naturally aligned");
+  s = check_workspace(workspace, workspace_bytes,
+                      rlk_logprob_from_logits_workspace_size(n_rows, vocab, dtype));
+  if (s != RLK_OK) return s;
+
+  rlk::RowArgs a{};
+  a.logits = logits;
+  a.n_rows = n_rows;
+  a.vocab = vocab;
+  a.row_stride = row_stride;
+  a.targets = targets;
+  a.temperature = temperature;
+  a.top_p = top_p;
+  a.t_row = temperature_per_row;
+  a.p_row = top_p_per_row;
+  a.lp_full = lp_full;
+  a.lp_trunc = lp_trunc;
+  a.ent_trunc = entropy_trunc;
+  a.ent_full = entropy_full;
+  a.nsize = nucleus_size;
+  a.thresh = threshold;
+  a.flags = flags;
+  return hip_status(rlk::launch_logits_rows(a, dtype, workspace,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                    "rlk_logprob_from_logits launch");
+}
+
+// ------------------------------------------------------------------ GRPO loss
+size_t rlk_grpo_token_loss_workspace_size(int64_t n_tokens, int64_t n_seqs) {
+  if (n_tokens < 0 || n_seqs < 0) return 0;
+  return rlk::grpo_workspace(n_tokens, n_seqs);
+}
+
+rlk_status rlk_grpo_token_loss(const float* lp_new, const float* lp_old, const float* lp_ref,
+                               const int64_t* cu_seqlens_host, int64_t n_seqs,
+                               const float* rewards, const float* advantages, int32_t group_size,
+                               const rlk_grpo_params* params, float* loss, float* grad_lp_new,
+                               float* token_loss, uint8_t* token_flags, float* metrics,
+                               float* adv_out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!params) return fail(RLK_EINVAL, "params is NULL");
+  if (params->struct_size < sizeof(rlk_grpo_params))
+    return fail(RLK_EINVAL, "params->struct_size=%u < %zu", params->struct_size,
+                sizeof(rlk_grpo_params));
+  const rlk_grpo_params& p = *params;
+  if (!(p.tis_cap > 0.f) || !std::isfinite(p.tis_cap))
+    return fail(RLK_EINVAL, "tis_cap must be finite and > 0");
+  if (!(p.eps_low >= 0.f && p.eps_low < 1.f)) return fail(RLK_EINVAL, "eps_low must lie in [0, 1)");
+  if (!(p.eps_high >= 0.f) || !std::isfinite(p.eps_high))
+    return fail(RLK_EINVAL, "eps_high must be finite and >= 0");
+  if (!(p.kl_coef >= 0.f) || !std::isfinite(p.kl_coef))
+    return fail(RLK_EINVAL, "kl_coef must be finite and >= 0");
+  if (!(p.adv_eps >= 0.f) || !std::isfinite(p.adv_eps))
+    return fail(RLK_EINVAL, "adv_eps must be finite and >= 0");
+  if (p.std_ddof != 0 && p.std_ddof != 1) return fail(RLK_EINVAL, "std_ddof must be 0 or 1");
+  if (n_seqs < 1) return fail(RLK_EINVAL, "n_seqs=%lld < 1", (long long)n_seqs);
+  if (!cu_seqlens_host) return fail(RLK_EINVAL, "cu_seqlens_host is NULL");
+  if (cu_seqlens_host[0] != 0) return fail(RLK_EINVAL, "cu_seqlens[0] must be 0");
+  for (int64_t j = 0; j < n_seqs; ++j)
+    if (cu_seqlens_host[j + 1] < cu_seqlens_host[j])
+      return fail(RLK_EINVAL, "cu_seqlens is not non-decreasing at %lld", (long long)j);
+  const int64_t n_tokens = cu_seqlens_host[n_seqs];
+  if (n_tokens > (int64_t(1) << 40)) return fail(RLK_EINVAL, "too many tokens");
+  if ((rewards == nullptr) == (advantages == nullptr))
+    return fail(RLK_EINVAL, "exactly one of rewards / advantages must be given");
+  if (rewards) {
+    if (group_size < 1 || n_seqs % group_size != 0)
+      return fail(RLK_EINVAL, "group_size=%d must be >= 1 and divide n_seqs=%lld", group_size,
+                  (long long)n_seqs);
+    if (p.normalize_std && group_size - p.std_ddof < 1)
+      return fail(RLK_EINVAL, "group_size=%d too small for a std with ddof=%d", group_size,
+                  p.std_ddof);
+  }
+  if (!loss) return fail(RLK_EINVAL, "loss is required");
+  if (n_tokens > 0 && (!lp_new || !lp_old || !grad_lp_new))
+    return fail(RLK_EINVAL, "lp_new, lp_old and grad_lp_new are required");
+  if (n_tokens > 0 && p.kl_coef != 0.f && !lp_ref)
+    return fail(RLK_EINVAL, "lp_ref is required when kl_coef != 0");
+  if (!aligned(lp_new, 4) || !aligned(lp_old, 4) || !aligned(lp_ref, 4) || !aligned(loss, 4) ||
+      !aligned(grad_lp_new, 4) || !aligned(token_loss, 4) || !aligned(metrics, 4) ||
+      !aligned(adv_out, 4) || !aligned(rewards, 4) || !aligned(advantages, 4))
+    return fail(RLK_EINVAL, "an array is not naturally aligned");
+  rlk_status s = check_workspace(workspace, workspace_bytes,
+                                 rlk_grpo_token_loss_workspace_size(n_tokens, n_seqs));
+  if (s != RLK_OK) return s;
+
+  rlk::GrpoArgs a{};
+  a.lp_new = lp_new;
+  a.lp_old = lp_old;
+  a.lp_ref = p.kl_coef != 0.f ? lp_ref : nullptr;
+  a.n_seqs = n_seqs;
+  a.n_tokens = n_tokens;
+  a.rewards = rewards;
+  a.advantages = advantages;
+  a.group_size = group_size;
+  a.tis_cap = p.tis_cap;
+  a.eps_low = p.eps_low;
+  a.eps_high = p.eps_high;
+  a.kl_coef = p.kl_coef;
+  a.adv_eps = p.adv_eps;
+  a.std_ddof = p.std_ddof;
+  a.normalize_std = p.normalize_std;
+  a.loss = loss;
+  a.grad = grad_lp_new;
+  a.token_loss = token_loss;
+  a.token_flags = token_flags;
+  a.metrics = metrics;
+  a.adv_out = adv_out;
+  return hip_status(rlk::launch_grpo(a, cu_seqlens_host, workspace,
+                                     reinterpret_cast<hipStream_t>(stream)),
+                    "rlk_grpo_token_loss launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal launch interfaces between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rlk {
+
+// ----------------------------------------------------------------- logits path
+struct RowArgs {
+  const void* logits;
+  int64_t n_rows, vocab, row_stride;
+  const int64_t* targets;
+  float temperature, top_p;
+  const float* t_row;     // nullable per-row temperature
+  const float* p_row;     // nullable per-row top-p
+  float* lp_full;
+  float* lp_trunc;
+  float* ent_trunc;
+  float* ent_full;        // nullable
+  int32_t* nsize;         // nullable
+  float* thresh;          // nullable
+  uint8_t* flags;         // nullable
+  uint8_t* fallback;      // workspace [n_rows]: rows the histogram path hands on
+};
+
+size_t logits_rows_workspace(int64_t n_rows, int64_t vocab, int dtype);
+hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipStream_t stream);
+
+// ------------------------------------------------------------------ GRPO loss
+struct GrpoArgs {
+  const float* lp_new;
+  const float* lp_old;
+  const float* lp_ref;        // nullable when kl_coef == 0
+  int64_t n_seqs, n_tokens;
+  const float* rewards;       // one of rewards / advantages
+  const float* advantages;
+  int32_t group_size;
+  float tis_cap, eps_low, eps_high, kl_coef, adv_eps;
+  int32_t std_ddof, normalize_std;
+  float* loss;
+  float* grad;
+  float* token_loss;          // nullable
+  uint8_t* token_flags;       // nullable
+  float* metrics;             // nullable
+  float* adv_out;             // nullable
+};
+
+size_t grpo_workspace(int64_t n_tokens, int64_t n_seqs);
+// cu_host: host copy of the packed offsets [n_seqs + 1]
+hipError_t launch_grpo(const GrpoArgs& a, const int64_t* cu_host, void* workspace,
+                       hipStream_t stream);
+
+}  // namespace rlk

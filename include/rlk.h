@@ -1,0 +1,229 @@
+/*
+ * rlk -- token log-probabilities, entropy and the GRPO token loss on MI355X (gfx950).
+ *
+ * A small C ABI over hand-written HIP kernels. It computes, per sampled
+ * response token, the log-probability and entropy of the policy's vocabulary
+ * softmax, in the temperature-scaled, top-p-truncated and renormalised form
+ * that rollout and training must agree on bitwise (RL-Kernel ROCm sparse
+ * performance page, profile paragraph: a consistency run fails on any
+ * compared logprob that is not bitwise equal), the fused LM-head form with its
+ * backward, and the GRPO/DAPO token loss built on them.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.    Arrays are DEVICE pointers unless marked "host". The caller owns
+ *              every buffer (inputs, outputs, workspace); the library never
+ *              allocates device memory and keeps no mutable global state.
+ * Streams.     `stream` is a hipStream_t (NULL = the default stream). All work
+ *              is enqueued on it; outputs are valid once the stream reaches them.
+ * Workspace.   Each entry point has a *_workspace_size query; pass at least
+ *              that many bytes, 256-byte aligned. Contents need no initialising.
+ * Errors.      Every argument is checked on the host before anything is
+ *              launched; on error nothing is written and nothing is launched,
+ *              and rlk_last_error() (thread-local) holds a message.
+ *              Per-row data conditions are not errors: they set flag bits.
+ * Determinism. Results are bitwise identical run to run. Per-row outputs do
+ *              not depend on the number of rows, their order, or the row
+ *              stride (reductions run in a fixed order fixed by the vocabulary
+ *              size alone: Qwen3-8B VIME train-rollout consistency page,
+ *              "Canonical topology strategy", combines vocabulary shards in one
+ *              fixed order so that reduction boundaries never move).
+ * Reentrancy.  Concurrent calls on different streams with distinct workspaces
+ *              and outputs are safe.
+ * Parameters.  Temperature must be finite and > 0; top-p must lie in (0, 1];
+ *              top-k must be 0 -- top-k filtering and temperature 0 are
+ *              rejected rather than ignored (consistency page, "ROCm MI300X
+ *              and gfx942").
+ */
+#ifndef RLK_H
+#define RLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t rlk_status;
+#define RLK_OK 0
+#define RLK_EINVAL 1        /* bad argument value, shape, stride or pointer */
+#define RLK_EUNSUPPORTED 2  /* a valid but unsupported request (e.g. top_k != 0) */
+#define RLK_EWORKSPACE 3    /* workspace missing, misaligned or too small */
+#define RLK_EHIP 4          /* a HIP runtime call failed */
+
+/* logits dtypes */
+#define RLK_DTYPE_F32 0
+#define RLK_DTYPE_BF16 1
+
+/* per-row flag bits (uint8) */
+#define RLK_FLAG_OUTSIDE 1u     /* target outside the nucleus: truncated logprob = -inf */
+#define RLK_FLAG_BAD_TARGET 2u  /* target id outside [0, V): logprobs NaN */
+#define RLK_FLAG_NONFINITE 4u   /* a NaN / +inf logit, or no finite logit: outputs NaN */
+#define RLK_FLAG_BOUNDARY 8u    /* nucleus mass within 1e-6 of top-p (advisory) */
+#define RLK_FLAG_BAD_PARAM 16u  /* per-row temperature or top-p out of range: outputs NaN */
+
+/* ABI version of this header: 1. */
+int32_t rlk_abi_version(void);
+
+/* Static text for a status code. */
+const char* rlk_status_str(rlk_status status);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char* rlk_last_error(void);
+
+/* --------------------------------------------------------------------------
+ * Logits in: full and top-p truncated log-probability and entropy per row.
+ *
+ * Consistency page, "ROCm MI300X and gfx942": temperature and top-p are user
+ * parameters, the complete retained (nucleus) token set is scored with no
+ * support cap, top-p = 1 uses the full vocabulary, and a "monitoring entropy"
+ * is fused with the logprob. RL-Kernel ROCm sparse performance page,
+ * quick-start command: temperature 0.7, top-p 0.95. Per-row top-p is part of
+ * that page's test suite (last paragraphs).
+ *
+ * For row n with logits z[0..V), target y = targets[n], T, p:
+ *   d_i = (z_i - max z) / T;  Z = sum exp(d_i)
+ *   lp_full[n]       = d_y - log Z
+ *   entropy_full[n]  = log Z - sum exp(d_i) d_i / Z
+ *   nucleus S        = {i : z_i >= tau}, tau the lowest row value whose
+ *                      strictly-higher mass is < p (so the token crossing p
+ *                      and every token tied with it are kept); p = 1 keeps all
+ *                      finite tokens and reports tau = -inf
+ *   lp_trunc[n]      = d_y - log sum_{i in S} exp(d_i), or -inf if y not in S
+ *   entropy_trunc[n] = entropy of the distribution renormalised over S
+ *
+ * logits        [n_rows, row_stride] fp32 or bf16 (dtype); only the first
+ *               `vocab` entries of each row are read (padded vocabularies).
+ *               -inf entries are allowed (probability 0).
+ * targets       [n_rows] int64 target ids.
+ * temperature, top_p   scalars used for every row, unless the per-row arrays
+ *               temperature_per_row / top_p_per_row ([n_rows] fp32, nullable)
+ *               are given; per-row values out of range set RLK_FLAG_BAD_PARAM.
+ * top_k         must be 0.
+ * lp_full, lp_trunc, entropy_trunc   [n_rows] fp32 outputs (required).
+ * entropy_full  [n_rows] fp32 (nullable).
+ * nucleus_size  [n_rows] int32 |S| (nullable).
+ * threshold     [n_rows] fp32 tau, the smallest kept logit value (nullable).
+ * flags         [n_rows] uint8 RLK_FLAG_* (nullable).
+ * Limits: 1 <= vocab <= 2^24, row_stride >= vocab, n_rows >= 0 (0 is a no-op),
+ * logits and outputs naturally aligned.
+ * -------------------------------------------------------------------------- */
+size_t rlk_logprob_from_logits_workspace_size(int64_t n_rows, int64_t vocab, int32_t dtype);
+
+rlk_status rlk_logprob_from_logits(
+    const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab, int64_t row_stride,
+    const int64_t* targets, float temperature, float top_p,
+    const float* temperature_per_row, const float* top_p_per_row, int32_t top_k,
+    float* lp_full, float* lp_trunc, float* entropy_trunc,
+    float* entropy_full, int32_t* nucleus_size, float* threshold, uint8_t* flags,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Fused LM head, forward: logprob and entropy of targets under softmax(h W^T / T)
+ * without materialising the [N, V] logits (prime-rl v0.10.0 release notes,
+ * "1. Trainer Performance": the loss is chunked torchtitan-style).
+ *
+ * hidden        [n_rows, h_stride] bf16, first hidden_size entries used.
+ * weight        [vocab, w_stride] bf16 LM-head rows, first hidden_size used.
+ * targets       [n_rows] int64.
+ * Logits are accumulated in fp32 over the hidden dimension and never rounded
+ * to bf16. With top_p < 1 the outputs are the truncated ones of the
+ * logits-in entry point (same nucleus rule); with top_p = 1 they are full.
+ * logprob, entropy   [n_rows] fp32 outputs (required).
+ * saved         [n_rows, 4] fp32 (nullable): (log Z_S, E_q[z/T], tau, 0) on the
+ *               scale z/T, consumed by rlk_logprob_fused_linear_bwd.
+ * nucleus_size  [n_rows] int32 (nullable).  flags [n_rows] uint8 (nullable).
+ * Limits: hidden_size % 64 == 0, 1 <= vocab <= 2^24, strides >= hidden_size
+ * and multiples of 8, hidden/weight 16-byte aligned.
+ * -------------------------------------------------------------------------- */
+size_t rlk_logprob_fused_linear_workspace_size(int64_t n_rows, int64_t hidden_size,
+                                                int64_t vocab, float top_p);
+
+rlk_status rlk_logprob_fused_linear(
+    const void* hidden, const void* weight, int64_t n_rows, int64_t hidden_size, int64_t vocab,
+    int64_t h_stride, int64_t w_stride, const int64_t* targets,
+    float temperature, float top_p, int32_t top_k,
+    float* logprob, float* entropy, float* saved, int32_t* nucleus_size, uint8_t* flags,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Fused LM head, backward by chunk recompute.
+ *
+ * Given per-row upstream gradients g_lp = dL/dlogprob and g_H = dL/dentropy
+ * (already divided by the token count: the loss seed is normalised before
+ * model derivatives, consistency page, "Canonical topology strategy"), with
+ * q the renormalised distribution on the nucleus S recorded in `saved`:
+ *   G[n,i] = (1/T) [ g_lp (delta_{i,y} - q_i) - g_H q_i (z_i/T - E_q[z/T]) ] on S, 0 off S
+ *   grad_hidden = G W   (bf16 out, fp32 accumulate)
+ *   grad_weight = G^T h (fp32 out, overwritten)
+ * A row whose target is outside S contributes only its entropy term.
+ * grad_logprob, grad_entropy  [n_rows] fp32 (nullable = zeros).
+ * saved         [n_rows, 4] fp32 from the forward call with the same inputs.
+ * Limits: as the forward.
+ * -------------------------------------------------------------------------- */
+size_t rlk_logprob_fused_linear_bwd_workspace_size(int64_t n_rows, int64_t hidden_size,
+                                                    int64_t vocab, float top_p);
+
+rlk_status rlk_logprob_fused_linear_bwd(
+    const void* hidden, const void* weight, int64_t n_rows, int64_t hidden_size, int64_t vocab,
+    int64_t h_stride, int64_t w_stride, const int64_t* targets, const float* saved,
+    const float* grad_logprob, const float* grad_entropy,
+    float temperature, float top_p, int32_t top_k,
+    void* grad_hidden, float* grad_weight,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * GRPO / DAPO token loss over a packed ragged batch.
+ *
+ * LumenRL README, "Key Features" (GRPO, DAPO, PPO) and "Rollout Correction"
+ * (TIS clips large ratios); RL-Kernel ROCm sparse performance page: KL
+ * coefficient 0.01 (quick-start command), GRPO standard-deviation
+ * normalisation and eight samples per prompt (profile paragraph).
+ * For response j (group g = j / group_size) and its tokens t:
+ *   A_j    = (r_j - mean_g r) / (std_g r + adv_eps)      (rewards given), or
+ *   A_j    = advantages[j]                               (advantages given)
+ *   rho    = exp(lp_new - lp_old),  rho~ = min(rho, tis_cap)
+ *   s      = min(rho~ A, clip(rho~, 1 - eps_low, 1 + eps_high) A)
+ *   k3     = exp(lp_ref - lp_new) - (lp_ref - lp_new) - 1
+ *   l_t    = -s + kl_coef k3;   loss = sum_t l_t / T_tot  (token mean)
+ *   dL/dlp_new = (-A rho [rho <= C, clip not binding] + kl_coef (1 - exp(lp_ref - lp_new))) / T_tot
+ * lp_new, lp_old, lp_ref  [T_tot] fp32 (lp_ref nullable when kl_coef == 0).
+ * cu_seqlens    HOST [n_seqs + 1] int64 packed offsets, non-decreasing from 0;
+ *               T_tot = cu_seqlens[n_seqs]. Copied into the workspace.
+ * rewards / advantages    [n_seqs] fp32: exactly one must be non-NULL.
+ * group_size    responses per prompt; must divide n_seqs (rewards mode).
+ * loss          device fp32 scalar (required).  grad_lp_new [T_tot] fp32 (required).
+ * token_loss    [T_tot] fp32 (nullable).  token_flags [T_tot] uint8 (nullable):
+ *               bit0 TIS cap binds (rho > C), bit1 clipped branch taken.
+ * metrics       [4] fp32 (nullable): token means of clip flag, TIS flag, k3, rho.
+ * adv_out       [n_seqs] fp32 (nullable): the advantages used.
+ * T_tot == 0 gives loss 0.
+ * -------------------------------------------------------------------------- */
+typedef struct rlk_grpo_params {
+    uint32_t struct_size;   /* sizeof(rlk_grpo_params) */
+    float tis_cap;          /* C > 0, e.g. 2.0 */
+    float eps_low;          /* in [0, 1), e.g. 0.2 */
+    float eps_high;         /* >= 0, e.g. 0.28 */
+    float kl_coef;          /* >= 0, e.g. 0.01 */
+    float adv_eps;          /* >= 0, e.g. 1e-6 */
+    int32_t std_ddof;       /* 0 or 1 */
+    int32_t normalize_std;  /* 1 = divide by the group std */
+} rlk_grpo_params;
+
+size_t rlk_grpo_token_loss_workspace_size(int64_t n_tokens, int64_t n_seqs);
+
+rlk_status rlk_grpo_token_loss(
+    const float* lp_new, const float* lp_old, const float* lp_ref,
+    const int64_t* cu_seqlens_host, int64_t n_seqs,
+    const float* rewards, const float* advantages, int32_t group_size,
+    const rlk_grpo_params* params,
+    float* loss, float* grad_lp_new, float* token_loss, uint8_t* token_flags,
+    float* metrics, float* adv_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_H */

@@ -35,7 +35,7 @@ import numpy as np
 
 # array ids inside a workload's seed space
 _A_LOGITS, _A_PEAKS, _A_GUMBEL, _A_HIDDEN, _A_WEIGHT, _A_TARGET = 1, 2, 3, 4, 5, 6
-_A_LENGTHS, _A_REWARD, _A_OLDNOISE, _A_REFNOISE, _A_PEAKPICK = 7, 8, 9, 10, 11
+_A_LENGTHS, _A_REWARD, _A_OLDNOISE, _A_REFNOISE = 7, 8, 9, 10
 
 
 @dataclasses.dataclass(frozen=True)
@@ -144,16 +144,16 @@ def gumbel_uniforms(w: Workload, row: int, n: int | None = None) -> np.ndarray:
 
 
 def peak_targets(w: Workload, rows) -> np.ndarray:
-    """A target id per row chosen uniformly among the row's peak tokens.
+    """A target id per row: the row's peak token with the largest added offset.
 
-    A generator-only rule (no softmax arithmetic) for runs that need a valid,
-    almost surely in-nucleus target without sampling it.
+    A generator-only rule (no softmax arithmetic) for runs that need a
+    plausible, usually in-nucleus target without sampling it.
     """
     rows = list(rows)
     out = np.empty(len(rows), dtype=np.int64)
     for i, r in enumerate(rows):
-        ids, _ = peak_ids(w, r)
-        out[i] = ids[int(_rng(w.seed, _A_PEAKPICK, r).integers(0, ids.size))]
+        ids, add = peak_ids(w, r)
+        out[i] = ids[int(np.argmax(add))]
     return out
 
 

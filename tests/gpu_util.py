@@ -1,0 +1,30 @@
+"""Shared helpers for the GPU tests (upload of seeded inputs, comparisons)."""
+import numpy as np
+import torch
+
+DEV = "cuda:0"
+
+
+def bf16_to_device(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> a bf16 tensor on the GPU (same bits)."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def f32_to_device(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def assert_close_rows(got, want, atol, rtol=0.0, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    both_inf = np.isinf(got) & np.isinf(want) & (np.sign(got) == np.sign(want))
+    both_nan = np.isnan(got) & np.isnan(want)
+    ok = both_inf | both_nan | (np.abs(got - want) <= atol + rtol * np.abs(want))
+    if not ok.all():
+        bad = np.flatnonzero(~ok)[:8]
+        raise AssertionError(f"{what}: {(~ok).sum()} rows off; first {bad.tolist()}: "
+                             f"got {got[bad].tolist()} want {want[bad].tolist()}")

@@ -1,0 +1,127 @@
+"""The C ABI on a host without a GPU: the library loads, exports every symbol
+include/rlk.h declares, and rejects bad arguments on the host before anything
+is launched. No call here passes validation (no compute runs without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from grpo_loss_rlk_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = ctypes.c_void_p
+FAKE = P(0x100000)          # a 256-aligned address that is never dereferenced
+WS = P(0x200000)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _native.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "rlk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(rlk_[a-z0-9_]+)\s*\(", src))
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared()
+    assert declared == set(_native.SIGNATURES), declared ^ set(_native.SIGNATURES)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_text(L):
+    assert L.rlk_abi_version() == 1
+    assert L.rlk_status_str(0) == b"ok"
+    assert b"workspace" in L.rlk_status_str(3)
+
+
+def _logits_call(L, **kw):
+    a = dict(logits=FAKE, dtype=1, n=4, V=1000, stride=1000, targets=FAKE, T=0.7, p=0.95,
+             t_row=None, p_row=None, top_k=0, lpf=FAKE, lpt=FAKE, ht=FAKE, hf=None, ns=None,
+             th=None, fl=None, ws=WS, ws_bytes=1 << 20)
+    a.update(kw)
+    return L.rlk_logprob_from_logits(a["logits"], a["dtype"], a["n"], a["V"], a["stride"],
+                                     a["targets"], a["T"], a["p"], a["t_row"], a["p_row"],
+                                     a["top_k"], a["lpf"], a["lpt"], a["ht"], a["hf"], a["ns"],
+                                     a["th"], a["fl"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=5), _native.RLK_EUNSUPPORTED),
+    (dict(T=0.0), _native.RLK_EINVAL),
+    (dict(T=-1.0), _native.RLK_EINVAL),
+    (dict(T=math.nan), _native.RLK_EINVAL),
+    (dict(T=math.inf), _native.RLK_EINVAL),
+    (dict(p=0.0), _native.RLK_EINVAL),
+    (dict(p=1.0000001), _native.RLK_EINVAL),
+    (dict(p=math.nan), _native.RLK_EINVAL),
+    (dict(dtype=7), _native.RLK_EINVAL),
+    (dict(V=0), _native.RLK_EINVAL),
+    (dict(V=(1 << 24) + 1, stride=(1 << 24) + 1), _native.RLK_EINVAL),
+    (dict(stride=999), _native.RLK_EINVAL),
+    (dict(n=-1), _native.RLK_EINVAL),
+    (dict(logits=None), _native.RLK_EINVAL),
+    (dict(targets=None), _native.RLK_EINVAL),
+    (dict(lpt=None), _native.RLK_EINVAL),
+    (dict(logits=P(0x100001)), _native.RLK_EINVAL),
+    (dict(targets=P(0x100004)), _native.RLK_EINVAL),
+    (dict(ws=None), _native.RLK_EWORKSPACE),
+    (dict(ws=P(0x200010)), _native.RLK_EWORKSPACE),
+    (dict(ws_bytes=0), _native.RLK_EWORKSPACE),
+])
+def test_logits_validation(L, kw, status):
+    assert _logits_call(L, **kw) == status
+    assert len(L.rlk_last_error()) > 0
+
+
+def test_logits_empty_batch_is_a_noop(L):
+    assert _logits_call(L, n=0, logits=None, targets=None, ws=None) == 0
+
+
+def test_workspace_queries(L):
+    assert L.rlk_logprob_from_logits_workspace_size(4096, 151936, 1) >= 4096
+    assert L.rlk_grpo_token_loss_workspace_size(1000, 32) > 0
+
+
+def _grpo(L, cu=(0, 3, 5), **kw):
+    prm = _native.GrpoParams(ctypes.sizeof(_native.GrpoParams), 2.0, 0.2, 0.28, 0.01, 1e-6, 1, 1)
+    for k, v in kw.pop("prm", {}).items():
+        setattr(prm, k, v)
+    cu_arr = None if cu is None else (ctypes.c_int64 * len(cu))(*cu)
+    a = dict(lp_new=FAKE, lp_old=FAKE, lp_ref=FAKE, n=2, rewards=FAKE, adv=None,
+             G=2, params=ctypes.byref(prm), loss=FAKE, grad=FAKE, ws=WS, ws_bytes=1 << 20,
+             cu=None if cu_arr is None else ctypes.cast(cu_arr, P))
+    a.update(kw)
+    return L.rlk_grpo_token_loss(a["lp_new"], a["lp_old"], a["lp_ref"], a["cu"], a["n"],
+                                 a["rewards"], a["adv"], a["G"], a["params"], a["loss"],
+                                 a["grad"], None, None, None, None, a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(params=None), _native.RLK_EINVAL),
+    (dict(prm=dict(struct_size=4)), _native.RLK_EINVAL),
+    (dict(prm=dict(tis_cap=0.0)), _native.RLK_EINVAL),
+    (dict(prm=dict(eps_low=1.0)), _native.RLK_EINVAL),
+    (dict(prm=dict(eps_high=-0.1)), _native.RLK_EINVAL),
+    (dict(prm=dict(kl_coef=-1.0)), _native.RLK_EINVAL),
+    (dict(prm=dict(std_ddof=2)), _native.RLK_EINVAL),
+    (dict(cu=(1, 3, 5)), _native.RLK_EINVAL),
+    (dict(cu=(0, 3, 2)), _native.RLK_EINVAL),
+    (dict(cu=None), _native.RLK_EINVAL),
+    (dict(adv=FAKE), _native.RLK_EINVAL),
+    (dict(rewards=None), _native.RLK_EINVAL),
+    (dict(G=3), _native.RLK_EINVAL),
+    (dict(G=1), _native.RLK_EINVAL),
+    (dict(lp_ref=None), _native.RLK_EINVAL),
+    (dict(grad=None), _native.RLK_EINVAL),
+    (dict(loss=None), _native.RLK_EINVAL),
+    (dict(ws_bytes=8), _native.RLK_EWORKSPACE),
+])
+def test_grpo_validation(L, kw, status):
+    assert _grpo(L, **kw) == status
+    assert len(L.rlk_last_error()) > 0

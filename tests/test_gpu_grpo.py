@@ -1,0 +1,93 @@
+"""GPU parity of rlk_grpo_token_loss against the fp64 oracle on identical fp32
+inputs: loss, metrics and dL/dlp_new within 1e-6 relative; per-token flags
+exact except tokens whose ratio sits within 1e-6 of a branch point."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import grpo as OG
+import grpo_loss_rlk_amd as rlk
+
+from gpu_util import f32_to_device, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, lengths, sd_old=0.05, sd_ref=0.1):
+    rng = np.random.default_rng(seed)
+    cu = synth.cu_seqlens(np.asarray(lengths))
+    T = int(cu[-1])
+    lp_new = rng.normal(-2.0, 1.5, T).astype(np.float32)
+    lp_old = (lp_new + rng.normal(0, sd_old, T)).astype(np.float32)
+    lp_ref = (lp_new + rng.normal(0, sd_ref, T)).astype(np.float32)
+    return cu, lp_new, lp_old, lp_ref
+
+
+def _compare(out, o, near):
+    assert float(host(out["loss"])) == pytest.approx(o.loss, rel=1e-6, abs=1e-9)
+    np.testing.assert_allclose(host(out["metrics"]), o.metrics, rtol=1e-6, atol=1e-9)
+    g = host(out["grad"])
+    keep = ~near
+    np.testing.assert_allclose(g[keep], o.grad[keep], rtol=1e-6, atol=1e-12)
+    np.testing.assert_allclose(host(out["token_loss"]), o.token_loss, rtol=1e-6, atol=1e-7)
+    np.testing.assert_array_equal(host(out["token_flags"])[keep], o.flags[keep])
+
+
+def test_ragged_grpo_workload():
+    """32 responses (4 prompts x 8), lengths U{256..6912}, Bernoulli rewards,
+    old/ref = new + N(0, 0.05^2) / N(0, 0.1^2), C=2, eps 0.2/0.28, beta=0.01."""
+    w = synth.workload("grpo")
+    lengths = synth.response_lengths(w)
+    cu, lp_new, lp_old, lp_ref = _inputs(4, lengths)
+    r = synth.rewards(w)
+    A = OG.advantages(r, 8)
+    o = OG.token_loss(lp_new, lp_old, lp_ref, cu, A)
+    print(f"  rlk_grpo_token_loss T_tot={cu[-1]} B={len(lengths)}", flush=True)
+    out = rlk.grpo_token_loss(f32_to_device(lp_new), f32_to_device(lp_old), f32_to_device(lp_ref),
+                              cu, rewards=r, group_size=8)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(out["advantages"]), A, rtol=1e-6)
+    _compare(out, o, o.near_branch)
+    # larger noise exercises every branch (clip high/low, TIS cap)
+    cu, lp_new, lp_old, lp_ref = _inputs(5, lengths, sd_old=0.6, sd_ref=0.5)
+    o = OG.token_loss(lp_new, lp_old, lp_ref, cu, A)
+    assert (o.flags & OG.FLAG_TIS).any() and (o.flags & OG.FLAG_CLIP).any()
+    out = rlk.grpo_token_loss(f32_to_device(lp_new), f32_to_device(lp_old), f32_to_device(lp_ref),
+                              cu, rewards=r, group_size=8)
+    _compare(out, o, o.near_branch)
+
+
+def test_advantages_mode_zero_length_and_params():
+    lengths = [5, 0, 17, 1, 0, 300, 2, 9]
+    cu, lp_new, lp_old, lp_ref = _inputs(6, lengths, sd_old=0.4, sd_ref=0.3)
+    A = np.random.default_rng(7).normal(0, 1, len(lengths)).astype(np.float32)
+    prm = OG.Params(tis_cap=1.5, eps_low=0.1, eps_high=0.2, kl_coef=0.05)
+    o = OG.token_loss(lp_new, lp_old, lp_ref, cu, A.astype(np.float64), prm)
+    out = rlk.grpo_token_loss(f32_to_device(lp_new), f32_to_device(lp_old), f32_to_device(lp_ref),
+                              cu, advantages=A, tis_cap=1.5, eps_low=0.1, eps_high=0.2,
+                              kl_coef=0.05)
+    _compare(out, o, o.near_branch)
+
+
+def test_on_policy_equal_lengths_is_zero_and_empty_batch():
+    cu = synth.cu_seqlens(np.full(16, 40))
+    lp = np.random.default_rng(8).normal(-1, 1, int(cu[-1])).astype(np.float32)
+    r = np.array([1, 0, 0, 1, 1, 1, 0, 0] * 2, dtype=np.float32)
+    x = f32_to_device(lp)
+    out = rlk.grpo_token_loss(x, x, x, cu, rewards=r, group_size=8)
+    assert abs(float(host(out["loss"]))) < 1e-7
+    out = rlk.grpo_token_loss(x[:0], x[:0], x[:0], np.zeros(3, np.int64), rewards=r[:2],
+                              group_size=2)
+    assert float(host(out["loss"])) == 0.0
+
+
+def test_bitwise_deterministic():
+    w = synth.workload("grpo")
+    cu, lp_new, lp_old, lp_ref = _inputs(9, synth.response_lengths(w))
+    args = [f32_to_device(a) for a in (lp_new, lp_old, lp_ref)]
+    r = synth.rewards(w)
+    a = rlk.grpo_token_loss(*args, cu, rewards=r, group_size=8)
+    b = rlk.grpo_token_loss(*args, cu, rewards=r, group_size=8)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
