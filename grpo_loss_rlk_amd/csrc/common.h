@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
 #include <cmath>
 
 #define RLK_DEV __device__ __forceinline__
@@ -122,6 +123,94 @@ RLK_DEV T block_inclusive_scan(T v, T* scratch, T* total) {
   __syncthreads();
   *total = tot;
   return base + v;
+}
+
+// ---------------------------------------------------------------------------
+// DPP wave primitives (gfx9 data-parallel primitives: row_shr / row_bcast).
+// Register-to-register lane moves with no LDS traffic. Fixed lane order, so
+// floating-point results are bitwise reproducible.
+// ---------------------------------------------------------------------------
+template <int kCtrl, int kRowMask = 0xf, int kBankMask = 0xf>
+RLK_DEV uint32_t dpp_u32(uint32_t fill, uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(fill), int(v), kCtrl, kRowMask, kBankMask, false));
+}
+
+template <int kCtrl, int kRowMask = 0xf, int kBankMask = 0xf>
+RLK_DEV double dpp_f64(double fill, double v) {
+  const uint64_t f = __double_as_longlong(fill), x = __double_as_longlong(v);
+  const uint32_t lo = dpp_u32<kCtrl, kRowMask, kBankMask>(uint32_t(f), uint32_t(x));
+  const uint32_t hi = dpp_u32<kCtrl, kRowMask, kBankMask>(uint32_t(f >> 32), uint32_t(x >> 32));
+  return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
+
+template <int kCtrl, int kRowMask = 0xf, int kBankMask = 0xf>
+RLK_DEV float dpp_f32(float fill, float v) {
+  return __uint_as_float(dpp_u32<kCtrl, kRowMask, kBankMask>(__float_as_uint(fill), __float_as_uint(v)));
+}
+
+template <int kCtrl, int kRowMask = 0xf, int kBankMask = 0xf>
+RLK_DEV int dpp_i32(int fill, int v) {
+  return int(dpp_u32<kCtrl, kRowMask, kBankMask>(uint32_t(fill), uint32_t(v)));
+}
+
+// Inclusive scan (sum) across the 64 lanes of a wave; lane i gets sum of lanes 0..i.
+#define RLK_DPP_SCAN(T, MOVE)                                            \
+  RLK_DEV T wave_scan_incl(T v) {                                        \
+    v += MOVE<0x111>(T(0), v);             /* row_shr:1 */              \
+    v += MOVE<0x112>(T(0), v);             /* row_shr:2 */              \
+    v += MOVE<0x114>(T(0), v);             /* row_shr:4 */              \
+    v += MOVE<0x118>(T(0), v);             /* row_shr:8 */              \
+    v += MOVE<0x142, 0xa>(T(0), v);        /* row_bcast:15 -> rows 1,3 */ \
+    v += MOVE<0x143, 0xc>(T(0), v);        /* row_bcast:31 -> rows 2,3 */ \
+    return v;                                                            \
+  }
+RLK_DPP_SCAN(double, dpp_f64)
+RLK_DPP_SCAN(float, dpp_f32)
+RLK_DPP_SCAN(int, dpp_i32)
+#undef RLK_DPP_SCAN
+
+RLK_DEV uint32_t readlane_u32(uint32_t v, int lane) {
+  return uint32_t(__builtin_amdgcn_readlane(int(v), lane));
+}
+RLK_DEV double readlane_f64(double v, int lane) {
+  const uint64_t x = __double_as_longlong(v);
+  const uint32_t lo = readlane_u32(uint32_t(x), lane), hi = readlane_u32(uint32_t(x >> 32), lane);
+  return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
+
+// Wave totals via the inclusive scan's last lane (uniform result).
+RLK_DEV double wave_total(double v) { return readlane_f64(wave_scan_incl(v), kWave - 1); }
+RLK_DEV int wave_total(int v) { return int(readlane_u32(uint32_t(wave_scan_incl(v)), kWave - 1)); }
+
+// Exclusive scan from an inclusive one: lane i gets lane i-1's value (lane 0: 0).
+RLK_DEV double wave_shift_up(double v) { return dpp_f64<0x138>(0.0, v); }   // wave_shr:1
+RLK_DEV int wave_shift_up(int v) { return dpp_i32<0x138>(0, v); }
+
+// Fold of per-wave partials p[0..n) (n <= 64) held in LDS: lane w loads p[w]
+// and the wave reduces with DPP. Uniform result, fixed order.
+RLK_DEV double fold_partials(const double* p, int n) {
+  const int lane = threadIdx.x & (kWave - 1);
+  return wave_total(lane < n ? p[lane] : 0.0);
+}
+RLK_DEV int fold_partials(const int* p, int n) {
+  const int lane = threadIdx.x & (kWave - 1);
+  return wave_total(lane < n ? p[lane] : 0);
+}
+
+// Wave max / min of ints (uniform result).
+RLK_DEV int wave_max_i32(int v) {
+#define RLK_STEP(C, RM) { const int o = dpp_i32<C, RM>(INT_MIN, v); v = o > v ? o : v; }
+  RLK_STEP(0x111, 0xf) RLK_STEP(0x112, 0xf) RLK_STEP(0x114, 0xf) RLK_STEP(0x118, 0xf)
+  RLK_STEP(0x142, 0xa) RLK_STEP(0x143, 0xc)
+#undef RLK_STEP
+  return int(readlane_u32(uint32_t(v), kWave - 1));
+}
+RLK_DEV int wave_min_i32(int v) {
+#define RLK_STEP(C, RM) { const int o = dpp_i32<C, RM>(INT_MAX, v); v = o < v ? o : v; }
+  RLK_STEP(0x111, 0xf) RLK_STEP(0x112, 0xf) RLK_STEP(0x114, 0xf) RLK_STEP(0x118, 0xf)
+  RLK_STEP(0x142, 0xa) RLK_STEP(0x143, 0xc)
+#undef RLK_STEP
+  return int(readlane_u32(uint32_t(v), kWave - 1));
 }
 
 }  // namespace rlk

@@ -68,6 +68,15 @@ RLK_DEV void hist_add(uint32_t* hist, uint32_t code) {
   atomicAdd(&hist[code & 0x7fffu], (code & 0x8000u) ? 0x10000u : 1u);
 }
 
+// Both bf16 patterns of a 32-bit word: word index = magnitude bits, the sign
+// picks the 16-bit half (increment 1 or 65536 = sign * 65535 + 1).
+RLK_DEV void hist_add2(uint32_t* hist, uint32_t x) {
+  char* base = reinterpret_cast<char*>(hist);
+  atomicAdd(reinterpret_cast<uint32_t*>(base + ((x << 2) & 0x1fffcu)),
+            __builtin_amdgcn_ubfe(x, 15, 1) * 65535u + 1u);
+  atomicAdd(reinterpret_cast<uint32_t*>(base + ((x >> 14) & 0x1fffcu)), (x >> 31) * 65535u + 1u);
+}
+
 // Merged key order over bf16 patterns: key = code | 0x8000 for positive codes,
 // ~code & 0xffff for negative ones; -0 (key 0x7fff) is folded into +0 (0x8000).
 // Returns the count of the value with this key, and the value.
@@ -90,246 +99,398 @@ RLK_DEV uint32_t bf16_key_merged(uint16_t code) {
   return (code & 0x8000u) ? ((~uint32_t(code)) & 0xffffu) : (uint32_t(code) | 0x8000u);
 }
 
+constexpr int kHW = kHT / kWave;       // waves per block
+constexpr int kPF = 4;                  // 16-byte vectors per thread prefetched for the next row
+
+// exp((v - m) / T) for a bf16 value v and the row max m, in fp32. dv = v - m
+// is exact (two bf16 values). With c = log2(e)/T split as c_hi + c_lo, the
+// exponent x = dv*c is rounded to x_hi = fl(dv*c_hi) and its residual
+// r = (dv*c_hi - x_hi) + dv*c_lo is recovered exactly enough by an fma, so
+// 2^x = 2^x_hi * (1 + r ln 2) carries ~1 ulp of error whatever |x| is.
+struct MassScale {
+  float c_hi, c_lo;
+};
+
+RLK_DEV MassScale mass_scale(double invT) {
+  const double c = 1.4426950408889634 * invT;
+  MassScale k;
+  k.c_hi = float(c);
+  k.c_lo = float(c - double(k.c_hi));
+  return k;
+}
+
+RLK_DEV float code_mass(float dv, MassScale k) {
+  const float xh = dv * k.c_hi;
+  const float r = fmaf(dv, k.c_hi, -xh) + dv * k.c_lo;
+  const float e = exp2f(xh);
+  return fmaf(e, r * 0.69314718f, e);
+}
+
+RLK_DEV void hist_add8(uint32_t* hist, const uint4& q) {
+  hist_add2(hist, q.x);
+  hist_add2(hist, q.y);
+  hist_add2(hist, q.z);
+  hist_add2(hist, q.w);
+}
+
+// Per-row scalars handed from the block's reductions to the single thread
+// that forms the outputs.
+struct RowFinish {
+  double Z, S, Zs, Ss, Mgt, invT;
+  float m, p;
+  uint32_t tau_key;
+  int size;
+  bool cut, pending;
+  uint8_t flags;
+  uint16_t cy;
+  int64_t row;
+};
+
+RLK_DEV float merged_key_value(uint32_t key) {
+  if (key == 0x8000u) return 0.f;
+  return key > 0x8000u ? bf16_to_f32(uint16_t(key - 0x8000u)) : bf16_to_f32(uint16_t(~key & 0xffffu));
+}
+
+RLK_DEV void finish_row(const RowArgs& a, const RowFinish& f) {
+  uint8_t flags = f.flags;
+  const double logZ = log(f.Z), logZs = log(f.Zs);
+  const float h_full = float(logZ - f.S / f.Z);
+  const float h_trunc = float(logZs - f.Ss / f.Zs);
+  float lpf = __builtin_nanf(""), lpt = __builtin_nanf("");
+  if (!(flags & kBadTarget)) {
+    const float vy = bf16_to_f32(f.cy);
+    if (vy == -INFINITY) {
+      lpf = -INFINITY;
+      lpt = -INFINITY;
+      flags |= kOutside;
+    } else {
+      const double dy = double(vy - f.m) * f.invT;
+      lpf = float(dy - logZ);
+      if (!f.cut || bf16_key_merged(f.cy) >= f.tau_key) {
+        lpt = float(dy - logZs);
+      } else {
+        lpt = -INFINITY;
+        flags |= kOutside;
+      }
+    }
+  }
+  float tau = -INFINITY;
+  if (f.cut) {
+    tau = merged_key_value(f.tau_key);
+    const double pp = double(f.p);
+    if (fabs(f.Mgt / f.Z - pp) <= kBoundaryEps || fabs(f.Zs / f.Z - pp) <= kBoundaryEps)
+      flags |= kBoundary;
+  }
+  store_row(a, f.row, lpf, lpt, h_full, h_trunc, f.size, tau, flags);
+}
+
+// One persistent block per CU walks rows blockIdx.x, +gridDim.x, ... While a
+// row's histogram is post-processed, the first kPF*kHT vectors of the next row
+// are already in flight, so HBM keeps streaming. Every reduction is a DPP wave
+// scan plus one barrier and a fixed-order fold over the 16 wave partials.
 template <bool kVec>
 __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
   __shared__ uint32_t hist[kHWords];
-  __shared__ double sd[kHT / kWave], sd2[kHT / kWave];
-  __shared__ int si[kHT / kWave];
-  __shared__ uint32_t su[kHT / kWave];
-  __shared__ double bcast_d[3];
-  __shared__ int bcast_i[1];
+  __shared__ int s_i[2][8][kHW];
+  __shared__ double s_d[2][4][kHW];
+  __shared__ double b_d[4];
+  __shared__ int b_i[2];
 
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int64_t V = a.vocab;
-  const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.logits) + row * a.row_stride;
+  const int64_t nvec = kVec ? (V >> 3) : 0;
 
-  // the target's logit is fetched early so its latency hides behind the pass
-  const int64_t y = a.targets[row];
-  const bool y_ok = y >= 0 && y < V;
-  uint16_t cy = 0;
-  if (tid == 0 && y_ok) cy = rowp[y];
-
-  {  // clear the histogram
+  {
     uint4* h4 = reinterpret_cast<uint4*>(hist);
     for (int i = tid; i < kHWords / 4; i += kHT) h4[i] = make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();
-
-  // ---- one streaming pass: count every bf16 pattern of the row ----
-  if (kVec) {
-    const uint4* v4 = reinterpret_cast<const uint4*>(rowp);
-    const int64_t nvec = V >> 3;
-    int64_t i = tid;
-    for (; i + 3 * kHT < nvec; i += 4 * kHT) {
-      uint4 q[4];
+  uint4 pf[kPF];
+  int64_t row = blockIdx.x;
+  if (kVec && row < a.n_rows) {
+    const uint4* v4 = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(a.logits) + row * a.row_stride);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) q[u] = v4[i + u * kHT];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        hist_add(hist, q[u].x & 0xffffu); hist_add(hist, q[u].x >> 16);
-        hist_add(hist, q[u].y & 0xffffu); hist_add(hist, q[u].y >> 16);
-        hist_add(hist, q[u].z & 0xffffu); hist_add(hist, q[u].z >> 16);
-        hist_add(hist, q[u].w & 0xffffu); hist_add(hist, q[u].w >> 16);
-      }
-    }
-    for (; i < nvec; i += kHT) {
-      const uint4 q = v4[i];
-      hist_add(hist, q.x & 0xffffu); hist_add(hist, q.x >> 16);
-      hist_add(hist, q.y & 0xffffu); hist_add(hist, q.y >> 16);
-      hist_add(hist, q.z & 0xffffu); hist_add(hist, q.z >> 16);
-      hist_add(hist, q.w & 0xffffu); hist_add(hist, q.w >> 16);
-    }
-    for (int64_t j = (nvec << 3) + tid; j < V; j += kHT) hist_add(hist, rowp[j]);
-  } else {
-    for (int64_t j = tid; j < V; j += kHT) hist_add(hist, rowp[j]);
+    for (int u = 0; u < kPF; ++u)
+      if (tid + u * kHT < nvec) pf[u] = v4[tid + u * kHT];
   }
+  __shared__ RowFinish fin;     // written and read by thread 0 only
+  if (tid == 0) fin.pending = false;
   __syncthreads();
 
-  // ---- checksum, max and non-finite detection over the counters ----
-  uint32_t tot = 0, n_neg_inf = 0;
-  int maxpos = -1, minneg = 0x8000, nonfinite = 0;
-  for (int j = 0; j < kWordsPerThread; ++j) {
-    const int w = tid + j * kHT;
-    const uint32_t x = hist[w];
-    const uint32_t lo = x & 0xffffu, hi = x >> 16;
-    tot += lo + hi;
-    if (w < int(kInfW)) {
-      if (lo) maxpos = w;
-      if (hi && w < minneg) minneg = w;
+  for (; row < a.n_rows; row += gridDim.x) {
+    const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.logits) + row * a.row_stride;
+    const int64_t y = a.targets[row];
+    const bool y_ok = y >= 0 && y < V;
+    uint16_t cy = 0;
+    if (tid == 0 && y_ok) cy = rowp[y];
+
+    // ---- one streaming pass: count every bf16 pattern of the row ----
+    if (kVec) {
+      const uint4* v4 = reinterpret_cast<const uint4*>(rowp);
+#pragma unroll
+      for (int u = 0; u < kPF; ++u)
+        if (tid + u * kHT < nvec) hist_add8(hist, pf[u]);
+      int64_t i = tid + kPF * kHT;
+      for (; i + 3 * kHT < nvec; i += 4 * kHT) {
+        uint4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q[u] = v4[i + u * kHT];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) hist_add8(hist, q[u]);
+      }
+      for (; i < nvec; i += kHT) hist_add8(hist, v4[i]);
+      for (int64_t j = (nvec << 3) + tid; j < V; j += kHT) hist_add(hist, rowp[j]);
     } else {
-      if (lo) nonfinite = 1;                         // +inf or NaN
-      if (hi && w > int(kInfW)) nonfinite = 1;       // NaN
-      if (w == int(kInfW)) n_neg_inf = hi;           // -inf
+      for (int64_t j = tid; j < V; j += kHT) hist_add(hist, rowp[j]);
     }
-  }
-  tot = block_sum(tot, su);
-  maxpos = block_max(maxpos, si);
-  minneg = block_min(minneg, si);
-  nonfinite = block_max(nonfinite, si);
-  n_neg_inf = block_sum(n_neg_inf, su);
+    __syncthreads();
 
-  if (tot != uint32_t(V)) {          // a 16-bit counter overflowed: generic kernel
-    if (tid == 0) a.fallback[row] = 1;
-    return;
-  }
-
-  float T = a.t_row ? a.t_row[row] : a.temperature;
-  float p = a.p_row ? a.p_row[row] : a.top_p;
-  uint8_t flags = 0;
-  if (!y_ok) flags |= kBadTarget;
-  if (!param_ok(T, p)) flags |= kBadParam;
-  const bool no_finite = (maxpos < 0 && minneg == 0x8000);
-  if (nonfinite || no_finite) flags |= kNonFinite;
-  if (flags & (kNonFinite | kBadParam)) {
-    if (tid == 0) {
-      a.fallback[row] = 0;
-      store_nan_row(a, row, flags);
+    // ---- the next row's first vectors go in flight now ----
+    const int64_t nxt = row + gridDim.x;
+    if (kVec && nxt < a.n_rows) {
+      const uint4* v4n = reinterpret_cast<const uint4*>(
+          reinterpret_cast<const uint16_t*>(a.logits) + nxt * a.row_stride);
+#pragma unroll
+      for (int u = 0; u < kPF; ++u)
+        if (tid + u * kHT < nvec) pf[u] = v4n[tid + u * kHT];
     }
-    return;
-  }
 
-  // max value and its merged key
-  float mval;
-  uint32_t kmax;
-  if (maxpos >= 0) {
-    mval = bf16_to_f32(uint16_t(maxpos));
-    kmax = 0x8000u + uint32_t(maxpos);
-  } else if (minneg == 0) {          // only -0 at the top: same value as +0
-    mval = 0.f;
-    kmax = 0x8000u;
-  } else {
-    mval = bf16_to_f32(uint16_t(0x8000 | minneg));
-    kmax = 0x7fffu - uint32_t(minneg);
-  }
-  const double m = double(mval);
-  const double invT = 1.0 / double(T);
-
-  // ---- Z and sum e*d over the distinct finite values (fp64) ----
-  double zt = 0.0, st = 0.0;
-  for (int j = 0; j < kWordsPerThread; ++j) {
-    const int w = tid + j * kHT;
-    if (w >= int(kInfW)) break;
-    const uint32_t x = hist[w];
-    const uint32_t lo = x & 0xffffu, hi = x >> 16;
-    if (lo) {
-      const double d = (double(bf16_to_f32(uint16_t(w))) - m) * invT;
-      const double e = exp(d) * double(lo);
-      zt += e;
-      st += e * d;
-    }
-    if (hi) {
-      const double d = (double(bf16_to_f32(uint16_t(0x8000 | w))) - m) * invT;
-      const double e = exp(d) * double(hi);
-      zt += e;
-      st += e * d;
-    }
-  }
-  const double Z = block_sum(zt, sd);
-  const double S = block_sum(st, sd);
-
-  // ---- top-p cut: walk merged keys downward from the max ----
-  double Zs = Z, Ss = S, Mgt = 0.0;
-  uint32_t tau_key = 0;
-  const bool cut = p < 1.f;
-  if (cut) {
-    const double thr = double(p) * Z;
-    double carry = 0.0, carry_s = 0.0;
-    bool found = false;
-    for (int k0 = int(kmax); k0 >= 0x0080 && !found; k0 -= kHT) {
-      const int key = k0 - tid;
-      double mass = 0.0, mass_s = 0.0;
-      if (key >= 0x0080) {                      // keys below 0x0080 are -inf / NaN
-        float v;
-        const uint32_t n = key_count(hist, uint32_t(key), &v);
-        if (n) {
-          const double d = (double(v) - m) * invT;
-          mass = exp(d) * double(n);
-          mass_s = mass * d;
-        }
+    // ---- phase A: checksum, occupied word range, non-finite detection ----
+    // thread t owns words t + kHT*j; a bit mask of its nonzero finite words
+    // gives the range [wmin, wmax] every later phase is limited to.
+    {
+      uint32_t tot = 0, nzmask = 0;
+      int nonfin = 0, nneg = 0;
+#pragma unroll
+      for (int j = 0; j < kWordsPerThread - 1; ++j) {
+        const uint32_t x = hist[tid + j * kHT];
+        tot = __builtin_amdgcn_sad_u16(x, 0u, tot);
+        nzmask |= x ? (1u << j) : 0u;
       }
-      double tot_c, tot_s;
-      const double incl = block_inclusive_scan(mass, sd, &tot_c);
-      const double incl_s = block_inclusive_scan(mass_s, sd2, &tot_s);
-      const int cand = (mass > 0.0 && carry + incl >= thr) ? tid : kHT;
-      const int first = block_min(cand, si);
-      if (first < kHT) {
-        if (tid == first) {
-          bcast_d[0] = carry + incl;
-          bcast_d[1] = carry_s + incl_s;
-          bcast_d[2] = carry + incl - mass;
-          bcast_i[0] = key;
-        }
-        __syncthreads();
-        Zs = bcast_d[0];
-        Ss = bcast_d[1];
-        Mgt = bcast_d[2];
-        tau_key = uint32_t(bcast_i[0]);
-        found = true;
-      } else {
-        carry += tot_c;
-        carry_s += tot_s;
-      }
-    }
-    if (!found) {   // rounding left the mass just short of p: keep every finite value
-      Zs = carry;
-      Ss = carry_s;
-      Mgt = carry;
-      tau_key = 0x0080;
-    }
-  }
-
-  // ---- |S| ----
-  uint32_t size;
-  if (cut) {
-    uint32_t cnt = 0;
-    for (int j = 0; j < kWordsPerThread; ++j) {
-      const int w = tid + j * kHT;
-      if (w >= int(kInfW)) break;
-      const uint32_t x = hist[w];
-      if (0x8000u + uint32_t(w) >= tau_key) cnt += x & 0xffffu;
-      const uint32_t kneg = (w == 0) ? 0x8000u : 0x7fffu - uint32_t(w);  // -0 merged into +0
-      if (kneg >= tau_key) cnt += x >> 16;
-    }
-    size = block_sum(cnt, su);
-  } else {
-    size = uint32_t(V) - n_neg_inf;
-  }
-
-  if (tid == 0) {
-    a.fallback[row] = 0;
-    const double logZ = log(Z), logZs = log(Zs);
-    const float h_full = float(logZ - S / Z);
-    const float h_trunc = float(logZs - Ss / Zs);
-    float lpf = __builtin_nanf(""), lpt = __builtin_nanf("");
-    if (!(flags & kBadTarget)) {
-      const float vy = bf16_to_f32(cy);
-      if (vy == -INFINITY) {
-        lpf = -INFINITY;
-        lpt = -INFINITY;
-        flags |= kOutside;
-      } else {
-        const double dy = (double(vy) - m) * invT;
-        lpf = float(dy - logZ);
-        if (!cut || bf16_key_merged(cy) >= tau_key) {
-          lpt = float(dy - logZs);
+      {
+        const int w = tid + (kWordsPerThread - 1) * kHT;
+        const uint32_t x = hist[w];
+        tot = __builtin_amdgcn_sad_u16(x, 0u, tot);
+        if (w < int(kInfW)) {
+          nzmask |= x ? (1u << (kWordsPerThread - 1)) : 0u;
         } else {
-          lpt = -INFINITY;
-          flags |= kOutside;
+          if (x & 0xffffu) nonfin = 1;                  // +inf or NaN
+          if ((x >> 16) && w > int(kInfW)) nonfin = 1;  // NaN
+          if (w == int(kInfW)) nneg = int(x >> 16);     // -inf
         }
       }
+      const int wmax = nzmask ? tid + kHT * (31 - __clz(nzmask)) : -1;
+      const int wmin = nzmask ? tid + kHT * (__ffs(nzmask) - 1) : 0x7fff;
+      const int t_w = wave_total(int(tot));
+      const int nneg_w = wave_total(nneg);
+      const int wmax_w = wave_max_i32(wmax);
+      const int wmin_w = wave_min_i32(wmin);
+      const int nonfin_w = wave_max_i32(nonfin);
+      if (lane == 0) {
+        s_i[0][0][wid] = t_w;
+        s_i[0][1][wid] = nneg_w;
+        s_i[0][2][wid] = wmax_w;
+        s_i[0][3][wid] = wmin_w;
+        s_i[0][4][wid] = nonfin_w;
+      }
     }
-    float tau = -INFINITY;
-    if (cut) {
-      float tv;
-      key_count(hist, tau_key, &tv);
-      tau = (tau_key == 0x8000u) ? 0.f : tv;
-      const double pp = double(p);
-      if (fabs(Mgt / Z - pp) <= kBoundaryEps || fabs(Zs / Z - pp) <= kBoundaryEps) flags |= kBoundary;
+    __syncthreads();
+    const int tot = fold_partials(s_i[0][0], kHW);
+    const int nneg = fold_partials(s_i[0][1], kHW);
+    const int wmax = wave_max_i32(lane < kHW ? s_i[0][2][lane] : -1);
+    const int wmin = wave_min_i32(lane < kHW ? s_i[0][3][lane] : 0x7fff);
+    const int nonfin = wave_max_i32(lane < kHW ? s_i[0][4][lane] : 0);
+
+    const float T = a.t_row ? a.t_row[row] : a.temperature;
+    const float p = a.p_row ? a.p_row[row] : a.top_p;
+    uint8_t flags = 0;
+    if (!y_ok) flags |= kBadTarget;
+    if (!param_ok(T, p)) flags |= kBadParam;
+    if (nonfin || wmax < 0) flags |= kNonFinite;
+    const bool overflow = tot != int(V);    // a 16-bit counter wrapped: the generic kernel redoes it
+    const bool live = !overflow && !(flags & (kNonFinite | kBadParam));
+    if (tid == 0) {
+      a.fallback[row] = overflow ? 1 : 0;
+      if (!overflow && !live) store_nan_row(a, row, flags);
     }
-    store_row(a, row, lpf, lpt, h_full, h_trunc, int32_t(size), tau, flags);
+
+    if (live) {
+      // largest positive pattern (highest word with a nonzero low half),
+      // searched down from wmax; if there is none, the smallest-magnitude
+      // negative one, searched up from wmin
+      int maxpos = -1, minneg = 0x8000;
+      for (int k = 0; k <= wmax - wmin && maxpos < 0; k += kHT) {
+        const int w = wmax - k - tid;
+        const uint32_t x = hist[w >= wmin ? w : wmin];
+        const int c = (w >= wmin && (x & 0xffffu)) ? w : -1;
+        const int cw = wave_max_i32(c);
+        if (lane == 0) s_i[1][2][wid] = cw;
+        __syncthreads();
+        maxpos = wave_max_i32(lane < kHW ? s_i[1][2][lane] : -1);
+        __syncthreads();
+      }
+      for (int k = 0; k <= wmax - wmin && maxpos < 0 && minneg == 0x8000; k += kHT) {
+        const int w = wmin + k + tid;
+        const uint32_t x = hist[w <= wmax ? w : wmax];
+        const int c = (w <= wmax && (x >> 16)) ? w : 0x8000;
+        const int cw = wave_min_i32(c);
+        if (lane == 0) s_i[1][3][wid] = cw;
+        __syncthreads();
+        minneg = wave_min_i32(lane < kHW ? s_i[1][3][lane] : 0x8000);
+        __syncthreads();
+      }
+      float mval;
+      uint32_t kmax;
+      if (maxpos >= 0) {
+        mval = bf16_to_f32(uint16_t(maxpos));
+        kmax = 0x8000u + uint32_t(maxpos);
+      } else if (minneg == 0) {      // only -0 at the top: same value as +0
+        mval = 0.f;
+        kmax = 0x8000u;
+      } else {
+        mval = bf16_to_f32(uint16_t(0x8000 | minneg));
+        kmax = 0x7fffu - uint32_t(minneg);
+      }
+      const double invT = 1.0 / double(T);
+      const float invTf = float(invT);
+      const MassScale ks = mass_scale(invT);
+
+      // ---- phase B: Z and sum e*d over the distinct finite values ----
+      {
+        double zt = 0.0, st = 0.0;
+        for (int w = wmin + tid; w <= wmax; w += kHT) {
+          const uint32_t x = hist[w];
+          if (x & 0xffffu) {
+            const float dv = bf16_to_f32(uint16_t(w)) - mval;
+            const float e = code_mass(dv, ks) * float(x & 0xffffu);
+            zt += double(e);
+            st += double(e) * double(dv * invTf);
+          }
+          if (x >> 16) {
+            const float dv = bf16_to_f32(uint16_t(0x8000 | w)) - mval;
+            const float e = code_mass(dv, ks) * float(x >> 16);
+            zt += double(e);
+            st += double(e) * double(dv * invTf);
+          }
+        }
+        zt = wave_total(zt);
+        st = wave_total(st);
+        if (lane == 0) {
+          s_d[0][0][wid] = zt;
+          s_d[0][1][wid] = st;
+        }
+      }
+      __syncthreads();
+      const double Z = fold_partials(s_d[0][0], kHW);
+      const double S = fold_partials(s_d[0][1], kHW);
+
+      // ---- phase C: top-p cut, walking merged keys down from the max ----
+      double Zs = Z, Ss = S, Mgt = 0.0;
+      uint32_t tau_key = 0;
+      int size = int(V) - nneg;
+      const bool cut = p < 1.f;
+      if (cut) {
+        const double thr = double(p) * Z;
+        double cz = 0.0, cs = 0.0;
+        int cn = 0;
+        bool found = false;
+        int par = 0;
+        for (int k0 = int(kmax); !found && k0 >= 0x0080; k0 -= kHT, par ^= 1) {
+          const int key = k0 - tid;
+          double mass = 0.0, ms = 0.0;
+          int n = 0;
+          if (key >= 0x0080) {              // keys below 0x0080 are -inf / NaN
+            float v;
+            n = int(key_count(hist, uint32_t(key), &v));
+            if (n) {
+              const float dv = v - mval;
+              const float e = code_mass(dv, ks) * float(n);
+              mass = double(e);
+              ms = mass * double(dv * invTf);
+            }
+          }
+          const double iz = wave_scan_incl(mass), is = wave_scan_incl(ms);
+          const int in = wave_scan_incl(n);
+          if (lane == kWave - 1) {
+            s_d[1][2 * par][wid] = iz;
+            s_d[1][2 * par + 1][wid] = is;
+            s_i[1][par][wid] = in;
+          }
+          __syncthreads();
+          // wave partials in lanes 0..kHW-1: exclusive prefixes and the
+          // inclusive value exactly as the crossing wave's last lane forms it
+          const double pz = lane < kHW ? s_d[1][2 * par][lane] : 0.0;
+          const double ps = lane < kHW ? s_d[1][2 * par + 1][lane] : 0.0;
+          const int pn = lane < kHW ? s_i[1][par][lane] : 0;
+          const double ez = wave_shift_up(wave_scan_incl(pz));
+          const double es = wave_shift_up(wave_scan_incl(ps));
+          const int en = wave_shift_up(wave_scan_incl(pn));
+          const uint64_t wcross = __ballot(lane < kHW && cz + (ez + pz) >= thr);
+          const int cross_wave = wcross ? __ffsll((unsigned long long)wcross) - 1 : -1;
+          const double bz = readlane_f64(ez, kHW - 1) + readlane_f64(pz, kHW - 1);
+          const double bs = readlane_f64(es, kHW - 1) + readlane_f64(ps, kHW - 1);
+          const int bn = int(readlane_u32(uint32_t(en), kHW - 1)) + int(readlane_u32(uint32_t(pn), kHW - 1));
+          if (cross_wave >= 0) {
+            if (wid == cross_wave) {
+              const double wbz = readlane_f64(ez, cross_wave);
+              const double wbs = readlane_f64(es, cross_wave);
+              const int wbn = int(readlane_u32(uint32_t(en), cross_wave));
+              const double incl = cz + (wbz + iz);
+              const uint64_t bal = __ballot(incl >= thr);
+              const int first = __ffsll((unsigned long long)bal) - 1;
+              if (lane == first) {
+                b_d[0] = incl;
+                b_d[1] = cs + (wbs + is);
+                b_d[2] = incl - mass;
+                b_i[0] = key;
+                b_i[1] = cn + wbn + in;
+              }
+            }
+            __syncthreads();
+            Zs = b_d[0];
+            Ss = b_d[1];
+            Mgt = b_d[2];
+            tau_key = uint32_t(b_i[0]);
+            size = b_i[1];
+            found = true;
+          } else {
+            cz += bz;
+            cs += bs;
+            cn += bn;
+          }
+        }
+        if (!found) {   // rounding left the mass just short of p: keep every finite value
+          Zs = cz;
+          Ss = cs;
+          Mgt = cz;
+          tau_key = 0x0080;
+          size = cn;
+        }
+      }
+
+      // the row's scalars, finished below once the counters are released
+      if (tid == 0) {
+        fin.Z = Z; fin.S = S; fin.Zs = Zs; fin.Ss = Ss; fin.Mgt = Mgt;
+        fin.m = mval; fin.invT = invT; fin.p = p; fin.tau_key = tau_key;
+        fin.size = size; fin.cut = cut; fin.flags = flags; fin.cy = cy; fin.row = row;
+        fin.pending = true;
+      }
+    }
+
+    // ---- clear the counters for the next row: every nonzero word lies in
+    // [wmin, wmax] or among the inf/NaN words ----
+    __syncthreads();
+    for (int w = wmin + tid; w <= wmax; w += kHT) hist[w] = 0;
+    if (tid + (kWordsPerThread - 1) * kHT >= int(kInfW)) hist[tid + (kWordsPerThread - 1) * kHT] = 0;
+    __syncthreads();
+    // thread 0 finishes the row (fp64 logs) while the other waves start streaming
+    if (tid == 0 && fin.pending) {
+      finish_row(a, fin);
+      fin.pending = false;
+    }
   }
 }
+
 
 // ===========================================================================
 // Generic radix-select kernel (fp32 or bf16 rows of any length)
@@ -568,10 +729,17 @@ hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipS
     return hipGetLastError();
   }
   const bool vec = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.row_stride % 8 == 0);
+  // one persistent block per CU (the 128 KB histogram allows one per CU anyway)
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu < 1)
+    n_cu = 256;
+  const dim3 pgrid(unsigned(a.n_rows < n_cu ? a.n_rows : n_cu));
   if (vec)
-    hipLaunchKernelGGL(bf16_hist_rows<true>, grid, dim3(kHT), 0, stream, args);
+    hipLaunchKernelGGL(bf16_hist_rows<true>, pgrid, dim3(kHT), 0, stream, args);
   else
-    hipLaunchKernelGGL(bf16_hist_rows<false>, grid, dim3(kHT), 0, stream, args);
+    hipLaunchKernelGGL(bf16_hist_rows<false>, pgrid, dim3(kHT), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.vocab > 65535) {   // a 16-bit counter can only overflow in rows this long
