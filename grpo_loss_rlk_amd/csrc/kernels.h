@@ -23,6 +23,7 @@ struct RowArgs {
   float* thresh;          // nullable
   uint8_t* flags;         // nullable
   uint8_t* fallback;      // workspace [n_rows]: rows the histogram path hands on
+  unsigned int* row_queue;   // workspace counter: next row for the persistent blocks
 };
 
 size_t logits_rows_workspace(int64_t n_rows, int64_t vocab, int dtype);

@@ -13,12 +13,16 @@
 //
 //  * bf16_hist_rows: bf16 rows with V >= 16384. A bf16 value has only 65536
 //    bit patterns, so one streaming pass that counts each pattern in LDS
-//    (16-bit counters, two per 32-bit word, 128 KB) captures the whole row.
-//    Everything after that -- max, Z, entropy, the top-p cut, the truncated
-//    sums -- is exact arithmetic over the distinct values (fp64, fixed
-//    order), so HBM is read once at 5 VALU ops per element. A 16-bit counter
-//    that would exceed 65535 (one value holding > 43% of a long row) is
-//    detected by a checksum and the row is handed to the generic kernel.
+//    captures the whole row. Everything after that -- max, Z, entropy, the
+//    top-p cut, the truncated sums -- is arithmetic over the distinct values
+//    (fp32 masses, fp64 sums in a fixed order), so HBM is read once at a few
+//    VALU ops per element. The counters (16-bit, a positive and a negative
+//    pattern per 32-bit word) cover the magnitudes with bf16 exponent field
+//    0x40..0xbf, |z| in [2^-63, 2^64): 64 KB per buffer. Two buffers let 12
+//    waves stream the next row while 4 waves post-process the previous
+//    one. Zeros and -inf are tallied on the side; a row holding +inf, NaN,
+//    extreme magnitudes or one value more than 65535 times is handed to the
+//    generic kernel.
 //
 //  * generic_rows: any dtype and size. Multi-pass over the row: max, then
 //    exp / Z / entropy with a 12-bit radix histogram of fixed-point masses,
@@ -59,39 +63,73 @@ RLK_DEV void store_nan_row(const RowArgs& a, int64_t row, uint8_t flags) {
 // ===========================================================================
 // bf16 pattern-count histogram kernel
 // ===========================================================================
-constexpr int kHT = 1024;              // threads per row
-constexpr int kHWords = 32768;         // word w: lo16 = count(code w), hi16 = count(code 0x8000|w)
-constexpr int kWordsPerThread = kHWords / kHT;
-constexpr uint32_t kInfW = 0x7f80;     // codes with w >= 0x7f80 are inf / NaN
+constexpr int kHT = 1024;                        // threads per block (one block per CU)
+constexpr int kFW = 4;                           // finisher waves (one per SIMD)
+constexpr int kFT = kFW * kWave;                 // finisher threads
+constexpr int kStreamWaves = kHT / kWave - kFW;  // streaming waves
+constexpr int kStreamers = kStreamWaves * kWave; // streaming threads
+constexpr int kHWords = 16384;                   // 64 KB of 16-bit counter pairs per buffer
+constexpr int kMagLo = 0x2000, kMagHi = 0x6000;  // counted magnitudes: |z| in [2^-63, 2^64)
+constexpr int kKeyLo = 0x7fff - (kMagHi - 1);    // lowest merged key of a counted value
+constexpr int kUnroll = 6;                       // 16-byte vectors in flight per streamer
 
-RLK_DEV void hist_add(uint32_t* hist, uint32_t code) {
-  atomicAdd(&hist[code & 0x7fffu], (code & 0x8000u) ? 0x10000u : 1u);
+// Counter index of a counted magnitude (a rotation of the window onto 0..16383).
+RLK_DEV int widx(int mag) { return mag & 0x3fff; }
+// Magnitude held by counter index i.
+RLK_DEV int wmag(int i) { return i < 0x2000 ? i + 0x4000 : i; }
+
+// One bf16 pattern: counted if its magnitude is in the window, else tallied
+// as zero (+-0), -inf, or other (+inf, NaN, extreme magnitudes).
+RLK_DEV void count_code(uint32_t* hist, uint32_t* special, uint32_t c) {
+  const uint32_t mag = c & 0x7fffu;
+  if (mag >= uint32_t(kMagLo) && mag < uint32_t(kMagHi))
+    atomicAdd(&hist[mag & 0x3fffu], (c & 0x8000u) ? 0x10000u : 1u);
+  else
+    atomicAdd(&special[mag == 0 ? 0 : (c == 0xff80u ? 1 : 2)], 1u);
 }
 
-// Both bf16 patterns of a 32-bit word: word index = magnitude bits, the sign
-// picks the 16-bit half (increment 1 or 65536 = sign * 65535 + 1).
-RLK_DEV void hist_add2(uint32_t* hist, uint32_t x) {
-  char* base = reinterpret_cast<char*>(hist);
-  atomicAdd(reinterpret_cast<uint32_t*>(base + ((x << 2) & 0x1fffcu)),
-            __builtin_amdgcn_ubfe(x, 15, 1) * 65535u + 1u);
-  atomicAdd(reinterpret_cast<uint32_t*>(base + ((x >> 14) & 0x1fffcu)), (x >> 31) * 65535u + 1u);
-}
-
-// Merged key order over bf16 patterns: key = code | 0x8000 for positive codes,
-// ~code & 0xffff for negative ones; -0 (key 0x7fff) is folded into +0 (0x8000).
-// Returns the count of the value with this key, and the value.
-RLK_DEV uint32_t key_count(const uint32_t* hist, uint32_t key, float* value) {
-  if (key >= 0x8000u) {
-    const uint32_t c = key - 0x8000u;
-    uint32_t n = hist[c] & 0xffffu;
-    if (c == 0) n += hist[0] >> 16;   // -0 joins +0
-    *value = bf16_to_f32(uint16_t(c));
-    return n;
+// Eight bf16 patterns (16 bytes). The counter pair at index magnitude & 0x3fff
+// holds the positive pattern in its low half and the negative one in its
+// high half. Bit 14 ^ bit 13 of a magnitude is 1 exactly inside the window;
+// when all eight pass that test (the normal case) they are counted directly.
+RLK_DEV void count8(uint32_t* hist, uint32_t* special, const uint4& q) {
+  const uint32_t t = (q.x ^ (q.x << 1)) & (q.y ^ (q.y << 1)) & (q.z ^ (q.z << 1)) &
+                     (q.w ^ (q.w << 1));
+  if ((t & 0x40004000u) == 0x40004000u) {
+    char* base = reinterpret_cast<char*>(hist);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      atomicAdd(reinterpret_cast<uint32_t*>(base + ((w[k] << 2) & 0xfffcu)),
+                (w[k] & 0x8000u) ? 0x10000u : 1u);
+      atomicAdd(reinterpret_cast<uint32_t*>(base + ((w[k] >> 14) & 0xfffcu)),
+                (w[k] & 0x80000000u) ? 0x10000u : 1u);
+    }
+  } else {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      count_code(hist, special, w[k] & 0xffffu);
+      count_code(hist, special, w[k] >> 16);
+    }
   }
-  const uint32_t c = (~key) & 0xffffu;   // negative code
-  *value = bf16_to_f32(uint16_t(c));
-  if (c == 0x8000u) return 0;            // -0 already counted with +0
-  return hist[c & 0x7fffu] >> 16;
+}
+
+// Count of the value with merged key `key` (key = code | 0x8000 for a positive
+// pattern, ~code & 0xffff for a negative one, 0x8000 for +-0), and the value.
+RLK_DEV uint32_t key_count(const uint32_t* hist, int key, float* value, uint32_t n_zero) {
+  if (key == 0x8000) {
+    *value = 0.f;
+    return n_zero;
+  }
+  if (key > 0x8000) {
+    const int mag = key - 0x8000;
+    *value = bf16_to_f32(uint16_t(mag));
+    return (mag >= kMagLo && mag < kMagHi) ? (hist[widx(mag)] & 0xffffu) : 0u;
+  }
+  const int mag = 0x7fff - key;
+  *value = bf16_to_f32(uint16_t(0x8000 | mag));
+  return (mag >= kMagLo && mag < kMagHi) ? (hist[widx(mag)] >> 16) : 0u;
 }
 
 RLK_DEV uint32_t bf16_key_merged(uint16_t code) {
@@ -99,13 +137,15 @@ RLK_DEV uint32_t bf16_key_merged(uint16_t code) {
   return (code & 0x8000u) ? ((~uint32_t(code)) & 0xffffu) : (uint32_t(code) | 0x8000u);
 }
 
-constexpr int kHW = kHT / kWave;       // waves per block
-constexpr int kPF = 4;                  // 16-byte vectors per thread prefetched for the next row
+RLK_DEV float merged_key_value(uint32_t key) {
+  if (key == 0x8000u) return 0.f;
+  return key > 0x8000u ? bf16_to_f32(uint16_t(key - 0x8000u)) : bf16_to_f32(uint16_t(~key & 0xffffu));
+}
 
 // exp((v - m) / T) for a bf16 value v and the row max m, in fp32. dv = v - m
 // is exact (two bf16 values). With c = log2(e)/T split as c_hi + c_lo, the
 // exponent x = dv*c is rounded to x_hi = fl(dv*c_hi) and its residual
-// r = (dv*c_hi - x_hi) + dv*c_lo is recovered exactly enough by an fma, so
+// r = (dv*c_hi - x_hi) + dv*c_lo is recovered by an fma, so
 // 2^x = 2^x_hi * (1 + r ln 2) carries ~1 ulp of error whatever |x| is.
 struct MassScale {
   float c_hi, c_lo;
@@ -126,371 +166,342 @@ RLK_DEV float code_mass(float dv, MassScale k) {
   return fmaf(e, r * 0.69314718f, e);
 }
 
-RLK_DEV void hist_add8(uint32_t* hist, const uint4& q) {
-  hist_add2(hist, q.x);
-  hist_add2(hist, q.y);
-  hist_add2(hist, q.z);
-  hist_add2(hist, q.w);
-}
-
-// Per-row scalars handed from the block's reductions to the single thread
-// that forms the outputs.
-struct RowFinish {
-  double Z, S, Zs, Ss, Mgt, invT;
-  float m, p;
-  uint32_t tau_key;
-  int size;
-  bool cut, pending;
-  uint8_t flags;
-  uint16_t cy;
-  int64_t row;
+// ---------------------------------------------------------------------------
+// Finisher group: waves kStreamWaves..15 post-process one row while the other
+// waves stream the next. They synchronise among themselves through an LDS
+// counter: every finisher wave runs the same uniform sequence of syncs, and
+// all of them are resident in the block, so each wait ends.
+// ---------------------------------------------------------------------------
+struct FinScratch {
+  int i[8][kFW];
+  double d[6][kFW];
+  double bd[3];
+  int bi[2];
+  unsigned int bar;
 };
 
-RLK_DEV float merged_key_value(uint32_t key) {
-  if (key == 0x8000u) return 0.f;
-  return key > 0x8000u ? bf16_to_f32(uint16_t(key - 0x8000u)) : bf16_to_f32(uint16_t(~key & 0xffffu));
+RLK_DEV void fsync(unsigned int* bar, unsigned int& epoch) {
+  epoch += kFW;
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  while (__hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < epoch)
+    __builtin_amdgcn_s_sleep(1);
 }
 
-RLK_DEV void finish_row(const RowArgs& a, const RowFinish& f) {
-  uint8_t flags = f.flags;
-  const double logZ = log(f.Z), logZs = log(f.Zs);
-  const float h_full = float(logZ - f.S / f.Z);
-  const float h_trunc = float(logZs - f.Ss / f.Zs);
-  float lpf = __builtin_nanf(""), lpt = __builtin_nanf("");
-  if (!(flags & kBadTarget)) {
-    const float vy = bf16_to_f32(f.cy);
-    if (vy == -INFINITY) {
-      lpf = -INFINITY;
-      lpt = -INFINITY;
-      flags |= kOutside;
-    } else {
-      const double dy = double(vy - f.m) * f.invT;
-      lpf = float(dy - logZ);
-      if (!f.cut || bf16_key_merged(f.cy) >= f.tau_key) {
-        lpt = float(dy - logZs);
-      } else {
-        lpt = -INFINITY;
-        flags |= kOutside;
+// Everything after counting, for one row: checksum and occupied range, max,
+// Z and entropy, the top-p walk, outputs (or the hand-off flag), and zeroing
+// the counters it used so the buffer is ready for the row after next.
+RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t* special,
+                        FinScratch& fs, unsigned int& epoch) {
+  const int ft = int(threadIdx.x) - kStreamers;   // 0 .. kFT-1
+  const int lane = ft & (kWave - 1), fw = ft / kWave;
+  const int64_t V = a.vocab;
+  const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.logits) + row * a.row_stride;
+  const int64_t y = a.targets[row];
+  const bool y_ok = y >= 0 && y < V;
+  const uint16_t cy = (ft == 0 && y_ok) ? rowp[y] : uint16_t(0);
+  const float T = a.t_row ? a.t_row[row] : a.temperature;
+  const float p = a.p_row ? a.p_row[row] : a.top_p;
+  const int n_zero = int(special[0]), n_neginf = int(special[1]), n_other = int(special[2]);
+
+  // ---- checksum and occupied magnitude range, 4 counters at a time ----
+  {
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist);
+    uint32_t t_acc = 0;
+    int tmin = 0x7fff, tmax = -1;
+#pragma unroll 4
+    for (int k = 0; k < kHWords / 4 / kFT; ++k) {
+      const int q = ft + k * kFT;
+      const uint4 x = h4[q];
+      t_acc = __builtin_amdgcn_sad_u16(x.x, 0u, t_acc);
+      t_acc = __builtin_amdgcn_sad_u16(x.y, 0u, t_acc);
+      t_acc = __builtin_amdgcn_sad_u16(x.z, 0u, t_acc);
+      t_acc = __builtin_amdgcn_sad_u16(x.w, 0u, t_acc);
+      if (x.x | x.y | x.z | x.w) {
+        const int m0 = wmag(4 * q);
+        tmin = min(tmin, m0);
+        tmax = max(tmax, m0 + 3);
       }
     }
+    const int t_w = wave_total(int(t_acc));
+    const int mn_w = wave_min_i32(tmin);
+    const int mx_w = wave_max_i32(tmax);
+    if (lane == 0) {
+      fs.i[0][fw] = t_w;
+      fs.i[1][fw] = mn_w;
+      fs.i[2][fw] = mx_w;
+    }
   }
-  float tau = -INFINITY;
-  if (f.cut) {
-    tau = merged_key_value(f.tau_key);
-    const double pp = double(f.p);
-    if (fabs(f.Mgt / f.Z - pp) <= kBoundaryEps || fabs(f.Zs / f.Z - pp) <= kBoundaryEps)
-      flags |= kBoundary;
+  fsync(&fs.bar, epoch);
+  const int tot = fold_partials(fs.i[0], kFW);
+  const int wmin = wave_min_i32(lane < kFW ? fs.i[1][lane] : 0x7fff);
+  const int wmax = wave_max_i32(lane < kFW ? fs.i[2][lane] : -1);
+
+  uint8_t flags = 0;
+  if (!y_ok) flags |= kBadTarget;
+  if (!param_ok(T, p)) flags |= kBadParam;
+  if (n_zero == 0 && n_neginf == int(V)) flags |= kNonFinite;
+  // a value held > 65535 times wraps its counter; +inf, NaN and extreme
+  // magnitudes are not counted: the generic kernel redoes such rows
+  const bool handoff = n_other != 0 || tot + n_zero + n_neginf != int(V);
+  const bool live = !handoff && !(flags & (kBadParam | kNonFinite));
+  if (ft == 0) {
+    a.fallback[row] = handoff ? 1 : 0;
+    if (!handoff && !live) store_nan_row(a, row, flags);
   }
-  store_row(a, f.row, lpf, lpt, h_full, h_trunc, f.size, tau, flags);
+
+  if (live) {
+    // largest value: highest magnitude with a positive pattern; else zero;
+    // else the negative pattern of smallest magnitude
+    int maxpos = -1, minneg = 0x8000;
+    for (int m0 = wmax; m0 >= wmin && maxpos < 0; m0 -= kFT) {
+      const int m = m0 - ft;
+      const bool hit = m >= wmin && (hist[widx(m >= wmin ? m : wmin)] & 0xffffu);
+      const uint64_t bal = __ballot(hit);
+      if (lane == 0) fs.i[3][fw] = bal ? m0 - fw * kWave - (__ffsll((unsigned long long)bal) - 1) : -1;
+      fsync(&fs.bar, epoch);
+      maxpos = wave_max_i32(lane < kFW ? fs.i[3][lane] : -1);
+      fsync(&fs.bar, epoch);
+    }
+    for (int m0 = wmin; m0 <= wmax && maxpos < 0 && n_zero == 0 && minneg == 0x8000; m0 += kFT) {
+      const int m = m0 + ft;
+      const bool hit = m <= wmax && (hist[widx(m <= wmax ? m : wmax)] >> 16);
+      const uint64_t bal = __ballot(hit);
+      if (lane == 0) fs.i[4][fw] = bal ? m0 + fw * kWave + (__ffsll((unsigned long long)bal) - 1) : 0x8000;
+      fsync(&fs.bar, epoch);
+      minneg = wave_min_i32(lane < kFW ? fs.i[4][lane] : 0x8000);
+      fsync(&fs.bar, epoch);
+    }
+    float mval;
+    int kmax;
+    if (maxpos >= 0) {
+      mval = bf16_to_f32(uint16_t(maxpos));
+      kmax = 0x8000 + maxpos;
+    } else if (n_zero > 0) {
+      mval = 0.f;
+      kmax = 0x8000;
+    } else {
+      mval = bf16_to_f32(uint16_t(0x8000 | minneg));
+      kmax = 0x7fff - minneg;
+    }
+    const double invT = 1.0 / double(T);
+    const float invTf = float(invT);
+    const MassScale ks = mass_scale(invT);
+
+    // ---- Z and sum e*d over the distinct values ----
+    {
+      double zt = 0.0, st = 0.0;
+      for (int m = wmin + ft; m <= wmax; m += kFT) {
+        const uint32_t x = hist[widx(m)];
+        if (x & 0xffffu) {
+          const float dv = bf16_to_f32(uint16_t(m)) - mval;
+          const float e = code_mass(dv, ks) * float(x & 0xffffu);
+          zt += double(e);
+          st += double(e) * double(dv * invTf);
+        }
+        if (x >> 16) {
+          const float dv = bf16_to_f32(uint16_t(0x8000 | m)) - mval;
+          const float e = code_mass(dv, ks) * float(x >> 16);
+          zt += double(e);
+          st += double(e) * double(dv * invTf);
+        }
+      }
+      if (ft == 0 && n_zero > 0) {   // the +-0 group
+        const float dv = -mval;
+        const float e = code_mass(dv, ks) * float(n_zero);
+        zt += double(e);
+        st += double(e) * double(dv * invTf);
+      }
+      zt = wave_total(zt);
+      st = wave_total(st);
+      if (lane == 0) {
+        fs.d[0][fw] = zt;
+        fs.d[1][fw] = st;
+      }
+    }
+    fsync(&fs.bar, epoch);
+    const double Z = fold_partials(fs.d[0], kFW);
+    const double S = fold_partials(fs.d[1], kFW);
+
+    // ---- top-p cut: walk merged keys down from the max, kFT at a time ----
+    double Zs = Z, Ss = S, Mgt = 0.0;
+    uint32_t tau_key = 0;
+    int size = int(V) - n_neginf;
+    const bool cut = p < 1.f;
+    if (cut) {
+      const double thr = double(p) * Z;
+      double cz = 0.0, cs = 0.0;
+      int cn = 0;
+      bool found = false;
+      int par = 0;
+      for (int k0 = kmax; !found && k0 >= kKeyLo; k0 -= kFT, par ^= 1) {
+        const int key = k0 - ft;
+        double mass = 0.0, ms = 0.0;
+        int n = 0;
+        if (key >= kKeyLo) {
+          float v;
+          n = int(key_count(hist, key, &v, uint32_t(n_zero)));
+          if (n) {
+            const float dv = v - mval;
+            const float e = code_mass(dv, ks) * float(n);
+            mass = double(e);
+            ms = mass * double(dv * invTf);
+          }
+        }
+        const double iz = wave_scan_incl(mass), is = wave_scan_incl(ms);
+        const int in = wave_scan_incl(n);
+        if (lane == kWave - 1) {
+          fs.d[2 + 2 * par][fw] = iz;
+          fs.d[3 + 2 * par][fw] = is;
+          fs.i[5 + par][fw] = in;
+        }
+        fsync(&fs.bar, epoch);
+        // wave partials in lanes 0..kFW-1: exclusive prefixes, and the
+        // inclusive value exactly as the crossing wave's last lane forms it
+        const double pz = lane < kFW ? fs.d[2 + 2 * par][lane] : 0.0;
+        const double ps = lane < kFW ? fs.d[3 + 2 * par][lane] : 0.0;
+        const int pn = lane < kFW ? fs.i[5 + par][lane] : 0;
+        const double ez = wave_shift_up(wave_scan_incl(pz));
+        const double es = wave_shift_up(wave_scan_incl(ps));
+        const int en = wave_shift_up(wave_scan_incl(pn));
+        const uint64_t wcross = __ballot(lane < kFW && cz + (ez + pz) >= thr);
+        const int cross_wave = wcross ? __ffsll((unsigned long long)wcross) - 1 : -1;
+        if (cross_wave >= 0) {
+          if (fw == cross_wave) {
+            const double wbz = readlane_f64(ez, cross_wave);
+            const double wbs = readlane_f64(es, cross_wave);
+            const int wbn = int(readlane_u32(uint32_t(en), cross_wave));
+            const double incl = cz + (wbz + iz);
+            const uint64_t bal = __ballot(incl >= thr);
+            const int first = __ffsll((unsigned long long)bal) - 1;
+            if (lane == first) {
+              fs.bd[0] = incl;
+              fs.bd[1] = cs + (wbs + is);
+              fs.bd[2] = incl - mass;
+              fs.bi[0] = key;
+              fs.bi[1] = cn + wbn + in;
+            }
+          }
+          fsync(&fs.bar, epoch);
+          Zs = fs.bd[0];
+          Ss = fs.bd[1];
+          Mgt = fs.bd[2];
+          tau_key = uint32_t(fs.bi[0]);
+          size = fs.bi[1];
+          found = true;
+        } else {
+          cz += readlane_f64(ez, kFW - 1) + readlane_f64(pz, kFW - 1);
+          cs += readlane_f64(es, kFW - 1) + readlane_f64(ps, kFW - 1);
+          cn += int(readlane_u32(uint32_t(en), kFW - 1)) + int(readlane_u32(uint32_t(pn), kFW - 1));
+        }
+      }
+      if (!found) {   // rounding left the mass just short of p: keep every value
+        Zs = cz;
+        Ss = cs;
+        Mgt = cz;
+        tau_key = uint32_t(kKeyLo);
+        size = cn;
+      }
+    }
+
+    if (ft == 0) {
+      const double logZ = log(Z), logZs = log(Zs);
+      const float h_full = float(logZ - S / Z);
+      const float h_trunc = float(logZs - Ss / Zs);
+      float lpf = __builtin_nanf(""), lpt = __builtin_nanf("");
+      if (y_ok) {
+        const float vy = bf16_to_f32(cy);
+        if (vy == -INFINITY) {
+          lpf = -INFINITY;
+          lpt = -INFINITY;
+          flags |= kOutside;
+        } else {
+          const double dy = double(vy - mval) * invT;
+          lpf = float(dy - logZ);
+          if (!cut || bf16_key_merged(cy) >= tau_key) {
+            lpt = float(dy - logZs);
+          } else {
+            lpt = -INFINITY;
+            flags |= kOutside;
+          }
+        }
+      }
+      float tau = -INFINITY;
+      if (cut) {
+        tau = merged_key_value(tau_key);
+        const double pp = double(p);
+        if (fabs(Mgt / Z - pp) <= kBoundaryEps || fabs(Zs / Z - pp) <= kBoundaryEps)
+          flags |= kBoundary;
+      }
+      store_row(a, row, lpf, lpt, h_full, h_trunc, size, tau, flags);
+    }
+  }
+
+  // ---- release the buffer: every nonzero counter lies in [wmin, wmax] ----
+  for (int m = wmin + ft; m <= wmax; m += kFT) hist[widx(m)] = 0;
+  if (ft == 0) special[0] = special[1] = special[2] = 0;
 }
 
-// One persistent block per CU walks rows blockIdx.x, +gridDim.x, ... While a
-// row's histogram is post-processed, the first kPF*kHT vectors of the next row
-// are already in flight, so HBM keeps streaming. Every reduction is a DPP wave
-// scan plus one barrier and a fixed-order fold over the 16 wave partials.
+// One persistent block per CU. Rows come from a queue (a counter starting at
+// gridDim.x), so a block that draws slow rows takes fewer. Step s: waves
+// 0..kStreamWaves-1 stream row R_s into counter buffer s & 1 while the
+// finisher waves post-process row R_{s-1} from the other buffer; one block
+// barrier separates the steps.
 template <bool kVec>
 __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
-  __shared__ uint32_t hist[kHWords];
-  __shared__ int s_i[2][8][kHW];
-  __shared__ double s_d[2][4][kHW];
-  __shared__ double b_d[4];
-  __shared__ int b_i[2];
+  __shared__ uint32_t hist[2][kHWords];
+  __shared__ uint32_t special[2][4];
+  __shared__ int64_t queued[2];
+  __shared__ FinScratch fs;
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int tid = threadIdx.x, wid = tid / kWave;
   const int64_t V = a.vocab;
   const int64_t nvec = kVec ? (V >> 3) : 0;
+  const int64_t N = a.n_rows;
 
   {
-    uint4* h4 = reinterpret_cast<uint4*>(hist);
-    for (int i = tid; i < kHWords / 4; i += kHT) h4[i] = make_uint4(0, 0, 0, 0);
+    uint4* h4 = reinterpret_cast<uint4*>(&hist[0][0]);
+    for (int i = tid; i < 2 * kHWords / 4; i += kHT) h4[i] = make_uint4(0, 0, 0, 0);
   }
-  uint4 pf[kPF];
-  int64_t row = blockIdx.x;
-  if (kVec && row < a.n_rows) {
-    const uint4* v4 = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(a.logits) + row * a.row_stride);
-#pragma unroll
-    for (int u = 0; u < kPF; ++u)
-      if (tid + u * kHT < nvec) pf[u] = v4[tid + u * kHT];
-  }
-  __shared__ RowFinish fin;     // written and read by thread 0 only
-  if (tid == 0) fin.pending = false;
+  if (tid < 8) special[tid >> 2][tid & 3] = 0;
+  if (tid == 0) fs.bar = 0;
+  unsigned int epoch = 0;
   __syncthreads();
 
-  for (; row < a.n_rows; row += gridDim.x) {
-    const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.logits) + row * a.row_stride;
-    const int64_t y = a.targets[row];
-    const bool y_ok = y >= 0 && y < V;
-    uint16_t cy = 0;
-    if (tid == 0 && y_ok) cy = rowp[y];
-
-    // ---- one streaming pass: count every bf16 pattern of the row ----
-    if (kVec) {
-      const uint4* v4 = reinterpret_cast<const uint4*>(rowp);
+  int64_t cur = blockIdx.x;   // streamed this step
+  int64_t prev = N;           // finished this step
+  for (int s = 0; cur < N || prev < N; ++s) {
+    const int b = s & 1;
+    if (wid < kStreamWaves) {
+      if (cur < N) {
+        if (tid == 0) queued[b] = int64_t(atomicAdd(a.row_queue, 1u));
+        const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.logits) + cur * a.row_stride;
+        uint32_t* h = hist[b];
+        uint32_t* sp = special[b];
+        if (kVec) {
+          const uint4* v4 = reinterpret_cast<const uint4*>(rowp);
+          int64_t i = tid;
+          for (; i + (kUnroll - 1) * kStreamers < nvec; i += kUnroll * kStreamers) {
+            uint4 q[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kPF; ++u)
-        if (tid + u * kHT < nvec) hist_add8(hist, pf[u]);
-      int64_t i = tid + kPF * kHT;
-      for (; i + 3 * kHT < nvec; i += 4 * kHT) {
-        uint4 q[4];
+            for (int u = 0; u < kUnroll; ++u) q[u] = v4[i + u * kStreamers];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) q[u] = v4[i + u * kHT];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) hist_add8(hist, q[u]);
-      }
-      for (; i < nvec; i += kHT) hist_add8(hist, v4[i]);
-      for (int64_t j = (nvec << 3) + tid; j < V; j += kHT) hist_add(hist, rowp[j]);
-    } else {
-      for (int64_t j = tid; j < V; j += kHT) hist_add(hist, rowp[j]);
-    }
-    __syncthreads();
-
-    // ---- the next row's first vectors go in flight now ----
-    const int64_t nxt = row + gridDim.x;
-    if (kVec && nxt < a.n_rows) {
-      const uint4* v4n = reinterpret_cast<const uint4*>(
-          reinterpret_cast<const uint16_t*>(a.logits) + nxt * a.row_stride);
-#pragma unroll
-      for (int u = 0; u < kPF; ++u)
-        if (tid + u * kHT < nvec) pf[u] = v4n[tid + u * kHT];
-    }
-
-    // ---- phase A: checksum, occupied word range, non-finite detection ----
-    // thread t owns words t + kHT*j; a bit mask of its nonzero finite words
-    // gives the range [wmin, wmax] every later phase is limited to.
-    {
-      uint32_t tot = 0, nzmask = 0;
-      int nonfin = 0, nneg = 0;
-#pragma unroll
-      for (int j = 0; j < kWordsPerThread - 1; ++j) {
-        const uint32_t x = hist[tid + j * kHT];
-        tot = __builtin_amdgcn_sad_u16(x, 0u, tot);
-        nzmask |= x ? (1u << j) : 0u;
-      }
-      {
-        const int w = tid + (kWordsPerThread - 1) * kHT;
-        const uint32_t x = hist[w];
-        tot = __builtin_amdgcn_sad_u16(x, 0u, tot);
-        if (w < int(kInfW)) {
-          nzmask |= x ? (1u << (kWordsPerThread - 1)) : 0u;
+            for (int u = 0; u < kUnroll; ++u) count8(h, sp, q[u]);
+          }
+          for (; i < nvec; i += kStreamers) count8(h, sp, v4[i]);
+          for (int64_t j = (nvec << 3) + tid; j < V; j += kStreamers) count_code(h, sp, rowp[j]);
         } else {
-          if (x & 0xffffu) nonfin = 1;                  // +inf or NaN
-          if ((x >> 16) && w > int(kInfW)) nonfin = 1;  // NaN
-          if (w == int(kInfW)) nneg = int(x >> 16);     // -inf
+          for (int64_t j = tid; j < V; j += kStreamers) count_code(h, sp, rowp[j]);
         }
       }
-      const int wmax = nzmask ? tid + kHT * (31 - __clz(nzmask)) : -1;
-      const int wmin = nzmask ? tid + kHT * (__ffs(nzmask) - 1) : 0x7fff;
-      const int t_w = wave_total(int(tot));
-      const int nneg_w = wave_total(nneg);
-      const int wmax_w = wave_max_i32(wmax);
-      const int wmin_w = wave_min_i32(wmin);
-      const int nonfin_w = wave_max_i32(nonfin);
-      if (lane == 0) {
-        s_i[0][0][wid] = t_w;
-        s_i[0][1][wid] = nneg_w;
-        s_i[0][2][wid] = wmax_w;
-        s_i[0][3][wid] = wmin_w;
-        s_i[0][4][wid] = nonfin_w;
-      }
+    } else if (prev < N) {
+      finish_row(a, prev, hist[b ^ 1], special[b ^ 1], fs, epoch);
     }
     __syncthreads();
-    const int tot = fold_partials(s_i[0][0], kHW);
-    const int nneg = fold_partials(s_i[0][1], kHW);
-    const int wmax = wave_max_i32(lane < kHW ? s_i[0][2][lane] : -1);
-    const int wmin = wave_min_i32(lane < kHW ? s_i[0][3][lane] : 0x7fff);
-    const int nonfin = wave_max_i32(lane < kHW ? s_i[0][4][lane] : 0);
-
-    const float T = a.t_row ? a.t_row[row] : a.temperature;
-    const float p = a.p_row ? a.p_row[row] : a.top_p;
-    uint8_t flags = 0;
-    if (!y_ok) flags |= kBadTarget;
-    if (!param_ok(T, p)) flags |= kBadParam;
-    if (nonfin || wmax < 0) flags |= kNonFinite;
-    const bool overflow = tot != int(V);    // a 16-bit counter wrapped: the generic kernel redoes it
-    const bool live = !overflow && !(flags & (kNonFinite | kBadParam));
-    if (tid == 0) {
-      a.fallback[row] = overflow ? 1 : 0;
-      if (!overflow && !live) store_nan_row(a, row, flags);
-    }
-
-    if (live) {
-      // largest positive pattern (highest word with a nonzero low half),
-      // searched down from wmax; if there is none, the smallest-magnitude
-      // negative one, searched up from wmin
-      int maxpos = -1, minneg = 0x8000;
-      for (int k = 0; k <= wmax - wmin && maxpos < 0; k += kHT) {
-        const int w = wmax - k - tid;
-        const uint32_t x = hist[w >= wmin ? w : wmin];
-        const int c = (w >= wmin && (x & 0xffffu)) ? w : -1;
-        const int cw = wave_max_i32(c);
-        if (lane == 0) s_i[1][2][wid] = cw;
-        __syncthreads();
-        maxpos = wave_max_i32(lane < kHW ? s_i[1][2][lane] : -1);
-        __syncthreads();
-      }
-      for (int k = 0; k <= wmax - wmin && maxpos < 0 && minneg == 0x8000; k += kHT) {
-        const int w = wmin + k + tid;
-        const uint32_t x = hist[w <= wmax ? w : wmax];
-        const int c = (w <= wmax && (x >> 16)) ? w : 0x8000;
-        const int cw = wave_min_i32(c);
-        if (lane == 0) s_i[1][3][wid] = cw;
-        __syncthreads();
-        minneg = wave_min_i32(lane < kHW ? s_i[1][3][lane] : 0x8000);
-        __syncthreads();
-      }
-      float mval;
-      uint32_t kmax;
-      if (maxpos >= 0) {
-        mval = bf16_to_f32(uint16_t(maxpos));
-        kmax = 0x8000u + uint32_t(maxpos);
-      } else if (minneg == 0) {      // only -0 at the top: same value as +0
-        mval = 0.f;
-        kmax = 0x8000u;
-      } else {
-        mval = bf16_to_f32(uint16_t(0x8000 | minneg));
-        kmax = 0x7fffu - uint32_t(minneg);
-      }
-      const double invT = 1.0 / double(T);
-      const float invTf = float(invT);
-      const MassScale ks = mass_scale(invT);
-
-      // ---- phase B: Z and sum e*d over the distinct finite values ----
-      {
-        double zt = 0.0, st = 0.0;
-        for (int w = wmin + tid; w <= wmax; w += kHT) {
-          const uint32_t x = hist[w];
-          if (x & 0xffffu) {
-            const float dv = bf16_to_f32(uint16_t(w)) - mval;
-            const float e = code_mass(dv, ks) * float(x & 0xffffu);
-            zt += double(e);
-            st += double(e) * double(dv * invTf);
-          }
-          if (x >> 16) {
-            const float dv = bf16_to_f32(uint16_t(0x8000 | w)) - mval;
-            const float e = code_mass(dv, ks) * float(x >> 16);
-            zt += double(e);
-            st += double(e) * double(dv * invTf);
-          }
-        }
-        zt = wave_total(zt);
-        st = wave_total(st);
-        if (lane == 0) {
-          s_d[0][0][wid] = zt;
-          s_d[0][1][wid] = st;
-        }
-      }
-      __syncthreads();
-      const double Z = fold_partials(s_d[0][0], kHW);
-      const double S = fold_partials(s_d[0][1], kHW);
-
-      // ---- phase C: top-p cut, walking merged keys down from the max ----
-      double Zs = Z, Ss = S, Mgt = 0.0;
-      uint32_t tau_key = 0;
-      int size = int(V) - nneg;
-      const bool cut = p < 1.f;
-      if (cut) {
-        const double thr = double(p) * Z;
-        double cz = 0.0, cs = 0.0;
-        int cn = 0;
-        bool found = false;
-        int par = 0;
-        for (int k0 = int(kmax); !found && k0 >= 0x0080; k0 -= kHT, par ^= 1) {
-          const int key = k0 - tid;
-          double mass = 0.0, ms = 0.0;
-          int n = 0;
-          if (key >= 0x0080) {              // keys below 0x0080 are -inf / NaN
-            float v;
-            n = int(key_count(hist, uint32_t(key), &v));
-            if (n) {
-              const float dv = v - mval;
-              const float e = code_mass(dv, ks) * float(n);
-              mass = double(e);
-              ms = mass * double(dv * invTf);
-            }
-          }
-          const double iz = wave_scan_incl(mass), is = wave_scan_incl(ms);
-          const int in = wave_scan_incl(n);
-          if (lane == kWave - 1) {
-            s_d[1][2 * par][wid] = iz;
-            s_d[1][2 * par + 1][wid] = is;
-            s_i[1][par][wid] = in;
-          }
-          __syncthreads();
-          // wave partials in lanes 0..kHW-1: exclusive prefixes and the
-          // inclusive value exactly as the crossing wave's last lane forms it
-          const double pz = lane < kHW ? s_d[1][2 * par][lane] : 0.0;
-          const double ps = lane < kHW ? s_d[1][2 * par + 1][lane] : 0.0;
-          const int pn = lane < kHW ? s_i[1][par][lane] : 0;
-          const double ez = wave_shift_up(wave_scan_incl(pz));
-          const double es = wave_shift_up(wave_scan_incl(ps));
-          const int en = wave_shift_up(wave_scan_incl(pn));
-          const uint64_t wcross = __ballot(lane < kHW && cz + (ez + pz) >= thr);
-          const int cross_wave = wcross ? __ffsll((unsigned long long)wcross) - 1 : -1;
-          const double bz = readlane_f64(ez, kHW - 1) + readlane_f64(pz, kHW - 1);
-          const double bs = readlane_f64(es, kHW - 1) + readlane_f64(ps, kHW - 1);
-          const int bn = int(readlane_u32(uint32_t(en), kHW - 1)) + int(readlane_u32(uint32_t(pn), kHW - 1));
-          if (cross_wave >= 0) {
-            if (wid == cross_wave) {
-              const double wbz = readlane_f64(ez, cross_wave);
-              const double wbs = readlane_f64(es, cross_wave);
-              const int wbn = int(readlane_u32(uint32_t(en), cross_wave));
-              const double incl = cz + (wbz + iz);
-              const uint64_t bal = __ballot(incl >= thr);
-              const int first = __ffsll((unsigned long long)bal) - 1;
-              if (lane == first) {
-                b_d[0] = incl;
-                b_d[1] = cs + (wbs + is);
-                b_d[2] = incl - mass;
-                b_i[0] = key;
-                b_i[1] = cn + wbn + in;
-              }
-            }
-            __syncthreads();
-            Zs = b_d[0];
-            Ss = b_d[1];
-            Mgt = b_d[2];
-            tau_key = uint32_t(b_i[0]);
-            size = b_i[1];
-            found = true;
-          } else {
-            cz += bz;
-            cs += bs;
-            cn += bn;
-          }
-        }
-        if (!found) {   // rounding left the mass just short of p: keep every finite value
-          Zs = cz;
-          Ss = cs;
-          Mgt = cz;
-          tau_key = 0x0080;
-          size = cn;
-        }
-      }
-
-      // the row's scalars, finished below once the counters are released
-      if (tid == 0) {
-        fin.Z = Z; fin.S = S; fin.Zs = Zs; fin.Ss = Ss; fin.Mgt = Mgt;
-        fin.m = mval; fin.invT = invT; fin.p = p; fin.tau_key = tau_key;
-        fin.size = size; fin.cut = cut; fin.flags = flags; fin.cy = cy; fin.row = row;
-        fin.pending = true;
-      }
-    }
-
-    // ---- clear the counters for the next row: every nonzero word lies in
-    // [wmin, wmax] or among the inf/NaN words ----
-    __syncthreads();
-    for (int w = wmin + tid; w <= wmax; w += kHT) hist[w] = 0;
-    if (tid + (kWordsPerThread - 1) * kHT >= int(kInfW)) hist[tid + (kWordsPerThread - 1) * kHT] = 0;
-    __syncthreads();
-    // thread 0 finishes the row (fp64 logs) while the other waves start streaming
-    if (tid == 0 && fin.pending) {
-      finish_row(a, fin);
-      fin.pending = false;
-    }
+    prev = cur;
+    cur = (cur < N) ? queued[b] : N;
   }
 }
-
 
 // ===========================================================================
 // Generic radix-select kernel (fp32 or bf16 rows of any length)
@@ -707,18 +718,22 @@ __global__ __launch_bounds__(kGT) void generic_rows(RowArgs a, int only_fallback
   }
 }
 
+__global__ void reset_queue(unsigned int* q, unsigned int start) { *q = start; }
+
 }  // namespace
 
+// workspace: [0, 256) row-queue counter, [256, 256 + n_rows) hand-off flags
 size_t logits_rows_workspace(int64_t n_rows, int64_t vocab, int dtype) {
   (void)vocab;
   (void)dtype;
-  return size_t((n_rows + 255) / 256 * 256);
+  return 256 + size_t((n_rows + 255) / 256 * 256);
 }
 
 hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
   RowArgs args = a;
-  args.fallback = reinterpret_cast<uint8_t*>(workspace);
+  args.row_queue = reinterpret_cast<unsigned int*>(workspace);
+  args.fallback = reinterpret_cast<uint8_t*>(workspace) + 256;
   const dim3 grid(unsigned(a.n_rows));
   if (dtype == 0) {  // fp32
     hipLaunchKernelGGL(generic_rows<float>, grid, dim3(kGT), 0, stream, args, 0);
@@ -729,24 +744,24 @@ hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipS
     return hipGetLastError();
   }
   const bool vec = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.row_stride % 8 == 0);
-  // one persistent block per CU (the 128 KB histogram allows one per CU anyway)
+  // one persistent block per CU (two 64 KB counter buffers)
   int dev = 0, n_cu = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       n_cu < 1)
     n_cu = 256;
-  const dim3 pgrid(unsigned(a.n_rows < n_cu ? a.n_rows : n_cu));
+  const int64_t nb = int64_t(n_cu);
+  const dim3 pgrid(unsigned(a.n_rows < nb ? a.n_rows : nb));
+  hipLaunchKernelGGL(reset_queue, dim3(1), dim3(1), 0, stream, args.row_queue, pgrid.x);
   if (vec)
     hipLaunchKernelGGL(bf16_hist_rows<true>, pgrid, dim3(kHT), 0, stream, args);
   else
     hipLaunchKernelGGL(bf16_hist_rows<false>, pgrid, dim3(kHT), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.vocab > 65535) {   // a 16-bit counter can only overflow in rows this long
-    hipLaunchKernelGGL(generic_rows<uint16_t>, grid, dim3(kGT), 0, stream, args, 1);
-    e = hipGetLastError();
-  }
-  return e;
+  // rows the histogram kernel handed on (wrapped counters, uncounted values)
+  hipLaunchKernelGGL(generic_rows<uint16_t>, grid, dim3(kGT), 0, stream, args, 1);
+  return hipGetLastError();
 }
 
 }  // namespace rlk

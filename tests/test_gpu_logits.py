@@ -156,6 +156,36 @@ def test_edge_rows(dtype, V, T, p):
     check(g, o, **(F32_TOL if dtype == "f32" else BF16_TOL))
 
 
+@pytest.mark.parametrize("T,p", [(0.7, 0.95), (1.0, 1.0), (0.7, 0.3)])
+def test_special_values_in_realistic_rows(T, p):
+    """Zeros, -0, -inf (vocabulary masking), tiny and huge magnitudes mixed
+    into Qwen-shaped rows: every row must match the oracle whichever kernel
+    path takes it."""
+    w = synth.workload("qwen")
+    N = 10
+    rows = synth.logits_rows(w, range(N))
+    z = synth.f32_from_bf16_bits(rows).copy()
+    rng = np.random.default_rng(77)
+    y = synth.peak_targets(w, range(N))
+    z[0, rng.choice(w.V, 1, replace=False)] = 0.0
+    z[1, rng.choice(w.V, 1000, replace=False)] = 0.0
+    z[2, rng.choice(w.V, 5, replace=False)] = -np.inf
+    z[3, rng.choice(w.V, 20000, replace=False)] = -np.inf
+    z[3, rng.choice(w.V, 300, replace=False)] = 0.0
+    z[4, rng.choice(w.V, 40, replace=False)] = -0.0
+    z[5, 11] = 0.0; y[5] = 11                           # target on a zero
+    z[6, 12] = -np.inf; y[6] = 12                       # target masked out
+    z[7, rng.choice(w.V, 3, replace=False)] = 1e-30     # below the counted window
+    z[8, :] = np.where(z[8] > 0, -z[8], z[8])           # all negative
+    z[8, rng.choice(w.V, 2, replace=False)] = 0.0       # ... with zeros at the top
+    z[9, rng.choice(w.V, 2, replace=False)] = 3e19      # above the counted window
+    arr = synth.bf16_bits_from_f32(np.where(np.isnan(z), 0, z)).reshape(z.shape)
+    zz = widen(arr, "bf16")
+    o = OL.logprob_from_logits(zz, y, OL.f32(T), OL.f32(p))
+    g = run(arr, "bf16", y, T, p)
+    check(g, o, **BF16_TOL)
+
+
 def test_per_row_temperature_and_top_p():
     w = synth.workload("qwen", V=32768)
     N = 16
