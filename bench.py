@@ -88,12 +88,41 @@ def leg_logits(torch, rlk, synth, steps, warmup, cpu_sample):
     return res
 
 
+def leg_fused(torch, rlk, synth, steps, warmup):
+    """Fused LM-head forward, Qwen3-8B head: hidden [8192, 4096], W [151936, 4096], T=1, p=1."""
+    w = synth.workload("fused")
+    t_gen = time.perf_counter()
+    hb = synth.hidden_rows(w, range(w.N))
+    wb = synth.weight_rows(w, range(w.V))
+    y = synth.uniform_targets(w, w.N)
+    h = torch.from_numpy(hb.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    W = torch.from_numpy(wb.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    yt = torch.from_numpy(y).to("cuda:0")
+    print(f"[bench] fused leg: hidden {tuple(h.shape)} W {tuple(W.shape)} generated in "
+          f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    fn = lambda: rlk.logprob_fused_linear(h, W, yt, w.temperature, 1.0)  # noqa: E731
+    mean_ms, total_ms, min_ms = _events_time(torch, fn, steps, warmup)
+    flops = 2.0 * w.N * w.V * w.H
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    return {
+        "workload": f"fused LM-head forward, hidden [{w.N},{w.H}] bf16, W [{w.V},{w.H}] bf16, "
+                    f"T={w.temperature}, top-p=1",
+        "tokens_per_s": w.N * steps / (total_ms * 1e-3),
+        "ms_per_step": total_ms / steps,
+        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "flops_per_token": 2.0 * w.V * w.H,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="logits")
+    ap.add_argument("--legs", default="logits,fused")
     ap.add_argument("--cpu-sample", type=int, default=256,
                     help="rows of the logits workload the CPU oracle is timed on (0 = skip)")
     args = ap.parse_args()
@@ -111,6 +140,8 @@ def main():
     if "logits" in legs:
         out_legs["logits"] = leg_logits(torch, rlk, synth, args.steps, args.warmup,
                                         args.cpu_sample)
+    if "fused" in legs:
+        out_legs["fused"] = leg_fused(torch, rlk, synth, max(3, args.steps // 4), 1)
     main_leg = out_legs["logits"]
     line = {
         "metric": METRIC,

@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "../../include/rlk.h"
+#include "fused_kernels.h"
 #include "kernels.h"
 
 namespace {
@@ -131,6 +132,96 @@ rlk_status rlk_logprob_from_logits(const void* logits, int32_t dtype, int64_t n_
   return hip_status(rlk::launch_logits_rows(a, dtype, workspace,
                                             reinterpret_cast<hipStream_t>(stream)),
                     "rlk_logprob_from_logits launch");
+}
+
+// ------------------------------------------------------------------ fused LM head
+namespace {
+
+rlk_status check_fused_shapes(const void* hidden, const void* weight, int64_t N, int64_t H,
+                              int64_t V, int64_t hs, int64_t ws, const int64_t* targets) {
+  if (N < 0) return fail(RLK_EINVAL, "n_rows=%lld < 0", (long long)N);
+  if (H < 64 || H % 64 != 0)
+    return fail(RLK_EINVAL, "hidden_size=%lld must be a positive multiple of 64", (long long)H);
+  if (V < 1 || V > kMaxVocab) return fail(RLK_EINVAL, "vocab=%lld outside [1, 2^24]", (long long)V);
+  if (hs < H || ws < H || hs % 8 != 0 || ws % 8 != 0)
+    return fail(RLK_EINVAL, "strides (h %lld, w %lld) must be >= hidden_size and multiples of 8",
+                (long long)hs, (long long)ws);
+  if (N == 0) return RLK_OK;
+  if (!hidden || !weight || !targets)
+    return fail(RLK_EINVAL, "hidden, weight and targets are required");
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(targets, 8))
+    return fail(RLK_EINVAL, "hidden and weight must be 16-byte aligned, targets 8-byte aligned");
+  return RLK_OK;
+}
+
+}  // namespace
+
+size_t rlk_logprob_fused_linear_workspace_size(int64_t n_rows, int64_t hidden_size, int64_t vocab,
+                                               float top_p) {
+  (void)top_p;
+  if (n_rows < 0 || vocab < 1) return 0;
+  return rlk::fused_fwd_workspace(n_rows, hidden_size, vocab);
+}
+
+rlk_status rlk_logprob_fused_linear(const void* hidden, const void* weight, int64_t n_rows,
+                                    int64_t hidden_size, int64_t vocab, int64_t h_stride,
+                                    int64_t w_stride, const int64_t* targets, float temperature,
+                                    float top_p, int32_t top_k, float* logprob, float* entropy,
+                                    float* saved, int32_t* nucleus_size, uint8_t* flags,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  rlk_status s = check_sampling(temperature, top_p, top_k);
+  if (s != RLK_OK) return s;
+  s = check_fused_shapes(hidden, weight, n_rows, hidden_size, vocab, h_stride, w_stride, targets);
+  if (s != RLK_OK) return s;
+  if (top_p < 1.f)
+    return fail(RLK_EUNSUPPORTED, "fused top-p < 1 is not implemented yet (use top_p = 1)");
+  if (n_rows == 0) return ok();
+  if (!logprob || !entropy) return fail(RLK_EINVAL, "logprob and entropy are required");
+  if (!aligned(logprob, 4) || !aligned(entropy, 4) || !aligned(saved, 4) ||
+      !aligned(nucleus_size, 4))
+    return fail(RLK_EINVAL, "an output array is not naturally aligned");
+  s = check_workspace(workspace, workspace_bytes,
+                      rlk_logprob_fused_linear_workspace_size(n_rows, hidden_size, vocab, top_p));
+  if (s != RLK_OK) return s;
+  rlk::FusedFwdArgs a{};
+  a.h = reinterpret_cast<const uint16_t*>(hidden);
+  a.w = reinterpret_cast<const uint16_t*>(weight);
+  a.N = n_rows;
+  a.H = hidden_size;
+  a.V = vocab;
+  a.hs = h_stride;
+  a.ws = w_stride;
+  a.targets = targets;
+  a.c2 = float(1.4426950408889634 / double(temperature));
+  a.logprob = logprob;
+  a.entropy = entropy;
+  a.saved = saved;
+  a.nsize = nucleus_size;
+  a.flags = flags;
+  return hip_status(rlk::launch_fused_fwd(a, workspace, reinterpret_cast<hipStream_t>(stream)),
+                    "rlk_logprob_fused_linear launch");
+}
+
+size_t rlk_logprob_fused_linear_bwd_workspace_size(int64_t n_rows, int64_t hidden_size,
+                                                   int64_t vocab, float top_p) {
+  (void)n_rows; (void)hidden_size; (void)vocab; (void)top_p;
+  return 0;
+}
+
+rlk_status rlk_logprob_fused_linear_bwd(const void* hidden, const void* weight, int64_t n_rows,
+                                        int64_t hidden_size, int64_t vocab, int64_t h_stride,
+                                        int64_t w_stride, const int64_t* targets,
+                                        const float* saved, const float* grad_logprob,
+                                        const float* grad_entropy, float temperature, float top_p,
+                                        int32_t top_k, void* grad_hidden, float* grad_weight,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  (void)saved; (void)grad_logprob; (void)grad_entropy; (void)grad_hidden; (void)grad_weight;
+  (void)workspace; (void)workspace_bytes; (void)stream;
+  rlk_status s = check_sampling(temperature, top_p, top_k);
+  if (s != RLK_OK) return s;
+  s = check_fused_shapes(hidden, weight, n_rows, hidden_size, vocab, h_stride, w_stride, targets);
+  if (s != RLK_OK) return s;
+  return fail(RLK_EUNSUPPORTED, "the fused backward is not implemented yet");
 }
 
 // ------------------------------------------------------------------ GRPO loss

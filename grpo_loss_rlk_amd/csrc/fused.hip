@@ -1,25 +1,297 @@
-// Fused LM-head forward/backward (placeholder until the MFMA kernels land).
+// Fused LM head: token log-probability and entropy under softmax(h W^T / T)
+// without materialising the [N, V] logits (prime-rl v0.10.0 release notes,
+// "1. Trainer Performance": the loss is chunked torchtitan-style).
+//
+// Forward, two launches:
+//  1. fwd_tile_stats: one block per (256-vocab x 256-token) tile. bf16 MFMA
+//     (v_mfma_f32_32x32x16_bf16) accumulates z = W h^T in fp32 over the hidden
+//     dimension, K staged through double-buffered, XOR-swizzled LDS. The
+//     epilogue folds the tile's 256 logits of each token into a partial
+//     (max z, sum 2^x, sum 2^x x) with x = (z - max) log2(e)/T, and the block
+//     whose vocabulary slice holds a token's target writes that target logit.
+//  2. fwd_merge: per token, the ceil(V/256) partials are merged in vocabulary
+//     order in fp64 (a fixed order that depends on V only, so results do not
+//     depend on the number of tokens or their order: the Qwen3-8B VIME
+//     consistency page, "Canonical topology strategy", combines vocabulary
+//     shards in one fixed order).
 #include <hip/hip_runtime.h>
 
-#include "../../include/rlk.h"
+#include <cmath>
 
-extern "C" {
+#include "common.h"
+#include "fused_kernels.h"
 
-size_t rlk_logprob_fused_linear_workspace_size(int64_t, int64_t, int64_t, float) { return 0; }
+namespace rlk {
 
-rlk_status rlk_logprob_fused_linear(const void*, const void*, int64_t, int64_t, int64_t, int64_t,
-                                    int64_t, const int64_t*, float, float, int32_t, float*, float*,
-                                    float*, int32_t*, uint8_t*, void*, size_t, void*) {
-  return RLK_EUNSUPPORTED;
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 256;   // vocabulary rows per block
+constexpr int kBN = 256;   // tokens per block
+constexpr int kBK = 64;    // hidden elements per stage
+constexpr int kT = 256;    // threads per block: 2 x 2 waves of 128 x 128
+constexpr int kChunks = kBK / 8;               // 16-byte chunks per staged row
+constexpr int kLoadsPerThread = kBM * kChunks / kT;   // 8 per operand
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+// LDS tile: [row][chunk], chunk index XOR-swizzled by (row & 7) so that the
+// 32 rows an MFMA fragment read touches spread over all banks.
+RLK_DEV int swz(int row, int chunk) { return row * kChunks + (chunk ^ (row & 7)); }
+
+// Stage one kBK-wide slice of `rows` rows (starting at row0, clamped to
+// [0, nrows)) of a [nrows, stride] bf16 matrix into registers.
+RLK_DEV void load_slice(uint4 (&r)[kLoadsPerThread], const uint16_t* base, int64_t row0,
+                        int64_t nrows, int64_t stride, int64_t k0) {
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) {
+    const int c = int(threadIdx.x) + i * kT;
+    const int row = c / kChunks, ch = c % kChunks;
+    const int64_t g = row0 + row;
+    if (g < nrows)
+      r[i] = *reinterpret_cast<const uint4*>(base + g * stride + k0 + ch * 8);
+    else
+      r[i] = make_uint4(0, 0, 0, 0);
+  }
 }
 
-size_t rlk_logprob_fused_linear_bwd_workspace_size(int64_t, int64_t, int64_t, float) { return 0; }
-
-rlk_status rlk_logprob_fused_linear_bwd(const void*, const void*, int64_t, int64_t, int64_t,
-                                        int64_t, int64_t, const int64_t*, const float*,
-                                        const float*, const float*, float, float, int32_t, void*,
-                                        float*, void*, size_t, void*) {
-  return RLK_EUNSUPPORTED;
+RLK_DEV void store_slice(uint4* lds, const uint4 (&r)[kLoadsPerThread]) {
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) {
+    const int c = int(threadIdx.x) + i * kT;
+    lds[swz(c / kChunks, c % kChunks)] = r[i];
+  }
 }
 
-}  // extern "C"
+// Merge of softmax partials (max m in z units, A = sum 2^x, B = sum 2^x x with
+// x in log2 units of the scaled logit). c2 = log2(e)/T.
+struct Part {
+  float m, A, B;
+};
+
+RLK_DEV Part merge_part(Part p, Part q, float c2) {
+  if (q.m == -INFINITY) return p;   // an empty partial (no valid vocabulary rows)
+  if (p.m == -INFINITY) return q;
+  const float m = fmaxf(p.m, q.m);
+  const float dp = (p.m - m) * c2, dq = (q.m - m) * c2;
+  const float sp = exp2f(dp), sq = exp2f(dq);
+  Part r;
+  r.m = m;
+  r.A = p.A * sp + q.A * sq;
+  r.B = sp * (p.B + dp * p.A) + sq * (q.B + dq * q.A);
+  return r;
+}
+
+__global__ __launch_bounds__(kT) void fwd_tile_stats(FusedFwdArgs a) {
+  __shared__ uint4 lds[2][2][kBM * kChunks];   // [buffer][A=W / B=h][swizzled tile]
+
+  const int nnt = int((a.N + kBN - 1) / kBN);
+  const int vt = int(blockIdx.x) / nnt, nt_blk = int(blockIdx.x) % nnt;
+  const int64_t v0 = int64_t(vt) * kBM, n0 = int64_t(nt_blk) * kBN;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;   // wave's 128-row vocab half / 128-token half
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = int(a.H / kBK);
+  uint4 ra[kLoadsPerThread], rb[kLoadsPerThread];
+  load_slice(ra, a.w, v0, a.V, a.ws, 0);
+  load_slice(rb, a.h, n0, a.N, a.hs, 0);
+  store_slice(lds[0][0], ra);
+  store_slice(lds[0][1], rb);
+  __syncthreads();
+
+  const int frow = lane & 31, fgrp = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) {
+      load_slice(ra, a.w, v0, a.V, a.ws, int64_t(kt + 1) * kBK);
+      load_slice(rb, a.h, n0, a.N, a.hs, int64_t(kt + 1) * kBK);
+    }
+    const uint4* As = lds[buf][0];
+    const uint4* Bs = lds[buf][1];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int ch = 2 * kk + fgrp;
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 x = As[swz(128 * wm + 32 * i + frow, ch)];
+        af[i] = __builtin_bit_cast(bf16x8, x);
+        const uint4 y = Bs[swz(128 * wn + 32 * i + frow, ch)];
+        bfr[i] = __builtin_bit_cast(bf16x8, y);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      store_slice(lds[buf ^ 1][0], ra);
+      store_slice(lds[buf ^ 1][1], rb);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: per token, fold this tile's logits ----
+  // accumulator acc[i][j][r] holds vocab row 128*wm + 32*i + 8*(r/4) + 4*fgrp + r%4
+  // and token 128*wn + 32*j + frow of the tile.
+  const float c2 = a.c2;
+  const int64_t vbase = v0 + 128 * wm;
+  const bool full = v0 + kBM <= a.V;
+  Part mine[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = vbase + 32 * i + 8 * (r >> 2) + 4 * fgrp + (r & 3);
+        if (full || row < a.V) mx = fmaxf(mx, acc[i][j][r]);
+      }
+    float A = 0.f, B = 0.f;
+    if (mx > -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = vbase + 32 * i + 8 * (r >> 2) + 4 * fgrp + (r & 3);
+          if (full || row < a.V) {
+            const float x = (acc[i][j][r] - mx) * c2;
+            const float e = exp2f(x);
+            A += e;
+            B = fmaf(e, x, B);
+          }
+        }
+    }
+    Part p{mx, A, B};
+    Part q;
+    q.m = __shfl_xor(p.m, 32, 64);
+    q.A = __shfl_xor(p.A, 32, 64);
+    q.B = __shfl_xor(p.B, 32, 64);
+    // lanes l and l^32 hold the same token: merge the lower half first
+    mine[j] = fgrp == 0 ? merge_part(p, q, c2) : merge_part(q, p, c2);
+
+    // target logit: the lane holding vocab row y of this token writes it
+    const int64_t n = n0 + 128 * wn + 32 * j + frow;
+    const int64_t y = n < a.N ? a.targets[n] : -1;
+    const int64_t rel = y - vbase;
+    const bool hit = rel >= 0 && rel < 128 && ((rel >> 2) & 1) == fgrp;
+    if (__any(hit)) {
+      const int ii = int(rel >> 5), ww = int(rel & 31);
+      const int rr = ((ww >> 3) << 2) | (ww & 3);
+      float val = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (i == ii && r == rr) val = acc[i][j][r];
+      if (hit) a.zy[n] = val;
+    }
+  }
+
+  // ---- combine the two vocab halves (wm = 0 then 1) and write partials ----
+  float* xch = reinterpret_cast<float*>(&lds[0][0][0]);   // [wn][128 tokens][3]
+  if (wm == 1 && fgrp == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 32 * j + frow;
+      xch[(wn * 128 + t) * 3 + 0] = mine[j].m;
+      xch[(wn * 128 + t) * 3 + 1] = mine[j].A;
+      xch[(wn * 128 + t) * 3 + 2] = mine[j].B;
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && fgrp == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 32 * j + frow;
+      const int64_t n = n0 + 128 * wn + t;
+      Part o{xch[(wn * 128 + t) * 3 + 0], xch[(wn * 128 + t) * 3 + 1],
+             xch[(wn * 128 + t) * 3 + 2]};
+      const Part r = merge_part(mine[j], o, c2);
+      if (n < a.N) a.part[int64_t(vt) * a.N + n] = make_float4(r.m, r.A, r.B, 0.f);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void fwd_merge(FusedFwdArgs a, int nvt) {
+  const int64_t n = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (n >= a.N) return;
+  const double c2 = double(a.c2);
+  double m = -INFINITY, A = 0.0, B = 0.0;   // B in log2 units
+  for (int vt = 0; vt < nvt; ++vt) {
+    const float4 p = a.part[int64_t(vt) * a.N + n];
+    if (double(p.x) == -INFINITY) continue;
+    const double pm = p.x;
+    if (m == -INFINITY) {
+      m = pm;
+      A = p.y;
+      B = p.z;
+      continue;
+    }
+    const double mm = pm > m ? pm : m;
+    const double d1 = (m - mm) * c2, d2 = (pm - mm) * c2;
+    const double s1 = exp2(d1), s2 = exp2(d2);
+    B = s1 * (B + d1 * A) + s2 * (double(p.z) + d2 * double(p.y));
+    A = A * s1 + double(p.y) * s2;
+    m = mm;
+  }
+  const double invT = c2 * double(kLn2);    // 1/T
+  const double lnA = log(A);
+  const double Ed = double(kLn2) * B / A;   // E_q[(z - m)/T] in nats
+  const double H = lnA - Ed;
+  const int64_t y = a.targets[n];
+  uint8_t flags = 0;
+  float lp;
+  if (y < 0 || y >= a.V) {
+    flags |= 2;
+    lp = __builtin_nanf("");
+  } else {
+    lp = float((double(a.zy[n]) - m) * invT - lnA);
+  }
+  a.logprob[n] = lp;
+  a.entropy[n] = float(H);
+  if (a.saved) {
+    a.saved[4 * n + 0] = float(m * invT + lnA);   // log Z of the scaled logits z/T
+    a.saved[4 * n + 1] = float(m * invT + Ed);    // E_q[z/T]
+    a.saved[4 * n + 2] = -INFINITY;              // no cut at top-p = 1
+    a.saved[4 * n + 3] = 0.f;
+  }
+  if (a.nsize) a.nsize[n] = int32_t(a.V);
+  if (a.flags) a.flags[n] = flags;
+}
+
+}  // namespace
+
+size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V) {
+  (void)H;
+  const int64_t nvt = (V + kBM - 1) / kBM;
+  return size_t(nvt * N) * 16 + size_t(N) * 4 + 512;
+}
+
+hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream) {
+  if (a.N == 0) return hipSuccess;
+  const int64_t nvt = (a.V + kBM - 1) / kBM, nnt = (a.N + kBN - 1) / kBN;
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.part = reinterpret_cast<float4*>(ws);
+  a.zy = reinterpret_cast<float*>(ws + (size_t(nvt * a.N) * 16 + 255) / 256 * 256);
+  hipLaunchKernelGGL(fwd_tile_stats, dim3(unsigned(nvt * nnt)), dim3(kT), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fwd_merge, dim3(unsigned((a.N + 255) / 256)), dim3(256), 0, stream, a,
+                     int(nvt));
+  return hipGetLastError();
+}
+
+}  // namespace rlk

@@ -1,0 +1,28 @@
+// Internal launch interfaces of the fused LM-head kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rlk {
+
+struct FusedFwdArgs {
+  const uint16_t* h;       // bf16 [N, hs]
+  const uint16_t* w;       // bf16 [V, ws]
+  int64_t N, H, V, hs, ws;
+  const int64_t* targets;  // [N]
+  float c2;                // log2(e) / T
+  float* logprob;          // [N]
+  float* entropy;          // [N]
+  float* saved;            // [N, 4] nullable
+  int32_t* nsize;          // [N] nullable
+  uint8_t* flags;          // [N] nullable
+  float4* part;            // workspace: [ceil(V/256), N] tile partials
+  float* zy;               // workspace: [N] target logits
+};
+
+size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V);
+hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream);
+
+}  // namespace rlk

@@ -31,3 +31,13 @@ def assert_close_rows(got, want, atol, rtol=0.0, what=""):
         bad = np.flatnonzero(~ok)[:8]
         raise AssertionError(f"{what}: {(~ok).sum()} rows off; first {bad.tolist()}: "
                              f"got {got[bad].tolist()} want {want[bad].tolist()}")
+
+
+def bits_equal(a, b) -> bool:
+    """Bitwise equality of two tensors (NaNs with equal payloads compare equal)."""
+    import torch
+    if a.dtype != b.dtype or a.shape != b.shape:
+        return False
+    if a.dtype in (torch.float32, torch.int32):
+        return torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
+    return torch.equal(a, b)
