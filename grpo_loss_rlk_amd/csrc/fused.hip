@@ -84,65 +84,13 @@ RLK_DEV Part merge_part(Part p, Part q, float c2) {
   return r;
 }
 
-__global__ __launch_bounds__(kT) void fwd_tile_stats(FusedFwdArgs a) {
-  __shared__ uint4 lds[2][2][kBM * kChunks];   // [buffer][A=W / B=h][swizzled tile]
-
-  const int nnt = int((a.N + kBN - 1) / kBN);
-  const int vt = int(blockIdx.x) / nnt, nt_blk = int(blockIdx.x) % nnt;
-  const int64_t v0 = int64_t(vt) * kBM, n0 = int64_t(nt_blk) * kBN;
+// Epilogue of a 256 x 256 tile: per token, fold this tile's logits into a
+// partial and write the target logit; `xch` is >= 3 KB of free LDS.
+RLK_DEV void tile_epilogue(const FusedFwdArgs& a, f32x16 (&acc)[4][4], int64_t v0, int64_t n0,
+                           int vt, float* xch) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;   // wave's 128-row vocab half / 128-token half
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nk = int(a.H / kBK);
-  uint4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-  load_slice(ra, a.w, v0, a.V, a.ws, 0);
-  load_slice(rb, a.h, n0, a.N, a.hs, 0);
-  store_slice(lds[0][0], ra);
-  store_slice(lds[0][1], rb);
-  __syncthreads();
-
+  const int wm = wid >> 1, wn = wid & 1;
   const int frow = lane & 31, fgrp = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      load_slice(ra, a.w, v0, a.V, a.ws, int64_t(kt + 1) * kBK);
-      load_slice(rb, a.h, n0, a.N, a.hs, int64_t(kt + 1) * kBK);
-    }
-    const uint4* As = lds[buf][0];
-    const uint4* Bs = lds[buf][1];
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int ch = 2 * kk + fgrp;
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 x = As[swz(128 * wm + 32 * i + frow, ch)];
-        af[i] = __builtin_bit_cast(bf16x8, x);
-        const uint4 y = Bs[swz(128 * wn + 32 * i + frow, ch)];
-        bfr[i] = __builtin_bit_cast(bf16x8, y);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      store_slice(lds[buf ^ 1][0], ra);
-      store_slice(lds[buf ^ 1][1], rb);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: per token, fold this tile's logits ----
   // accumulator acc[i][j][r] holds vocab row 128*wm + 32*i + 8*(r/4) + 4*fgrp + r%4
   // and token 128*wn + 32*j + frow of the tile.
   const float c2 = a.c2;
@@ -201,7 +149,6 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats(FusedFwdArgs a) {
   }
 
   // ---- combine the two vocab halves (wm = 0 then 1) and write partials ----
-  float* xch = reinterpret_cast<float*>(&lds[0][0][0]);   // [wn][128 tokens][3]
   if (wm == 1 && fgrp == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -223,6 +170,169 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats(FusedFwdArgs a) {
       if (n < a.N) a.part[int64_t(vt) * a.N + n] = make_float4(r.m, r.A, r.B, 0.f);
     }
   }
+}
+
+__global__ __launch_bounds__(kT) void fwd_tile_stats(FusedFwdArgs a) {
+  __shared__ uint4 lds[2][2][kBM * kChunks];   // [buffer][A=W / B=h][swizzled tile]
+
+  const int nnt = int((a.N + kBN - 1) / kBN);
+  const int vt = int(blockIdx.x) / nnt, nt_blk = int(blockIdx.x) % nnt;
+  const int64_t v0 = int64_t(vt) * kBM, n0 = int64_t(nt_blk) * kBN;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;   // wave's 128-row vocab half / 128-token half
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = int(a.H / kBK);
+  uint4 ra[kLoadsPerThread], rb[kLoadsPerThread];
+  load_slice(ra, a.w, v0, a.V, a.ws, 0);
+  load_slice(rb, a.h, n0, a.N, a.hs, 0);
+  store_slice(lds[0][0], ra);
+  store_slice(lds[0][1], rb);
+  __syncthreads();
+
+  const int frow = lane & 31, fgrp = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) {
+      load_slice(ra, a.w, v0, a.V, a.ws, int64_t(kt + 1) * kBK);
+      load_slice(rb, a.h, n0, a.N, a.hs, int64_t(kt + 1) * kBK);
+    }
+    const uint4* As = lds[buf][0];
+    const uint4* Bs = lds[buf][1];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int ch = 2 * kk + fgrp;
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 x = As[swz(128 * wm + 32 * i + frow, ch)];
+        af[i] = __builtin_bit_cast(bf16x8, x);
+        const uint4 y = Bs[swz(128 * wn + 32 * i + frow, ch)];
+        bfr[i] = __builtin_bit_cast(bf16x8, y);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      store_slice(lds[buf ^ 1][0], ra);
+      store_slice(lds[buf ^ 1][1], rb);
+    }
+    __syncthreads();
+  }
+
+  tile_epilogue(a, acc, v0, n0, vt, reinterpret_cast<float*>(&lds[0][0][0]));
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined tile kernel. Each 64-wide slice of W and h goes global ->
+// registers -> LDS: the loads of slice s+1 are issued before slice s is
+// multiplied and written to the other LDS buffer after it, one barrier per
+// slice. Inside a slice the fragments of k-step kk+1 are read from LDS while
+// the 16 MFMAs of k-step kk run. Rows past the end are clamped to the last
+// row (no branches in the load path); the epilogue masks their results.
+// ---------------------------------------------------------------------------
+// Per-thread element offsets (row * stride + chunk * 8) of the 8 chunks this
+// thread stages from a [nrows, stride] matrix, rows clamped to the last one.
+// 32-bit: the host routes matrices of 2^31 elements or more elsewhere.
+RLK_DEV void slice_offsets(uint32_t (&off)[kLoadsPerThread], int64_t row0, int64_t nrows,
+                           int64_t stride) {
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) {
+    const int c = int(threadIdx.x) + i * kT;
+    int64_t g = row0 + c / kChunks;
+    g = g < nrows ? g : nrows - 1;
+    off[i] = uint32_t(g * stride + (c % kChunks) * 8);
+  }
+}
+
+RLK_DEV void load_slice_off(uint4 (&r)[kLoadsPerThread], const uint16_t* base_k,
+                            const uint32_t (&off)[kLoadsPerThread]) {
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i)
+    r[i] = *reinterpret_cast<const uint4*>(base_k + off[i]);
+}
+
+RLK_DEV void read_frags(bf16x8 (&af)[4], bf16x8 (&bfr)[4], const uint4* As, const uint4* Bs,
+                        int wm, int wn, int frow, int ch) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    af[i] = __builtin_bit_cast(bf16x8, As[swz(128 * wm + 32 * i + frow, ch)]);
+    bfr[i] = __builtin_bit_cast(bf16x8, Bs[swz(128 * wn + 32 * i + frow, ch)]);
+  }
+}
+
+RLK_DEV void mma_stage(f32x16 (&acc)[4][4], const uint4* As, const uint4* Bs, int wm, int wn,
+                       int frow, int fgrp) {
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  read_frags(a0, b0, As, Bs, wm, wn, frow, fgrp);
+#pragma unroll
+  for (int kk = 0; kk < kBK / 16; kk += 2) {
+    read_frags(a1, b1, As, Bs, wm, wn, frow, 2 * (kk + 1) + fgrp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+    if (kk + 2 < kBK / 16) read_frags(a0, b0, As, Bs, wm, wn, frow, 2 * (kk + 2) + fgrp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kT) void fwd_tile_stats_pipe(FusedFwdArgs a) {
+  __shared__ uint4 LA[2][kBM * kChunks], LB[2][kBN * kChunks];
+
+  const int nnt = int((a.N + kBN - 1) / kBN);
+  const int vt = int(blockIdx.x) / nnt, nt_blk = int(blockIdx.x) % nnt;
+  const int64_t v0 = int64_t(vt) * kBM, n0 = int64_t(nt_blk) * kBN;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1, frow = lane & 31, fgrp = lane >> 5;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = int(a.H / kBK);
+  uint32_t oa[kLoadsPerThread], ob[kLoadsPerThread];
+  slice_offsets(oa, v0, a.V, a.ws);
+  slice_offsets(ob, n0, a.N, a.hs);
+  uint4 ra[kLoadsPerThread], rb[kLoadsPerThread];
+  load_slice_off(ra, a.w, oa);
+  load_slice_off(rb, a.h, ob);
+  store_slice(LA[0], ra);
+  store_slice(LB[0], rb);
+  __syncthreads();
+
+  for (int s = 0; s + 1 < nk; ++s) {
+    const int buf = s & 1;
+    // slice s+1 in flight while slice s is multiplied
+    load_slice_off(ra, a.w + int64_t(s + 1) * kBK, oa);
+    load_slice_off(rb, a.h + int64_t(s + 1) * kBK, ob);
+    mma_stage(acc, LA[buf], LB[buf], wm, wn, frow, fgrp);
+    store_slice(LA[buf ^ 1], ra);
+    store_slice(LB[buf ^ 1], rb);
+    __syncthreads();
+  }
+  mma_stage(acc, LA[(nk - 1) & 1], LB[(nk - 1) & 1], wm, wn, frow, fgrp);
+  __syncthreads();
+  tile_epilogue(a, acc, v0, n0, vt, reinterpret_cast<float*>(&LA[0][0]));
 }
 
 __global__ __launch_bounds__(256) void fwd_merge(FusedFwdArgs a, int nvt) {
@@ -286,7 +396,10 @@ hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream)
   char* ws = reinterpret_cast<char*>(workspace);
   a.part = reinterpret_cast<float4*>(ws);
   a.zy = reinterpret_cast<float*>(ws + (size_t(nvt * a.N) * 16 + 255) / 256 * 256);
-  hipLaunchKernelGGL(fwd_tile_stats, dim3(unsigned(nvt * nnt)), dim3(kT), 0, stream, a);
+  if (a.V * a.ws < (int64_t(1) << 31) && a.N * a.hs < (int64_t(1) << 31))
+    hipLaunchKernelGGL(fwd_tile_stats_pipe, dim3(unsigned(nvt * nnt)), dim3(kT), 0, stream, a);
+  else
+    hipLaunchKernelGGL(fwd_tile_stats, dim3(unsigned(nvt * nnt)), dim3(kT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fwd_merge, dim3(unsigned((a.N + 255) / 256)), dim3(256), 0, stream, a,
