@@ -335,6 +335,179 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats_pipe(FusedFwdArgs a) {
   tile_epilogue(a, acc, v0, n0, vt, reinterpret_cast<float*>(&LA[0][0]));
 }
 
+// ---------------------------------------------------------------------------
+// LDS-DMA tile kernel. 32-wide hidden slices ("stages") of W and h are copied
+// global -> LDS by global_load_lds_dwordx4 (no register staging), four stages
+// resident: while stage s is multiplied, stage s+1 is read into fragment
+// registers and stages s+2..s+4 are in flight, so about 96 KB per CU is
+// outstanding to cover L2/MALL latency. One barrier per stage, preceded by
+// an explicit vmcnt wait for this wave's copies of the next stage (the copies
+// are invisible to the compiler's wait-count tracking, so every wait on them
+// is written out here). Byte offsets are 32-bit: matrices of 2^32 bytes or
+// more take fwd_tile_stats.
+// ---------------------------------------------------------------------------
+constexpr int kDK = 32;                     // hidden elements per stage
+constexpr int kDStages = 4;                 // stages resident in LDS
+constexpr int kDChunks = kDK / 8;           // 16-byte chunks per staged row
+constexpr int kDOpSlots = kBM * kDChunks;   // 16-byte slots per operand per stage
+constexpr int kDLoads = kDOpSlots / kT;     // copies per thread per operand per stage
+constexpr int kDVm = 2 * kDLoads;           // vmcnt of one stage (W and h)
+
+// Physical chunk of (row, logical chunk): XOR with a 2-bit hash of the row so
+// that both 8- and 16-lane groups of a 32-row fragment read hit distinct
+// 16-byte bank groups.
+RLK_DEV int dswz(int row) { return ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1); }
+RLK_DEV int dslot(int row, int lc) { return row * kDChunks + (lc ^ dswz(row)); }
+
+// Byte offsets of this thread's copies: copy j of wave w fills slots
+// [64 q, 64 q + 64) with q = w * kDLoads + j, lane l writing slot 64 q + l.
+RLK_DEV void dma_offsets(uint32_t (&off)[kDLoads], int64_t row0, int64_t nrows, int64_t stride) {
+  const int w = int(threadIdx.x) >> 6, lane = int(threadIdx.x) & 63;
+#pragma unroll
+  for (int j = 0; j < kDLoads; ++j) {
+    const int slot = (w * kDLoads + j) * 64 + lane;
+    const int row = slot / kDChunks, lc = (slot % kDChunks) ^ dswz(row);
+    int64_t g = row0 + row;
+    g = g < nrows ? g : nrows - 1;
+    off[j] = uint32_t((g * stride + lc * 8) * 2);
+  }
+}
+
+RLK_DEV void dma_issue(uint4* lds_op, const uint16_t* gbase, const uint32_t (&off)[kDLoads]) {
+  const int w = int(threadIdx.x) >> 6;
+#pragma unroll
+  for (int j = 0; j < kDLoads; ++j) {
+    const uint32_t m0 = uint32_t(reinterpret_cast<uintptr_t>(lds_op + (w * kDLoads + j) * 64));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(off[j]), "s"(gbase)
+                 : "memory", "m0");
+  }
+}
+
+// Wait until at most N of this wave's vector-memory operations (here: LDS
+// copies) are outstanding and its LDS reads are done, then barrier.
+template <int N>
+RLK_DEV void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+struct Frags {
+  bf16x8 a[2][4], b[2][4];   // [k-step][32-row group]
+};
+
+// Fragment rows 128 wm + 32 x + frow: the swizzle hash depends on row & 15
+// = frow & 15 only, so a read's address is a per-lane part (one per k-step)
+// plus a uniform part.
+struct FragAddr {
+  uint32_t lane_off[2];   // bytes, per k-step
+  uint32_t a_off, b_off;  // bytes: the wave's W rows and h rows inside a stage
+};
+
+RLK_DEV FragAddr frag_addr(int wm, int wn, int frow, int fgrp) {
+  FragAddr f;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) f.lane_off[kk] = uint32_t(dslot(frow, 2 * kk + fgrp)) * 16u;
+  f.a_off = uint32_t(128 * wm * kDChunks * 16);
+  f.b_off = uint32_t(kDOpSlots * 16 + 128 * wn * kDChunks * 16);
+  return f;
+}
+
+RLK_DEV void read_frag(Frags& f, int r, const char* stage, const FragAddr& fa) {
+  const int kk = r >> 3, x = r & 7;
+  if (x < 4)
+    f.a[kk][x] = *reinterpret_cast<const bf16x8*>(stage + fa.a_off + fa.lane_off[kk] +
+                                                  x * 32 * kDChunks * 16);
+  else
+    f.b[kk][x - 4] = *reinterpret_cast<const bf16x8*>(stage + fa.b_off + fa.lane_off[kk] +
+                                                      (x - 4) * 32 * kDChunks * 16);
+}
+
+// The 32 MFMAs of one stage; with kRead the 16 fragment reads of the next
+// stage are interleaved, one after every second MFMA.
+template <bool kRead>
+RLK_DEV void stage_mma(f32x16 (&acc)[4][4], const Frags& cur, Frags& nxt, const char* stage,
+                       const FragAddr& fa) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[kk][i], cur.b[kk][j], acc[i][j],
+                                                            0, 0, 0);
+        const int m = kk * 16 + i * 4 + j;
+        if (kRead && (m & 1)) {
+          read_frag(nxt, m >> 1, stage, fa);
+          // keep the issue order as written: the scheduler would otherwise
+          // sink the reads to their uses in the next stage
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+}
+
+constexpr int kDStageBytes = 2 * kDOpSlots * 16;   // 32 KB: W then h
+
+__global__ __launch_bounds__(kT) void fwd_tile_stats_dma(FusedFwdArgs a) {
+  __shared__ uint4 smem[kDStages][2][kDOpSlots];   // [stage][W, h][slot]: 128 KB
+  const char* sbase = reinterpret_cast<const char*>(&smem[0][0][0]);
+
+  const int nnt = int((a.N + kBN - 1) / kBN);
+  const int vt = int(blockIdx.x) / nnt, nt_blk = int(blockIdx.x) % nnt;
+  const int64_t v0 = int64_t(vt) * kBM, n0 = int64_t(nt_blk) * kBN;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1, frow = lane & 31, fgrp = lane >> 5;
+  const FragAddr fa = frag_addr(wm, wn, frow, fgrp);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // nk is even (the hidden size is a multiple of 64). Every step issues one
+  // stage of copies, past the end a repeat of the last stage into the buffer
+  // no later step reads, so the wait counts are the same at every step.
+  const int nk = int(a.H / kDK);
+  uint32_t oa[kDLoads], ob[kDLoads];
+  dma_offsets(oa, v0, a.V, a.ws);
+  dma_offsets(ob, n0, a.N, a.hs);
+#pragma unroll
+  for (int t = 0; t < kDStages; ++t) {
+    const int64_t k0 = int64_t(t < nk ? t : nk - 1) * kDK;
+    dma_issue(smem[t][0], a.w + k0, oa);
+    dma_issue(smem[t][1], a.h + k0, ob);
+  }
+  vm_wait_barrier<(kDStages - 1) * kDVm>();
+  Frags f0, f1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) read_frag(f0, r, sbase, fa);
+
+  // Step s: stage s (fragments in registers) is multiplied while stage s+1
+  // is read; after the barrier (stage s+1 landed, stage s's buffer free)
+  // stage s+4 is copied into stage s's buffer.
+  for (int s = 0; s < nk; s += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = s + h;
+      vm_wait_barrier<(kDStages - 2) * kDVm>();
+      const int b = t % kDStages;
+      const int64_t k0 = int64_t(t + kDStages < nk ? t + kDStages : nk - 1) * kDK;
+      dma_issue(smem[b][0], a.w + k0, oa);
+      dma_issue(smem[b][1], a.h + k0, ob);
+      const char* nxt = sbase + ((t + 1) % kDStages) * kDStageBytes;
+      if (h == 0)
+        stage_mma<true>(acc, f0, f1, nxt, fa);
+      else
+        stage_mma<true>(acc, f1, f0, nxt, fa);
+    }
+  }
+  vm_wait_barrier<0>();
+  tile_epilogue(a, acc, v0, n0, vt, reinterpret_cast<float*>(&smem[0][0][0]));
+}
+
 __global__ __launch_bounds__(256) void fwd_merge(FusedFwdArgs a, int nvt) {
   const int64_t n = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (n >= a.N) return;
@@ -396,8 +569,8 @@ hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream)
   char* ws = reinterpret_cast<char*>(workspace);
   a.part = reinterpret_cast<float4*>(ws);
   a.zy = reinterpret_cast<float*>(ws + (size_t(nvt * a.N) * 16 + 255) / 256 * 256);
-  if (a.V * a.ws < (int64_t(1) << 31) && a.N * a.hs < (int64_t(1) << 31))
-    hipLaunchKernelGGL(fwd_tile_stats_pipe, dim3(unsigned(nvt * nnt)), dim3(kT), 0, stream, a);
+  if (a.V * a.ws < (int64_t(1) << 31) && a.N * a.hs < (int64_t(1) << 31) && a.H % kDK == 0)
+    hipLaunchKernelGGL(fwd_tile_stats_dma, dim3(unsigned(nvt * nnt)), dim3(kT), 0, stream, a);
   else
     hipLaunchKernelGGL(fwd_tile_stats, dim3(unsigned(nvt * nnt)), dim3(kT), 0, stream, a);
   hipError_t e = hipGetLastError();
