@@ -337,17 +337,18 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats_pipe(FusedFwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // LDS-DMA tile kernel. 32-wide hidden slices ("stages") of W and h are copied
-// global -> LDS by global_load_lds_dwordx4 (no register staging), four stages
-// resident: while stage s is multiplied, stage s+1 is read into fragment
-// registers and stages s+2..s+4 are in flight, so about 96 KB per CU is
-// outstanding to cover L2/MALL latency. One barrier per stage, preceded by
-// an explicit vmcnt wait for this wave's copies of the next stage (the copies
-// are invisible to the compiler's wait-count tracking, so every wait on them
-// is written out here). Byte offsets are 32-bit: matrices of 2^32 bytes or
-// more take fwd_tile_stats.
+// global -> LDS by global_load_lds_dwordx4 (no register staging). Five stage
+// buffers (160 KB): while stage s is multiplied, stage s+1 is read into
+// fragment registers and up to three later stages are in flight. Copies are
+// issued two stages at a time (s+4 and s+5 at even steps), interleaved, so
+// the two 64-byte halves of each 128-byte line of a row are requested
+// together. One barrier per stage, preceded by an explicit vmcnt wait for
+// this wave's copies of the next stage (the copies are invisible to the
+// compiler's wait-count tracking, so every wait on them is written out here).
+// Byte offsets are 32-bit: matrices of 2^32 bytes or more take fwd_tile_stats.
 // ---------------------------------------------------------------------------
 constexpr int kDK = 32;                     // hidden elements per stage
-constexpr int kDStages = 4;                 // stages resident in LDS
+constexpr int kDStages = 5;                 // stage buffers resident in LDS
 constexpr int kDChunks = kDK / 8;           // 16-byte chunks per staged row
 constexpr int kDOpSlots = kBM * kDChunks;   // 16-byte slots per operand per stage
 constexpr int kDLoads = kDOpSlots / kT;     // copies per thread per operand per stage
@@ -373,15 +374,22 @@ RLK_DEV void dma_offsets(uint32_t (&off)[kDLoads], int64_t row0, int64_t nrows, 
   }
 }
 
-RLK_DEV void dma_issue(uint4* lds_op, const uint16_t* gbase, const uint32_t (&off)[kDLoads]) {
+// Copies of stages t and t+1 (64-byte halves of the same rows), interleaved.
+RLK_DEV void dma_issue_pair(uint4* lds_t, uint4* lds_t1, const uint16_t* gbase_t,
+                            const uint32_t (&off)[kDLoads]) {
   const int w = int(threadIdx.x) >> 6;
+  const uint16_t* gbase_t1 = gbase_t + kDK;
 #pragma unroll
   for (int j = 0; j < kDLoads; ++j) {
-    const uint32_t m0 = uint32_t(reinterpret_cast<uintptr_t>(lds_op + (w * kDLoads + j) * 64));
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(off[j]), "s"(gbase)
-                 : "memory", "m0");
+    const uint32_t m0a = uint32_t(reinterpret_cast<uintptr_t>(lds_t + (w * kDLoads + j) * 64));
+    const uint32_t m0b = uint32_t(reinterpret_cast<uintptr_t>(lds_t1 + (w * kDLoads + j) * 64));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %4"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(m0a)), "s"(__builtin_amdgcn_readfirstlane(m0b)),
+          "v"(off[j]), "s"(gbase_t), "s"(gbase_t1)
+        : "memory", "m0");
   }
 }
 
@@ -424,7 +432,8 @@ RLK_DEV void read_frag(Frags& f, int r, const char* stage, const FragAddr& fa) {
 }
 
 // The 32 MFMAs of one stage; with kRead the 16 fragment reads of the next
-// stage are interleaved, one after every second MFMA.
+// stage are interleaved with the first 16 MFMAs, so they have landed before
+// the barrier that ends the stage.
 template <bool kRead>
 RLK_DEV void stage_mma(f32x16 (&acc)[4][4], const Frags& cur, Frags& nxt, const char* stage,
                        const FragAddr& fa) {
@@ -437,8 +446,8 @@ RLK_DEV void stage_mma(f32x16 (&acc)[4][4], const Frags& cur, Frags& nxt, const 
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[kk][i], cur.b[kk][j], acc[i][j],
                                                             0, 0, 0);
         const int m = kk * 16 + i * 4 + j;
-        if (kRead && (m & 1)) {
-          read_frag(nxt, m >> 1, stage, fa);
+        if (kRead && m < 16) {
+          read_frag(nxt, m, stage, fa);
           // keep the issue order as written: the scheduler would otherwise
           // sink the reads to their uses in the next stage
           __builtin_amdgcn_sched_barrier(0);
@@ -447,13 +456,31 @@ RLK_DEV void stage_mma(f32x16 (&acc)[4][4], const Frags& cur, Frags& nxt, const 
 }
 
 constexpr int kDStageBytes = 2 * kDOpSlots * 16;   // 32 KB: W then h
+constexpr int kXcds = 8;      // workgroups are dealt to the XCDs round-robin
+constexpr int kGroupVt = 8;   // vocabulary tiles per group of the tile order
+
+// Tile of a workgroup. Each XCD takes a contiguous range of the tile order,
+// so its L2 serves one region of W and h; within the order, groups of
+// kGroupVt vocabulary tiles sweep all token tiles with the vocabulary tile
+// fastest, so the 32 workgroups an XCD runs at once cover about 8 W tiles
+// and 4 h tiles.
+RLK_DEV void tile_of_block(int nvt, int nnt, int& vt, int& nt) {
+  const int T = nvt * nnt, b = int(blockIdx.x);
+  const int x = b % kXcds, q = T / kXcds, r = T % kXcds;
+  const int lid = x * q + (x < r ? x : r) + b / kXcds;
+  const int grp = lid / (kGroupVt * nnt), rem = lid % (kGroupVt * nnt);
+  const int gv = kGroupVt < nvt - grp * kGroupVt ? kGroupVt : nvt - grp * kGroupVt;
+  vt = grp * kGroupVt + rem % gv;
+  nt = rem / gv;
+}
 
 __global__ __launch_bounds__(kT) void fwd_tile_stats_dma(FusedFwdArgs a) {
   __shared__ uint4 smem[kDStages][2][kDOpSlots];   // [stage][W, h][slot]: 128 KB
   const char* sbase = reinterpret_cast<const char*>(&smem[0][0][0]);
 
   const int nnt = int((a.N + kBN - 1) / kBN);
-  const int vt = int(blockIdx.x) / nnt, nt_blk = int(blockIdx.x) % nnt;
+  int vt, nt_blk;
+  tile_of_block(int(gridDim.x) / nnt, nnt, vt, nt_blk);
   const int64_t v0 = int64_t(vt) * kBM, n0 = int64_t(nt_blk) * kBN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid >> 1, wn = wid & 1, frow = lane & 31, fgrp = lane >> 5;
@@ -467,42 +494,34 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats_dma(FusedFwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // nk is even (the hidden size is a multiple of 64). Every step issues one
-  // stage of copies, past the end a repeat of the last stage into the buffer
-  // no later step reads, so the wait counts are the same at every step.
+  // nk is even (the hidden size is a multiple of 64). Copies past the end
+  // repeat the last stage into buffers no later step reads, so the wait
+  // counts are the same at every step.
   const int nk = int(a.H / kDK);
   uint32_t oa[kDLoads], ob[kDLoads];
   dma_offsets(oa, v0, a.V, a.ws);
   dma_offsets(ob, n0, a.N, a.hs);
-#pragma unroll
-  for (int t = 0; t < kDStages; ++t) {
-    const int64_t k0 = int64_t(t < nk ? t : nk - 1) * kDK;
-    dma_issue(smem[t][0], a.w + k0, oa);
-    dma_issue(smem[t][1], a.h + k0, ob);
-  }
-  vm_wait_barrier<(kDStages - 1) * kDVm>();
+  auto issue_pair = [&](int t) __attribute__((always_inline)) {   // stages t, t+1 (t even)
+    const int64_t k0 = int64_t(t < nk ? t : nk - 2) * kDK;
+    dma_issue_pair(smem[t % kDStages][0], smem[(t + 1) % kDStages][0], a.w + k0, oa);
+    dma_issue_pair(smem[t % kDStages][1], smem[(t + 1) % kDStages][1], a.h + k0, ob);
+  };
+  issue_pair(0);
+  issue_pair(2);
+  vm_wait_barrier<3 * kDVm>();
   Frags f0, f1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) read_frag(f0, r, sbase, fa);
 
   // Step s: stage s (fragments in registers) is multiplied while stage s+1
-  // is read; after the barrier (stage s+1 landed, stage s's buffer free)
-  // stage s+4 is copied into stage s's buffer.
+  // is read. Even s: after the barrier (stage s+1 landed; stages s-1 and s
+  // consumed) stages s+4 and s+5 are copied into the buffers of s-1 and s.
   for (int s = 0; s < nk; s += 2) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = s + h;
-      vm_wait_barrier<(kDStages - 2) * kDVm>();
-      const int b = t % kDStages;
-      const int64_t k0 = int64_t(t + kDStages < nk ? t + kDStages : nk - 1) * kDK;
-      dma_issue(smem[b][0], a.w + k0, oa);
-      dma_issue(smem[b][1], a.h + k0, ob);
-      const char* nxt = sbase + ((t + 1) % kDStages) * kDStageBytes;
-      if (h == 0)
-        stage_mma<true>(acc, f0, f1, nxt, fa);
-      else
-        stage_mma<true>(acc, f1, f0, nxt, fa);
-    }
+    vm_wait_barrier<2 * kDVm>();   // in flight: s+2, s+3
+    issue_pair(s + 4);
+    stage_mma<true>(acc, f0, f1, sbase + ((s + 1) % kDStages) * kDStageBytes, fa);
+    vm_wait_barrier<3 * kDVm>();   // in flight: s+3, s+4, s+5
+    stage_mma<true>(acc, f1, f0, sbase + ((s + 2) % kDStages) * kDStageBytes, fa);
   }
   vm_wait_barrier<0>();
   tile_epilogue(a, acc, v0, n0, vt, reinterpret_cast<float*>(&smem[0][0][0]));
