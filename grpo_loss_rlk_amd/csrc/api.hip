@@ -55,6 +55,11 @@ rlk_status check_workspace(const void* ws, size_t have, size_t need) {
 }
 
 constexpr int64_t kMaxVocab = int64_t(1) << 24;
+// Fused path: the tile GEMM addresses 256 rows of an operand with 32-bit byte
+// offsets, so row lengths (strides, padded vocabulary and token counts of the
+// transposed backward operands) stay below 2^23 elements.
+constexpr int64_t kMaxStride = int64_t(1) << 23;
+constexpr int64_t kMaxFusedRows = int64_t(1) << 23;
 
 }  // namespace
 
@@ -146,6 +151,10 @@ rlk_status check_fused_shapes(const void* hidden, const void* weight, int64_t N,
   if (hs < H || ws < H || hs % 8 != 0 || ws % 8 != 0)
     return fail(RLK_EINVAL, "strides (h %lld, w %lld) must be >= hidden_size and multiples of 8",
                 (long long)hs, (long long)ws);
+  if (hs >= kMaxStride || ws >= kMaxStride)
+    return fail(RLK_EINVAL, "strides (h %lld, w %lld) must be below 2^23", (long long)hs,
+                (long long)ws);
+  if (N >= kMaxFusedRows) return fail(RLK_EINVAL, "n_rows=%lld must be below 2^23", (long long)N);
   if (N == 0) return RLK_OK;
   if (!hidden || !weight || !targets)
     return fail(RLK_EINVAL, "hidden, weight and targets are required");
@@ -204,8 +213,9 @@ rlk_status rlk_logprob_fused_linear(const void* hidden, const void* weight, int6
 
 size_t rlk_logprob_fused_linear_bwd_workspace_size(int64_t n_rows, int64_t hidden_size,
                                                    int64_t vocab, float top_p) {
-  (void)n_rows; (void)hidden_size; (void)vocab; (void)top_p;
-  return 0;
+  (void)top_p;
+  if (n_rows < 0 || hidden_size < 1 || vocab < 1) return 0;
+  return rlk::fused_bwd_workspace(n_rows, hidden_size, vocab);
 }
 
 rlk_status rlk_logprob_fused_linear_bwd(const void* hidden, const void* weight, int64_t n_rows,
@@ -215,13 +225,43 @@ rlk_status rlk_logprob_fused_linear_bwd(const void* hidden, const void* weight, 
                                         const float* grad_entropy, float temperature, float top_p,
                                         int32_t top_k, void* grad_hidden, float* grad_weight,
                                         void* workspace, size_t workspace_bytes, void* stream) {
-  (void)saved; (void)grad_logprob; (void)grad_entropy; (void)grad_hidden; (void)grad_weight;
-  (void)workspace; (void)workspace_bytes; (void)stream;
   rlk_status s = check_sampling(temperature, top_p, top_k);
   if (s != RLK_OK) return s;
   s = check_fused_shapes(hidden, weight, n_rows, hidden_size, vocab, h_stride, w_stride, targets);
   if (s != RLK_OK) return s;
-  return fail(RLK_EUNSUPPORTED, "the fused backward is not implemented yet");
+  if (top_p < 1.f)
+    return fail(RLK_EUNSUPPORTED, "the fused backward supports top_p = 1 only");
+  if (vocab >= kMaxFusedRows)
+    return fail(RLK_EINVAL, "vocab=%lld must be below 2^23 for the backward", (long long)vocab);
+  if (!grad_weight) return fail(RLK_EINVAL, "grad_weight is required");
+  if (!aligned(grad_weight, 4)) return fail(RLK_EINVAL, "grad_weight must be 4-byte aligned");
+  if (n_rows > 0) {
+    if (!saved || !grad_hidden) return fail(RLK_EINVAL, "saved and grad_hidden are required");
+    if (!aligned(saved, 4) || !aligned(grad_hidden, 2) || !aligned(grad_logprob, 4) ||
+        !aligned(grad_entropy, 4))
+      return fail(RLK_EINVAL, "an array is not naturally aligned");
+  }
+  s = check_workspace(workspace, workspace_bytes,
+                      rlk_logprob_fused_linear_bwd_workspace_size(n_rows, hidden_size, vocab,
+                                                                  top_p));
+  if (s != RLK_OK) return s;
+  rlk::FusedBwdArgs a{};
+  a.h = reinterpret_cast<const uint16_t*>(hidden);
+  a.w = reinterpret_cast<const uint16_t*>(weight);
+  a.N = n_rows;
+  a.H = hidden_size;
+  a.V = vocab;
+  a.hs = h_stride;
+  a.ws = w_stride;
+  a.targets = targets;
+  a.saved = saved;
+  a.g_lp = grad_logprob;
+  a.g_H = grad_entropy;
+  a.inv_t = float(1.0 / double(temperature));
+  a.dh = reinterpret_cast<uint16_t*>(grad_hidden);
+  a.dW = grad_weight;
+  return hip_status(rlk::launch_fused_bwd(a, workspace, reinterpret_cast<hipStream_t>(stream)),
+                    "rlk_logprob_fused_linear_bwd launch");
 }
 
 // ------------------------------------------------------------------ GRPO loss

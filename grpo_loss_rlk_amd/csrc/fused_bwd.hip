@@ -1,0 +1,288 @@
+// Fused LM head, backward by chunk recompute (prime-rl v0.10.0 release
+// notes, "1. Trainer Performance": the chunked loss recomputes the logits of
+// a vocabulary chunk instead of storing them).
+//
+// With z = h W^T, x = z/T, q = exp(x - log Z) and the forward's saved
+// statistics (log Z and E_q[x] per token), the gradient with respect to the
+// logits is
+//   G[n,i] = (1/T) [ g_lp (delta_{i,y} - q_i) - g_H q_i (x_i - E_q[x]) ],
+// and grad_hidden = G W, grad_weight = G^T h. Per vocabulary chunk c of
+// kBwdChunk rows, in a fixed chunk order:
+//   1. bwd_g_tile:  S_c = W_c h^T on MFMA; the epilogue forms G_c in bf16 and
+//      stores it twice, as [N, C] (token rows) and as [C, N] (vocabulary rows),
+//      zero-padded, so that both products below read K-contiguous operands.
+//   2. bwd_dh_tile: dh (+)= G_c W_c, with W^T (transposed once per call) as the
+//      K-contiguous operand; fp32 partial sums across chunks, bf16 at the end.
+//   3. bwd_dw_tile: dW_c = G_c^T h, with h^T (transposed once per call).
+// All three are the tile GEMM of mfma_gemm.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "common.h"
+#include "fused_kernels.h"
+#include "mfma_gemm.h"
+
+namespace rlk {
+
+namespace {
+
+using gemm::f32x16;
+constexpr int kTile = gemm::kTile;
+constexpr int kT = gemm::kThreads;
+constexpr float kLog2e = 1.4426950408889634f;
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+RLK_DEV uint16_t to_bf16(float f) {   // round to nearest even; NaN stays NaN
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
+  return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// dst[c, r] = src[r, c] for c < cols, r < rows; zero for rows <= r < dst_ld.
+// One 64 x 64 block per workgroup: grid (dst_ld / 64, cols / 64).
+__global__ __launch_bounds__(256) void transpose_pad(const uint16_t* src, int64_t rows,
+                                                     int64_t src_ld, uint16_t* dst,
+                                                     int64_t dst_ld) {
+  __shared__ uint16_t t[64][66];
+  const int64_t r0 = int64_t(blockIdx.x) * 64, c0 = int64_t(blockIdx.y) * 64;
+  const int tid = threadIdx.x, row = tid >> 2, seg = tid & 3;
+  {
+    const int64_t r = r0 + row;
+    uint4 v[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    if (r < rows) {
+      const uint4* p = reinterpret_cast<const uint4*>(src + r * src_ld + c0 + seg * 16);
+      v[0] = p[0];
+      v[1] = p[1];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t x = k < 4 ? (&v[0].x)[k] : (&v[1].x)[k - 4];
+      t[row][seg * 16 + 2 * k] = uint16_t(x);
+      t[row][seg * 16 + 2 * k + 1] = uint16_t(x >> 16);
+    }
+  }
+  __syncthreads();
+  {
+    const int c = row;   // output row (input column) c0 + c, output columns r0 + seg*16 ..
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[k] = uint32_t(t[seg * 16 + 2 * k][c]) | (uint32_t(t[seg * 16 + 2 * k + 1][c]) << 16);
+    uint4* q = reinterpret_cast<uint4*>(dst + (c0 + c) * dst_ld + r0 + seg * 16);
+    q[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    q[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_f32(float* p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
+    p[i] = 0.f;
+}
+
+struct ChunkArgs {
+  int64_t c0, csz, cpad;   // chunk start, rows, rows padded to a multiple of 64
+  int64_t cap;             // row length of g_nc (chunk capacity, multiple of 64)
+  int64_t npad;            // tokens padded to a multiple of 64
+  uint16_t* g_nc;          // bf16 [N, cap]    G_c, token rows
+  uint16_t* g_cn;          // bf16 [cap, npad] G_c^T, vocabulary rows
+  const uint16_t* wt;      // bf16 [H, vpad]   W^T
+  int64_t vpad;
+  const uint16_t* ht;      // bf16 [H, npad]   h^T
+  float* dh_acc;           // fp32 [N, H] partial sums over chunks (several chunks only)
+};
+
+// S_c tile (vocabulary rows of the chunk x tokens) and its G epilogue.
+__global__ __launch_bounds__(kT) void bwd_g_tile(FusedBwdArgs a, ChunkArgs c) {
+  __shared__ gemm::Smem smem;
+  const int nvt = int((c.csz + kTile - 1) / kTile), nnt = int((a.N + kTile - 1) / kTile);
+  int vt, nt;
+  gemm::tile_of_block(nvt, nnt, vt, nt);
+  const int64_t v0 = int64_t(vt) * kTile, n0 = int64_t(nt) * kTile;
+  f32x16 acc[4][4];
+  gemm::gemm_nt_tile(acc, smem, a.w + c.c0 * a.ws, v0, c.csz, a.ws, a.h, n0, a.N, a.hs, a.H);
+
+  const float inv_t = a.inv_t;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + gemm::acc_b_row(j);
+    float lse = 0.f, eq = 0.f, glp = 0.f, gh = 0.f;
+    int64_t yl = -1;   // target relative to the chunk (-1: no lp term here)
+    if (n < a.N) {
+      lse = a.saved[4 * n + 0];
+      eq = a.saved[4 * n + 1];
+      gh = a.g_H ? a.g_H[n] : 0.f;
+      const int64_t y = a.targets[n];
+      if (y >= 0 && y < a.V) {   // a row without a valid target keeps only its entropy term
+        glp = a.g_lp ? a.g_lp[n] : 0.f;
+        yl = y - c.c0;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int64_t vb = v0 + gemm::acc_a_row(i, 4 * s);   // 4 consecutive rows vb .. vb+3
+        uint16_t gb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t v = vb + e;
+          float g = 0.f;
+          if (v < c.csz && n < a.N) {
+            const float x = acc[i][j][4 * s + e] * inv_t;
+            const float q = exp2f((x - lse) * kLog2e);
+            g = -q * fmaf(gh, x - eq, glp);
+            if (v == yl) g += glp;
+            g *= inv_t;
+          }
+          gb[e] = to_bf16(g);
+          if (v < c.cpad && n < c.npad) c.g_cn[v * c.npad + n] = gb[e];
+        }
+        if (vb < c.cpad && n < a.N) {
+          uint2 pk;
+          pk.x = uint32_t(gb[0]) | (uint32_t(gb[1]) << 16);
+          pk.y = uint32_t(gb[2]) | (uint32_t(gb[3]) << 16);
+          *reinterpret_cast<uint2*>(c.g_nc + n * c.cap + vb) = pk;
+        }
+      }
+  }
+}
+
+enum DhMode { kDhOnly = 0, kDhFirst = 1, kDhMiddle = 2, kDhLast = 3 };
+
+// dh tile (tokens x hidden columns) += G_c W_c over the chunk's vocabulary.
+template <int kMode>
+__global__ __launch_bounds__(kT) void bwd_dh_tile(FusedBwdArgs a, ChunkArgs c) {
+  __shared__ gemm::Smem smem;
+  const int nnt = int((a.N + kTile - 1) / kTile), nht = int((a.H + kTile - 1) / kTile);
+  int nt, ht;
+  gemm::tile_of_block(nnt, nht, nt, ht);
+  const int64_t n0 = int64_t(nt) * kTile, k0 = int64_t(ht) * kTile;
+  f32x16 acc[4][4];
+  gemm::gemm_nt_tile(acc, smem, c.g_nc, n0, a.N, c.cap, c.wt + c.c0, k0, a.H, c.vpad, c.cpad);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t col = k0 + gemm::acc_b_row(j);
+    if (col >= a.H) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t n = n0 + gemm::acc_a_row(i, r);
+        if (n >= a.N) continue;
+        const int64_t o = n * a.H + col;
+        const float v = acc[i][j][r];
+        if (kMode == kDhOnly) a.dh[o] = to_bf16(v);
+        if (kMode == kDhFirst) c.dh_acc[o] = v;
+        if (kMode == kDhMiddle) c.dh_acc[o] += v;
+        if (kMode == kDhLast) a.dh[o] = to_bf16(c.dh_acc[o] + v);
+      }
+  }
+}
+
+// dW tile (chunk vocabulary rows x hidden columns) = G_c^T h over all tokens.
+__global__ __launch_bounds__(kT) void bwd_dw_tile(FusedBwdArgs a, ChunkArgs c) {
+  __shared__ gemm::Smem smem;
+  const int nvt = int((c.csz + kTile - 1) / kTile), nht = int((a.H + kTile - 1) / kTile);
+  int vt, ht;
+  gemm::tile_of_block(nvt, nht, vt, ht);
+  const int64_t v0 = int64_t(vt) * kTile, k0 = int64_t(ht) * kTile;
+  f32x16 acc[4][4];
+  gemm::gemm_nt_tile(acc, smem, c.g_cn, v0, c.csz, c.npad, c.ht, k0, a.H, c.npad, c.npad);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t col = k0 + gemm::acc_b_row(j);
+    if (col >= a.H) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t v = v0 + gemm::acc_a_row(i, r);
+        if (v < c.csz) a.dW[(c.c0 + v) * a.H + col] = acc[i][j][r];
+      }
+  }
+}
+
+struct BwdLayout {
+  int64_t npad, vpad, cap, nchunks;
+  size_t off_wt, off_ht, off_gnc, off_gcn, off_acc, total;
+};
+
+BwdLayout bwd_layout(int64_t N, int64_t H, int64_t V) {
+  BwdLayout L{};
+  L.npad = round_up(N > 0 ? N : 1, 64);
+  L.vpad = round_up(V, 64);
+  L.cap = L.vpad < kBwdChunk ? L.vpad : kBwdChunk;
+  L.nchunks = (V + kBwdChunk - 1) / kBwdChunk;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  L.off_wt = take(size_t(H) * size_t(L.vpad) * 2);
+  L.off_ht = take(size_t(H) * size_t(L.npad) * 2);
+  L.off_gnc = take(size_t(N) * size_t(L.cap) * 2);
+  L.off_gcn = take(size_t(L.cap) * size_t(L.npad) * 2);
+  L.off_acc = take(L.nchunks > 1 ? size_t(N) * size_t(H) * 4 : 0);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+size_t fused_bwd_workspace(int64_t N, int64_t H, int64_t V) { return bwd_layout(N, H, V).total; }
+
+hipError_t launch_fused_bwd(const FusedBwdArgs& a, void* workspace, hipStream_t stream) {
+  if (a.N == 0) {   // no tokens: dW = 0, dh is empty
+    const int64_t n = a.V * a.H;
+    const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+    hipLaunchKernelGGL(fill_f32, dim3(unsigned(blocks)), dim3(256), 0, stream, a.dW, n);
+    return hipGetLastError();
+  }
+  const BwdLayout L = bwd_layout(a.N, a.H, a.V);
+  char* ws = reinterpret_cast<char*>(workspace);
+  ChunkArgs c{};
+  c.cap = L.cap;
+  c.npad = L.npad;
+  c.vpad = L.vpad;
+  c.g_nc = reinterpret_cast<uint16_t*>(ws + L.off_gnc);
+  c.g_cn = reinterpret_cast<uint16_t*>(ws + L.off_gcn);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + L.off_wt);
+  uint16_t* ht = reinterpret_cast<uint16_t*>(ws + L.off_ht);
+  c.wt = wt;
+  c.ht = ht;
+  c.dh_acc = reinterpret_cast<float*>(ws + L.off_acc);
+
+  hipLaunchKernelGGL(transpose_pad, dim3(unsigned(L.vpad / 64), unsigned(a.H / 64)), dim3(256), 0,
+                     stream, a.w, a.V, a.ws, wt, L.vpad);
+  hipLaunchKernelGGL(transpose_pad, dim3(unsigned(L.npad / 64), unsigned(a.H / 64)), dim3(256), 0,
+                     stream, a.h, a.N, a.hs, ht, L.npad);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int64_t nnt = (a.N + kTile - 1) / kTile, nht = (a.H + kTile - 1) / kTile;
+  for (int64_t k = 0; k < L.nchunks; ++k) {
+    c.c0 = k * kBwdChunk;
+    c.csz = a.V - c.c0 < kBwdChunk ? a.V - c.c0 : kBwdChunk;
+    c.cpad = round_up(c.csz, 64);
+    const int64_t nvt = (c.csz + kTile - 1) / kTile;
+    hipLaunchKernelGGL(bwd_g_tile, dim3(unsigned(nvt * nnt)), dim3(kT), 0, stream, a, c);
+    const dim3 gdh(unsigned(nnt * nht));
+    if (L.nchunks == 1)
+      hipLaunchKernelGGL(bwd_dh_tile<kDhOnly>, gdh, dim3(kT), 0, stream, a, c);
+    else if (k == 0)
+      hipLaunchKernelGGL(bwd_dh_tile<kDhFirst>, gdh, dim3(kT), 0, stream, a, c);
+    else if (k + 1 < L.nchunks)
+      hipLaunchKernelGGL(bwd_dh_tile<kDhMiddle>, gdh, dim3(kT), 0, stream, a, c);
+    else
+      hipLaunchKernelGGL(bwd_dh_tile<kDhLast>, gdh, dim3(kT), 0, stream, a, c);
+    hipLaunchKernelGGL(bwd_dw_tile, dim3(unsigned(nvt * nht)), dim3(kT), 0, stream, a, c);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace rlk

@@ -25,4 +25,24 @@ struct FusedFwdArgs {
 size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V);
 hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream);
 
+struct FusedBwdArgs {
+  const uint16_t* h;       // bf16 [N, hs]
+  const uint16_t* w;       // bf16 [V, ws]
+  int64_t N, H, V, hs, ws;
+  const int64_t* targets;  // [N]
+  const float* saved;      // [N, 4]: log Z of z/T, E_q[z/T], (cut), (unused)
+  const float* g_lp;       // [N] nullable (zeros)
+  const float* g_H;        // [N] nullable (zeros)
+  float inv_t;             // 1 / T
+  uint16_t* dh;            // bf16 [N, H] out
+  float* dW;               // fp32 [V, H] out
+};
+
+// Vocabulary rows per chunk of the backward: fixed, so that the summation
+// order of a row of dh does not depend on the number of rows.
+constexpr int64_t kBwdChunk = 32768;
+
+size_t fused_bwd_workspace(int64_t N, int64_t H, int64_t V);
+hipError_t launch_fused_bwd(const FusedBwdArgs& a, void* workspace, hipStream_t stream);
+
 }  // namespace rlk

@@ -1,0 +1,239 @@
+// Device-side core of the fused LM-head kernels: one 256 x 256 output tile
+// of C = A B^T with bf16 operands whose K dimension is contiguous (row-major
+// [rows, ld] matrices), accumulated in fp32 on v_mfma_f32_32x32x16_bf16.
+//
+// Block: 256 threads = 2 x 2 waves, each wave owning 128 A rows x 128 B rows
+// as 4 x 4 MFMA blocks of 32 x 32 (acc[i][j], 256 accumulator registers).
+// After gemm_nt_tile, acc[i][j][r] holds
+//   A row  a_row0 + 128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
+//   B row  b_row0 + 128 wn + 32 j + lane % 32,
+// with wm = wave / 2, wn = wave % 2. Rows past the end of A or B are clamped
+// to the last row when loading (no branches); their results must be masked.
+//
+// K streams through LDS in 32-wide stages copied global -> LDS by
+// global_load_lds_dwordx4 (no register staging). Five stage buffers
+// (5 x 32 KB = 160 KB): while stage s is multiplied, stage s+1 is read into
+// fragment registers and up to three later stages are in flight. Copies are
+// issued two stages at a time (s+4 and s+5 at even steps), interleaved, so
+// the two 64-byte halves of each 128-byte line of a row are requested
+// together. One barrier per stage, preceded by an explicit vmcnt wait for
+// this wave's copies of the next stage: the copies are inline assembly,
+// invisible to the compiler's wait-count tracking, so every wait on them is
+// written out here, and the loop issues the same number of copies at every
+// step (past the end it repeats the last stages into buffers that no later
+// step reads) so the wait counts are constants.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace rlk {
+namespace gemm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTile = 256;                    // rows of A and of B per tile
+constexpr int kThreads = 256;                 // 2 x 2 waves of 128 x 128
+constexpr int kStageK = 32;                   // K elements per stage
+constexpr int kStages = 5;                    // stage buffers resident in LDS
+constexpr int kChunks = kStageK / 8;          // 16-byte chunks per staged row
+constexpr int kOpSlots = kTile * kChunks;     // 16-byte slots per operand per stage
+constexpr int kLoads = kOpSlots / kThreads;   // copies per thread per operand per stage
+constexpr int kVmPerStage = 2 * kLoads;       // vmcnt of one stage (A and B)
+constexpr int kStageBytes = 2 * kOpSlots * 16;  // 32 KB: A then B
+constexpr int kKMultiple = 2 * kStageK;       // K must be a multiple of this
+constexpr int64_t kMaxLd = int64_t(1) << 23;  // 255 * ld * 2 bytes must fit 32 bits
+
+// LDS of one block: [stage][A, B][slot].
+typedef uint4 Smem[kStages][2][kOpSlots];
+
+// Physical chunk of (row, logical chunk): XOR with a 2-bit hash of the row so
+// that both the 8- and the 16-lane groups of a 32-row fragment read hit
+// distinct 16-byte bank groups.
+RLK_DEV int swz_hash(int row) {
+  return ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1);
+}
+RLK_DEV int slot_of(int row, int lc) { return row * kChunks + (lc ^ swz_hash(row)); }
+
+// Byte offsets, relative to the tile's first row, of this thread's copies:
+// copy j of wave w fills slots [64 q, 64 q + 64) with q = w * kLoads + j,
+// lane l writing slot 64 q + l.
+RLK_DEV void copy_offsets(uint32_t (&off)[kLoads], int64_t row0, int64_t nrows, int64_t ld) {
+  const int w = int(threadIdx.x) >> 6, lane = int(threadIdx.x) & 63;
+  const int last = int(nrows - 1 - row0 < kTile - 1 ? nrows - 1 - row0 : kTile - 1);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int slot = (w * kLoads + j) * 64 + lane;
+    const int row = slot / kChunks, lc = (slot % kChunks) ^ swz_hash(row);
+    const int r = row < last ? row : last;
+    off[j] = uint32_t((int64_t(r) * ld + lc * 8) * 2);
+  }
+}
+
+// Copies of stages t and t+1 (the 64-byte halves of the same rows), interleaved.
+// The copy reads its LDS destination from M0, which the statement sets and
+// declares clobbered (clang warns that M0 is reserved; declaring it is what
+// keeps the compiler from relying on an M0 value across the statement).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+RLK_DEV void copy_pair(uint4* lds_t, uint4* lds_t1, const uint16_t* gbase_t,
+                       const uint32_t (&off)[kLoads]) {
+  const int w = int(threadIdx.x) >> 6;
+  const uint16_t* gbase_t1 = gbase_t + kStageK;
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const uint32_t m0a = uint32_t(reinterpret_cast<uintptr_t>(lds_t + (w * kLoads + j) * 64));
+    const uint32_t m0b = uint32_t(reinterpret_cast<uintptr_t>(lds_t1 + (w * kLoads + j) * 64));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %4"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(m0a)), "s"(__builtin_amdgcn_readfirstlane(m0b)),
+          "v"(off[j]), "s"(gbase_t), "s"(gbase_t1)
+        : "memory", "m0");
+  }
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's vector-memory operations (here: LDS
+// copies) are outstanding and its LDS reads are done, then barrier.
+template <int N>
+RLK_DEV void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+struct Frags {
+  bf16x8 a[2][4], b[2][4];   // [k-step][32-row group]
+};
+
+// Fragment rows 128 wm + 32 x + lane % 32: the swizzle hash depends on
+// row & 15 only, so a read's address is a per-lane part (one per k-step) plus
+// a uniform part.
+struct FragAddr {
+  uint32_t lane_off[2];   // bytes, per k-step
+  uint32_t a_off, b_off;  // bytes: the wave's A rows and B rows inside a stage
+};
+
+RLK_DEV FragAddr frag_addr() {
+  const int lane = int(threadIdx.x) & 63, wid = int(threadIdx.x) >> 6;
+  const int wm = wid >> 1, wn = wid & 1, frow = lane & 31, fgrp = lane >> 5;
+  FragAddr f;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) f.lane_off[kk] = uint32_t(slot_of(frow, 2 * kk + fgrp)) * 16u;
+  f.a_off = uint32_t(128 * wm * kChunks * 16);
+  f.b_off = uint32_t(kOpSlots * 16 + 128 * wn * kChunks * 16);
+  return f;
+}
+
+RLK_DEV void read_frag(Frags& f, int r, const char* stage, const FragAddr& fa) {
+  const int kk = r >> 3, x = r & 7;
+  if (x < 4)
+    f.a[kk][x] = *reinterpret_cast<const bf16x8*>(stage + fa.a_off + fa.lane_off[kk] +
+                                                  x * 32 * kChunks * 16);
+  else
+    f.b[kk][x - 4] = *reinterpret_cast<const bf16x8*>(stage + fa.b_off + fa.lane_off[kk] +
+                                                      (x - 4) * 32 * kChunks * 16);
+}
+
+// The 32 MFMAs of one stage, with the 16 fragment reads of the next stage
+// interleaved into the first 16 so that they have landed before the barrier
+// that ends the stage.
+RLK_DEV void stage_mma(f32x16 (&acc)[4][4], const Frags& cur, Frags& nxt, const char* next_stage,
+                       const FragAddr& fa) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[kk][i], cur.b[kk][j], acc[i][j],
+                                                            0, 0, 0);
+        const int m = kk * 16 + i * 4 + j;
+        if (m < 16) {
+          read_frag(nxt, m, next_stage, fa);
+          // keep the issue order as written: the scheduler would otherwise
+          // sink the reads to their uses in the next stage
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+}
+
+// acc = A[a_row0 .. +256) . B[b_row0 .. +256)^T over k in [0, K); K is a
+// positive multiple of kKMultiple. Ends with a barrier after which `smem` may
+// be reused.
+RLK_DEV void gemm_nt_tile(f32x16 (&acc)[4][4], Smem& smem, const uint16_t* A, int64_t a_row0,
+                          int64_t a_rows, int64_t lda, const uint16_t* B, int64_t b_row0,
+                          int64_t b_rows, int64_t ldb, int64_t K) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const char* sbase = reinterpret_cast<const char*>(&smem[0][0][0]);
+  const FragAddr fa = frag_addr();
+  const int nk = int(K / kStageK);   // even
+  uint32_t oa[kLoads], ob[kLoads];
+  copy_offsets(oa, a_row0, a_rows, lda);
+  copy_offsets(ob, b_row0, b_rows, ldb);
+  const uint16_t* a_base = A + a_row0 * lda;
+  const uint16_t* b_base = B + b_row0 * ldb;
+  auto issue_pair = [&](int t) __attribute__((always_inline)) {   // stages t, t+1 (t even)
+    const int64_t k0 = int64_t(t < nk ? t : nk - 2) * kStageK;
+    copy_pair(smem[t % kStages][0], smem[(t + 1) % kStages][0], a_base + k0, oa);
+    copy_pair(smem[t % kStages][1], smem[(t + 1) % kStages][1], b_base + k0, ob);
+  };
+  issue_pair(0);
+  issue_pair(2);
+  vm_wait_barrier<3 * kVmPerStage>();
+  Frags f0, f1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) read_frag(f0, r, sbase, fa);
+
+  // Step s: stage s (fragments in registers) is multiplied while stage s+1
+  // is read. Even s: after the barrier (stage s+1 landed; stages s-1 and s
+  // consumed) stages s+4 and s+5 are copied into the buffers of s-1 and s.
+  for (int s = 0; s < nk; s += 2) {
+    vm_wait_barrier<2 * kVmPerStage>();   // in flight: s+2, s+3
+    issue_pair(s + 4);
+    stage_mma(acc, f0, f1, sbase + ((s + 1) % kStages) * kStageBytes, fa);
+    vm_wait_barrier<3 * kVmPerStage>();   // in flight: s+3, s+4, s+5
+    stage_mma(acc, f1, f0, sbase + ((s + 2) % kStages) * kStageBytes, fa);
+  }
+  vm_wait_barrier<0>();
+}
+
+constexpr int kXcds = 8;      // workgroups are dealt to the XCDs round-robin
+constexpr int kGroupA = 8;    // A tiles per group of the tile order
+
+// Tile (ta, tb) of this workgroup in an na x nb grid. Each XCD takes a
+// contiguous range of the tile order, so its L2 serves one region of A and
+// B; within the order, groups of kGroupA A-tiles sweep all B-tiles with the
+// A-tile fastest, so the 32 workgroups an XCD runs at once cover about 8
+// A-tiles and 4 B-tiles.
+RLK_DEV void tile_of_block(int na, int nb, int& ta, int& tb) {
+  const int T = na * nb, b = int(blockIdx.x);
+  const int x = b % kXcds, q = T / kXcds, r = T % kXcds;
+  const int lid = x * q + (x < r ? x : r) + b / kXcds;
+  const int grp = lid / (kGroupA * nb), rem = lid % (kGroupA * nb);
+  const int ga = kGroupA < na - grp * kGroupA ? kGroupA : na - grp * kGroupA;
+  ta = grp * kGroupA + rem % ga;
+  tb = rem / ga;
+}
+
+// Row of acc[i][j][r] inside the A and B halves of the tile (see the top).
+RLK_DEV int acc_a_row(int i, int r) {
+  const int lane = int(threadIdx.x) & 63, wm = int(threadIdx.x) >> 7;
+  return 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+RLK_DEV int acc_b_row(int j) {
+  const int lane = int(threadIdx.x) & 63, wn = (int(threadIdx.x) >> 6) & 1;
+  return 128 * wn + 32 * j + (lane & 31);
+}
+
+}  // namespace gemm
+}  // namespace rlk

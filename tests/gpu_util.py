@@ -40,4 +40,6 @@ def bits_equal(a, b) -> bool:
         return False
     if a.dtype in (torch.float32, torch.int32):
         return torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
+    if a.dtype in (torch.bfloat16, torch.float16):
+        return torch.equal(a.contiguous().view(torch.int16), b.contiguous().view(torch.int16))
     return torch.equal(a, b)
