@@ -117,12 +117,51 @@ def leg_fused(torch, rlk, synth, steps, warmup):
     }
 
 
+def leg_fused_bwd(torch, rlk, synth, steps, warmup):
+    """Fused LM-head forward + backward, Llama-3-70B head: hidden [16384, 8192],
+    W [128256, 8192], T=1, p=1, loss = -mean lp - 0.001 mean H (seeds
+    g_lp = -1/N, g_H = -0.001/N)."""
+    w = synth.workload("llama70b")
+    t_gen = time.perf_counter()
+    hb = synth.hidden_rows(w, range(w.N))
+    wb = synth.weight_rows(w, range(w.V))
+    y = synth.uniform_targets(w, w.N)
+    h = torch.from_numpy(hb.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    W = torch.from_numpy(wb.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    del hb, wb
+    yt = torch.from_numpy(y).to("cuda:0")
+    g_lp = torch.full((w.N,), -1.0 / w.N, device="cuda:0")
+    g_h = torch.full((w.N,), -0.001 / w.N, device="cuda:0")
+    print(f"[bench] fused fwd+bwd leg: hidden {tuple(h.shape)} W {tuple(W.shape)} generated in "
+          f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    def step():
+        out = rlk.logprob_fused_linear(h, W, yt, w.temperature, 1.0)
+        return rlk.logprob_fused_linear_bwd(h, W, yt, out["saved"], g_lp, g_h, w.temperature, 1.0)
+
+    mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
+    flops = 8.0 * w.N * w.V * w.H      # forward 2VH + recompute 2VH + dh 2VH + dW 2VH per token
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    return {
+        "workload": f"fused LM-head forward+backward, hidden [{w.N},{w.H}] bf16, "
+                    f"W [{w.V},{w.H}] bf16, T=1, top-p=1, loss -mean lp - 0.001 mean H",
+        "tokens_per_s": w.N * steps / (total_ms * 1e-3),
+        "ms_per_step": total_ms / steps,
+        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "flops_per_token_executed": 8.0 * w.V * w.H,
+        "frac_useful_6vh": round(0.75 * achieved / BF16_PEAK_TFLOPS, 4),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="logits,fused")
+    ap.add_argument("--legs", default="logits,fused,fused_bwd")
     ap.add_argument("--cpu-sample", type=int, default=256,
                     help="rows of the logits workload the CPU oracle is timed on (0 = skip)")
     args = ap.parse_args()
@@ -142,6 +181,8 @@ def main():
                                         args.cpu_sample)
     if "fused" in legs:
         out_legs["fused"] = leg_fused(torch, rlk, synth, max(3, args.steps // 4), 1)
+    if "fused_bwd" in legs:
+        out_legs["fused_bwd"] = leg_fused_bwd(torch, rlk, synth, 3, 1)
     main_leg = out_legs.get("logits") or next(iter(out_legs.values()))
     line = {
         "metric": METRIC,
