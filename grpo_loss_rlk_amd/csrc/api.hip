@@ -169,7 +169,7 @@ size_t rlk_logprob_fused_linear_workspace_size(int64_t n_rows, int64_t hidden_si
                                                float top_p) {
   (void)top_p;
   if (n_rows < 0 || vocab < 1) return 0;
-  return rlk::fused_fwd_workspace(n_rows, hidden_size, vocab);
+  return rlk::fused_fwd_workspace(n_rows, hidden_size, vocab, top_p);
 }
 
 rlk_status rlk_logprob_fused_linear(const void* hidden, const void* weight, int64_t n_rows,
@@ -182,8 +182,6 @@ rlk_status rlk_logprob_fused_linear(const void* hidden, const void* weight, int6
   if (s != RLK_OK) return s;
   s = check_fused_shapes(hidden, weight, n_rows, hidden_size, vocab, h_stride, w_stride, targets);
   if (s != RLK_OK) return s;
-  if (top_p < 1.f)
-    return fail(RLK_EUNSUPPORTED, "fused top-p < 1 is not implemented yet (use top_p = 1)");
   if (n_rows == 0) return ok();
   if (!logprob || !entropy) return fail(RLK_EINVAL, "logprob and entropy are required");
   if (!aligned(logprob, 4) || !aligned(entropy, 4) || !aligned(saved, 4) ||
@@ -202,6 +200,8 @@ rlk_status rlk_logprob_fused_linear(const void* hidden, const void* weight, int6
   a.ws = w_stride;
   a.targets = targets;
   a.c2 = float(1.4426950408889634 / double(temperature));
+  a.temperature = temperature;
+  a.top_p = top_p;
   a.logprob = logprob;
   a.entropy = entropy;
   a.saved = saved;

@@ -2,7 +2,7 @@
 // without materialising the [N, V] logits (prime-rl v0.10.0 release notes,
 // "1. Trainer Performance": the loss is chunked torchtitan-style).
 //
-// Forward, two launches:
+// Forward at top-p = 1, two launches:
 //  1. fwd_tile_stats: one block per (256-vocab x 256-token) tile; z = W h^T
 //     in fp32 on bf16 MFMA (mfma_gemm.h). The epilogue folds the tile's 256
 //     logits of each token into a partial (max z, sum 2^x, sum 2^x x) with
@@ -13,12 +13,19 @@
 //     depend on the number of tokens or their order: the Qwen3-8B VIME
 //     consistency page, "Canonical topology strategy", combines vocabulary
 //     shards in one fixed order).
+//
+// Forward at top-p < 1 (the cut needs the whole row's distribution): per
+// block of kTopPRowBlock tokens, fwd_logits_tile writes the block's fp32
+// logits z = h W^T to a workspace scratch [rows, Vs] and the logits-in row
+// kernel (max, nucleus by value histogram, truncated statistics) cuts each
+// row at the tempered top-p threshold.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 
 #include "common.h"
 #include "fused_kernels.h"
+#include "kernels.h"
 #include "mfma_gemm.h"
 
 namespace rlk {
@@ -149,6 +156,32 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats(FusedFwdArgs a) {
   tile_epilogue(a, acc, v0, n0, vt, reinterpret_cast<float*>(&smem[0][0][0]));
 }
 
+// Logits of a row block: A = h (tokens), B = W (vocabulary), so that the
+// lanes of an accumulator register hold consecutive vocabulary ids of one
+// token and each store writes 128 contiguous bytes of a scratch row.
+__global__ __launch_bounds__(kT) void fwd_logits_tile(FusedFwdArgs a, int64_t r0, int64_t rows,
+                                                      float* z, int64_t zs) {
+  __shared__ gemm::Smem smem;
+  const int nnt = int((rows + kBN - 1) / kBN), nvt = int((a.V + kBM - 1) / kBM);
+  int nt, vt;
+  gemm::tile_of_block(nnt, nvt, nt, vt);
+  const int64_t n0 = int64_t(nt) * kBN, v0 = int64_t(vt) * kBM;
+  f32x16 acc[4][4];
+  gemm::gemm_nt_tile(acc, smem, a.h + r0 * a.hs, n0, rows, a.hs, a.w, v0, a.V, a.ws, a.H);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t v = v0 + gemm::acc_b_row(j);
+    if (v >= a.V) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t n = n0 + gemm::acc_a_row(i, r);
+        if (n < rows) z[n * zs + v] = acc[i][j][r];
+      }
+  }
+}
+
 __global__ __launch_bounds__(256) void fwd_merge(FusedFwdArgs a, int nvt) {
   const int64_t n = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (n >= a.N) return;
@@ -198,16 +231,59 @@ __global__ __launch_bounds__(256) void fwd_merge(FusedFwdArgs a, int nvt) {
 
 }  // namespace
 
-size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V) {
+namespace {
+
+int64_t logits_ld(int64_t V) { return (V + 63) / 64 * 64; }
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V, float top_p) {
   (void)H;
+  if (top_p < 1.f) {
+    const int64_t R = N < kTopPRowBlock ? N : kTopPRowBlock;
+    return align256(size_t(R) * size_t(logits_ld(V)) * 4) + align256(size_t(N) * 4) +
+           logits_rows_workspace(R, V, 0);
+  }
   const int64_t nvt = (V + kBM - 1) / kBM;
   return size_t(nvt * N) * 16 + size_t(N) * 4 + 512;
 }
 
 hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream) {
   if (a.N == 0) return hipSuccess;
-  const int64_t nvt = (a.V + kBM - 1) / kBM, nnt = (a.N + kBN - 1) / kBN;
   char* ws = reinterpret_cast<char*>(workspace);
+  if (a.top_p < 1.f) {
+    const int64_t R = a.N < kTopPRowBlock ? a.N : kTopPRowBlock, zs = logits_ld(a.V);
+    float* z = reinterpret_cast<float*>(ws);
+    float* lp_full = reinterpret_cast<float*>(ws + align256(size_t(R) * size_t(zs) * 4));
+    void* rows_ws = ws + align256(size_t(R) * size_t(zs) * 4) + align256(size_t(a.N) * 4);
+    for (int64_t r0 = 0; r0 < a.N; r0 += R) {
+      const int64_t rows = a.N - r0 < R ? a.N - r0 : R;
+      const int64_t nnt = (rows + kBN - 1) / kBN, nvt = (a.V + kBM - 1) / kBM;
+      hipLaunchKernelGGL(fwd_logits_tile, dim3(unsigned(nnt * nvt)), dim3(kT), 0, stream, a, r0,
+                         rows, z, zs);
+      RowArgs ra{};
+      ra.logits = z;
+      ra.n_rows = rows;
+      ra.vocab = a.V;
+      ra.row_stride = zs;
+      ra.targets = a.targets + r0;
+      ra.temperature = a.temperature;
+      ra.top_p = a.top_p;
+      ra.lp_full = lp_full + r0;
+      ra.lp_trunc = a.logprob + r0;
+      ra.ent_trunc = a.entropy + r0;
+      ra.nsize = a.nsize ? a.nsize + r0 : nullptr;
+      ra.flags = a.flags ? a.flags + r0 : nullptr;
+      ra.saved4 = a.saved ? a.saved + 4 * r0 : nullptr;
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      e = launch_logits_rows(ra, 0, rows_ws, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const int64_t nvt = (a.V + kBM - 1) / kBM, nnt = (a.N + kBN - 1) / kBN;
   a.part = reinterpret_cast<float4*>(ws);
   a.zy = reinterpret_cast<float*>(ws + (size_t(nvt * a.N) * 16 + 255) / 256 * 256);
   hipLaunchKernelGGL(fwd_tile_stats, dim3(unsigned(nvt * nnt)), dim3(kT), 0, stream, a);

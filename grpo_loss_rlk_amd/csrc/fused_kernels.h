@@ -20,9 +20,14 @@ struct FusedFwdArgs {
   uint8_t* flags;          // [N] nullable
   float4* part;            // workspace: [ceil(V/256), N] tile partials
   float* zy;               // workspace: [N] target logits
+  float temperature, top_p;
 };
 
-size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V);
+// Tokens per row block of the top-p < 1 path: the block's fp32 logits are
+// written to a workspace scratch and cut by the logits-in row kernel.
+constexpr int64_t kTopPRowBlock = 4096;
+
+size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V, float top_p);
 hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream);
 
 struct FusedBwdArgs {

@@ -44,8 +44,16 @@ RLK_DEV bool param_ok(float T, float p) {
   return T > 0.f && T <= 3.4e38f && p > 0.f && p <= 1.f;  // NaN fails every compare
 }
 
+// lse_s, eq_s: log Z_S and E_q[z/T] over the nucleus, in units of z/T.
 RLK_DEV void store_row(const RowArgs& a, int64_t row, float lp_full, float lp_trunc,
-                       float h_full, float h_trunc, int32_t size, float tau, uint8_t flags) {
+                       float h_full, float h_trunc, int32_t size, float tau, uint8_t flags,
+                       float lse_s, float eq_s) {
+  if (a.saved4) {
+    a.saved4[4 * row + 0] = lse_s;
+    a.saved4[4 * row + 1] = eq_s;
+    a.saved4[4 * row + 2] = tau;
+    a.saved4[4 * row + 3] = 0.f;
+  }
   a.lp_full[row] = lp_full;
   a.lp_trunc[row] = lp_trunc;
   a.ent_trunc[row] = h_trunc;
@@ -57,7 +65,7 @@ RLK_DEV void store_row(const RowArgs& a, int64_t row, float lp_full, float lp_tr
 
 RLK_DEV void store_nan_row(const RowArgs& a, int64_t row, uint8_t flags) {
   const float nan = __builtin_nanf("");
-  store_row(a, row, nan, nan, nan, nan, 0, nan, flags);
+  store_row(a, row, nan, nan, nan, nan, 0, nan, flags, nan, nan);
 }
 
 // ===========================================================================
@@ -433,7 +441,9 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
         if (fabs(Mgt / Z - pp) <= kBoundaryEps || fabs(Zs / Z - pp) <= kBoundaryEps)
           flags |= kBoundary;
       }
-      store_row(a, row, lpf, lpt, h_full, h_trunc, size, tau, flags);
+      const double mT = double(mval) * invT;
+      store_row(a, row, lpf, lpt, h_full, h_trunc, size, tau, flags, float(mT + logZs),
+                float(mT + Ss / Zs));
     }
   }
 
@@ -714,7 +724,7 @@ __global__ __launch_bounds__(kGT) void generic_rows(RowArgs a, int only_fallback
     }
     const float tau = cut ? key_f32(tau_key) : -INFINITY;
     store_row(a, row, lpf, lpt, float(logZ - S / Z), float(logZs - Ss / Zs), int32_t(size), tau,
-              flags);
+              flags, float(m * invT + logZs), float(m * invT + Ss / Zs));
   }
 }
 

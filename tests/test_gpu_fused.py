@@ -102,10 +102,3 @@ def test_bad_target_and_bitwise_batch_invariance():
     pr = rlk.logprob_fused_linear(h[perm.to(DEV)].contiguous(), W, yt[perm], 0.7)
     for k in ("logprob", "entropy", "saved"):
         assert bits_equal(ref[k][perm.to(DEV)], pr[k]), k
-
-
-def test_top_p_below_one_not_yet_supported():
-    w, hb, wb, y = _inputs("fused", 8, 64, 100)
-    with pytest.raises(rlk.RlkError) as ei:
-        _run(hb, wb, y, 0.7, 0.95)
-    assert ei.value.status == 2

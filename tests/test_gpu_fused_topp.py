@@ -1,0 +1,156 @@
+"""GPU parity of the fused LM head at top-p < 1 and of the fused-forward +
+GRPO-loss pipeline (ragged packed responses) against the fp64 oracle.
+
+The GPU forms the logits in fp32 (MFMA, fp32 accumulate) and cuts each row
+with the logits-in row kernel; the oracle forms them in fp64 from the same
+bf16 operands. Tolerances as for bf16 inputs: |d lp| <= 2e-3, |d H| <= 1e-3
+|H| (1e-5 floor), loss <= 1e-3 relative; nucleus size exact except on rows
+the oracle flags as within 1e-6 of the top-p boundary, where either valid set
+passes; the saved threshold within 1e-4 of the oracle's (fp32 vs fp64
+logits).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import grpo_loss_rlk_amd as rlk
+from oracle import fused as OF
+from oracle import grpo as OG
+from oracle import logprob as OL
+from oracle import sampling as OS
+
+from gpu_util import DEV, assert_close_rows, bf16_to_device, bits_equal, f32_to_device, host
+
+pytestmark = pytest.mark.gpu
+
+LP_TOL, H_RTOL, H_ATOL = 2e-3, 1e-3, 1e-5
+
+
+def _gumbel_targets(w, z64, rows, T, p):
+    return np.array([OS.gumbel_max_target(z64[i], T, p, synth.gumbel_uniforms(w, r, z64.shape[1]))
+                     for i, r in enumerate(rows)], dtype=np.int64)
+
+
+def _run(h, W, y, T, p):
+    print(f"  rlk_logprob_fused_linear N={h.shape[0]} H={h.shape[1]} V={W.shape[0]} T={T} p={p}",
+          flush=True)
+    out = rlk.logprob_fused_linear(h, W, torch.as_tensor(y), T, p)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items()}
+
+
+def _check(g, o, z64, y, T):
+    """GPU outputs g (host arrays of the checked rows) vs oracle BatchResult o."""
+    bnd = (o.flags & OL.FLAG_BOUNDARY) != 0
+    size, lpt, ht = o.size.astype(np.int64), o.lp_trunc.copy(), o.h_trunc.copy()
+    for n in np.flatnonzero(bnd):
+        for (s2, l2, h2) in o.alts[n]:
+            if g["nucleus_size"][n] == s2:
+                size[n], lpt[n], ht[n] = s2, l2, h2
+    np.testing.assert_array_equal(g["nucleus_size"], size, err_msg="nucleus size")
+    assert_close_rows(g["logprob"], lpt, LP_TOL, what="logprob")
+    assert_close_rows(g["entropy"], ht, H_ATOL, H_RTOL, what="entropy")
+    outside = np.isneginf(g["logprob"])
+    np.testing.assert_array_equal((g["flags"] & rlk.FLAG_OUTSIDE) != 0, outside, err_msg="outside")
+    ok = ~bnd & np.isfinite(lpt)
+    # saved: log Z_S and E_q over S of z/T (from the oracle: z_y/T - lp, then minus H), threshold
+    Tf = OL.f32(T)
+    lse = z64[np.arange(len(y)), y] / Tf - lpt
+    assert_close_rows(g["saved"][ok, 0], lse[ok], LP_TOL, what="saved log Z_S")
+    assert_close_rows(g["saved"][ok, 1], (lse - ht)[ok], LP_TOL, what="saved E_q")
+    assert_close_rows(g["saved"][~bnd, 2], o.tau[~bnd], 1e-4, 1e-5, what="saved threshold")
+
+
+@pytest.mark.parametrize("N,H,V,T,p", [(300, 256, 1000, 0.7, 0.95), (77, 128, 515, 1.3, 0.5),
+                                       (257, 64, 5003, 0.7, 0.95), (4100, 64, 300, 0.7, 0.9)])
+def test_fused_top_p_shapes(N, H, V, T, p):
+    """Ragged tiles; N = 4100 spans two row blocks of the logits scratch."""
+    w = synth.workload("grpo", N=N, H=H, V=V, temperature=T, top_p=p)
+    hb = synth.hidden_rows(w, range(N))
+    wb = synth.weight_rows(w, range(V))
+    z64 = OF.logits(OL.widen_bf16(hb), OL.widen_bf16(wb))
+    Tf, pf = OL.f32(T), OL.f32(p)
+    y = _gumbel_targets(w, z64, range(N), Tf, pf)
+    y[1] = int(np.argmin(z64[1]))     # almost surely outside the nucleus
+    y[2] = V                          # out of range
+    o = OL.logprob_from_logits(z64, y, Tf, pf)
+    g = _run(bf16_to_device(hb), bf16_to_device(wb), y, T, p)
+    assert g["flags"][2] & rlk.FLAG_BAD_TARGET and np.isnan(g["logprob"][2])
+    keep = np.arange(N) != 2
+    _check({k: v[keep] for k, v in g.items()},
+           OL.logprob_from_logits(z64[keep], y[keep], Tf, pf), z64[keep], y[keep], T)
+    assert o.flags[1] & OL.FLAG_OUTSIDE
+
+
+def test_fused_top_p_bitwise_and_batch_invariant():
+    w = synth.workload("grpo", N=600, H=128, V=2000)
+    hb = synth.hidden_rows(w, range(w.N))
+    wb = synth.weight_rows(w, range(w.V))
+    h, W = bf16_to_device(hb), bf16_to_device(wb)
+    y = torch.as_tensor(synth.uniform_targets(w, w.N))
+    ref = rlk.logprob_fused_linear(h, W, y, 0.7, 0.95)
+    again = rlk.logprob_fused_linear(h, W, y, 0.7, 0.95)
+    for k in ("logprob", "entropy", "saved", "nucleus_size"):
+        assert bits_equal(ref[k], again[k]), k
+    for split in (1, 255, 599):
+        a = rlk.logprob_fused_linear(h[:split].contiguous(), W, y[:split], 0.7, 0.95)
+        b = rlk.logprob_fused_linear(h[split:].contiguous(), W, y[split:], 0.7, 0.95)
+        for k in ("logprob", "entropy", "saved", "nucleus_size"):
+            assert bits_equal(ref[k], torch.cat([a[k], b[k]])), (k, split)
+
+
+def test_grpo_pipeline_small():
+    """Config-4 pipeline on a scaled-down shape: 4 prompts x 8 samples, lengths
+    U{4..40}, H=128, V=3001, T=0.7, p=0.95, Gumbel-max targets from the
+    nucleus; old/ref = the oracle's logprob + N(0,0.05^2) / N(0,0.1^2) stored
+    as fp32; rewards Bernoulli(0.5); C=2, eps 0.2/0.28, beta=0.01."""
+    w = synth.workload("grpo", len_lo=4, len_hi=40, H=128, V=3001)
+    lengths = synth.response_lengths(w)
+    cu = synth.cu_seqlens(lengths)
+    T_tot = int(cu[-1])
+    hb = synth.hidden_rows(w, range(T_tot))
+    wb = synth.weight_rows(w, range(w.V))
+    z64 = OF.logits(OL.widen_bf16(hb), OL.widen_bf16(wb))
+    Tf, pf = OL.f32(w.temperature), OL.f32(w.top_p)
+    y = _gumbel_targets(w, z64, range(T_tot), Tf, pf)
+    o = OL.logprob_from_logits(z64, y, Tf, pf)
+    n_old, n_ref = synth.logprob_noise(w, T_tot)
+    lp_old = (o.lp_trunc + n_old).astype(np.float32)
+    lp_ref = (o.lp_trunc + n_ref).astype(np.float32)
+    r = synth.rewards(w)
+    A = OG.advantages(r, w.group_size)
+    ol = OG.token_loss(o.lp_trunc, lp_old, lp_ref, cu, A)
+
+    g = _run(bf16_to_device(hb), bf16_to_device(wb), y, w.temperature, w.top_p)
+    _check(g, o, z64, y, w.temperature)
+    print(f"  rlk_grpo_token_loss T_tot={T_tot}", flush=True)
+    out = rlk.grpo_token_loss(f32_to_device(g["logprob"]), f32_to_device(lp_old),
+                              f32_to_device(lp_ref), cu, rewards=r, group_size=w.group_size)
+    torch.cuda.synchronize()
+    assert float(host(out["loss"])) == pytest.approx(ol.loss, rel=1e-3, abs=1e-6)
+    gr = host(out["grad"])
+    keep = ~ol.near_branch
+    # dL/dlp scales with rho = exp(lp - lp_old): the lp tolerance (2e-3) carries over
+    np.testing.assert_allclose(gr[keep], ol.grad[keep], rtol=5e-3, atol=1e-9)
+
+
+def test_grpo_workload_full_size_sampled_rows():
+    """The full config-4 launch: 32 packed responses (T_tot ~ 115k tokens),
+    H=4096, V=151936, T=0.7, p=0.95; 6 rows checked against the oracle one by
+    one (each row's logits formed in fp64)."""
+    w = synth.workload("grpo")
+    cu = synth.cu_seqlens(synth.response_lengths(w))
+    T_tot = int(cu[-1])
+    wb = synth.weight_rows(w, range(w.V))
+    hb = synth.hidden_rows(w, range(T_tot))
+    rows = np.random.default_rng(4).choice(T_tot, 6, replace=False)
+    W64 = OL.widen_bf16(wb)
+    z64 = OL.widen_bf16(hb[rows]) @ W64.T
+    Tf, pf = OL.f32(w.temperature), OL.f32(w.top_p)
+    y = synth.uniform_targets(w, T_tot)
+    y[rows] = _gumbel_targets(w, z64, rows, Tf, pf)
+    g = _run(bf16_to_device(hb), bf16_to_device(wb), y, w.temperature, w.top_p)
+    o = OL.logprob_from_logits(z64, y[rows], Tf, pf)
+    _check({k: v[rows] for k, v in g.items()}, o, z64, y[rows], w.temperature)
+    assert np.all(g["nucleus_size"] >= 1) and np.all(g["nucleus_size"] <= w.V)
