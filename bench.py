@@ -156,12 +156,57 @@ def leg_fused_bwd(torch, rlk, synth, steps, warmup):
     }
 
 
+def leg_grpo(torch, rlk, synth, steps, warmup):
+    """Fused LM head at T=0.7, top-p=0.95 over 32 packed responses (4 prompts x 8,
+    lengths U{256..6912}), H=4096, V=151936, then the GRPO/DAPO token loss."""
+    w = synth.workload("grpo")
+    cu = synth.cu_seqlens(synth.response_lengths(w))
+    T_tot = int(cu[-1])
+    t_gen = time.perf_counter()
+    hb = synth.hidden_rows(w, range(T_tot))
+    wb = synth.weight_rows(w, range(w.V))
+    h = torch.from_numpy(hb.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    W = torch.from_numpy(wb.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    del hb, wb
+    yt = torch.from_numpy(synth.uniform_targets(w, T_tot)).to("cuda:0")
+    r = synth.rewards(w)
+    print(f"[bench] grpo leg: T_tot={T_tot} hidden {tuple(h.shape)} W {tuple(W.shape)} "
+          f"generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    # old / ref logprobs: the new ones plus N(0, 0.05^2) / N(0, 0.1^2) noise,
+    # prepared once before the timed region
+    lp0 = rlk.logprob_fused_linear(h, W, yt, w.temperature, w.top_p)["logprob"]
+    n_old, n_ref = synth.logprob_noise(w, T_tot)
+    lp_old = (lp0 + torch.from_numpy(n_old).to(lp0)).contiguous()
+    lp_ref = (lp0 + torch.from_numpy(n_ref).to(lp0)).contiguous()
+    rw = torch.from_numpy(r).to("cuda:0")
+
+    def step():
+        out = rlk.logprob_fused_linear(h, W, yt, w.temperature, w.top_p)
+        return rlk.grpo_token_loss(out["logprob"], lp_old, lp_ref, cu, rewards=rw,
+                                   group_size=w.group_size)
+
+    mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
+    flops = 2.0 * T_tot * w.V * w.H
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    return {
+        "workload": f"fused LM head top-p + GRPO loss, {T_tot} packed tokens (32 responses), "
+                    f"H={w.H}, V={w.V}, T={w.temperature}, top-p={w.top_p}",
+        "tokens_per_s": T_tot * steps / (total_ms * 1e-3),
+        "ms_per_step": total_ms / steps,
+        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "flops_per_token": 2.0 * w.V * w.H,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="logits,fused,fused_bwd")
+    ap.add_argument("--legs", default="logits,fused,grpo,fused_bwd")
     ap.add_argument("--cpu-sample", type=int, default=256,
                     help="rows of the logits workload the CPU oracle is timed on (0 = skip)")
     args = ap.parse_args()
@@ -181,6 +226,8 @@ def main():
                                         args.cpu_sample)
     if "fused" in legs:
         out_legs["fused"] = leg_fused(torch, rlk, synth, max(3, args.steps // 4), 1)
+    if "grpo" in legs:
+        out_legs["grpo"] = leg_grpo(torch, rlk, synth, 3, 1)
     if "fused_bwd" in legs:
         out_legs["fused_bwd"] = leg_fused_bwd(torch, rlk, synth, 3, 1)
     main_leg = out_legs.get("logits") or next(iter(out_legs.values()))
