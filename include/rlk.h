@@ -129,13 +129,17 @@ rlk_status rlk_logprob_from_logits(
  * targets       [n_rows] int64.
  * Logits are accumulated in fp32 over the hidden dimension and never rounded
  * to bf16. With top_p < 1 the outputs are the truncated ones of the
- * logits-in entry point (same nucleus rule); with top_p = 1 they are full.
+ * logits-in entry point (same nucleus rule; the fp32 logits of up to 4096
+ * rows at a time are formed in the workspace and cut by the logits-in row
+ * kernel); with top_p = 1 they are full and no logits are stored.
  * logprob, entropy   [n_rows] fp32 outputs (required).
- * saved         [n_rows, 4] fp32 (nullable): (log Z_S, E_q[z/T], tau, 0) on the
- *               scale z/T, consumed by rlk_logprob_fused_linear_bwd.
+ * saved         [n_rows, 4] fp32 (nullable): (log Z_S and E_q[z/T] over the
+ *               nucleus, both on the scale z/T; tau, the smallest kept logit,
+ *               -inf at top_p = 1; 0), consumed by rlk_logprob_fused_linear_bwd.
  * nucleus_size  [n_rows] int32 (nullable).  flags [n_rows] uint8 (nullable).
- * Limits: hidden_size % 64 == 0, 1 <= vocab <= 2^24, strides >= hidden_size
- * and multiples of 8, hidden/weight 16-byte aligned.
+ * Limits: hidden_size % 64 == 0, 1 <= vocab <= 2^24, 0 <= n_rows < 2^23,
+ * strides >= hidden_size, multiples of 8 and < 2^23, hidden/weight 16-byte
+ * aligned.
  * -------------------------------------------------------------------------- */
 size_t rlk_logprob_fused_linear_workspace_size(int64_t n_rows, int64_t hidden_size,
                                                 int64_t vocab, float top_p);
@@ -157,10 +161,19 @@ rlk_status rlk_logprob_fused_linear(
  *   G[n,i] = (1/T) [ g_lp (delta_{i,y} - q_i) - g_H q_i (z_i/T - E_q[z/T]) ] on S, 0 off S
  *   grad_hidden = G W   (bf16 out, fp32 accumulate)
  *   grad_weight = G^T h (fp32 out, overwritten)
- * A row whose target is outside S contributes only its entropy term.
+ * A row whose target is outside S (or out of range) contributes only its
+ * entropy term.
  * grad_logprob, grad_entropy  [n_rows] fp32 (nullable = zeros).
  * saved         [n_rows, 4] fp32 from the forward call with the same inputs.
- * Limits: as the forward.
+ * grad_hidden   [n_rows, hidden_size] bf16, dense (required when n_rows > 0).
+ * grad_weight   [vocab, hidden_size] fp32, dense (required; zeros when n_rows = 0).
+ * The vocabulary is processed in chunks of 32768 rows in a fixed order (so a
+ * row of grad_hidden does not depend on the other rows); the workspace holds
+ * W^T and h^T (bf16, padded to multiples of 64), G of one chunk in both
+ * orientations (bf16) and, when vocab > 32768, an fp32 [n_rows, hidden_size]
+ * partial sum of grad_hidden.
+ * Limits: as the forward, and top_p must be 1 (the backward through the
+ * top-p cut returns RLK_EUNSUPPORTED), vocab < 2^23.
  * -------------------------------------------------------------------------- */
 size_t rlk_logprob_fused_linear_bwd_workspace_size(int64_t n_rows, int64_t hidden_size,
                                                     int64_t vocab, float top_p);

@@ -125,3 +125,73 @@ def _grpo(L, cu=(0, 3, 5), **kw):
 def test_grpo_validation(L, kw, status):
     assert _grpo(L, **kw) == status
     assert len(L.rlk_last_error()) > 0
+
+
+def _fused(L, **kw):
+    a = dict(h=FAKE, w=FAKE, n=4, H=128, V=1000, hs=128, wsd=128, targets=FAKE, T=1.0, p=1.0,
+             top_k=0, lp=FAKE, ent=FAKE, saved=FAKE, ns=None, fl=None, ws=WS, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.rlk_logprob_fused_linear(a["h"], a["w"], a["n"], a["H"], a["V"], a["hs"], a["wsd"],
+                                      a["targets"], a["T"], a["p"], a["top_k"], a["lp"],
+                                      a["ent"], a["saved"], a["ns"], a["fl"], a["ws"],
+                                      a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=3), _native.RLK_EUNSUPPORTED),
+    (dict(T=0.0), _native.RLK_EINVAL),
+    (dict(p=1.5), _native.RLK_EINVAL),
+    (dict(H=100, hs=128, wsd=128), _native.RLK_EINVAL),
+    (dict(H=0, hs=128, wsd=128), _native.RLK_EINVAL),
+    (dict(hs=120), _native.RLK_EINVAL),
+    (dict(hs=132), _native.RLK_EINVAL),
+    (dict(wsd=1 << 23), _native.RLK_EINVAL),
+    (dict(V=0), _native.RLK_EINVAL),
+    (dict(n=1 << 23), _native.RLK_EINVAL),
+    (dict(h=None), _native.RLK_EINVAL),
+    (dict(w=P(0x100008)), _native.RLK_EINVAL),
+    (dict(lp=None), _native.RLK_EINVAL),
+    (dict(ws=None), _native.RLK_EWORKSPACE),
+    (dict(ws_bytes=16), _native.RLK_EWORKSPACE),
+    (dict(p=0.9, ws_bytes=1 << 12), _native.RLK_EWORKSPACE),
+])
+def test_fused_validation(L, kw, status):
+    assert _fused(L, **kw) == status
+    assert len(L.rlk_last_error()) > 0
+
+
+def _fused_bwd(L, **kw):
+    a = dict(h=FAKE, w=FAKE, n=4, H=128, V=1000, hs=128, wsd=128, targets=FAKE, saved=FAKE,
+             glp=FAKE, gh=None, T=1.0, p=1.0, top_k=0, dh=FAKE, dw=FAKE, ws=WS, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.rlk_logprob_fused_linear_bwd(a["h"], a["w"], a["n"], a["H"], a["V"], a["hs"],
+                                          a["wsd"], a["targets"], a["saved"], a["glp"], a["gh"],
+                                          a["T"], a["p"], a["top_k"], a["dh"], a["dw"], a["ws"],
+                                          a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=0.95), _native.RLK_EUNSUPPORTED),
+    (dict(top_k=1), _native.RLK_EUNSUPPORTED),
+    (dict(T=math.inf), _native.RLK_EINVAL),
+    (dict(H=96, hs=128, wsd=128), _native.RLK_EINVAL),
+    (dict(V=1 << 23), _native.RLK_EINVAL),
+    (dict(dw=None), _native.RLK_EINVAL),
+    (dict(dh=None), _native.RLK_EINVAL),
+    (dict(saved=None), _native.RLK_EINVAL),
+    (dict(dw=P(0x100002)), _native.RLK_EINVAL),
+    (dict(ws=None), _native.RLK_EWORKSPACE),
+    (dict(ws_bytes=1 << 10), _native.RLK_EWORKSPACE),
+])
+def test_fused_bwd_validation(L, kw, status):
+    assert _fused_bwd(L, **kw) == status
+    assert len(L.rlk_last_error()) > 0
+
+
+def test_fused_workspace_queries(L):
+    # top-p < 1 stores a block of fp32 logits: 4096 rows x V (padded to 64) x 4 bytes
+    assert L.rlk_logprob_fused_linear_workspace_size(8192, 4096, 151936, 0.95) >= 4096 * 151936 * 4
+    assert L.rlk_logprob_fused_linear_workspace_size(8192, 4096, 151936, 1.0) < 4096 * 151936
+    # backward: W^T and h^T in bf16 plus two bf16 copies of one 32768-row chunk of G
+    need = 2 * 4096 * 151936 + 2 * 4096 * 8192 + 2 * 2 * 8192 * 32768
+    assert L.rlk_logprob_fused_linear_bwd_workspace_size(8192, 4096, 151936, 1.0) >= need
