@@ -28,6 +28,30 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6          # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk
 
 
+def _profile_traffic(name):
+    """HBM bytes per launch from the committed counter summary profiles/<name>.md,
+    or None when that summary is missing or the kernel's sources have changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name + ".md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "|", "#")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for f in fields["source_files"].split():
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest()[:16] != fields["source_sha256_16"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def _events_time(torch, fn, steps, warmup):
     """Mean and total ms of `fn` over `steps` calls, HIP events on the current stream."""
     for _ in range(warmup):
@@ -71,7 +95,8 @@ def leg_logits(torch, rlk, synth, steps, warmup, cpu_sample):
         "ms_per_step": total_ms / steps,
         "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _profile_traffic("bf16_hist_rows_qwen3_logits_4096x151936")},
         "bytes_per_row": bytes_per_row,
     }
     if cpu_sample > 0:
@@ -112,7 +137,7 @@ def leg_fused(torch, rlk, synth, steps, warmup):
         "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": _profile_traffic("fwd_tile_stats_qwen3_head_8192x4096x151936")},
         "flops_per_token": 2.0 * w.V * w.H,
     }
 
@@ -201,13 +226,30 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
     }
 
 
+def leg_copy(torch, steps, warmup):
+    """A plain 1 GiB device-to-device copy: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters (its algorithmic traffic is exactly
+    1 GiB read + 1 GiB written per launch)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    mean_ms, total_ms, min_ms = _events_time(torch, lambda: dst.copy_(src), steps, warmup)
+    return {"workload": "device copy, 1 GiB", "bytes_read": n, "bytes_written": n,
+            "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+            "tokens_per_s": 0.0, "ms_per_step": total_ms / steps,
+            "roofline": {"bound": "hbm", "achieved": round(2 * n / (mean_ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(2 * n / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="logits,fused,grpo,fused_bwd")
-    ap.add_argument("--cpu-sample", type=int, default=256,
+    ap.add_argument("--cpu-sample", type=int, default=1024,
                     help="rows of the logits workload the CPU oracle is timed on (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -226,6 +268,8 @@ def main():
                                         args.cpu_sample)
     if "fused" in legs:
         out_legs["fused"] = leg_fused(torch, rlk, synth, max(3, args.steps // 4), 1)
+    if "copy" in legs:
+        out_legs["copy"] = leg_copy(torch, args.steps, args.warmup)
     if "grpo" in legs:
         out_legs["grpo"] = leg_grpo(torch, rlk, synth, 3, 1)
     if "fused_bwd" in legs:
