@@ -728,6 +728,264 @@ __global__ __launch_bounds__(kGT) void generic_rows(RowArgs a, int only_fallback
   }
 }
 
+// ===========================================================================
+// fp32 rows: three streaming passes with float4 loads (one 1024-thread block
+// per row). Pass 1: max and finite count. Pass 2: Z, sum e d and a histogram
+// of fixed-point masses over bins of equal width in d = (z - max)/T (64 bins
+// per nat; a bin index never increases with z, so every bin above the
+// crossing bin holds only larger values). Pass 3: the truncated sums of the
+// bins above the crossing bin, and the keys of the crossing bin's elements
+// collected in LDS; sorted there, they give the exact threshold. A row whose
+// crossing bin holds more than kCand elements is handed to generic_rows.
+// ===========================================================================
+constexpr int kF32T = 1024;           // threads per block
+constexpr int kFBins = 4096;          // bins of d: [b / 64, (b + 1) / 64) nats below the max
+constexpr float kFBinPerNat = 64.f;
+constexpr int kCand = 8192;           // crossing-bin elements resolved in LDS
+
+template <int NT>
+RLK_DEV int walk_bins(const uint64_t* bins, int nbins, uint64_t thr, uint64_t* above,
+                      uint64_t* su64, int* si, uint64_t* bslot) {
+  uint64_t carry = 0;
+  for (int base = 0; base < nbins; base += NT) {
+    const int b = base + int(threadIdx.x);
+    const uint64_t v = b < nbins ? bins[b] : 0ull;
+    uint64_t tot;
+    const uint64_t incl = block_inclusive_scan(v, su64, &tot);
+    const int cand = (v != 0ull && carry + incl >= thr) ? int(threadIdx.x) : NT;
+    const int first = block_min(cand, si);
+    if (first < NT) {
+      if (int(threadIdx.x) == first) *bslot = carry + incl - v;
+      __syncthreads();
+      *above = *bslot;
+      __syncthreads();
+      return base + first;
+    }
+    carry += tot;
+  }
+  *above = carry;
+  return -1;
+}
+
+template <bool kVec, typename F>
+RLK_DEV void for_each_f32(const float* rowp, int64_t V, F&& f) {
+  if (kVec) {
+    const int64_t V4 = V >> 2;
+    const float4* p4 = reinterpret_cast<const float4*>(rowp);
+    for (int64_t i = threadIdx.x; i < V4; i += kF32T) {
+      const float4 v = p4[i];
+      f(v.x, 4 * i);
+      f(v.y, 4 * i + 1);
+      f(v.z, 4 * i + 2);
+      f(v.w, 4 * i + 3);
+    }
+    for (int64_t i = 4 * V4 + threadIdx.x; i < V; i += kF32T) f(rowp[i], i);
+  } else {
+    for (int64_t i = threadIdx.x; i < V; i += kF32T) f(rowp[i], i);
+  }
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
+  __shared__ uint64_t hist[kFBins];
+  __shared__ uint32_t cand[kCand];
+  __shared__ double sd[kF32T / kWave];
+  __shared__ uint64_t su64[kF32T / kWave];
+  __shared__ int si[kF32T / kWave];
+  __shared__ float sf[kF32T / kWave];
+  __shared__ uint64_t bslot;
+  __shared__ unsigned int ncand_s;
+
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t V = a.vocab;
+  const float* rowp = reinterpret_cast<const float*>(a.logits) + row * a.row_stride;
+  if (tid == 0) a.fallback[row] = 0;
+
+  const float Tv = a.t_row ? a.t_row[row] : a.temperature;
+  const float p = a.p_row ? a.p_row[row] : a.top_p;
+  const int64_t y = a.targets[row];
+  uint8_t flags = 0;
+  if (y < 0 || y >= V) flags |= kBadTarget;
+  if (!param_ok(Tv, p)) {
+    if (tid == 0) store_nan_row(a, row, flags | kBadParam);
+    return;
+  }
+
+  // ---- pass 1: max, finite count, non-finite detection ----
+  float mx = -INFINITY;
+  int bad = 0;
+  uint32_t nfin = 0;
+  for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
+    if (z != z || z == INFINITY) bad = 1;
+    else if (z > -INFINITY) {
+      mx = fmaxf(mx, z);
+      ++nfin;
+    }
+  });
+  mx = block_max(mx, sf);
+  bad = block_max(bad, si);
+  nfin = uint32_t(block_sum(uint64_t(nfin), su64));
+  if (bad || nfin == 0) {
+    if (tid == 0) store_nan_row(a, row, flags | kNonFinite);
+    return;
+  }
+  const double m = double(mx);
+  const double invT = 1.0 / double(Tv);
+  const float cbin = float(invT) * kFBinPerNat;
+  const bool cut = p < 1.f;
+  auto bin_of = [&](float z) {
+    const float u = (mx - z) * cbin;
+    return u < float(kFBins - 1) ? int(u) : kFBins - 1;
+  };
+
+  // ---- pass 2: Z, sum e d, histogram of fixed-point masses over d bins ----
+  if (cut) {
+    for (int i = tid; i < kFBins; i += kF32T) hist[i] = 0ull;
+    if (tid == 0) ncand_s = 0;
+    __syncthreads();
+  }
+  double zt = 0.0, st = 0.0;
+  uint64_t wt = 0;
+  for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
+    if (!(z > -INFINITY)) return;
+    double d;
+    const float e = mass_of(z, m, invT, &d);
+    zt += double(e);
+    st += double(e) * d;
+    if (cut) {
+      const uint64_t w = fixed_mass(e);
+      if (w) {
+        wt += w;
+        atomicAdd(reinterpret_cast<unsigned long long*>(&hist[bin_of(z)]), (unsigned long long)w);
+      }
+    }
+  });
+  const double Z = block_sum(zt, sd);
+  const double S = block_sum(st, sd);
+
+  double Zs = Z, Ss = S;
+  uint32_t tau_key = 0;
+  uint32_t size = nfin;
+  if (cut) {
+    const uint64_t W = block_sum(wt, su64);
+    const uint64_t thr = uint64_t(ceil(double(p) * double(W)));
+    uint64_t above = 0;
+    int bstar = walk_bins<kF32T>(hist, kFBins, thr, &above, su64, si, &bslot);
+    if (bstar < 0) bstar = kFBins - 1;   // unreachable: the total mass reaches thr
+
+    // ---- pass 3: sums above the crossing bin; its elements' keys to LDS ----
+    double zs = 0.0, ss = 0.0;
+    uint32_t cnt = 0;
+    for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
+      if (!(z > -INFINITY)) return;
+      const int b = bin_of(z);
+      if (b < bstar) {
+        double d;
+        const float e = mass_of(z, m, invT, &d);
+        zs += double(e);
+        ss += double(e) * d;
+        ++cnt;
+      } else if (b == bstar) {
+        const unsigned int slot = atomicAdd(&ncand_s, 1u);
+        if (slot < unsigned(kCand)) cand[slot] = f32_key(z);
+      }
+    });
+    __syncthreads();
+    const int nc = int(ncand_s);
+    if (nc > kCand) {   // too many elements in one bin: the generic kernel resolves the row
+      if (tid == 0) a.fallback[row] = 1;
+      return;
+    }
+    // sort the crossing bin's keys, descending (bitonic over a power of two)
+    int n2 = 1;
+    while (n2 < nc) n2 <<= 1;
+    for (int i = nc + tid; i < n2; i += kF32T) cand[i] = 0u;
+    __syncthreads();
+    for (int k = 2; k <= n2; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += kF32T) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const uint32_t x = cand[i], w = cand[ixj];
+            if (((i & k) == 0) ? (x < w) : (x > w)) {
+              cand[i] = w;
+              cand[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    // walk the sorted keys until the cumulative mass reaches thr
+    uint64_t carry = above;
+    int tau_idx = nc - 1;
+    for (int base = 0; base < nc; base += kF32T) {
+      const int i = base + tid;
+      double d;
+      const uint64_t v = i < nc ? fixed_mass(mass_of(key_f32(cand[i]), m, invT, &d)) : 0ull;
+      uint64_t tot;
+      const uint64_t incl = block_inclusive_scan(v, su64, &tot);
+      const int c = (i < nc && carry + incl >= thr) ? tid : kF32T;
+      const int first = block_min(c, si);
+      if (first < kF32T) {
+        tau_idx = base + first;
+        break;
+      }
+      carry += tot;
+    }
+    tau_key = cand[tau_idx];
+    // truncated sums over the crossing bin's kept keys (key >= tau), in sorted order
+    uint64_t mgt = 0, mat = 0;
+    for (int i = tid; i < nc; i += kF32T) {
+      const uint32_t k = cand[i];
+      if (k < tau_key) continue;
+      double d;
+      const float e = mass_of(key_f32(k), m, invT, &d);
+      zs += double(e);
+      ss += double(e) * d;
+      ++cnt;
+      if (k > tau_key) mgt += fixed_mass(e);
+      else mat += fixed_mass(e);
+    }
+    Zs = block_sum(zs, sd);
+    Ss = block_sum(ss, sd);
+    size = uint32_t(block_sum(uint64_t(cnt), su64));
+    mgt = above + block_sum(mgt, su64);
+    mat = block_sum(mat, su64);
+    if (tid == 0) {
+      const double pp = double(p);
+      if (fabs(double(mgt) / double(W) - pp) <= kBoundaryEps ||
+          fabs(double(mgt + mat) / double(W) - pp) <= kBoundaryEps)
+        flags |= kBoundary;
+    }
+  }
+
+  if (tid == 0) {
+    const double logZ = log(Z), logZs = log(Zs);
+    float lpf = __builtin_nanf(""), lpt = __builtin_nanf("");
+    if (!(flags & kBadTarget)) {
+      const float zy = rowp[y];
+      if (!(zy > -INFINITY)) {
+        lpf = -INFINITY;
+        lpt = -INFINITY;
+        flags |= kOutside;
+      } else {
+        const double dy = (double(zy) - m) * invT;
+        lpf = float(dy - logZ);
+        if (!cut || f32_key(zy) >= tau_key) {
+          lpt = float(dy - logZs);
+        } else {
+          lpt = -INFINITY;
+          flags |= kOutside;
+        }
+      }
+    }
+    const float tau = cut ? key_f32(tau_key) : -INFINITY;
+    store_row(a, row, lpf, lpt, float(logZ - S / Z), float(logZs - Ss / Zs), int32_t(size), tau,
+              flags, float(m * invT + logZs), float(m * invT + Ss / Zs));
+  }
+}
+
 __global__ void reset_queue(unsigned int* q, unsigned int start) { *q = start; }
 
 }  // namespace
@@ -745,8 +1003,15 @@ hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipS
   args.row_queue = reinterpret_cast<unsigned int*>(workspace);
   args.fallback = reinterpret_cast<uint8_t*>(workspace) + 256;
   const dim3 grid(unsigned(a.n_rows));
-  if (dtype == 0) {  // fp32
-    hipLaunchKernelGGL(generic_rows<float>, grid, dim3(kGT), 0, stream, args, 0);
+  if (dtype == 0) {  // fp32: streaming kernel, then the rows it handed on
+    const bool vec4 = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.row_stride % 4 == 0);
+    if (vec4)
+      hipLaunchKernelGGL(f32_rows<true>, grid, dim3(kF32T), 0, stream, args);
+    else
+      hipLaunchKernelGGL(f32_rows<false>, grid, dim3(kF32T), 0, stream, args);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(generic_rows<float>, grid, dim3(kGT), 0, stream, args, 1);
     return hipGetLastError();
   }
   if (a.vocab < 16384) {
