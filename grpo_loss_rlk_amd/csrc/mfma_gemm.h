@@ -73,28 +73,34 @@ RLK_DEV void copy_offsets(uint32_t (&off)[kLoads], int64_t row0, int64_t nrows, 
   }
 }
 
-// Copies of stages t and t+1 (the 64-byte halves of the same rows), interleaved.
-// The copy reads its LDS destination from M0, which the statement sets and
-// declares clobbered (clang warns that M0 is reserved; declaring it is what
-// keeps the compiler from relying on an M0 value across the statement).
+// Copies of stages t and t+1 of one operand for one of this thread's slots
+// (the 64-byte halves of the same rows, back to back). The copy reads its
+// LDS destination from M0, which the statement sets and declares clobbered
+// (clang warns that M0 is reserved; declaring it is what keeps the compiler
+// from relying on an M0 value across the statement).
+struct CopyPlan {
+  uint4* lds_t[2];          // [A, B] stage t buffers
+  uint4* lds_t1[2];         // [A, B] stage t+1 buffers
+  const uint16_t* g_t[2];   // [A, B] global base of stage t
+};
+
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-RLK_DEV void copy_pair(uint4* lds_t, uint4* lds_t1, const uint16_t* gbase_t,
-                       const uint32_t (&off)[kLoads]) {
+RLK_DEV void copy_unit(const CopyPlan& cp, int u, const uint32_t (&oa)[kLoads],
+                       const uint32_t (&ob)[kLoads]) {
+  const int op = u / kLoads, j = u % kLoads;
   const int w = int(threadIdx.x) >> 6;
-  const uint16_t* gbase_t1 = gbase_t + kStageK;
-#pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
-    const uint32_t m0a = uint32_t(reinterpret_cast<uintptr_t>(lds_t + (w * kLoads + j) * 64));
-    const uint32_t m0b = uint32_t(reinterpret_cast<uintptr_t>(lds_t1 + (w * kLoads + j) * 64));
-    asm volatile(
-        "s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
-        "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %4"
-        :
-        : "s"(__builtin_amdgcn_readfirstlane(m0a)), "s"(__builtin_amdgcn_readfirstlane(m0b)),
-          "v"(off[j]), "s"(gbase_t), "s"(gbase_t1)
-        : "memory", "m0");
-  }
+  const uint32_t m0a = uint32_t(reinterpret_cast<uintptr_t>(cp.lds_t[op] + (w * kLoads + j) * 64));
+  const uint32_t m0b = uint32_t(reinterpret_cast<uintptr_t>(cp.lds_t1[op] + (w * kLoads + j) * 64));
+  const uint16_t* g0 = cp.g_t[op];
+  const uint16_t* g1 = g0 + kStageK;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %4"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(m0a)), "s"(__builtin_amdgcn_readfirstlane(m0b)),
+        "v"(op == 0 ? oa[j] : ob[j]), "s"(g0), "s"(g1)
+      : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -138,11 +144,27 @@ RLK_DEV void read_frag(Frags& f, int r, const char* stage, const FragAddr& fa) {
                                                       (x - 4) * 32 * kChunks * 16);
 }
 
-// The 32 MFMAs of one stage, with the 16 fragment reads of the next stage
-// interleaved into the first 16 so that they have landed before the barrier
-// that ends the stage.
+// Issue schedule inside a stage's 32 MFMAs (m = MFMA index): the 16
+// fragment reads of the next stage go after MFMAs read_slot(r), and the
+// stage's 4 copy units after MFMAs copy_slot(u), so that LDS reads and LDS
+// copies are spread over the stage and the last read lands before the
+// barrier that ends it.
+#ifndef RLK_GEMM_SCHED
+#define RLK_GEMM_SCHED 0
+#endif
+constexpr int read_slot(int r) {
+  return RLK_GEMM_SCHED == 0 ? r : (r / 2) * 3 + (r % 2);
+}
+constexpr int copy_slot(int u) {
+  return RLK_GEMM_SCHED == 0 ? 16 + 4 * u : 2 + 6 * u;
+}
+
+// The 32 MFMAs of one stage, the next stage's fragment reads and (with
+// kCopyOp = 0 or 1) the copy units of operand A or B of two later stages.
+template <int kCopyOp>
 RLK_DEV void stage_mma(f32x16 (&acc)[4][4], const Frags& cur, Frags& nxt, const char* next_stage,
-                       const FragAddr& fa) {
+                       const FragAddr& fa, const CopyPlan& cp, const uint32_t (&oa)[kLoads],
+                       const uint32_t (&ob)[kLoads]) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -152,12 +174,17 @@ RLK_DEV void stage_mma(f32x16 (&acc)[4][4], const Frags& cur, Frags& nxt, const 
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[kk][i], cur.b[kk][j], acc[i][j],
                                                             0, 0, 0);
         const int m = kk * 16 + i * 4 + j;
-        if (m < 16) {
-          read_frag(nxt, m, next_stage, fa);
-          // keep the issue order as written: the scheduler would otherwise
-          // sink the reads to their uses in the next stage
-          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (read_slot(r) == m) read_frag(nxt, r, next_stage, fa);
+        if (kCopyOp >= 0) {
+#pragma unroll
+          for (int u = 0; u < kLoads; ++u)
+            if (copy_slot(u) == m) copy_unit(cp, kCopyOp * kLoads + u, oa, ob);
         }
+        // keep the issue order as written: the scheduler would otherwise
+        // sink the reads to their uses in the next stage
+        __builtin_amdgcn_sched_barrier(0);
       }
 }
 
@@ -182,27 +209,42 @@ RLK_DEV void gemm_nt_tile(f32x16 (&acc)[4][4], Smem& smem, const uint16_t* A, in
   copy_offsets(ob, b_row0, b_rows, ldb);
   const uint16_t* a_base = A + a_row0 * lda;
   const uint16_t* b_base = B + b_row0 * ldb;
-  auto issue_pair = [&](int t) __attribute__((always_inline)) {   // stages t, t+1 (t even)
+  // copies of stages t, t+1 (t even); past the end, a repeat of the last two
+  auto plan = [&](int t) __attribute__((always_inline)) {
     const int64_t k0 = int64_t(t < nk ? t : nk - 2) * kStageK;
-    copy_pair(smem[t % kStages][0], smem[(t + 1) % kStages][0], a_base + k0, oa);
-    copy_pair(smem[t % kStages][1], smem[(t + 1) % kStages][1], b_base + k0, ob);
+    CopyPlan cp;
+    cp.lds_t[0] = smem[t % kStages][0];
+    cp.lds_t[1] = smem[t % kStages][1];
+    cp.lds_t1[0] = smem[(t + 1) % kStages][0];
+    cp.lds_t1[1] = smem[(t + 1) % kStages][1];
+    cp.g_t[0] = a_base + k0;
+    cp.g_t[1] = b_base + k0;
+    return cp;
   };
-  issue_pair(0);
-  issue_pair(2);
-  vm_wait_barrier<3 * kVmPerStage>();
+  {
+    const CopyPlan c0 = plan(0), c2 = plan(2);
+#pragma unroll
+    for (int u = 0; u < 2 * kLoads; ++u) copy_unit(c0, u, oa, ob);
+#pragma unroll
+    for (int u = 0; u < 2 * kLoads; ++u) copy_unit(c2, u, oa, ob);
+  }
+  vm_wait_barrier<2 * kVmPerStage>();   // stages 0 and 1 landed
   Frags f0, f1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) read_frag(f0, r, sbase, fa);
 
   // Step s: stage s (fragments in registers) is multiplied while stage s+1
-  // is read. Even s: after the barrier (stage s+1 landed; stages s-1 and s
-  // consumed) stages s+4 and s+5 are copied into the buffers of s-1 and s.
+  // is read. Stages s+4 and s+5 are copied into the buffers of stages s-1
+  // and s (both consumed before step s): operand A during step s, operand B
+  // during step s+1 (s even). Copies complete in issue order, so at the top
+  // of an even step the wait leaves the last 16 copies (pair s+2, s+3) in
+  // flight and at the top of an odd step the last 8 (A of pair s+4, s+5).
   for (int s = 0; s < nk; s += 2) {
-    vm_wait_barrier<2 * kVmPerStage>();   // in flight: s+2, s+3
-    issue_pair(s + 4);
-    stage_mma(acc, f0, f1, sbase + ((s + 1) % kStages) * kStageBytes, fa);
-    vm_wait_barrier<3 * kVmPerStage>();   // in flight: s+3, s+4, s+5
-    stage_mma(acc, f1, f0, sbase + ((s + 2) % kStages) * kStageBytes, fa);
+    vm_wait_barrier<2 * kVmPerStage>();   // stage s+1 landed
+    const CopyPlan cp = plan(s + 4);
+    stage_mma<0>(acc, f0, f1, sbase + ((s + 1) % kStages) * kStageBytes, fa, cp, oa, ob);
+    vm_wait_barrier<kVmPerStage>();       // stage s+2 landed
+    stage_mma<1>(acc, f1, f0, sbase + ((s + 2) % kStages) * kStageBytes, fa, cp, oa, ob);
   }
   vm_wait_barrier<0>();
 }

@@ -145,8 +145,8 @@ def _edge_rows(V, dtype):
     return arr, np.array(tg, dtype=np.int64)
 
 
-@pytest.mark.parametrize("dtype,V", [("f32", 5000), ("bf16", 151936), ("bf16", 20000),
-                                     ("bf16", 1000)])
+@pytest.mark.parametrize("dtype,V", [("f32", 5000), ("f32", 20000), ("bf16", 151936),
+                                     ("bf16", 20000), ("bf16", 1000)])
 @pytest.mark.parametrize("T,p", [(0.7, 0.95), (1.0, 1.0), (0.2, 1e-6), (1.8, 0.5)])
 def test_edge_rows(dtype, V, T, p):
     arr, y = _edge_rows(V, dtype)
