@@ -52,8 +52,22 @@ def _profile_traffic(name):
         return None
 
 
+def _spin_up(torch, seconds=0.3):
+    """Keep the GPU busy for a moment with unrelated bf16 matmuls so that the
+    timed steps see the clocks of sustained load (as inside a training step),
+    not the ramp out of idle while inputs were generated on the host."""
+    a = torch.randn(4096, 4096, device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(4096, 4096, device="cuda:0", dtype=torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+
+
 def _events_time(torch, fn, steps, warmup):
     """Mean and total ms of `fn` over `steps` calls, HIP events on the current stream."""
+    _spin_up(torch)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -246,8 +260,8 @@ def leg_copy(torch, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--legs", default="logits,fused,grpo,fused_bwd")
     ap.add_argument("--cpu-sample", type=int, default=1024,
                     help="rows of the logits workload the CPU oracle is timed on (0 = skip)")
@@ -267,7 +281,7 @@ def main():
         out_legs["logits"] = leg_logits(torch, rlk, synth, args.steps, args.warmup,
                                         args.cpu_sample)
     if "fused" in legs:
-        out_legs["fused"] = leg_fused(torch, rlk, synth, max(3, args.steps // 4), 1)
+        out_legs["fused"] = leg_fused(torch, rlk, synth, min(20, max(3, args.steps // 4)), 1)
     if "copy" in legs:
         out_legs["copy"] = leg_copy(torch, args.steps, args.warmup)
     if "grpo" in legs:

@@ -24,7 +24,6 @@ struct RowArgs {
   uint8_t* flags;         // nullable
   float* saved4;          // nullable [n_rows, 4]: log Z_S and E_q over S of z/T, threshold, 0
   uint8_t* fallback;      // workspace [n_rows]: rows the histogram path hands on
-  unsigned int* row_queue;   // workspace counter: next row for the persistent blocks
 };
 
 size_t logits_rows_workspace(int64_t n_rows, int64_t vocab, int dtype);

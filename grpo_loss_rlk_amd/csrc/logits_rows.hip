@@ -69,6 +69,237 @@ RLK_DEV void store_nan_row(const RowArgs& a, int64_t row, uint8_t flags) {
 }
 
 // ===========================================================================
+// Generic radix-select kernel (fp32 or bf16 rows of any length)
+// ===========================================================================
+constexpr int kGT = 256;
+constexpr int kBins1 = 4096;          // round 1: top 12 key bits
+constexpr int kBins2 = 1024;          // rounds 2, 3: 10 bits each
+constexpr double kFix = 549755813888.0;   // 2^39: fixed-point unit of mass (max element = 2^39)
+
+template <typename T>
+RLK_DEV float load_val(const T* p, int64_t i);
+template <>
+RLK_DEV float load_val<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+RLK_DEV float load_val<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+// exp((z - m) / T) in fp32 from an fp64 argument, and d = (z - m)/T in fp64
+RLK_DEV float mass_of(float z, double m, double invT, double* d) {
+  *d = (double(z) - m) * invT;
+  return expf(float(*d));
+}
+
+RLK_DEV uint64_t fixed_mass(float e) { return uint64_t(double(e) * kFix + 0.5); }
+
+// Walk `bins` from index `start` downward until carry + running sum >= thr.
+// Returns the bin, or -1; *above receives the mass strictly above that bin.
+template <int NT>
+RLK_DEV int walk_down(const uint64_t* bins, int start, uint64_t thr, uint64_t carry,
+                      uint64_t* above, uint64_t* su64, int* si, uint64_t* bslot) {
+  for (int base = start; base >= 0; base -= NT) {
+    const int b = base - int(threadIdx.x);
+    const uint64_t v = b >= 0 ? bins[b] : 0ull;
+    uint64_t tot;
+    const uint64_t incl = block_inclusive_scan(v, su64, &tot);
+    const int cand = (v != 0ull && carry + incl >= thr) ? int(threadIdx.x) : NT;
+    const int first = block_min(cand, si);
+    if (first < NT) {
+      if (int(threadIdx.x) == first) *bslot = carry + incl - v;
+      __syncthreads();
+      *above = *bslot;
+      __syncthreads();
+      return base - first;
+    }
+    carry += tot;
+  }
+  *above = carry;
+  return -1;
+}
+
+// LDS of the generic path: 4096 u64 bins plus reduction scratch.
+struct GenScratch {
+  uint64_t hist[kBins1];
+  double sd[16];
+  uint64_t su64[16];
+  int si[16];
+  float sf[16];
+  uint64_t bslot;
+};
+
+// One row by the generic multi-pass algorithm, with a block of NT threads.
+template <typename T, int NT>
+RLK_DEV void generic_row(const RowArgs& a, int64_t row, GenScratch& g) {
+  uint64_t* hist = g.hist;
+  double* sd = g.sd;
+  uint64_t* su64 = g.su64;
+  int* si = g.si;
+  float* sf = g.sf;
+  uint64_t& bslot = g.bslot;
+  const int tid = threadIdx.x;
+  const int64_t V = a.vocab;
+  const T* rowp = reinterpret_cast<const T*>(a.logits) + row * a.row_stride;
+
+  float Tv = a.t_row ? a.t_row[row] : a.temperature;
+  float p = a.p_row ? a.p_row[row] : a.top_p;
+  const int64_t y = a.targets[row];
+  uint8_t flags = 0;
+  if (y < 0 || y >= V) flags |= kBadTarget;
+  if (!param_ok(Tv, p)) {
+    if (tid == 0) store_nan_row(a, row, flags | kBadParam);
+    return;
+  }
+
+  // ---- pass 1: max, finite count, non-finite detection ----
+  float mx = -INFINITY;
+  int bad = 0;
+  uint32_t nfin = 0;
+  for (int64_t i = tid; i < V; i += NT) {
+    const float z = load_val(rowp, i);
+    if (z != z || z == INFINITY) bad = 1;
+    else if (z > -INFINITY) {
+      mx = fmaxf(mx, z);
+      ++nfin;
+    }
+  }
+  mx = block_max(mx, sf);
+  bad = block_max(bad, si);
+  nfin = uint32_t(block_sum(uint64_t(nfin), su64));
+  if (bad || nfin == 0) {
+    if (tid == 0) store_nan_row(a, row, flags | kNonFinite);
+    return;
+  }
+  const double m = double(mx);
+  const double invT = 1.0 / double(Tv);
+  const bool cut = p < 1.f;
+
+  // ---- pass 2: Z, sum e*d, round-1 histogram of fixed-point masses ----
+  for (int i = tid; i < kBins1; i += NT) hist[i] = 0ull;
+  __syncthreads();
+  double zt = 0.0, st = 0.0;
+  uint64_t wt = 0;
+  for (int64_t i = tid; i < V; i += NT) {
+    const float z = load_val(rowp, i);
+    if (!(z > -INFINITY)) continue;
+    double d;
+    const float e = mass_of(z, m, invT, &d);
+    zt += double(e);
+    st += double(e) * d;
+    if (cut) {
+      const uint64_t w = fixed_mass(e);
+      if (w) {
+        wt += w;
+        atomicAdd(reinterpret_cast<unsigned long long*>(&hist[f32_key(z) >> 20]),
+                  (unsigned long long)w);
+      }
+    }
+  }
+  const double Z = block_sum(zt, sd);
+  const double S = block_sum(st, sd);
+
+  double Zs = Z, Ss = S;
+  uint32_t tau_key = 0;
+  uint32_t size = nfin;
+  if (cut) {
+    const uint64_t W = block_sum(wt, su64);
+    const uint64_t thr = uint64_t(ceil(double(p) * double(W)));
+    // round 1
+    uint64_t above = 0;
+    int d1 = walk_down<NT>(hist, kBins1 - 1, thr, 0ull, &above, su64, si, &bslot);
+    if (d1 < 0) d1 = 0;   // unreachable: the total mass reaches thr
+    // round 2
+    __syncthreads();
+    for (int i = tid; i < kBins2; i += NT) hist[i] = 0ull;
+    __syncthreads();
+    for (int64_t i = tid; i < V; i += NT) {
+      const float z = load_val(rowp, i);
+      if (!(z > -INFINITY)) continue;
+      const uint32_t k = f32_key(z);
+      if (int(k >> 20) != d1) continue;
+      double d;
+      const uint64_t w = fixed_mass(mass_of(z, m, invT, &d));
+      if (w) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[(k >> 10) & 0x3ffu]),
+                       (unsigned long long)w);
+    }
+    __syncthreads();
+    int d2 = walk_down<NT>(hist, kBins2 - 1, thr, above, &above, su64, si, &bslot);
+    if (d2 < 0) d2 = 0;
+    // round 3
+    __syncthreads();
+    for (int i = tid; i < kBins2; i += NT) hist[i] = 0ull;
+    __syncthreads();
+    const uint32_t pre = (uint32_t(d1) << 10) | uint32_t(d2);
+    for (int64_t i = tid; i < V; i += NT) {
+      const float z = load_val(rowp, i);
+      if (!(z > -INFINITY)) continue;
+      const uint32_t k = f32_key(z);
+      if ((k >> 10) != pre) continue;
+      double d;
+      const uint64_t w = fixed_mass(mass_of(z, m, invT, &d));
+      if (w) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[k & 0x3ffu]),
+                       (unsigned long long)w);
+    }
+    __syncthreads();
+    int d3 = walk_down<NT>(hist, kBins2 - 1, thr, above, &above, su64, si, &bslot);
+    if (d3 < 0) d3 = 0;
+    tau_key = (pre << 10) | uint32_t(d3);
+    const uint64_t at = hist[d3];
+    if (tid == 0) {
+      const double pp = double(p);
+      if (fabs(double(above) / double(W) - pp) <= kBoundaryEps ||
+          fabs(double(above + at) / double(W) - pp) <= kBoundaryEps)
+        flags |= kBoundary;
+    }
+    // final pass: truncated sums over S = {key >= tau}
+    double zs = 0.0, ss = 0.0;
+    uint32_t cnt = 0;
+    for (int64_t i = tid; i < V; i += NT) {
+      const float z = load_val(rowp, i);
+      if (!(z > -INFINITY) || f32_key(z) < tau_key) continue;
+      double d;
+      const float e = mass_of(z, m, invT, &d);
+      zs += double(e);
+      ss += double(e) * d;
+      ++cnt;
+    }
+    Zs = block_sum(zs, sd);
+    Ss = block_sum(ss, sd);
+    size = uint32_t(block_sum(uint64_t(cnt), su64));
+  }
+
+  if (tid == 0) {
+    const double logZ = log(Z), logZs = log(Zs);
+    float lpf = __builtin_nanf(""), lpt = __builtin_nanf("");
+    if (!(flags & kBadTarget)) {
+      const float zy = load_val(rowp, y);
+      if (!(zy > -INFINITY)) {
+        lpf = -INFINITY;
+        lpt = -INFINITY;
+        flags |= kOutside;
+      } else {
+        const double dy = (double(zy) - m) * invT;
+        lpf = float(dy - logZ);
+        if (!cut || f32_key(zy) >= tau_key) {
+          lpt = float(dy - logZs);
+        } else {
+          lpt = -INFINITY;
+          flags |= kOutside;
+        }
+      }
+    }
+    const float tau = cut ? key_f32(tau_key) : -INFINITY;
+    store_row(a, row, lpf, lpt, float(logZ - S / Z), float(logZs - Ss / Zs), int32_t(size), tau,
+              flags, float(m * invT + logZs), float(m * invT + Ss / Zs));
+  }
+}
+
+
+template <typename T>
+__global__ __launch_bounds__(kGT) void generic_rows(RowArgs a) {
+  __shared__ GenScratch g;
+  generic_row<T, kGT>(a, int64_t(blockIdx.x), g);
+}
+
+// ===========================================================================
 // bf16 pattern-count histogram kernel
 // ===========================================================================
 constexpr int kHT = 1024;                        // threads per block (one block per CU)
@@ -452,17 +683,18 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
   if (ft == 0) special[0] = special[1] = special[2] = 0;
 }
 
-// One persistent block per CU. Rows come from a queue (a counter starting at
-// gridDim.x), so a block that draws slow rows takes fewer. Step s: waves
-// 0..kStreamWaves-1 stream row R_s into counter buffer s & 1 while the
-// finisher waves post-process row R_{s-1} from the other buffer; one block
-// barrier separates the steps.
+// One persistent block per CU; block b takes rows b, b + G, b + 2G, ...
+// (G = gridDim.x). Step s: waves 0..kStreamWaves-1 stream row R_s into
+// counter buffer s & 1 while the finisher waves post-process row R_{s-1}
+// from the other buffer; one block barrier separates the steps. Rows the
+// finishers hand on (see finish_row) are then redone by the whole block with
+// the generic algorithm, in the same launch.
 template <bool kVec>
 __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
   __shared__ uint32_t hist[2][kHWords];
   __shared__ uint32_t special[2][4];
-  __shared__ int64_t queued[2];
   __shared__ FinScratch fs;
+  static_assert(sizeof(GenScratch) <= sizeof(hist), "generic scratch reuses the counters");
 
   const int tid = threadIdx.x, wid = tid / kWave;
   const int64_t V = a.vocab;
@@ -484,7 +716,6 @@ __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
     const int b = s & 1;
     if (wid < kStreamWaves) {
       if (cur < N) {
-        if (tid == 0) queued[b] = int64_t(atomicAdd(a.row_queue, 1u));
         const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.logits) + cur * a.row_stride;
         uint32_t* h = hist[b];
         uint32_t* sp = special[b];
@@ -509,222 +740,16 @@ __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
     }
     __syncthreads();
     prev = cur;
-    cur = (cur < N) ? queued[b] : N;
+    cur = (cur < N) ? cur + int64_t(gridDim.x) : N;
   }
-}
-
-// ===========================================================================
-// Generic radix-select kernel (fp32 or bf16 rows of any length)
-// ===========================================================================
-constexpr int kGT = 256;
-constexpr int kBins1 = 4096;          // round 1: top 12 key bits
-constexpr int kBins2 = 1024;          // rounds 2, 3: 10 bits each
-constexpr double kFix = 549755813888.0;   // 2^39: fixed-point unit of mass (max element = 2^39)
-
-template <typename T>
-RLK_DEV float load_val(const T* p, int64_t i);
-template <>
-RLK_DEV float load_val<float>(const float* p, int64_t i) { return p[i]; }
-template <>
-RLK_DEV float load_val<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
-
-// exp((z - m) / T) in fp32 from an fp64 argument, and d = (z - m)/T in fp64
-RLK_DEV float mass_of(float z, double m, double invT, double* d) {
-  *d = (double(z) - m) * invT;
-  return expf(float(*d));
-}
-
-RLK_DEV uint64_t fixed_mass(float e) { return uint64_t(double(e) * kFix + 0.5); }
-
-// Walk `bins` from index `start` downward until carry + running sum >= thr.
-// Returns the bin, or -1; *above receives the mass strictly above that bin.
-RLK_DEV int walk_down(const uint64_t* bins, int start, uint64_t thr, uint64_t carry,
-                      uint64_t* above, uint64_t* su64, int* si, uint64_t* bslot) {
-  for (int base = start; base >= 0; base -= kGT) {
-    const int b = base - int(threadIdx.x);
-    const uint64_t v = b >= 0 ? bins[b] : 0ull;
-    uint64_t tot;
-    const uint64_t incl = block_inclusive_scan(v, su64, &tot);
-    const int cand = (v != 0ull && carry + incl >= thr) ? int(threadIdx.x) : kGT;
-    const int first = block_min(cand, si);
-    if (first < kGT) {
-      if (int(threadIdx.x) == first) *bslot = carry + incl - v;
+  // rows handed on by this block's finishers (flags written before the last
+  // barrier), redone with the counters' LDS as scratch
+  GenScratch& gs = *reinterpret_cast<GenScratch*>(&hist[0][0]);
+  for (int64_t row = blockIdx.x; row < N; row += gridDim.x) {
+    if (a.fallback[row]) {
+      generic_row<uint16_t, kHT>(a, row, gs);
       __syncthreads();
-      *above = *bslot;
-      __syncthreads();
-      return base - first;
     }
-    carry += tot;
-  }
-  *above = carry;
-  return -1;
-}
-
-template <typename T>
-__global__ __launch_bounds__(kGT) void generic_rows(RowArgs a, int only_fallback) {
-  __shared__ uint64_t hist[kBins1];
-  __shared__ double sd[kGT / kWave];
-  __shared__ uint64_t su64[kGT / kWave];
-  __shared__ int si[kGT / kWave];
-  __shared__ float sf[kGT / kWave];
-  __shared__ uint64_t bslot;
-
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  if (only_fallback && a.fallback[row] == 0) return;
-  const int64_t V = a.vocab;
-  const T* rowp = reinterpret_cast<const T*>(a.logits) + row * a.row_stride;
-
-  float Tv = a.t_row ? a.t_row[row] : a.temperature;
-  float p = a.p_row ? a.p_row[row] : a.top_p;
-  const int64_t y = a.targets[row];
-  uint8_t flags = 0;
-  if (y < 0 || y >= V) flags |= kBadTarget;
-  if (!param_ok(Tv, p)) {
-    if (tid == 0) store_nan_row(a, row, flags | kBadParam);
-    return;
-  }
-
-  // ---- pass 1: max, finite count, non-finite detection ----
-  float mx = -INFINITY;
-  int bad = 0;
-  uint32_t nfin = 0;
-  for (int64_t i = tid; i < V; i += kGT) {
-    const float z = load_val(rowp, i);
-    if (z != z || z == INFINITY) bad = 1;
-    else if (z > -INFINITY) {
-      mx = fmaxf(mx, z);
-      ++nfin;
-    }
-  }
-  mx = block_max(mx, sf);
-  bad = block_max(bad, si);
-  nfin = uint32_t(block_sum(uint64_t(nfin), su64));
-  if (bad || nfin == 0) {
-    if (tid == 0) store_nan_row(a, row, flags | kNonFinite);
-    return;
-  }
-  const double m = double(mx);
-  const double invT = 1.0 / double(Tv);
-  const bool cut = p < 1.f;
-
-  // ---- pass 2: Z, sum e*d, round-1 histogram of fixed-point masses ----
-  for (int i = tid; i < kBins1; i += kGT) hist[i] = 0ull;
-  __syncthreads();
-  double zt = 0.0, st = 0.0;
-  uint64_t wt = 0;
-  for (int64_t i = tid; i < V; i += kGT) {
-    const float z = load_val(rowp, i);
-    if (!(z > -INFINITY)) continue;
-    double d;
-    const float e = mass_of(z, m, invT, &d);
-    zt += double(e);
-    st += double(e) * d;
-    if (cut) {
-      const uint64_t w = fixed_mass(e);
-      if (w) {
-        wt += w;
-        atomicAdd(reinterpret_cast<unsigned long long*>(&hist[f32_key(z) >> 20]),
-                  (unsigned long long)w);
-      }
-    }
-  }
-  const double Z = block_sum(zt, sd);
-  const double S = block_sum(st, sd);
-
-  double Zs = Z, Ss = S;
-  uint32_t tau_key = 0;
-  uint32_t size = nfin;
-  if (cut) {
-    const uint64_t W = block_sum(wt, su64);
-    const uint64_t thr = uint64_t(ceil(double(p) * double(W)));
-    // round 1
-    uint64_t above = 0;
-    int d1 = walk_down(hist, kBins1 - 1, thr, 0ull, &above, su64, si, &bslot);
-    if (d1 < 0) d1 = 0;   // unreachable: the total mass reaches thr
-    // round 2
-    __syncthreads();
-    for (int i = tid; i < kBins2; i += kGT) hist[i] = 0ull;
-    __syncthreads();
-    for (int64_t i = tid; i < V; i += kGT) {
-      const float z = load_val(rowp, i);
-      if (!(z > -INFINITY)) continue;
-      const uint32_t k = f32_key(z);
-      if (int(k >> 20) != d1) continue;
-      double d;
-      const uint64_t w = fixed_mass(mass_of(z, m, invT, &d));
-      if (w) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[(k >> 10) & 0x3ffu]),
-                       (unsigned long long)w);
-    }
-    __syncthreads();
-    int d2 = walk_down(hist, kBins2 - 1, thr, above, &above, su64, si, &bslot);
-    if (d2 < 0) d2 = 0;
-    // round 3
-    __syncthreads();
-    for (int i = tid; i < kBins2; i += kGT) hist[i] = 0ull;
-    __syncthreads();
-    const uint32_t pre = (uint32_t(d1) << 10) | uint32_t(d2);
-    for (int64_t i = tid; i < V; i += kGT) {
-      const float z = load_val(rowp, i);
-      if (!(z > -INFINITY)) continue;
-      const uint32_t k = f32_key(z);
-      if ((k >> 10) != pre) continue;
-      double d;
-      const uint64_t w = fixed_mass(mass_of(z, m, invT, &d));
-      if (w) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[k & 0x3ffu]),
-                       (unsigned long long)w);
-    }
-    __syncthreads();
-    int d3 = walk_down(hist, kBins2 - 1, thr, above, &above, su64, si, &bslot);
-    if (d3 < 0) d3 = 0;
-    tau_key = (pre << 10) | uint32_t(d3);
-    const uint64_t at = hist[d3];
-    if (tid == 0) {
-      const double pp = double(p);
-      if (fabs(double(above) / double(W) - pp) <= kBoundaryEps ||
-          fabs(double(above + at) / double(W) - pp) <= kBoundaryEps)
-        flags |= kBoundary;
-    }
-    // final pass: truncated sums over S = {key >= tau}
-    double zs = 0.0, ss = 0.0;
-    uint32_t cnt = 0;
-    for (int64_t i = tid; i < V; i += kGT) {
-      const float z = load_val(rowp, i);
-      if (!(z > -INFINITY) || f32_key(z) < tau_key) continue;
-      double d;
-      const float e = mass_of(z, m, invT, &d);
-      zs += double(e);
-      ss += double(e) * d;
-      ++cnt;
-    }
-    Zs = block_sum(zs, sd);
-    Ss = block_sum(ss, sd);
-    size = uint32_t(block_sum(uint64_t(cnt), su64));
-  }
-
-  if (tid == 0) {
-    const double logZ = log(Z), logZs = log(Zs);
-    float lpf = __builtin_nanf(""), lpt = __builtin_nanf("");
-    if (!(flags & kBadTarget)) {
-      const float zy = load_val(rowp, y);
-      if (!(zy > -INFINITY)) {
-        lpf = -INFINITY;
-        lpt = -INFINITY;
-        flags |= kOutside;
-      } else {
-        const double dy = (double(zy) - m) * invT;
-        lpf = float(dy - logZ);
-        if (!cut || f32_key(zy) >= tau_key) {
-          lpt = float(dy - logZs);
-        } else {
-          lpt = -INFINITY;
-          flags |= kOutside;
-        }
-      }
-    }
-    const float tau = cut ? key_f32(tau_key) : -INFINITY;
-    store_row(a, row, lpf, lpt, float(logZ - S / Z), float(logZs - Ss / Zs), int32_t(size), tau,
-              flags, float(m * invT + logZs), float(m * invT + Ss / Zs));
   }
 }
 
@@ -736,7 +761,8 @@ __global__ __launch_bounds__(kGT) void generic_rows(RowArgs a, int only_fallback
 // crossing bin holds only larger values). Pass 3: the truncated sums of the
 // bins above the crossing bin, and the keys of the crossing bin's elements
 // collected in LDS; sorted there, they give the exact threshold. A row whose
-// crossing bin holds more than kCand elements is handed to generic_rows.
+// crossing bin holds more than kCand elements is redone by the generic
+// algorithm in the same block.
 // ===========================================================================
 constexpr int kF32T = 1024;           // threads per block
 constexpr int kFBins = 4096;          // bins of d: [b / 64, (b + 1) / 64) nats below the max
@@ -787,8 +813,15 @@ RLK_DEV void for_each_f32(const float* rowp, int64_t V, F&& f) {
 
 template <bool kVec>
 __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
-  __shared__ uint64_t hist[kFBins];
-  __shared__ uint32_t cand[kCand];
+  __shared__ union {
+    struct {
+      uint64_t hist[kFBins];
+      uint32_t cand[kCand];
+    } f;
+    GenScratch g;
+  } sm;
+  uint64_t* hist = sm.f.hist;
+  uint32_t* cand = sm.f.cand;
   __shared__ double sd[kF32T / kWave];
   __shared__ uint64_t su64[kF32T / kWave];
   __shared__ int si[kF32T / kWave];
@@ -800,7 +833,6 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
   const int64_t row = blockIdx.x;
   const int64_t V = a.vocab;
   const float* rowp = reinterpret_cast<const float*>(a.logits) + row * a.row_stride;
-  if (tid == 0) a.fallback[row] = 0;
 
   const float Tv = a.t_row ? a.t_row[row] : a.temperature;
   const float p = a.p_row ? a.p_row[row] : a.top_p;
@@ -893,8 +925,9 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
     });
     __syncthreads();
     const int nc = int(ncand_s);
-    if (nc > kCand) {   // too many elements in one bin: the generic kernel resolves the row
-      if (tid == 0) a.fallback[row] = 1;
+    if (nc > kCand) {   // too many elements in one bin: the generic algorithm resolves the row
+      __syncthreads();
+      generic_row<float, kF32T>(a, row, sm.g);
       return;
     }
     // sort the crossing bin's keys, descending (bitonic over a power of two)
@@ -986,36 +1019,31 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
   }
 }
 
-__global__ void reset_queue(unsigned int* q, unsigned int start) { *q = start; }
 
 }  // namespace
 
-// workspace: [0, 256) row-queue counter, [256, 256 + n_rows) hand-off flags
+// workspace: [0, n_rows) hand-off flags of the bf16 histogram path
 size_t logits_rows_workspace(int64_t n_rows, int64_t vocab, int dtype) {
   (void)vocab;
   (void)dtype;
-  return 256 + size_t((n_rows + 255) / 256 * 256);
+  return size_t((n_rows + 255) / 256 * 256);
 }
 
 hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
   RowArgs args = a;
-  args.row_queue = reinterpret_cast<unsigned int*>(workspace);
-  args.fallback = reinterpret_cast<uint8_t*>(workspace) + 256;
+  args.fallback = reinterpret_cast<uint8_t*>(workspace);
   const dim3 grid(unsigned(a.n_rows));
-  if (dtype == 0) {  // fp32: streaming kernel, then the rows it handed on
+  if (dtype == 0) {  // fp32
     const bool vec4 = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.row_stride % 4 == 0);
     if (vec4)
       hipLaunchKernelGGL(f32_rows<true>, grid, dim3(kF32T), 0, stream, args);
     else
       hipLaunchKernelGGL(f32_rows<false>, grid, dim3(kF32T), 0, stream, args);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(generic_rows<float>, grid, dim3(kGT), 0, stream, args, 1);
     return hipGetLastError();
   }
   if (a.vocab < 16384) {
-    hipLaunchKernelGGL(generic_rows<uint16_t>, grid, dim3(kGT), 0, stream, args, 0);
+    hipLaunchKernelGGL(generic_rows<uint16_t>, grid, dim3(kGT), 0, stream, args);
     return hipGetLastError();
   }
   const bool vec = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.row_stride % 8 == 0);
@@ -1027,15 +1055,10 @@ hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipS
     n_cu = 256;
   const int64_t nb = int64_t(n_cu);
   const dim3 pgrid(unsigned(a.n_rows < nb ? a.n_rows : nb));
-  hipLaunchKernelGGL(reset_queue, dim3(1), dim3(1), 0, stream, args.row_queue, pgrid.x);
   if (vec)
     hipLaunchKernelGGL(bf16_hist_rows<true>, pgrid, dim3(kHT), 0, stream, args);
   else
     hipLaunchKernelGGL(bf16_hist_rows<false>, pgrid, dim3(kHT), 0, stream, args);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // rows the histogram kernel handed on (wrapped counters, uncounted values)
-  hipLaunchKernelGGL(generic_rows<uint16_t>, grid, dim3(kGT), 0, stream, args, 1);
   return hipGetLastError();
 }
 
