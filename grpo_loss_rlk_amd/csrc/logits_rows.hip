@@ -683,6 +683,14 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
   if (ft == 0) special[0] = special[1] = special[2] = 0;
 }
 
+// 16 bytes of a row read once: a non-temporal load, so the stream does not
+// displace reusable lines in the caches.
+RLK_DEV uint4 stream_load(const uint4* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // One persistent block per CU; block b takes rows b, b + G, b + 2G, ...
 // (G = gridDim.x). Step s: waves 0..kStreamWaves-1 stream row R_s into
 // counter buffer s & 1 while the finisher waves post-process row R_{s-1}
@@ -725,11 +733,11 @@ __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
           for (; i + (kUnroll - 1) * kStreamers < nvec; i += kUnroll * kStreamers) {
             uint4 q[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) q[u] = v4[i + u * kStreamers];
+            for (int u = 0; u < kUnroll; ++u) q[u] = stream_load(v4 + i + u * kStreamers);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) count8(h, sp, q[u]);
           }
-          for (; i < nvec; i += kStreamers) count8(h, sp, v4[i]);
+          for (; i < nvec; i += kStreamers) count8(h, sp, stream_load(v4 + i));
           for (int64_t j = (nvec << 3) + tid; j < V; j += kStreamers) count_code(h, sp, rowp[j]);
         } else {
           for (int64_t j = tid; j < V; j += kStreamers) count_code(h, sp, rowp[j]);
