@@ -304,7 +304,6 @@ __global__ __launch_bounds__(kGT) void generic_rows(RowArgs a) {
 // ===========================================================================
 constexpr int kHT = 1024;                        // threads per block (one block per CU)
 constexpr int kFW = 4;                           // finisher waves (one per SIMD)
-constexpr int kFT = kFW * kWave;                 // finisher threads
 constexpr int kStreamWaves = kHT / kWave - kFW;  // streaming waves
 constexpr int kStreamers = kStreamWaves * kWave; // streaming threads
 constexpr int kHWords = 16384;                   // 64 KB of 16-bit counter pairs per buffer
@@ -411,16 +410,18 @@ RLK_DEV float code_mass(float dv, MassScale k) {
 // counter: every finisher wave runs the same uniform sequence of syncs, and
 // all of them are resident in the block, so each wait ends.
 // ---------------------------------------------------------------------------
+constexpr int kMaxFW = kHT / kWave;              // every wave finishes the block's last row
 struct FinScratch {
-  int i[8][kFW];
-  double d[6][kFW];
+  int i[8][kMaxFW];
+  double d[6][kMaxFW];
   double bd[3];
   int bi[2];
   unsigned int bar;
 };
 
+template <int FW>
 RLK_DEV void fsync(unsigned int* bar, unsigned int& epoch) {
-  epoch += kFW;
+  epoch += FW;
   if ((threadIdx.x & (kWave - 1)) == 0)
     __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   while (__hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < epoch)
@@ -430,9 +431,11 @@ RLK_DEV void fsync(unsigned int* bar, unsigned int& epoch) {
 // Everything after counting, for one row: checksum and occupied range, max,
 // Z and entropy, the top-p walk, outputs (or the hand-off flag), and zeroing
 // the counters it used so the buffer is ready for the row after next.
+template <int FW>
 RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t* special,
                         FinScratch& fs, unsigned int& epoch) {
-  const int ft = int(threadIdx.x) - kStreamers;   // 0 .. kFT-1
+  constexpr int FT = FW * kWave;                  // finisher threads: the last FT of the block
+  const int ft = int(threadIdx.x) - (kHT - FT);    // 0 .. FT-1
   const int lane = ft & (kWave - 1), fw = ft / kWave;
   const int64_t V = a.vocab;
   const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.logits) + row * a.row_stride;
@@ -449,8 +452,8 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
     uint32_t t_acc = 0;
     int tmin = 0x7fff, tmax = -1;
 #pragma unroll 4
-    for (int k = 0; k < kHWords / 4 / kFT; ++k) {
-      const int q = ft + k * kFT;
+    for (int k = 0; k < kHWords / 4 / FT; ++k) {
+      const int q = ft + k * FT;
       const uint4 x = h4[q];
       t_acc = __builtin_amdgcn_sad_u16(x.x, 0u, t_acc);
       t_acc = __builtin_amdgcn_sad_u16(x.y, 0u, t_acc);
@@ -471,10 +474,10 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
       fs.i[2][fw] = mx_w;
     }
   }
-  fsync(&fs.bar, epoch);
-  const int tot = fold_partials(fs.i[0], kFW);
-  const int wmin = wave_min_i32(lane < kFW ? fs.i[1][lane] : 0x7fff);
-  const int wmax = wave_max_i32(lane < kFW ? fs.i[2][lane] : -1);
+  fsync<FW>(&fs.bar, epoch);
+  const int tot = fold_partials(fs.i[0], FW);
+  const int wmin = wave_min_i32(lane < FW ? fs.i[1][lane] : 0x7fff);
+  const int wmax = wave_max_i32(lane < FW ? fs.i[2][lane] : -1);
 
   uint8_t flags = 0;
   if (!y_ok) flags |= kBadTarget;
@@ -493,23 +496,23 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
     // largest value: highest magnitude with a positive pattern; else zero;
     // else the negative pattern of smallest magnitude
     int maxpos = -1, minneg = 0x8000;
-    for (int m0 = wmax; m0 >= wmin && maxpos < 0; m0 -= kFT) {
+    for (int m0 = wmax; m0 >= wmin && maxpos < 0; m0 -= FT) {
       const int m = m0 - ft;
       const bool hit = m >= wmin && (hist[widx(m >= wmin ? m : wmin)] & 0xffffu);
       const uint64_t bal = __ballot(hit);
       if (lane == 0) fs.i[3][fw] = bal ? m0 - fw * kWave - (__ffsll((unsigned long long)bal) - 1) : -1;
-      fsync(&fs.bar, epoch);
-      maxpos = wave_max_i32(lane < kFW ? fs.i[3][lane] : -1);
-      fsync(&fs.bar, epoch);
+      fsync<FW>(&fs.bar, epoch);
+      maxpos = wave_max_i32(lane < FW ? fs.i[3][lane] : -1);
+      fsync<FW>(&fs.bar, epoch);
     }
-    for (int m0 = wmin; m0 <= wmax && maxpos < 0 && n_zero == 0 && minneg == 0x8000; m0 += kFT) {
+    for (int m0 = wmin; m0 <= wmax && maxpos < 0 && n_zero == 0 && minneg == 0x8000; m0 += FT) {
       const int m = m0 + ft;
       const bool hit = m <= wmax && (hist[widx(m <= wmax ? m : wmax)] >> 16);
       const uint64_t bal = __ballot(hit);
       if (lane == 0) fs.i[4][fw] = bal ? m0 + fw * kWave + (__ffsll((unsigned long long)bal) - 1) : 0x8000;
-      fsync(&fs.bar, epoch);
-      minneg = wave_min_i32(lane < kFW ? fs.i[4][lane] : 0x8000);
-      fsync(&fs.bar, epoch);
+      fsync<FW>(&fs.bar, epoch);
+      minneg = wave_min_i32(lane < FW ? fs.i[4][lane] : 0x8000);
+      fsync<FW>(&fs.bar, epoch);
     }
     float mval;
     int kmax;
@@ -530,7 +533,7 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
     // ---- Z and sum e*d over the distinct values ----
     {
       double zt = 0.0, st = 0.0;
-      for (int m = wmin + ft; m <= wmax; m += kFT) {
+      for (int m = wmin + ft; m <= wmax; m += FT) {
         const uint32_t x = hist[widx(m)];
         if (x & 0xffffu) {
           const float dv = bf16_to_f32(uint16_t(m)) - mval;
@@ -558,11 +561,11 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
         fs.d[1][fw] = st;
       }
     }
-    fsync(&fs.bar, epoch);
-    const double Z = fold_partials(fs.d[0], kFW);
-    const double S = fold_partials(fs.d[1], kFW);
+    fsync<FW>(&fs.bar, epoch);
+    const double Z = fold_partials(fs.d[0], FW);
+    const double S = fold_partials(fs.d[1], FW);
 
-    // ---- top-p cut: walk merged keys down from the max, kFT at a time ----
+    // ---- top-p cut: walk merged keys down from the max, FT at a time ----
     double Zs = Z, Ss = S, Mgt = 0.0;
     uint32_t tau_key = 0;
     int size = int(V) - n_neginf;
@@ -573,7 +576,7 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
       int cn = 0;
       bool found = false;
       int par = 0;
-      for (int k0 = kmax; !found && k0 >= kKeyLo; k0 -= kFT, par ^= 1) {
+      for (int k0 = kmax; !found && k0 >= kKeyLo; k0 -= FT, par ^= 1) {
         const int key = k0 - ft;
         double mass = 0.0, ms = 0.0;
         int n = 0;
@@ -594,16 +597,16 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
           fs.d[3 + 2 * par][fw] = is;
           fs.i[5 + par][fw] = in;
         }
-        fsync(&fs.bar, epoch);
-        // wave partials in lanes 0..kFW-1: exclusive prefixes, and the
+        fsync<FW>(&fs.bar, epoch);
+        // wave partials in lanes 0..FW-1: exclusive prefixes, and the
         // inclusive value exactly as the crossing wave's last lane forms it
-        const double pz = lane < kFW ? fs.d[2 + 2 * par][lane] : 0.0;
-        const double ps = lane < kFW ? fs.d[3 + 2 * par][lane] : 0.0;
-        const int pn = lane < kFW ? fs.i[5 + par][lane] : 0;
+        const double pz = lane < FW ? fs.d[2 + 2 * par][lane] : 0.0;
+        const double ps = lane < FW ? fs.d[3 + 2 * par][lane] : 0.0;
+        const int pn = lane < FW ? fs.i[5 + par][lane] : 0;
         const double ez = wave_shift_up(wave_scan_incl(pz));
         const double es = wave_shift_up(wave_scan_incl(ps));
         const int en = wave_shift_up(wave_scan_incl(pn));
-        const uint64_t wcross = __ballot(lane < kFW && cz + (ez + pz) >= thr);
+        const uint64_t wcross = __ballot(lane < FW && cz + (ez + pz) >= thr);
         const int cross_wave = wcross ? __ffsll((unsigned long long)wcross) - 1 : -1;
         if (cross_wave >= 0) {
           if (fw == cross_wave) {
@@ -621,7 +624,7 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
               fs.bi[1] = cn + wbn + in;
             }
           }
-          fsync(&fs.bar, epoch);
+          fsync<FW>(&fs.bar, epoch);
           Zs = fs.bd[0];
           Ss = fs.bd[1];
           Mgt = fs.bd[2];
@@ -629,9 +632,9 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
           size = fs.bi[1];
           found = true;
         } else {
-          cz += readlane_f64(ez, kFW - 1) + readlane_f64(pz, kFW - 1);
-          cs += readlane_f64(es, kFW - 1) + readlane_f64(ps, kFW - 1);
-          cn += int(readlane_u32(uint32_t(en), kFW - 1)) + int(readlane_u32(uint32_t(pn), kFW - 1));
+          cz += readlane_f64(ez, FW - 1) + readlane_f64(pz, FW - 1);
+          cs += readlane_f64(es, FW - 1) + readlane_f64(ps, FW - 1);
+          cn += int(readlane_u32(uint32_t(en), FW - 1)) + int(readlane_u32(uint32_t(pn), FW - 1));
         }
       }
       if (!found) {   // rounding left the mass just short of p: keep every value
@@ -679,7 +682,7 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
   }
 
   // ---- release the buffer: every nonzero counter lies in [wmin, wmax] ----
-  for (int m = wmin + ft; m <= wmax; m += kFT) hist[widx(m)] = 0;
+  for (int m = wmin + ft; m <= wmax; m += FT) hist[widx(m)] = 0;
   if (ft == 0) special[0] = special[1] = special[2] = 0;
 }
 
@@ -691,12 +694,36 @@ RLK_DEV uint4 stream_load(const uint4* p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// Stream one row into a counter buffer with threads 0..NS-1 of the block.
+template <bool kVec, int NS>
+RLK_DEV void stream_row(const RowArgs& a, int64_t row, int64_t nvec, uint32_t* h, uint32_t* sp) {
+  const int tid = threadIdx.x;
+  const int64_t V = a.vocab;
+  const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.logits) + row * a.row_stride;
+  if (kVec) {
+    const uint4* v4 = reinterpret_cast<const uint4*>(rowp);
+    int64_t i = tid;
+    for (; i + (kUnroll - 1) * NS < nvec; i += kUnroll * NS) {
+      uint4 q[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) q[u] = stream_load(v4 + i + u * NS);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) count8(h, sp, q[u]);
+    }
+    for (; i < nvec; i += NS) count8(h, sp, stream_load(v4 + i));
+    for (int64_t j = (nvec << 3) + tid; j < V; j += NS) count_code(h, sp, rowp[j]);
+  } else {
+    for (int64_t j = tid; j < V; j += NS) count_code(h, sp, rowp[j]);
+  }
+}
+
 // One persistent block per CU; block b takes rows b, b + G, b + 2G, ...
-// (G = gridDim.x). Step s: waves 0..kStreamWaves-1 stream row R_s into
-// counter buffer s & 1 while the finisher waves post-process row R_{s-1}
-// from the other buffer; one block barrier separates the steps. Rows the
-// finishers hand on (see finish_row) are then redone by the whole block with
-// the generic algorithm, in the same launch.
+// (G = gridDim.x). The first row is streamed by all 16 waves. Then, step s:
+// waves 0..kStreamWaves-1 stream row R_s into counter buffer s & 1 while the
+// finisher waves post-process row R_{s-1} from the other buffer, one block
+// barrier between steps; the last row is post-processed by all 16 waves.
+// Rows the finishers hand on (see finish_row) are then redone by the whole
+// block with the generic algorithm, in the same launch.
 template <bool kVec>
 __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
   __shared__ uint32_t hist[2][kHWords];
@@ -708,6 +735,7 @@ __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
   const int64_t V = a.vocab;
   const int64_t nvec = kVec ? (V >> 3) : 0;
   const int64_t N = a.n_rows;
+  const int64_t G = gridDim.x;
 
   {
     uint4* h4 = reinterpret_cast<uint4*>(&hist[0][0]);
@@ -718,37 +746,23 @@ __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
   unsigned int epoch = 0;
   __syncthreads();
 
-  int64_t cur = blockIdx.x;   // streamed this step
-  int64_t prev = N;           // finished this step
-  for (int s = 0; cur < N || prev < N; ++s) {
+  int64_t prev = blockIdx.x;   // the row in the buffer the finishers read next
+  if (prev < N) stream_row<kVec, kHT>(a, prev, nvec, hist[0], special[0]);
+  __syncthreads();
+  int s = 1;
+  for (int64_t cur = prev + G; cur < N; cur += G, ++s) {
     const int b = s & 1;
-    if (wid < kStreamWaves) {
-      if (cur < N) {
-        const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.logits) + cur * a.row_stride;
-        uint32_t* h = hist[b];
-        uint32_t* sp = special[b];
-        if (kVec) {
-          const uint4* v4 = reinterpret_cast<const uint4*>(rowp);
-          int64_t i = tid;
-          for (; i + (kUnroll - 1) * kStreamers < nvec; i += kUnroll * kStreamers) {
-            uint4 q[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) q[u] = stream_load(v4 + i + u * kStreamers);
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) count8(h, sp, q[u]);
-          }
-          for (; i < nvec; i += kStreamers) count8(h, sp, stream_load(v4 + i));
-          for (int64_t j = (nvec << 3) + tid; j < V; j += kStreamers) count_code(h, sp, rowp[j]);
-        } else {
-          for (int64_t j = tid; j < V; j += kStreamers) count_code(h, sp, rowp[j]);
-        }
-      }
-    } else if (prev < N) {
-      finish_row(a, prev, hist[b ^ 1], special[b ^ 1], fs, epoch);
-    }
+    if (wid < kStreamWaves)
+      stream_row<kVec, kStreamers>(a, cur, nvec, hist[b], special[b]);
+    else
+      finish_row<kFW>(a, prev, hist[b ^ 1], special[b ^ 1], fs, epoch);
     __syncthreads();
     prev = cur;
-    cur = (cur < N) ? cur + int64_t(gridDim.x) : N;
+  }
+  if (prev < N) {   // the last row: every wave finishes it
+    epoch = __hip_atomic_load(&fs.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    finish_row<kMaxFW>(a, prev, hist[(s & 1) ^ 1], special[(s & 1) ^ 1], fs, epoch);
+    __syncthreads();
   }
   // rows handed on by this block's finishers (flags written before the last
   // barrier), redone with the counters' LDS as scratch
