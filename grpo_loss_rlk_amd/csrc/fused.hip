@@ -159,8 +159,12 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats(FusedFwdArgs a) {
 // Logits of a row block: A = h (tokens), B = W (vocabulary), so that the
 // lanes of an accumulator register hold consecutive vocabulary ids of one
 // token and each store writes 128 contiguous bytes of a scratch row.
+// Also per token: the max logit over the tile (as an order key, merged with
+// atomicMax, which is order-free) and whether a non-finite logit appeared,
+// so that the row kernel can skip its max pass.
 __global__ __launch_bounds__(kT) void fwd_logits_tile(FusedFwdArgs a, int64_t r0, int64_t rows,
-                                                      float* z, int64_t zs) {
+                                                      float* z, int64_t zs, uint32_t* zmax_key,
+                                                      uint32_t* zbad) {
   __shared__ gemm::Smem smem;
   const int nnt = int((rows + kBN - 1) / kBN), nvt = int((a.V + kBM - 1) / kBM);
   int nt, vt;
@@ -180,6 +184,38 @@ __global__ __launch_bounds__(kT) void fwd_logits_tile(FusedFwdArgs a, int64_t r0
         if (n < rows) z[n * zs + v] = acc[i][j][r];
       }
   }
+  // lanes l and l ^ k (k < 32) hold the same tokens and different vocabulary ids
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float m = -INFINITY;
+      bool nonfinite = false;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t v = v0 + gemm::acc_b_row(j);
+        if (v < a.V) {
+          const float x = acc[i][j][r];
+          m = fmaxf(m, x);
+          nonfinite |= !(fabsf(x) <= 3.402823466e38f);
+        }
+      }
+#pragma unroll
+      for (int k = 1; k < 32; k <<= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
+      const uint64_t nf = __ballot(nonfinite);
+      const int64_t n = n0 + gemm::acc_a_row(i, r);
+      if ((lane & 31) == 0 && n < rows) {
+        if (m > -INFINITY) atomicMax(&zmax_key[n], f32_key(m));
+        if ((nf >> (lane & 32)) & 0xffffffffull) atomicOr(&zbad[n], 1u);
+      }
+    }
+}
+
+__global__ void clear_u32(uint32_t* p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0u;
 }
 
 __global__ __launch_bounds__(256) void fwd_merge(FusedFwdArgs a, int nvt) {
@@ -243,7 +279,7 @@ size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V, float top_p) {
   if (top_p < 1.f) {
     const int64_t R = N < kTopPRowBlock ? N : kTopPRowBlock;
     return align256(size_t(R) * size_t(logits_ld(V)) * 4) + align256(size_t(N) * 4) +
-           logits_rows_workspace(R, V, 0);
+           2 * align256(size_t(R) * 4) + logits_rows_workspace(R, V, 0);
   }
   const int64_t nvt = (V + kBM - 1) / kBM;
   return size_t(nvt * N) * 16 + size_t(N) * 4 + 512;
@@ -255,13 +291,22 @@ hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream)
   if (a.top_p < 1.f) {
     const int64_t R = a.N < kTopPRowBlock ? a.N : kTopPRowBlock, zs = logits_ld(a.V);
     float* z = reinterpret_cast<float*>(ws);
-    float* lp_full = reinterpret_cast<float*>(ws + align256(size_t(R) * size_t(zs) * 4));
-    void* rows_ws = ws + align256(size_t(R) * size_t(zs) * 4) + align256(size_t(a.N) * 4);
+    size_t off = align256(size_t(R) * size_t(zs) * 4);
+    float* lp_full = reinterpret_cast<float*>(ws + off);
+    off += align256(size_t(a.N) * 4);
+    uint32_t* zmax_key = reinterpret_cast<uint32_t*>(ws + off);
+    off += align256(size_t(R) * 4);
+    uint32_t* zbad = reinterpret_cast<uint32_t*>(ws + off);
+    off += align256(size_t(R) * 4);
+    void* rows_ws = ws + off;
+    // the row kernel clears both per-row arrays after reading them
+    hipLaunchKernelGGL(clear_u32, dim3(unsigned((2 * align256(size_t(R) * 4) / 4 + 255) / 256)),
+                       dim3(256), 0, stream, zmax_key, int64_t(2 * align256(size_t(R) * 4) / 4));
     for (int64_t r0 = 0; r0 < a.N; r0 += R) {
       const int64_t rows = a.N - r0 < R ? a.N - r0 : R;
       const int64_t nnt = (rows + kBN - 1) / kBN, nvt = (a.V + kBM - 1) / kBM;
       hipLaunchKernelGGL(fwd_logits_tile, dim3(unsigned(nnt * nvt)), dim3(kT), 0, stream, a, r0,
-                         rows, z, zs);
+                         rows, z, zs, zmax_key, zbad);
       RowArgs ra{};
       ra.logits = z;
       ra.n_rows = rows;
@@ -276,6 +321,8 @@ hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream)
       ra.nsize = a.nsize ? a.nsize + r0 : nullptr;
       ra.flags = a.flags ? a.flags + r0 : nullptr;
       ra.saved4 = a.saved ? a.saved + 4 * r0 : nullptr;
+      ra.zmax_key = zmax_key;
+      ra.zbad = zbad;
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       e = launch_logits_rows(ra, 0, rows_ws, stream);

@@ -23,6 +23,11 @@ struct RowArgs {
   float* thresh;          // nullable
   uint8_t* flags;         // nullable
   float* saved4;          // nullable [n_rows, 4]: log Z_S and E_q over S of z/T, threshold, 0
+  // fp32 rows produced by the fused LM head (nullable, both or neither):
+  // per row, the order key of the max logit and a non-finite flag, written
+  // by the producer; read and cleared to 0 here
+  uint32_t* zmax_key;
+  uint32_t* zbad;
   uint8_t* fallback;      // workspace [n_rows]: rows the histogram path hands on
 };
 

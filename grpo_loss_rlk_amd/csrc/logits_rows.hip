@@ -815,12 +815,57 @@ RLK_DEV int walk_bins(const uint64_t* bins, int nbins, uint64_t thr, uint64_t* a
   return -1;
 }
 
+// exp((z - m)/T) in fp32 for fp32 z and row max m, to about 1 ulp: the
+// difference z - m is carried exactly as s + err (TwoSum), and with
+// c = log2(e)/T split as c_hi + c_lo the exponent's rounding residual is
+// recovered by an fma, 2^x = 2^x_hi (1 + r ln 2). *d receives (z - m)/T.
+RLK_DEV float f32_mass(float z, float m, MassScale k, float invT, float* d) {
+  const float s = z - m;
+  const float bb = s - z;
+  const float err = (z - (s - bb)) + (-m - bb);
+  const float xh = s * k.c_hi;
+  const float r = fmaf(s, k.c_hi, -xh) + fmaf(s, k.c_lo, err * k.c_hi);
+  const float e = exp2f(xh);
+  *d = s * invT;
+  return fmaf(e, r * 0.69314718f, e);
+}
+
+// round(e * 2^39) for e in [0, 1] from the fp32 bits (half up, as fixed_mass).
+RLK_DEV uint64_t f32_fixed(float e) {
+  const uint32_t u = __float_as_uint(e);
+  const int ex = int(u >> 23);
+  if (ex == 0) return 0ull;   // zero or subnormal: below 2^-126
+  const uint64_t mant = uint64_t((u & 0x7fffffu) | 0x800000u);
+  const int sh = ex - 111;    // value = mant * 2^(ex - 150); times 2^39
+  if (sh >= 0) return mant << sh;
+  if (sh < -24) return 0ull;
+  return (mant + (uint64_t(1) << (-sh - 1))) >> (-sh);
+}
+
+// Visit every element of a row, 16 bytes per lane per load with kF32Unroll
+// loads in flight per thread (the loads of a group are issued before any of
+// them is used).
+constexpr int kF32Unroll = 8;
 template <bool kVec, typename F>
 RLK_DEV void for_each_f32(const float* rowp, int64_t V, F&& f) {
   if (kVec) {
     const int64_t V4 = V >> 2;
     const float4* p4 = reinterpret_cast<const float4*>(rowp);
-    for (int64_t i = threadIdx.x; i < V4; i += kF32T) {
+    int64_t i = threadIdx.x;
+    for (; i + (kF32Unroll - 1) * kF32T < V4; i += kF32Unroll * kF32T) {
+      float4 q[kF32Unroll];
+#pragma unroll
+      for (int u = 0; u < kF32Unroll; ++u) q[u] = p4[i + u * kF32T];
+#pragma unroll
+      for (int u = 0; u < kF32Unroll; ++u) {
+        const int64_t e = 4 * (i + u * kF32T);
+        f(q[u].x, e);
+        f(q[u].y, e + 1);
+        f(q[u].z, e + 2);
+        f(q[u].w, e + 3);
+      }
+    }
+    for (; i < V4; i += kF32T) {
       const float4 v = p4[i];
       f(v.x, 4 * i);
       f(v.y, 4 * i + 1);
@@ -856,6 +901,22 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
   const int64_t V = a.vocab;
   const float* rowp = reinterpret_cast<const float*>(a.logits) + row * a.row_stride;
 
+  // the producer's per-row max (order key) and non-finite flag, cleared for
+  // the producer's next block of rows
+  bool known = false;
+  float known_max = 0.f;
+  if (a.zmax_key) {
+    const uint32_t k = a.zmax_key[row], zb = a.zbad[row];
+    __syncthreads();
+    if (tid == 0) {
+      a.zmax_key[row] = 0u;
+      a.zbad[row] = 0u;
+    }
+    if (zb == 0u && k != 0u) {
+      known = true;
+      known_max = key_f32(k);
+    }
+  }
   const float Tv = a.t_row ? a.t_row[row] : a.temperature;
   const float p = a.p_row ? a.p_row[row] : a.top_p;
   const int64_t y = a.targets[row];
@@ -866,27 +927,35 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
     return;
   }
 
-  // ---- pass 1: max, finite count, non-finite detection ----
+  // ---- pass 1: max, finite count, non-finite detection (or the producer's
+  // max when it saw only finite logits) ----
   float mx = -INFINITY;
   int bad = 0;
   uint32_t nfin = 0;
-  for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
-    if (z != z || z == INFINITY) bad = 1;
-    else if (z > -INFINITY) {
-      mx = fmaxf(mx, z);
-      ++nfin;
-    }
-  });
-  mx = block_max(mx, sf);
-  bad = block_max(bad, si);
-  nfin = uint32_t(block_sum(uint64_t(nfin), su64));
+  if (known) {
+    mx = known_max;
+    nfin = uint32_t(V);
+  } else {
+    for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
+      if (z != z || z == INFINITY) bad = 1;
+      else if (z > -INFINITY) {
+        mx = fmaxf(mx, z);
+        ++nfin;
+      }
+    });
+    mx = block_max(mx, sf);
+    bad = block_max(bad, si);
+    nfin = uint32_t(block_sum(uint64_t(nfin), su64));
+  }
   if (bad || nfin == 0) {
     if (tid == 0) store_nan_row(a, row, flags | kNonFinite);
     return;
   }
   const double m = double(mx);
   const double invT = 1.0 / double(Tv);
-  const float cbin = float(invT) * kFBinPerNat;
+  const float invTf = float(invT);
+  const MassScale ks = mass_scale(invT);
+  const float cbin = invTf * kFBinPerNat;
   const bool cut = p < 1.f;
   auto bin_of = [&](float z) {
     const float u = (mx - z) * cbin;
@@ -903,12 +972,12 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
   uint64_t wt = 0;
   for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
     if (!(z > -INFINITY)) return;
-    double d;
-    const float e = mass_of(z, m, invT, &d);
+    float d;
+    const float e = f32_mass(z, mx, ks, invTf, &d);
     zt += double(e);
-    st += double(e) * d;
+    st += double(e) * double(d);
     if (cut) {
-      const uint64_t w = fixed_mass(e);
+      const uint64_t w = f32_fixed(e);
       if (w) {
         wt += w;
         atomicAdd(reinterpret_cast<unsigned long long*>(&hist[bin_of(z)]), (unsigned long long)w);
@@ -935,10 +1004,10 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
       if (!(z > -INFINITY)) return;
       const int b = bin_of(z);
       if (b < bstar) {
-        double d;
-        const float e = mass_of(z, m, invT, &d);
+        float d;
+        const float e = f32_mass(z, mx, ks, invTf, &d);
         zs += double(e);
-        ss += double(e) * d;
+        ss += double(e) * double(d);
         ++cnt;
       } else if (b == bstar) {
         const unsigned int slot = atomicAdd(&ncand_s, 1u);
@@ -976,8 +1045,8 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
     int tau_idx = nc - 1;
     for (int base = 0; base < nc; base += kF32T) {
       const int i = base + tid;
-      double d;
-      const uint64_t v = i < nc ? fixed_mass(mass_of(key_f32(cand[i]), m, invT, &d)) : 0ull;
+      float d;
+      const uint64_t v = i < nc ? f32_fixed(f32_mass(key_f32(cand[i]), mx, ks, invTf, &d)) : 0ull;
       uint64_t tot;
       const uint64_t incl = block_inclusive_scan(v, su64, &tot);
       const int c = (i < nc && carry + incl >= thr) ? tid : kF32T;
@@ -994,13 +1063,13 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
     for (int i = tid; i < nc; i += kF32T) {
       const uint32_t k = cand[i];
       if (k < tau_key) continue;
-      double d;
-      const float e = mass_of(key_f32(k), m, invT, &d);
+      float d;
+      const float e = f32_mass(key_f32(k), mx, ks, invTf, &d);
       zs += double(e);
-      ss += double(e) * d;
+      ss += double(e) * double(d);
       ++cnt;
-      if (k > tau_key) mgt += fixed_mass(e);
-      else mat += fixed_mass(e);
+      if (k > tau_key) mgt += f32_fixed(e);
+      else mat += f32_fixed(e);
     }
     Zs = block_sum(zs, sd);
     Ss = block_sum(ss, sd);
