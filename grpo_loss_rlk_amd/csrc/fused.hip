@@ -8,11 +8,11 @@
 //     logits of each token into a partial (max z, sum 2^x, sum 2^x x) with
 //     x = (z - max) log2(e)/T, and the block whose vocabulary slice holds a
 //     token's target writes that target logit.
-//  2. fwd_merge: per token, the ceil(V/256) partials are merged in vocabulary
-//     order in fp64 (a fixed order that depends on V only, so results do not
-//     depend on the number of tokens or their order: the Qwen3-8B VIME
-//     consistency page, "Canonical topology strategy", combines vocabulary
-//     shards in one fixed order).
+//  2. fwd_merge: per token, the ceil(V/256) partials are merged in fp64 in a
+//     fixed order that depends on V only, so results do not depend on the
+//     number of tokens or their order (the Qwen3-8B VIME consistency page,
+//     "Canonical topology strategy", combines vocabulary shards in one fixed
+//     order).
 //
 // Forward at top-p < 1 (the cut needs the whole row's distribution): per
 // block of kTopPRowBlock tokens, fwd_logits_tile writes the block's fp32
@@ -218,27 +218,49 @@ __global__ void clear_u32(uint32_t* p, int64_t n) {
     p[i] = 0u;
 }
 
-__global__ __launch_bounds__(256) void fwd_merge(FusedFwdArgs a, int nvt) {
-  const int64_t n = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (n >= a.N) return;
+// Merge of the per-tile partials of each token, in fp64: the row max m is
+// the max of the tile maxima (exact), then A = sum_t A_t 2^{(m_t - m) c2} and
+// B = sum_t 2^{(m_t - m) c2} (B_t + (m_t - m) c2 A_t). A block holds 32 tokens
+// x 8 slices; slice s sums tiles s, s + 8, s + 16, ... in increasing order and
+// the slices are added in slice order, so the summation order depends on the
+// number of vocabulary tiles only.
+constexpr int kMergeTok = 32, kMergeSlices = 8;
+
+__global__ __launch_bounds__(kMergeTok * kMergeSlices) void fwd_merge(FusedFwdArgs a, int nvt) {
+  __shared__ double sh[3][kMergeSlices][kMergeTok];
+  const int tok = threadIdx.x & (kMergeTok - 1), sl = threadIdx.x / kMergeTok;
+  const int64_t n = int64_t(blockIdx.x) * kMergeTok + tok;
+  const bool live = n < a.N;
   const double c2 = double(a.c2);
-  double m = -INFINITY, A = 0.0, B = 0.0;   // B in log2 units
-  for (int vt = 0; vt < nvt; ++vt) {
-    const float4 p = a.part[int64_t(vt) * a.N + n];
-    if (double(p.x) == -INFINITY) continue;
-    const double pm = p.x;
-    if (m == -INFINITY) {
-      m = pm;
-      A = p.y;
-      B = p.z;
-      continue;
+
+  float mx = -INFINITY;
+  if (live)
+    for (int vt = sl; vt < nvt; vt += kMergeSlices) mx = fmaxf(mx, a.part[int64_t(vt) * a.N + n].x);
+  sh[0][sl][tok] = double(mx);
+  __syncthreads();
+  double m = -INFINITY;
+  for (int k = 0; k < kMergeSlices; ++k) m = sh[0][k][tok] > m ? sh[0][k][tok] : m;
+  __syncthreads();
+
+  double A = 0.0, B = 0.0;   // B in log2 units
+  if (live && m > -INFINITY)
+    for (int vt = sl; vt < nvt; vt += kMergeSlices) {
+      const float4 p = a.part[int64_t(vt) * a.N + n];
+      if (!(p.x > -INFINITY)) continue;   // a tile with no valid vocabulary row
+      const double d = (double(p.x) - m) * c2;
+      const double sc = exp2(d);
+      A += double(p.y) * sc;
+      B += sc * (double(p.z) + d * double(p.y));
     }
-    const double mm = pm > m ? pm : m;
-    const double d1 = (m - mm) * c2, d2 = (pm - mm) * c2;
-    const double s1 = exp2(d1), s2 = exp2(d2);
-    B = s1 * (B + d1 * A) + s2 * (double(p.z) + d2 * double(p.y));
-    A = A * s1 + double(p.y) * s2;
-    m = mm;
+  sh[1][sl][tok] = A;
+  sh[2][sl][tok] = B;
+  __syncthreads();
+  if (sl != 0 || !live) return;
+  A = 0.0;
+  B = 0.0;
+  for (int k = 0; k < kMergeSlices; ++k) {
+    A += sh[1][k][tok];
+    B += sh[2][k][tok];
   }
   const double invT = c2 * double(kLn2);    // 1/T
   const double lnA = log(A);
@@ -336,8 +358,8 @@ hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream)
   hipLaunchKernelGGL(fwd_tile_stats, dim3(unsigned(nvt * nnt)), dim3(kT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fwd_merge, dim3(unsigned((a.N + 255) / 256)), dim3(256), 0, stream, a,
-                     int(nvt));
+  hipLaunchKernelGGL(fwd_merge, dim3(unsigned((a.N + kMergeTok - 1) / kMergeTok)),
+                     dim3(kMergeTok * kMergeSlices), 0, stream, a, int(nvt));
   return hipGetLastError();
 }
 
