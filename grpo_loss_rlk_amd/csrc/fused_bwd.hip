@@ -103,6 +103,9 @@ __global__ __launch_bounds__(kT) void bwd_g_tile(FusedBwdArgs a, ChunkArgs c) {
   f32x16 acc[4][4];
   gemm::gemm_nt_tile(acc, smem, a.w + c.c0 * a.ws, v0, c.csz, a.ws, a.h, n0, a.N, a.hs, a.H);
 
+  // G of the tile, [vocabulary][token] in LDS, for the row-contiguous G^T stores
+  uint16_t* tg = reinterpret_cast<uint16_t*>(&smem[0][0][0]);
+  static_assert(sizeof(gemm::Smem) >= kTile * kTile * 2, "the G tile fits the GEMM's LDS");
   const float inv_t = a.inv_t;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(kT) void bwd_g_tile(FusedBwdArgs a, ChunkArgs c) {
             g *= inv_t;
           }
           gb[e] = to_bf16(g);
-          if (v < c.cpad && n < c.npad) c.g_cn[v * c.npad + n] = gb[e];
+          tg[(vb - v0 + e) * kTile + (n - n0)] = gb[e];
         }
         if (vb < c.cpad && n < a.N) {
           uint2 pk;
@@ -146,6 +149,17 @@ __global__ __launch_bounds__(kT) void bwd_g_tile(FusedBwdArgs a, ChunkArgs c) {
           *reinterpret_cast<uint2*>(c.g_nc + n * c.cap + vb) = pk;
         }
       }
+  }
+  __syncthreads();
+  // G^T rows: 256 tokens (512 bytes) per vocabulary row, 16 bytes per thread
+  constexpr int kRowChunks = kTile * 2 / 16;
+#pragma unroll 4
+  for (int q = int(threadIdx.x); q < kTile * kRowChunks; q += kT) {
+    const int vl = q / kRowChunks, ch = q % kRowChunks;
+    const int64_t v = v0 + vl, n = n0 + ch * 8;
+    if (v < c.cpad && n < c.npad)
+      *reinterpret_cast<uint4*>(c.g_cn + v * c.npad + n) =
+          *reinterpret_cast<const uint4*>(tg + vl * kTile + ch * 8);
   }
 }
 

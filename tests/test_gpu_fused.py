@@ -102,3 +102,22 @@ def test_bad_target_and_bitwise_batch_invariance():
     pr = rlk.logprob_fused_linear(h[perm.to(DEV)].contiguous(), W, yt[perm], 0.7)
     for k in ("logprob", "entropy", "saved"):
         assert bits_equal(ref[k][perm.to(DEV)], pr[k]), k
+
+
+def test_qwen_head_full_size_sampled_rows():
+    """The full Qwen3-8B head launch the benchmark times (hidden [8192, 4096],
+    W [151936, 4096], T=1, p=1); 8 rows checked against the oracle one by one
+    (each row's logits formed in fp64)."""
+    w = synth.workload("fused")
+    hb = synth.hidden_rows(w, range(w.N))
+    wb = synth.weight_rows(w, range(w.V))
+    y = synth.uniform_targets(w, w.N)
+    out = _run(hb, wb, y, w.temperature)
+    rows = np.random.default_rng(3).choice(w.N, 8, replace=False)
+    W64 = OL.widen_bf16(wb)
+    z = OL.widen_bf16(hb[rows]) @ W64.T
+    o = OL.logprob_from_logits(z, y[rows], OL.f32(w.temperature), 1.0)
+    assert_close_rows(host(out["logprob"])[rows], o.lp_trunc, LP_TOL, what="logprob")
+    assert_close_rows(host(out["entropy"])[rows], o.h_trunc, H_ATOL, H_RTOL, what="entropy")
+    assert np.all(np.isfinite(host(out["logprob"])))
+
