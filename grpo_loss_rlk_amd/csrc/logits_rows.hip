@@ -30,6 +30,8 @@
 //    bin, then the truncated sums. Masses are integers (2^-39 of the max
 //    element's mass) so LDS atomics are order-free and the cut is bitwise
 //    deterministic.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -815,37 +817,41 @@ RLK_DEV int walk_bins(const uint64_t* bins, int nbins, uint64_t thr, uint64_t* a
   return -1;
 }
 
-// exp((z - m)/T) in fp32 for fp32 z and row max m, to about 1 ulp: the
-// difference z - m is carried exactly as s + err (TwoSum), and with
-// c = log2(e)/T split as c_hi + c_lo the exponent's rounding residual is
-// recovered by an fma, 2^x = 2^x_hi (1 + r ln 2). *d receives (z - m)/T.
-RLK_DEV float f32_mass(float z, float m, MassScale k, float invT, float* d) {
-  const float s = z - m;
-  const float bb = s - z;
-  const float err = (z - (s - bb)) + (-m - bb);
-  const float xh = s * k.c_hi;
-  const float r = fmaf(s, k.c_hi, -xh) + fmaf(s, k.c_lo, err * k.c_hi);
-  const float e = exp2f(xh);
-  *d = s * invT;
+// Per-row constants of the fp32 kernel.
+struct F32Scale {
+  double m;      // row max
+  double c;      // log2(e) / T
+  double invT;   // 1 / T
+  double cneg;   // -(bins per nat) / T: bin of s = z - m is floor(s * cneg)
+};
+
+// exp((z - m)/T) in fp32 to about 1 ulp. s = z - m is exact in fp64 (two
+// fp32 values); the exponent x = s log2(e)/T is formed in fp64, rounded to
+// fp32 x_hi for the hardware exp2, and its residual restored to first order,
+// 2^x = 2^x_hi (1 + (x - x_hi) ln 2) (|x - x_hi| <= 2^-18 wherever the mass
+// is above 2^-64). Below 2^-126 a mass is far under the fixed-point unit and
+// the sums' resolution, whatever the denormal handling. *s receives z - m.
+RLK_DEV float f32_mass(float z, const F32Scale& k, double* s) {
+  const double sd = double(z) - k.m;
+  const double x = sd * k.c;
+  const float xh = float(x);
+  const float r = float(x - double(xh));
+  const float e = __builtin_amdgcn_exp2f(xh);
+  *s = sd;
   return fmaf(e, r * 0.69314718f, e);
 }
 
-// round(e * 2^39) for e in [0, 1] from the fp32 bits (half up, as fixed_mass).
-RLK_DEV uint64_t f32_fixed(float e) {
-  const uint32_t u = __float_as_uint(e);
-  const int ex = int(u >> 23);
-  if (ex == 0) return 0ull;   // zero or subnormal: below 2^-126
-  const uint64_t mant = uint64_t((u & 0x7fffffu) | 0x800000u);
-  const int sh = ex - 111;    // value = mant * 2^(ex - 150); times 2^39
-  if (sh >= 0) return mant << sh;
-  if (sh < -24) return 0ull;
-  return (mant + (uint64_t(1) << (-sh - 1))) >> (-sh);
+// round(e * 2^39) for e in [0, 1], ties to even: adding 2^52 in fp64 leaves
+// the integer in the low bits of the significand.
+RLK_DEV uint64_t f32_fixed(double e) {
+  const double v = fma(e, 549755813888.0, 4503599627370496.0);
+  return uint64_t(__double_as_longlong(v)) - 0x4330000000000000ull;
 }
 
 // Visit every element of a row, 16 bytes per lane per load with kF32Unroll
 // loads in flight per thread (the loads of a group are issued before any of
 // them is used).
-constexpr int kF32Unroll = 8;
+constexpr int kF32Unroll = 4;
 template <bool kVec, typename F>
 RLK_DEV void for_each_f32(const float* rowp, int64_t V, F&& f) {
   if (kVec) {
@@ -872,7 +878,7 @@ RLK_DEV void for_each_f32(const float* rowp, int64_t V, F&& f) {
       f(v.z, 4 * i + 2);
       f(v.w, 4 * i + 3);
     }
-    for (int64_t i = 4 * V4 + threadIdx.x; i < V; i += kF32T) f(rowp[i], i);
+    for (int64_t j = 4 * V4 + threadIdx.x; j < V; j += kF32T) f(rowp[j], j);
   } else {
     for (int64_t i = threadIdx.x; i < V; i += kF32T) f(rowp[i], i);
   }
@@ -953,13 +959,18 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
   }
   const double m = double(mx);
   const double invT = 1.0 / double(Tv);
-  const float invTf = float(invT);
-  const MassScale ks = mass_scale(invT);
-  const float cbin = invTf * kFBinPerNat;
+  F32Scale ks;
+  ks.m = m;
+  ks.c = 1.4426950408889634 * invT;
+  ks.invT = invT;
+  ks.cneg = -double(kFBinPerNat) * invT;
+  // every element below this has zero mass at fp32 precision; clamping -inf
+  // to it keeps the arithmetic free of inf - inf
+  const float zfloor = float(m - 1e30);
   const bool cut = p < 1.f;
-  auto bin_of = [&](float z) {
-    const float u = (mx - z) * cbin;
-    return u < float(kFBins - 1) ? int(u) : kFBins - 1;
+  auto bin_of = [&](double s) {   // s = z - m <= 0
+    const double u = s * ks.cneg;
+    return u < double(kFBins - 1) ? int(u) : kFBins - 1;
   };
 
   // ---- pass 2: Z, sum e d, histogram of fixed-point masses over d bins ----
@@ -968,22 +979,28 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
     if (tid == 0) ncand_s = 0;
     __syncthreads();
   }
+  // Per element without branches except the atomic; the top-p histogram is
+  // a compile-time variant.
   double zt = 0.0, st = 0.0;
   uint64_t wt = 0;
-  for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
-    if (!(z > -INFINITY)) return;
-    float d;
-    const float e = f32_mass(z, mx, ks, invTf, &d);
-    zt += double(e);
-    st += double(e) * double(d);
-    if (cut) {
-      const uint64_t w = f32_fixed(e);
-      if (w) {
+  auto pass2 = [&](auto with_hist) {
+    for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
+      double dz;
+      const float e = f32_mass(fmaxf(z, zfloor), ks, &dz);
+      const double ed = double(e);
+      zt += ed;
+      st = fma(ed, dz * invT, st);
+      if constexpr (decltype(with_hist)::value) {
+        const uint64_t w = f32_fixed(ed);
         wt += w;
-        atomicAdd(reinterpret_cast<unsigned long long*>(&hist[bin_of(z)]), (unsigned long long)w);
+        if (w)
+          atomicAdd(reinterpret_cast<unsigned long long*>(&hist[bin_of(dz)]),
+                    (unsigned long long)w);
       }
-    }
-  });
+    });
+  };
+  if (cut) pass2(std::true_type{});
+  else pass2(std::false_type{});
   const double Z = block_sum(zt, sd);
   const double S = block_sum(st, sd);
 
@@ -998,18 +1015,22 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
     if (bstar < 0) bstar = kFBins - 1;   // unreachable: the total mass reaches thr
 
     // ---- pass 3: sums above the crossing bin; its elements' keys to LDS ----
+    // The sums take exp2 of the fp32-rounded exponent: about 2^-24 |x| ln 2
+    // relative per element, and weighted by mass |x| averages at most log2 of
+    // the element count (x = log2 of the element's mass relative to the max),
+    // so the sums are off by under 2e-6 relative. The cut never uses it.
     double zs = 0.0, ss = 0.0;
     uint32_t cnt = 0;
     for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
-      if (!(z > -INFINITY)) return;
-      const int b = bin_of(z);
-      if (b < bstar) {
-        float d;
-        const float e = f32_mass(z, mx, ks, invTf, &d);
-        zs += double(e);
-        ss += double(e) * double(d);
-        ++cnt;
-      } else if (b == bstar) {
+      const double dz = double(fmaxf(z, zfloor)) - m;
+      const int b = z > -INFINITY ? bin_of(dz) : kFBins;   // -inf: in no bin
+      const bool in = b < bstar;
+      const float e = in ? __builtin_amdgcn_exp2f(float(dz * ks.c)) : 0.f;
+      const double ed = double(e);
+      zs += ed;
+      ss = fma(ed, dz * invT, ss);
+      cnt += in ? 1u : 0u;
+      if (b == bstar) {
         const unsigned int slot = atomicAdd(&ncand_s, 1u);
         if (slot < unsigned(kCand)) cand[slot] = f32_key(z);
       }
@@ -1045,8 +1066,8 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
     int tau_idx = nc - 1;
     for (int base = 0; base < nc; base += kF32T) {
       const int i = base + tid;
-      float d;
-      const uint64_t v = i < nc ? f32_fixed(f32_mass(key_f32(cand[i]), mx, ks, invTf, &d)) : 0ull;
+      double dz;
+      const uint64_t v = i < nc ? f32_fixed(double(f32_mass(key_f32(cand[i]), ks, &dz))) : 0ull;
       uint64_t tot;
       const uint64_t incl = block_inclusive_scan(v, su64, &tot);
       const int c = (i < nc && carry + incl >= thr) ? tid : kF32T;
@@ -1063,13 +1084,13 @@ __global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
     for (int i = tid; i < nc; i += kF32T) {
       const uint32_t k = cand[i];
       if (k < tau_key) continue;
-      float d;
-      const float e = f32_mass(key_f32(k), mx, ks, invTf, &d);
-      zs += double(e);
-      ss += double(e) * double(d);
+      double dz;
+      const double ed = double(f32_mass(key_f32(k), ks, &dz));
+      zs += ed;
+      ss = fma(ed, dz * invT, ss);
       ++cnt;
-      if (k > tau_key) mgt += f32_fixed(e);
-      else mat += f32_fixed(e);
+      if (k > tau_key) mgt += f32_fixed(ed);
+      else mat += f32_fixed(ed);
     }
     Zs = block_sum(zs, sd);
     Ss = block_sum(ss, sd);
