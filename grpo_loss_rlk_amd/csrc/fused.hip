@@ -57,6 +57,35 @@ RLK_DEV Part merge_part(Part p, Part q, float c2) {
   return r;
 }
 
+// This lane's 64 logits of token column j folded into (max, sum 2^x, sum 2^x x).
+// kFull: every vocabulary row of the tile exists; else rows from `rem` on
+// (relative to this lane's first row) are past the vocabulary.
+template <bool kFull>
+RLK_DEV Part fold_lane(const f32x16 (&acc)[4][4], int j, int rem, float c2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (kFull || 32 * i + 8 * (r >> 2) + (r & 3) < rem) mx = fmaxf(mx, acc[i][j][r]);
+  float A = 0.f, B = 0.f;
+  if (mx > -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kFull || 32 * i + 8 * (r >> 2) + (r & 3) < rem) {
+          // x <= 0; below 2^-126 a term is far under the sum's resolution,
+          // whatever the denormal handling of the hardware exp2
+          const float x = (acc[i][j][r] - mx) * c2;
+          const float e = __builtin_amdgcn_exp2f(x);
+          A += e;
+          B = fmaf(e, x, B);
+        }
+  }
+  return Part{mx, A, B};
+}
+
 // Epilogue of a 256 x 256 tile: per token, fold this tile's logits into a
 // partial and write the target logit; `xch` is >= 3 KB of free LDS.
 RLK_DEV void tile_epilogue(const FusedFwdArgs& a, f32x16 (&acc)[4][4], int64_t v0, int64_t n0,
@@ -69,33 +98,12 @@ RLK_DEV void tile_epilogue(const FusedFwdArgs& a, f32x16 (&acc)[4][4], int64_t v
   const float c2 = a.c2;
   const int64_t vbase = v0 + 128 * wm;
   const bool full = v0 + kBM <= a.V;
+  const int64_t rem64 = a.V - vbase - 4 * fgrp;
+  const int rem = int(rem64 < 256 ? rem64 : 256);
   Part mine[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = vbase + 32 * i + 8 * (r >> 2) + 4 * fgrp + (r & 3);
-        if (full || row < a.V) mx = fmaxf(mx, acc[i][j][r]);
-      }
-    float A = 0.f, B = 0.f;
-    if (mx > -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = vbase + 32 * i + 8 * (r >> 2) + 4 * fgrp + (r & 3);
-          if (full || row < a.V) {
-            const float x = (acc[i][j][r] - mx) * c2;
-            const float e = exp2f(x);
-            A += e;
-            B = fmaf(e, x, B);
-          }
-        }
-    }
-    Part p{mx, A, B};
+    const Part p = full ? fold_lane<true>(acc, j, rem, c2) : fold_lane<false>(acc, j, rem, c2);
     Part q;
     q.m = __shfl_xor(p.m, 32, 64);
     q.A = __shfl_xor(p.A, 32, 64);
