@@ -93,6 +93,65 @@ struct ChunkArgs {
   float* dh_acc;           // fp32 [N, H] partial sums over chunks (several chunks only)
 };
 
+// G of one S_c tile from the accumulators: each element to bf16, into the
+// LDS tile tg [vocabulary][token] and, four vocabulary rows at a time, to the
+// token-row copy g_nc. kFullV: all 256 vocabulary rows of the tile are in the
+// chunk. A token past N gets lse = +huge, so q = 0 and G = +0 without a mask.
+template <bool kFullV>
+RLK_DEV void g_epilogue(const FusedBwdArgs& a, const ChunkArgs& c, const f32x16 (&acc)[4][4],
+                        int64_t v0, int64_t n0, uint16_t* tg) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const int rbase = gemm::acc_a_row(0, 0);   // 128 wm + 4 (lane / 32): this lane's first row
+  const float inv_t = a.inv_t, c1 = inv_t * kLog2e;
+  const int vrem = int(c.csz - v0 < 2 * kTile ? c.csz - v0 : 2 * kTile) - rbase;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int nl = gemm::acc_b_row(j);
+    const int64_t n = n0 + nl;
+    float lse2 = 1e30f, eq = 0.f, glp = 0.f, gh = 0.f;
+    int ty = -1;   // target row relative to this lane's first row (-1: none here)
+    if (n < a.N) {
+      lse2 = a.saved[4 * n + 0] * kLog2e;
+      eq = a.saved[4 * n + 1];
+      gh = a.g_H ? a.g_H[n] : 0.f;
+      const int64_t y = a.targets[n];
+      if (y >= 0 && y < a.V) {   // a row without a valid target keeps only its entropy term
+        glp = a.g_lp ? a.g_lp[n] : 0.f;
+        const int64_t rel = y - c.c0 - v0 - rbase;
+        ty = rel >= 0 && rel < kTile ? int(rel) : -1;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int k0 = 32 * i + 8 * s;   // rows rbase + k0 .. + 3
+        float g4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float z = acc[i][j][4 * s + e];
+          const float q = __builtin_amdgcn_exp2f(fmaf(z, c1, -lse2));
+          float g = fmaf(-q, fmaf(gh, fmaf(z, inv_t, -eq), glp), 0.f);   // +0 when q = 0
+          if (k0 + e == ty) g += glp;
+          g *= inv_t;
+          if (!kFullV && k0 + e >= vrem) g = 0.f;
+          g4[e] = g;
+        }
+        const bf16x2 lo = {(__bf16)g4[0], (__bf16)g4[1]};
+        const bf16x2 hi = {(__bf16)g4[2], (__bf16)g4[3]};
+        const uint32_t plo = __builtin_bit_cast(uint32_t, lo), phi = __builtin_bit_cast(uint32_t, hi);
+        uint16_t* t = tg + (rbase + k0) * kTile + nl;
+        t[0] = uint16_t(plo);
+        t[kTile] = uint16_t(plo >> 16);
+        t[2 * kTile] = uint16_t(phi);
+        t[3 * kTile] = uint16_t(phi >> 16);
+        const int64_t vb = v0 + rbase + k0;
+        if (vb < c.cpad && n < a.N)
+          *reinterpret_cast<uint2*>(c.g_nc + n * c.cap + vb) = make_uint2(plo, phi);
+      }
+  }
+}
+
 // S_c tile (vocabulary rows of the chunk x tokens) and its G epilogue.
 __global__ __launch_bounds__(kT) void bwd_g_tile(FusedBwdArgs a, ChunkArgs c) {
   __shared__ gemm::Smem smem;
@@ -106,50 +165,10 @@ __global__ __launch_bounds__(kT) void bwd_g_tile(FusedBwdArgs a, ChunkArgs c) {
   // G of the tile, [vocabulary][token] in LDS, for the row-contiguous G^T stores
   uint16_t* tg = reinterpret_cast<uint16_t*>(&smem[0][0][0]);
   static_assert(sizeof(gemm::Smem) >= kTile * kTile * 2, "the G tile fits the GEMM's LDS");
-  const float inv_t = a.inv_t;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + gemm::acc_b_row(j);
-    float lse = 0.f, eq = 0.f, glp = 0.f, gh = 0.f;
-    int64_t yl = -1;   // target relative to the chunk (-1: no lp term here)
-    if (n < a.N) {
-      lse = a.saved[4 * n + 0];
-      eq = a.saved[4 * n + 1];
-      gh = a.g_H ? a.g_H[n] : 0.f;
-      const int64_t y = a.targets[n];
-      if (y >= 0 && y < a.V) {   // a row without a valid target keeps only its entropy term
-        glp = a.g_lp ? a.g_lp[n] : 0.f;
-        yl = y - c.c0;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int64_t vb = v0 + gemm::acc_a_row(i, 4 * s);   // 4 consecutive rows vb .. vb+3
-        uint16_t gb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t v = vb + e;
-          float g = 0.f;
-          if (v < c.csz && n < a.N) {
-            const float x = acc[i][j][4 * s + e] * inv_t;
-            const float q = exp2f((x - lse) * kLog2e);
-            g = -q * fmaf(gh, x - eq, glp);
-            if (v == yl) g += glp;
-            g *= inv_t;
-          }
-          gb[e] = to_bf16(g);
-          tg[(vb - v0 + e) * kTile + (n - n0)] = gb[e];
-        }
-        if (vb < c.cpad && n < a.N) {
-          uint2 pk;
-          pk.x = uint32_t(gb[0]) | (uint32_t(gb[1]) << 16);
-          pk.y = uint32_t(gb[2]) | (uint32_t(gb[3]) << 16);
-          *reinterpret_cast<uint2*>(c.g_nc + n * c.cap + vb) = pk;
-        }
-      }
-  }
+  if (v0 + kTile <= c.csz)
+    g_epilogue<true>(a, c, acc, v0, n0, tg);
+  else
+    g_epilogue<false>(a, c, acc, v0, n0, tg);
   __syncthreads();
   // G^T rows: 256 tokens (512 bytes) per vocabulary row, 16 bytes per thread
   constexpr int kRowChunks = kTile * 2 / 16;
