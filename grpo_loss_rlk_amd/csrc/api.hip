@@ -229,8 +229,6 @@ rlk_status rlk_logprob_fused_linear_bwd(const void* hidden, const void* weight, 
   if (s != RLK_OK) return s;
   s = check_fused_shapes(hidden, weight, n_rows, hidden_size, vocab, h_stride, w_stride, targets);
   if (s != RLK_OK) return s;
-  if (top_p < 1.f)
-    return fail(RLK_EUNSUPPORTED, "the fused backward supports top_p = 1 only");
   if (vocab >= kMaxFusedRows)
     return fail(RLK_EINVAL, "vocab=%lld must be below 2^23 for the backward", (long long)vocab);
   if (!grad_weight) return fail(RLK_EINVAL, "grad_weight is required");

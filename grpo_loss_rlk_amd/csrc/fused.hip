@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kMergeTok * kMergeSlices) void fwd_merge(FusedFwdAr
     a.saved[4 * n + 0] = float(m * invT + lnA);   // log Z of the scaled logits z/T
     a.saved[4 * n + 1] = float(m * invT + Ed);    // E_q[z/T]
     a.saved[4 * n + 2] = -INFINITY;              // no cut at top-p = 1
-    a.saved[4 * n + 3] = 0.f;
+    a.saved[4 * n + 3] = (flags & 2) ? 0.f : 1.f;  // the lp term is live (target in range)
   }
   if (a.nsize) a.nsize[n] = int32_t(a.V);
   if (a.flags) a.flags[n] = flags;

@@ -97,6 +97,10 @@ struct ChunkArgs {
 // LDS tile tg [vocabulary][token] and, four vocabulary rows at a time, to the
 // token-row copy g_nc. kFullV: all 256 vocabulary rows of the tile are in the
 // chunk. A token past N gets lse = +huge, so q = 0 and G = +0 without a mask.
+// The nucleus is the forward's: logits >= tau (saved slot 2, -inf at top-p =
+// 1) are kept, the recomputed logits being the forward's fp32 sums over the
+// same k order; the lp term counts only where the forward found the target
+// kept (saved slot 3).
 template <bool kFullV>
 RLK_DEV void g_epilogue(const FusedBwdArgs& a, const ChunkArgs& c, const f32x16 (&acc)[4][4],
                         int64_t v0, int64_t n0, uint16_t* tg) {
@@ -108,14 +112,17 @@ RLK_DEV void g_epilogue(const FusedBwdArgs& a, const ChunkArgs& c, const f32x16 
   for (int j = 0; j < 4; ++j) {
     const int nl = gemm::acc_b_row(j);
     const int64_t n = n0 + nl;
-    float lse2 = 1e30f, eq = 0.f, glp = 0.f, gh = 0.f;
+    float lse2 = 1e30f, eq = 0.f, glp = 0.f, gh = 0.f, tau = -INFINITY;
     int ty = -1;   // target row relative to this lane's first row (-1: none here)
     if (n < a.N) {
       lse2 = a.saved[4 * n + 0] * kLog2e;
       eq = a.saved[4 * n + 1];
+      tau = a.saved[4 * n + 2];
       gh = a.g_H ? a.g_H[n] : 0.f;
       const int64_t y = a.targets[n];
-      if (y >= 0 && y < a.V) {   // a row without a valid target keeps only its entropy term
+      // a row whose target is out of range or outside the nucleus keeps only
+      // its entropy term
+      if (y >= 0 && y < a.V && a.saved[4 * n + 3] != 0.f) {
         glp = a.g_lp ? a.g_lp[n] : 0.f;
         const int64_t rel = y - c.c0 - v0 - rbase;
         ty = rel >= 0 && rel < kTile ? int(rel) : -1;
@@ -130,7 +137,7 @@ RLK_DEV void g_epilogue(const FusedBwdArgs& a, const ChunkArgs& c, const f32x16 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float z = acc[i][j][4 * s + e];
-          const float q = __builtin_amdgcn_exp2f(fmaf(z, c1, -lse2));
+          const float q = !(z < tau) ? __builtin_amdgcn_exp2f(fmaf(z, c1, -lse2)) : 0.f;  // NaN stays
           float g = fmaf(-q, fmaf(gh, fmaf(z, inv_t, -eq), glp), 0.f);   // +0 when q = 0
           if (k0 + e == ty) g += glp;
           g *= inv_t;

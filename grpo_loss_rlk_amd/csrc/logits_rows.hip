@@ -46,15 +46,16 @@ RLK_DEV bool param_ok(float T, float p) {
   return T > 0.f && T <= 3.4e38f && p > 0.f && p <= 1.f;  // NaN fails every compare
 }
 
-// lse_s, eq_s: log Z_S and E_q[z/T] over the nucleus, in units of z/T.
+// lse_s, eq_s: log Z_S and E_q[z/T] over the nucleus, in units of z/T;
+// the fused backward reads them, with tau and the lp-term flag, from saved4.
 RLK_DEV void store_row(const RowArgs& a, int64_t row, float lp_full, float lp_trunc,
                        float h_full, float h_trunc, int32_t size, float tau, uint8_t flags,
                        float lse_s, float eq_s) {
-  if (a.saved4) {
+  if (a.saved4) {   // slot 3: 1 when the row's lp term is live (target in range and kept)
     a.saved4[4 * row + 0] = lse_s;
     a.saved4[4 * row + 1] = eq_s;
     a.saved4[4 * row + 2] = tau;
-    a.saved4[4 * row + 3] = 0.f;
+    a.saved4[4 * row + 3] = (flags & (kOutside | kBadTarget | kNonFinite | kBadParam)) ? 0.f : 1.f;
   }
   a.lp_full[row] = lp_full;
   a.lp_trunc[row] = lp_trunc;

@@ -135,7 +135,9 @@ rlk_status rlk_logprob_from_logits(
  * logprob, entropy   [n_rows] fp32 outputs (required).
  * saved         [n_rows, 4] fp32 (nullable): (log Z_S and E_q[z/T] over the
  *               nucleus, both on the scale z/T; tau, the smallest kept logit,
- *               -inf at top_p = 1; 0), consumed by rlk_logprob_fused_linear_bwd.
+ *               -inf at top_p = 1; 1 when the row's logprob term is live -- target
+ *               in range and kept -- else 0), consumed by
+ *               rlk_logprob_fused_linear_bwd.
  * nucleus_size  [n_rows] int32 (nullable).  flags [n_rows] uint8 (nullable).
  * Limits: hidden_size % 64 == 0, 1 <= vocab <= 2^24, 0 <= n_rows < 2^23,
  * strides >= hidden_size, multiples of 8 and < 2^23, hidden/weight 16-byte
@@ -161,8 +163,10 @@ rlk_status rlk_logprob_fused_linear(
  *   G[n,i] = (1/T) [ g_lp (delta_{i,y} - q_i) - g_H q_i (z_i/T - E_q[z/T]) ] on S, 0 off S
  *   grad_hidden = G W   (bf16 out, fp32 accumulate)
  *   grad_weight = G^T h (fp32 out, overwritten)
- * A row whose target is outside S (or out of range) contributes only its
- * entropy term.
+ * The nucleus is the forward's, held fixed (the cut is not differentiated):
+ * S = {i : z_i >= tau} with tau from `saved`, the recomputed fp32 logits being
+ * summed over the hidden dimension in the forward's order. A row whose target
+ * is outside S (or out of range) contributes only its entropy term.
  * grad_logprob, grad_entropy  [n_rows] fp32 (nullable = zeros).
  * saved         [n_rows, 4] fp32 from the forward call with the same inputs.
  * grad_hidden   [n_rows, hidden_size] bf16, dense (required when n_rows > 0).
@@ -172,8 +176,9 @@ rlk_status rlk_logprob_fused_linear(
  * W^T and h^T (bf16, padded to multiples of 64), G of one chunk in both
  * orientations (bf16) and, when vocab > 32768, an fp32 [n_rows, hidden_size]
  * partial sum of grad_hidden.
- * Limits: as the forward, and top_p must be 1 (the backward through the
- * top-p cut returns RLK_EUNSUPPORTED), vocab < 2^23.
+ * temperature and top_p must be the forward call's (top_p is validated; the
+ * nucleus itself comes from `saved`).
+ * Limits: as the forward, and vocab < 2^23.
  * -------------------------------------------------------------------------- */
 size_t rlk_logprob_fused_linear_bwd_workspace_size(int64_t n_rows, int64_t hidden_size,
                                                     int64_t vocab, float top_p);

@@ -171,7 +171,7 @@ def _fused_bwd(L, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(p=0.95), _native.RLK_EUNSUPPORTED),
+    (dict(p=0.0), _native.RLK_EINVAL),
     (dict(top_k=1), _native.RLK_EUNSUPPORTED),
     (dict(T=math.inf), _native.RLK_EINVAL),
     (dict(H=96, hs=128, wsd=128), _native.RLK_EINVAL),
