@@ -195,9 +195,16 @@ def leg_fused_bwd(torch, rlk, synth, steps, warmup):
     }
 
 
-def leg_grpo(torch, rlk, synth, steps, warmup):
-    """Fused LM head at T=0.7, top-p=0.95 over 32 packed responses (4 prompts x 8,
-    lengths U{256..6912}), H=4096, V=151936, then the GRPO/DAPO token loss."""
+_GRPO_INPUTS = {}
+
+
+def _grpo_inputs(torch, rlk, synth):
+    """The config-4 batch (generated once per process): 32 packed responses
+    (4 prompts x 8, lengths U{256..6912}), hidden/W, in-nucleus targets,
+    old/ref logprobs (the new ones plus N(0, 0.05^2) / N(0, 0.1^2) noise),
+    rewards."""
+    if _GRPO_INPUTS:
+        return _GRPO_INPUTS
     w = synth.workload("grpo")
     cu = synth.cu_seqlens(synth.response_lengths(w))
     T_tot = int(cu[-1])
@@ -207,22 +214,34 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
     h = torch.from_numpy(hb.view(np.int16)).to("cuda:0").view(torch.bfloat16)
     W = torch.from_numpy(wb.view(np.int16)).to("cuda:0").view(torch.bfloat16)
     del hb, wb
-    yt = torch.from_numpy(synth.uniform_targets(w, T_tot)).to("cuda:0")
-    r = synth.rewards(w)
-    print(f"[bench] grpo leg: T_tot={T_tot} hidden {tuple(h.shape)} W {tuple(W.shape)} "
+    # targets: each row's top token (always kept by the nucleus, so every
+    # logprob and the loss are finite), from bf16 logits formed by torch
+    # outside the timed region; the timing does not depend on which token
+    yt = torch.empty(T_tot, dtype=torch.int64, device="cuda:0")
+    for r0 in range(0, T_tot, 8192):
+        yt[r0:r0 + 8192] = torch.mm(h[r0:r0 + 8192], W.t()).argmax(dim=1)
+    print(f"[bench] grpo inputs: T_tot={T_tot} hidden {tuple(h.shape)} W {tuple(W.shape)} "
           f"generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
-    # old / ref logprobs: the new ones plus N(0, 0.05^2) / N(0, 0.1^2) noise,
-    # prepared once before the timed region
     lp0 = rlk.logprob_fused_linear(h, W, yt, w.temperature, w.top_p)["logprob"]
     n_old, n_ref = synth.logprob_noise(w, T_tot)
-    lp_old = (lp0 + torch.from_numpy(n_old).to(lp0)).contiguous()
-    lp_ref = (lp0 + torch.from_numpy(n_ref).to(lp0)).contiguous()
-    rw = torch.from_numpy(r).to("cuda:0")
+    _GRPO_INPUTS.update(
+        w=w, cu=cu, T_tot=T_tot, h=h, W=W, yt=yt,
+        lp_old=(lp0 + torch.from_numpy(n_old).to(lp0)).contiguous(),
+        lp_ref=(lp0 + torch.from_numpy(n_ref).to(lp0)).contiguous(),
+        rw=torch.from_numpy(synth.rewards(w)).to("cuda:0"))
+    return _GRPO_INPUTS
+
+
+def leg_grpo(torch, rlk, synth, steps, warmup):
+    """Fused LM head at T=0.7, top-p=0.95 over the config-4 batch, H=4096,
+    V=151936, then the GRPO/DAPO token loss."""
+    g = _grpo_inputs(torch, rlk, synth)
+    w, T_tot = g["w"], g["T_tot"]
 
     def step():
-        out = rlk.logprob_fused_linear(h, W, yt, w.temperature, w.top_p)
-        return rlk.grpo_token_loss(out["logprob"], lp_old, lp_ref, cu, rewards=rw,
-                                   group_size=w.group_size)
+        out = rlk.logprob_fused_linear(g["h"], g["W"], g["yt"], w.temperature, w.top_p)
+        return rlk.grpo_token_loss(out["logprob"], g["lp_old"], g["lp_ref"], g["cu"],
+                                   rewards=g["rw"], group_size=w.group_size)
 
     mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
     flops = 2.0 * T_tot * w.V * w.H
@@ -237,6 +256,37 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": None},
         "flops_per_token": 2.0 * w.V * w.H,
+    }
+
+
+def leg_grpo_train(torch, rlk, synth, steps, warmup):
+    """A config-4 training step of the LM head: fused forward at top-p 0.95,
+    the GRPO/DAPO token loss and its dL/dlogprob, then the fused backward
+    through the same nucleus (dL/dhidden, dL/dW)."""
+    g = _grpo_inputs(torch, rlk, synth)
+    w, T_tot = g["w"], g["T_tot"]
+
+    def step():
+        out = rlk.logprob_fused_linear(g["h"], g["W"], g["yt"], w.temperature, w.top_p)
+        loss = rlk.grpo_token_loss(out["logprob"], g["lp_old"], g["lp_ref"], g["cu"],
+                                   rewards=g["rw"], group_size=w.group_size)
+        return rlk.logprob_fused_linear_bwd(g["h"], g["W"], g["yt"], out["saved"], loss["grad"],
+                                            None, w.temperature, w.top_p)
+
+    mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
+    flops = 8.0 * T_tot * w.V * w.H    # forward 2VH + recompute 2VH + dh 2VH + dW 2VH per token
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    return {
+        "workload": f"LM-head GRPO training step: fused top-p forward + GRPO loss + backward "
+                    f"through the nucleus, {T_tot} packed tokens, H={w.H}, V={w.V}, "
+                    f"T={w.temperature}, top-p={w.top_p}",
+        "tokens_per_s": T_tot * steps / (total_ms * 1e-3),
+        "ms_per_step": total_ms / steps,
+        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "flops_per_token_executed": 8.0 * w.V * w.H,
     }
 
 
@@ -262,7 +312,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--legs", default="logits,fused,grpo,fused_bwd")
+    ap.add_argument("--legs", default="logits,fused,grpo,grpo_train,fused_bwd")
     ap.add_argument("--cpu-sample", type=int, default=1024,
                     help="rows of the logits workload the CPU oracle is timed on (0 = skip)")
     args = ap.parse_args()
@@ -286,6 +336,8 @@ def main():
         out_legs["copy"] = leg_copy(torch, args.steps, args.warmup)
     if "grpo" in legs:
         out_legs["grpo"] = leg_grpo(torch, rlk, synth, 3, 1)
+    if "grpo_train" in legs:
+        out_legs["grpo_train"] = leg_grpo_train(torch, rlk, synth, 3, 1)
     if "fused_bwd" in legs:
         out_legs["fused_bwd"] = leg_fused_bwd(torch, rlk, synth, 3, 1)
     main_leg = out_legs.get("logits") or next(iter(out_legs.values()))

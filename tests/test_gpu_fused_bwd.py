@@ -164,18 +164,11 @@ def test_bwd_top_p_determinism_and_dh_batch_invariance():
         assert bits_equal(dh, torch.cat([dha, dhb])), split
 
 
-def _oracle_dh_row(h_row64, W64, y, g_lp, g_h, T):
-    """fp64 dh row of one token from the full logit row (blockwise over vocab)."""
-    z = W64 @ h_row64
-    d = (z - z.max()) / T
-    e = np.exp(d)
-    q = e / e.sum()
-    Ed = (q * d).sum()
-    g = -g_h * q * (d - Ed)
-    if 0 <= y < z.size:
-        g[y] += g_lp
-        g -= g_lp * q
-    return (g / T) @ W64
+def _oracle_dh_row(h_row64, W64, y, g_lp, g_h, T, p=1.0):
+    """fp64 dh row of one token: the oracle's G row from the full fp64 logit row."""
+    z = (W64 @ h_row64)[None, :]
+    G = OF.grad_logits(z, np.array([y]), np.array([g_lp]), np.array([g_h]), T, p)[0]
+    return G @ W64
 
 
 def test_bwd_llama70b_full_size_sampled():
@@ -195,5 +188,39 @@ def test_bwd_llama70b_full_size_sampled():
     W64 = OL.widen_bf16(wb)
     for n in (0, N - 1):
         want = _oracle_dh_row(OL.widen_bf16(hb[n]), W64, int(y[n]), -1.0 / N, -0.001 / N, 1.0)
+        got = host(dh[n].float()).astype(np.float64)
+        assert _rel(got, want) <= ROW_TOL, (n, _rel(got, want))
+
+
+def test_bwd_grpo_full_size_sampled():
+    """Config-4 LM-head backward at full size (T_tot ~ 110k packed tokens,
+    H=4096, V=151936, T=0.7, p=0.95) through the GPU forward's nucleus, with
+    upstream g_lp ~ N(0,1)/T_tot and no entropy term (the GRPO loss has none):
+    three dh rows (Gumbel-max targets from the nucleus) against the oracle row
+    by row, and the zero-sum property of dW columns (each row of G sums to
+    zero over the nucleus)."""
+    w = synth.workload("grpo")
+    cu = synth.cu_seqlens(synth.response_lengths(w))
+    T_tot = int(cu[-1])
+    wb = synth.weight_rows(w, range(w.V))
+    hb = synth.hidden_rows(w, range(T_tot))
+    rows = np.array([0, T_tot // 2, T_tot - 1])
+    W64 = OL.widen_bf16(wb)
+    z64 = OL.widen_bf16(hb[rows]) @ W64.T
+    Tf, pf = OL.f32(w.temperature), OL.f32(w.top_p)
+    y = synth.uniform_targets(w, T_tot)
+    y[rows] = [OS.gumbel_max_target(z64[i], Tf, pf, synth.gumbel_uniforms(w, int(r), w.V))
+               for i, r in enumerate(rows)]
+    g_lp = (np.random.default_rng(11).standard_normal(T_tot) / T_tot).astype(np.float32)
+    h, W, yt = bf16_to_device(hb), bf16_to_device(wb), torch.as_tensor(y)
+    print(f"  rlk fused fwd+bwd T_tot={T_tot} p={w.top_p}", flush=True)
+    fwd = rlk.logprob_fused_linear(h, W, yt, w.temperature, w.top_p)
+    dh, dw = rlk.logprob_fused_linear_bwd(h, W, yt, fwd["saved"], torch.as_tensor(g_lp).to(DEV),
+                                          None, w.temperature, w.top_p)
+    torch.cuda.synchronize()
+    colsum = host(torch.sum(dw, dim=0, dtype=torch.float64))
+    assert np.abs(colsum).max() <= 3e-4, np.abs(colsum).max()
+    for i, n in enumerate(rows):
+        want = _oracle_dh_row(OL.widen_bf16(hb[n]), W64, int(y[n]), float(g_lp[n]), 0.0, Tf, pf)
         got = host(dh[n].float()).astype(np.float64)
         assert _rel(got, want) <= ROW_TOL, (n, _rel(got, want))

@@ -104,7 +104,9 @@ def test_grpo_pipeline_small():
     """Config-4 pipeline on a scaled-down shape: 4 prompts x 8 samples, lengths
     U{4..40}, H=128, V=3001, T=0.7, p=0.95, Gumbel-max targets from the
     nucleus; old/ref = the oracle's logprob + N(0,0.05^2) / N(0,0.1^2) stored
-    as fp32; rewards Bernoulli(0.5); C=2, eps 0.2/0.28, beta=0.01."""
+    as fp32; rewards Bernoulli(0.5); C=2, eps 0.2/0.28, beta=0.01. Forward,
+    token loss and its dL/dlogprob, then the backward through the nucleus
+    (normwise 5e-3 for dh and dW)."""
     w = synth.workload("grpo", len_lo=4, len_hi=40, H=128, V=3001)
     lengths = synth.response_lengths(w)
     cu = synth.cu_seqlens(lengths)
@@ -133,6 +135,22 @@ def test_grpo_pipeline_small():
     keep = ~ol.near_branch
     # dL/dlp scales with rho = exp(lp - lp_old): the lp tolerance (2e-3) carries over
     np.testing.assert_allclose(gr[keep], ol.grad[keep], rtol=5e-3, atol=1e-9)
+
+    # backward through the nucleus with the kernel's dL/dlp as the upstream
+    # gradient (rows within 1e-6 of the top-p boundary get none, on both sides)
+    bnd = (o.flags & OL.FLAG_BOUNDARY) != 0
+    g_up = np.where(bnd, 0.0, gr).astype(np.float32)
+    print(f"  rlk_logprob_fused_linear_bwd T_tot={T_tot} p={w.top_p}", flush=True)
+    h, W = bf16_to_device(hb), bf16_to_device(wb)
+    fwd = rlk.logprob_fused_linear(h, W, torch.as_tensor(y), w.temperature, w.top_p)
+    dh, dw = rlk.logprob_fused_linear_bwd(h, W, torch.as_tensor(y), fwd["saved"],
+                                          f32_to_device(g_up), None, w.temperature, w.top_p)
+    torch.cuda.synchronize()
+    dh_ref, dw_ref = OF.backward(OL.widen_bf16(hb), OL.widen_bf16(wb), y, g_up.astype(np.float64),
+                                 np.zeros(T_tot), Tf, pf)
+    for got, want in ((host(dh.float()), dh_ref), (host(dw), dw_ref)):
+        got = got.astype(np.float64)
+        assert np.linalg.norm(got - want) <= 5e-3 * np.linalg.norm(want)
 
 
 def test_grpo_workload_full_size_sampled_rows():
