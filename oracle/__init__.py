@@ -17,6 +17,9 @@ computes, written in fp64 numpy from the definitions:
   same statistics; the backward through them (prime-rl v0.10.0 release notes,
   "1. Trainer Performance": chunked loss; consistency page, "Canonical
   topology strategy": the loss seed is normalised before model derivatives).
+* ``support``  -- the same statistics over a caller-supplied retained set (CSR),
+  and whether that set is a valid nucleus (consistency page, "ROCm MI300X
+  and gfx942": the sampler's retained set is scored by the logprob kernel).
 * ``grpo``     -- group-normalised advantages and the DAPO-style token loss with
   a TIS-truncated ratio and k3 KL (LumenRL README, "Key Features" and
   "Rollout Correction"; RL-Kernel quick-start command: KL coefficient).
@@ -25,4 +28,4 @@ It shares no code with the HIP path. Inputs come from ``synth`` (seeded
 random numbers only). Every function is pinned by CPU tests against closed
 forms, library routines, brute force and finite differences (tests/test_oracle_*.py).
 """
-from . import logprob, sampling, fused, grpo  # noqa: F401
+from . import logprob, sampling, fused, grpo, support  # noqa: F401
