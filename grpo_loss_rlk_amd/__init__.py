@@ -14,8 +14,9 @@ import numpy as np
 import torch
 
 from . import _native
-from ._native import (DTYPE_BF16, DTYPE_F32, FLAG_BAD_PARAM, FLAG_BAD_TARGET,  # noqa: F401
-                      FLAG_BOUNDARY, FLAG_NONFINITE, FLAG_OUTSIDE, RlkError, lib)
+from ._native import (DTYPE_BF16, DTYPE_F32, FLAG_BAD_PARAM, FLAG_BAD_SUPPORT,  # noqa: F401
+                      FLAG_BAD_TARGET, FLAG_BOUNDARY, FLAG_MISMATCH, FLAG_NONFINITE,
+                      FLAG_OUTSIDE, RlkError, lib)
 
 __all__ = ["logprob_from_logits", "logprob_fused_linear", "logprob_fused_linear_bwd",
            "grpo_token_loss", "lib", "RlkError"]
@@ -84,6 +85,47 @@ def logprob_from_logits(logits: torch.Tensor, targets: torch.Tensor, temperature
         _ptr(out["entropy_full"]), _ptr(out["nucleus_size"]), _ptr(out["threshold"]),
         _ptr(out["flags"]), _ptr(ws), ws_n, _stream(dev))
     _native.check(st, "rlk_logprob_from_logits")
+    return out
+
+
+def logprob_from_support(logits: torch.Tensor, targets: torch.Tensor, temperature: float,
+                         support_offsets: torch.Tensor, support_ids: torch.Tensor, *,
+                         vocab: int | None = None, check_top_p: float = 0.0) -> dict:
+    """Logprob / entropy of each row over a caller-supplied retained set (CSR).
+
+    ``support_offsets`` [N + 1] int64 and ``support_ids`` int32 (strictly
+    increasing ids per row) on the GPU. ``check_top_p`` in (0, 1] also
+    recomputes each row's nucleus and flags a set that differs from it.
+    Returns logprob, entropy, flags.
+    """
+    if logits.dtype == torch.float32:
+        dtype = DTYPE_F32
+    elif logits.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+    else:
+        raise TypeError(f"logits dtype {logits.dtype} is not float32 or bfloat16")
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D tensor with unit column stride")
+    N, width = logits.shape
+    V = width if vocab is None else int(vocab)
+    dev = logits.device
+    targets = targets.to(device=dev, dtype=torch.int64).contiguous()
+    offsets = support_offsets.to(device=dev, dtype=torch.int64).contiguous()
+    ids = support_ids.to(device=dev, dtype=torch.int32).contiguous()
+    if offsets.numel() != N + 1:
+        raise ValueError("support_offsets must hold n_rows + 1 entries")
+    f = dict(device=dev, dtype=torch.float32)
+    out = {"logprob": torch.empty(N, **f), "entropy": torch.empty(N, **f),
+           "flags": torch.empty(N, device=dev, dtype=torch.uint8)}
+    L = lib()
+    ws_n = L.rlk_logprob_from_support_workspace_size(N, V, dtype, float(check_top_p))
+    ws = _workspace(ws_n, dev)
+    st = L.rlk_logprob_from_support(
+        _ptr(logits), dtype, N, V, logits.stride(0) if N > 0 else V, _ptr(targets),
+        float(temperature), _ptr(offsets), _ptr(ids) if ids.numel() else None, ids.numel(),
+        float(check_top_p), _ptr(out["logprob"]), _ptr(out["entropy"]), _ptr(out["flags"]),
+        _ptr(ws), ws_n, _stream(dev))
+    _native.check(st, "rlk_logprob_from_support")
     return out
 
 

@@ -17,6 +17,7 @@ c_i32, c_i64, c_f32, c_sz, c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_floa
 RLK_OK, RLK_EINVAL, RLK_EUNSUPPORTED, RLK_EWORKSPACE, RLK_EHIP = 0, 1, 2, 3, 4
 DTYPE_F32, DTYPE_BF16 = 0, 1
 FLAG_OUTSIDE, FLAG_BAD_TARGET, FLAG_NONFINITE, FLAG_BOUNDARY, FLAG_BAD_PARAM = 1, 2, 4, 8, 16
+FLAG_BAD_SUPPORT, FLAG_MISMATCH = 32, 64
 
 
 class GrpoParams(ctypes.Structure):
@@ -34,6 +35,10 @@ SIGNATURES = {
     "rlk_logprob_from_logits": (c_i32, [
         c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_f32, c_vp, c_vp, c_i32,
         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "rlk_logprob_from_support_workspace_size": (c_sz, [c_i64, c_i64, c_i32, c_f32]),
+    "rlk_logprob_from_support": (c_i32, [
+        c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_vp, c_vp, c_i64, c_f32,
+        c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "rlk_logprob_fused_linear_workspace_size": (c_sz, [c_i64, c_i64, c_i64, c_f32]),
     "rlk_logprob_fused_linear": (c_i32, [
         c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_f32, c_f32, c_i32,

@@ -11,6 +11,7 @@
 #include "../../include/rlk.h"
 #include "fused_kernels.h"
 #include "kernels.h"
+#include "support_kernels.h"
 
 namespace {
 
@@ -137,6 +138,101 @@ rlk_status rlk_logprob_from_logits(const void* logits, int32_t dtype, int64_t n_
   return hip_status(rlk::launch_logits_rows(a, dtype, workspace,
                                             reinterpret_cast<hipStream_t>(stream)),
                     "rlk_logprob_from_logits launch");
+}
+
+// ------------------------------------------------------------ retained support
+namespace {
+
+// workspace of the nucleus check: lp_full, lp_trunc, entropy_trunc and
+// threshold (fp32), nucleus size (int32), flags (uint8), each rounded up to
+// 256 bytes, then the logits-in workspace
+size_t support_slot(int64_t n, size_t esz) { return (size_t(n) * esz + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t rlk_logprob_from_support_workspace_size(int64_t n_rows, int64_t vocab, int32_t dtype,
+                                                float check_top_p) {
+  if (n_rows < 0 || !(check_top_p > 0.f)) return 0;
+  return 5 * support_slot(n_rows, 4) + support_slot(n_rows, 1) +
+         rlk::logits_rows_workspace(n_rows, vocab, dtype);
+}
+
+rlk_status rlk_logprob_from_support(const void* logits, int32_t dtype, int64_t n_rows,
+                                    int64_t vocab, int64_t row_stride, const int64_t* targets,
+                                    float temperature, const int64_t* support_offsets,
+                                    const int32_t* support_ids, int64_t n_support,
+                                    float check_top_p, float* logprob, float* entropy,
+                                    uint8_t* flags, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (dtype != RLK_DTYPE_F32 && dtype != RLK_DTYPE_BF16)
+    return fail(RLK_EINVAL, "dtype=%d is not RLK_DTYPE_F32 or RLK_DTYPE_BF16", dtype);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(RLK_EINVAL, "temperature=%g must be finite and > 0", double(temperature));
+  const bool check = check_top_p != 0.f;
+  if (check && !(check_top_p > 0.f && check_top_p <= 1.f))
+    return fail(RLK_EINVAL, "check_top_p=%g must be 0 or lie in (0, 1]", double(check_top_p));
+  if (n_rows < 0) return fail(RLK_EINVAL, "n_rows=%lld < 0", (long long)n_rows);
+  if (n_rows >= (int64_t(1) << 31))
+    return fail(RLK_EINVAL, "n_rows=%lld must be below 2^31", (long long)n_rows);
+  if (vocab < 1 || vocab > kMaxVocab)
+    return fail(RLK_EINVAL, "vocab=%lld outside [1, 2^24]", (long long)vocab);
+  if (row_stride < vocab)
+    return fail(RLK_EINVAL, "row_stride=%lld < vocab=%lld", (long long)row_stride,
+                (long long)vocab);
+  if (n_support < 0) return fail(RLK_EINVAL, "n_support=%lld < 0", (long long)n_support);
+  if (n_rows == 0) return ok();
+  const size_t esz = dtype == RLK_DTYPE_F32 ? 4 : 2;
+  if (!logits || !targets || !support_offsets || !logprob || !entropy ||
+      (n_support > 0 && !support_ids))
+    return fail(RLK_EINVAL,
+                "logits, targets, support_offsets, support_ids, logprob and entropy are required");
+  if (!aligned(logits, esz) || !aligned(targets, 8) || !aligned(support_offsets, 8) ||
+      !aligned(support_ids, 4) || !aligned(logprob, 4) || !aligned(entropy, 4))
+    return fail(RLK_EINVAL, "an array is not naturally aligned");
+  rlk_status s = check_workspace(
+      workspace, workspace_bytes,
+      rlk_logprob_from_support_workspace_size(n_rows, vocab, dtype, check_top_p));
+  if (s != RLK_OK) return s;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  rlk::SupportArgs a{};
+  a.logits = logits;
+  a.n_rows = n_rows;
+  a.vocab = vocab;
+  a.row_stride = row_stride;
+  a.targets = targets;
+  a.temperature = temperature;
+  a.offsets = support_offsets;
+  a.ids = support_ids;
+  a.n_support = n_support;
+  a.lp = logprob;
+  a.ent = entropy;
+  a.flags = flags;
+  if (check) {   // the nucleus of every row, into the workspace
+    char* w = static_cast<char*>(workspace);
+    const size_t f4 = support_slot(n_rows, 4);
+    rlk::RowArgs r{};
+    r.logits = logits;
+    r.n_rows = n_rows;
+    r.vocab = vocab;
+    r.row_stride = row_stride;
+    r.targets = targets;
+    r.temperature = temperature;
+    r.top_p = check_top_p;
+    r.lp_full = reinterpret_cast<float*>(w);
+    r.lp_trunc = reinterpret_cast<float*>(w + f4);
+    r.ent_trunc = reinterpret_cast<float*>(w + 2 * f4);
+    r.thresh = reinterpret_cast<float*>(w + 3 * f4);
+    r.nsize = reinterpret_cast<int32_t*>(w + 4 * f4);
+    r.flags = reinterpret_cast<uint8_t*>(w + 5 * f4);
+    s = hip_status(rlk::launch_logits_rows(r, dtype, w + 5 * f4 + support_slot(n_rows, 1), st),
+                   "rlk_logprob_from_support nucleus launch");
+    if (s != RLK_OK) return s;
+    a.nsize = r.nsize;
+    a.thresh = r.thresh;
+    a.nflags = r.flags;
+  }
+  return hip_status(rlk::launch_support_rows(a, dtype, st), "rlk_logprob_from_support launch");
 }
 
 // ------------------------------------------------------------------ fused LM head

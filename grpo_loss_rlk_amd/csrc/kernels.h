@@ -22,7 +22,8 @@ struct RowArgs {
   int32_t* nsize;         // nullable
   float* thresh;          // nullable
   uint8_t* flags;         // nullable
-  float* saved4;          // nullable [n_rows, 4]: log Z_S and E_q over S of z/T, threshold, 0
+  float* saved4;          // nullable [n_rows, 4]: log Z_S and E_q over S of z/T, threshold,
+                          // 1 when the lp term is live (target in range and kept) else 0
   // fp32 rows produced by the fused LM head (nullable, both or neither):
   // per row, the order key of the max logit and a non-finite flag, written
   // by the producer; read and cleared to 0 here

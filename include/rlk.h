@@ -62,6 +62,10 @@ typedef int32_t rlk_status;
 #define RLK_FLAG_NONFINITE 4u   /* a NaN / +inf logit, or no finite logit: outputs NaN */
 #define RLK_FLAG_BOUNDARY 8u    /* nucleus mass within 1e-6 of top-p (advisory) */
 #define RLK_FLAG_BAD_PARAM 16u  /* per-row temperature or top-p out of range: outputs NaN */
+#define RLK_FLAG_BAD_SUPPORT 32u /* retained-support scoring: the row's set is empty, out of
+                                    range or not strictly increasing: outputs NaN */
+#define RLK_FLAG_MISMATCH 64u   /* retained-support scoring with a top-p check: the set is not
+                                    the nucleus recomputed from the logits */
 
 /* ABI version of this header: 1. */
 int32_t rlk_abi_version(void);
@@ -117,6 +121,49 @@ rlk_status rlk_logprob_from_logits(
     const float* temperature_per_row, const float* top_p_per_row, int32_t top_k,
     float* lp_full, float* lp_trunc, float* entropy_trunc,
     float* entropy_full, int32_t* nucleus_size, float* threshold, uint8_t* flags,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Logits in, retained support: log-probability and entropy over a
+ * caller-supplied token set per row.
+ *
+ * Consistency page, "ROCm MI300X and gfx942": below top-p 1 the rollout
+ * sampler hands its complete finite retained-token set to the deterministic
+ * logprob kernel, which scores the selected token and the monitoring entropy
+ * over that set (the sparse path); prime-rl v0.10.0 release notes,
+ * "Breaking changes": the sampling mask travels in CSR form.
+ *
+ * For row n with S = support_ids[support_offsets[n] .. support_offsets[n+1]):
+ *   d_i = (z_i - max_{j in S} z_j) / T,  Z_S = sum_{i in S} exp(d_i)
+ *   logprob[n] = d_y - log Z_S, or -inf with RLK_FLAG_OUTSIDE if y is not in S
+ *   entropy[n] = log Z_S - sum_{i in S} exp(d_i) d_i / Z_S
+ * logits, dtype, n_rows, vocab, row_stride, targets, temperature   as for
+ *               rlk_logprob_from_logits.
+ * support_offsets  [n_rows + 1] int64 (device): row n's ids are entries
+ *               support_offsets[n] .. support_offsets[n+1] - 1 of support_ids.
+ * support_ids   [n_support] int32 (device) token ids; a row's ids must be
+ *               strictly increasing, in [0, vocab), non-empty and name finite
+ *               logits, else the row gets NaN outputs and RLK_FLAG_BAD_SUPPORT
+ *               (or RLK_FLAG_NONFINITE). Offsets outside [0, n_support] make
+ *               the row invalid; nothing past n_support is read.
+ * check_top_p   0: no check. In (0, 1]: each row's nucleus at (temperature,
+ *               check_top_p) is recomputed from the logits as by
+ *               rlk_logprob_from_logits, and RLK_FLAG_MISMATCH marks a set that
+ *               differs from it (RLK_FLAG_BOUNDARY: the row lies within 1e-6 of
+ *               the top-p boundary, where another set is equally valid).
+ * logprob, entropy [n_rows] fp32 outputs (required); flags [n_rows] uint8
+ *               (nullable). Outputs of a row depend on that row only.
+ * Workspace: none without the check; with it, the nucleus outputs of every row
+ * and the logits-in workspace.
+ * -------------------------------------------------------------------------- */
+size_t rlk_logprob_from_support_workspace_size(int64_t n_rows, int64_t vocab, int32_t dtype,
+                                                float check_top_p);
+
+rlk_status rlk_logprob_from_support(
+    const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab, int64_t row_stride,
+    const int64_t* targets, float temperature,
+    const int64_t* support_offsets, const int32_t* support_ids, int64_t n_support,
+    float check_top_p, float* logprob, float* entropy, uint8_t* flags,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------------------

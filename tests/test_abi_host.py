@@ -195,3 +195,46 @@ def test_fused_workspace_queries(L):
     # backward: W^T and h^T in bf16 plus two bf16 copies of one 32768-row chunk of G
     need = 2 * 4096 * 151936 + 2 * 4096 * 8192 + 2 * 2 * 8192 * 32768
     assert L.rlk_logprob_fused_linear_bwd_workspace_size(8192, 4096, 151936, 1.0) >= need
+
+
+def _support(L, **kw):
+    a = dict(logits=FAKE, dtype=1, n=4, V=1000, stride=1000, targets=FAKE, T=1.0, off=FAKE,
+             ids=FAKE, nnz=10, p=0.0, lp=FAKE, ent=FAKE, fl=None, ws=WS, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.rlk_logprob_from_support(a["logits"], a["dtype"], a["n"], a["V"], a["stride"],
+                                      a["targets"], a["T"], a["off"], a["ids"], a["nnz"], a["p"],
+                                      a["lp"], a["ent"], a["fl"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), _native.RLK_EINVAL),
+    (dict(T=0.0), _native.RLK_EINVAL),
+    (dict(T=math.inf), _native.RLK_EINVAL),
+    (dict(p=1.5), _native.RLK_EINVAL),
+    (dict(p=-0.25), _native.RLK_EINVAL),
+    (dict(p=math.nan), _native.RLK_EINVAL),
+    (dict(n=-1), _native.RLK_EINVAL),
+    (dict(n=1 << 31), _native.RLK_EINVAL),
+    (dict(V=0), _native.RLK_EINVAL),
+    (dict(stride=999), _native.RLK_EINVAL),
+    (dict(nnz=-1), _native.RLK_EINVAL),
+    (dict(off=None), _native.RLK_EINVAL),
+    (dict(ids=None), _native.RLK_EINVAL),
+    (dict(lp=None), _native.RLK_EINVAL),
+    (dict(ent=None), _native.RLK_EINVAL),
+    (dict(logits=P(0x100001)), _native.RLK_EINVAL),
+    (dict(off=P(0x100004)), _native.RLK_EINVAL),
+    (dict(p=0.9, ws=None), _native.RLK_EWORKSPACE),
+    (dict(p=0.9, ws_bytes=16), _native.RLK_EWORKSPACE),
+])
+def test_support_validation(L, kw, status):
+    assert _support(L, **kw) == status
+    assert len(L.rlk_last_error()) > 0
+
+
+def test_support_empty_batch_and_workspace(L):
+    assert _support(L, n=0, logits=None, targets=None, off=None, ids=None, lp=None,
+                    ent=None) == _native.RLK_OK
+    assert L.rlk_logprob_from_support_workspace_size(4096, 151936, 1, 0.0) == 0
+    need = L.rlk_logprob_from_support_workspace_size(4096, 151936, 1, 0.95)
+    assert need >= 4096 * (5 * 4 + 1) + L.rlk_logprob_from_logits_workspace_size(4096, 151936, 1)
