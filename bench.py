@@ -127,6 +127,63 @@ def leg_logits(torch, rlk, synth, steps, warmup, cpu_sample):
     return res
 
 
+def leg_support(torch, rlk, synth, steps, warmup):
+    """Retained-support scoring on the config-2 logits (4096 x 151936 bf16,
+    T=0.7): each row's set is its top-p 0.95 nucleus (picked with torch
+    outside the timed region: sort, tempered softmax, cumulative mass), as the
+    rollout sampler would hand it over in CSR form; timed without and with the
+    check against the recomputed nucleus."""
+    w = synth.workload("qwen")
+    arr = synth.logits_rows(w, range(w.N))
+    y = synth.peak_targets(w, range(w.N))
+    x = torch.from_numpy(arr.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    sets = []
+    for r0 in range(0, w.N, 256):
+        zs, idx = torch.sort(x[r0:r0 + 256].float() / w.temperature, dim=1, descending=True)
+        c = torch.cumsum(torch.softmax(zs, dim=1), dim=1)
+        k = (c < w.top_p).sum(dim=1) + 1
+        for i in range(idx.shape[0]):
+            sets.append(torch.sort(idx[i, :int(k[i])]).values.to(torch.int32))
+    sizes = torch.tensor([t.numel() for t in sets], dtype=torch.int64)
+    offsets = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(sizes, 0)]).to("cuda:0")
+    ids = torch.cat(sets).contiguous()
+    # targets: a member of each set (the first id), as a sampled token would be
+    yt = torch.stack([t[0] for t in sets]).to(torch.int64).contiguous()
+    nnz = int(ids.numel())
+    del y
+    print(f"[bench] support leg: {w.N} rows, {nnz} retained ids (median "
+          f"{int(sizes.median())}, max {int(sizes.max())})", file=sys.stderr, flush=True)
+    fn = lambda: rlk.logprob_from_support(x, yt, w.temperature, offsets, ids)  # noqa: E731
+    mean_ms, total_ms, min_ms = _events_time(torch, fn, steps, warmup)
+    fnc = lambda: rlk.logprob_from_support(x, yt, w.temperature, offsets, ids,  # noqa: E731
+                                           check_top_p=w.top_p)
+    mean_c, total_c, min_c = _events_time(torch, fnc, max(3, steps // 4), warmup)
+    # A gather moves whole 64-byte sectors: the bytes a perfect kernel must
+    # move are the ids (4 B each), every distinct 64-byte sector of logits the
+    # sets touch (32 bf16 ids per sector; a row's ids are sorted), and per row
+    # the offsets, target and 9 B of outputs.
+    sec = torch.div(ids, 32, rounding_mode="floor")
+    same = sec[1:] == sec[:-1]
+    starts = offsets[1:-1]
+    same[starts[starts > 0] - 1] = False
+    sectors = nnz - int(same.sum())
+    alg = nnz * 4 + sectors * 64 + w.N * (8 + 8 + 9)
+    achieved = alg / (mean_ms * 1e-3) / 1e9
+    return {
+        "workload": f"retained-support scoring, {w.N} rows x V={w.V} bf16, T={w.temperature}, "
+                    f"sets = top-p {w.top_p} nuclei ({nnz} ids)",
+        "tokens_per_s": w.N * steps / (total_ms * 1e-3),
+        "ms_per_step": total_ms / steps,
+        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "distinct_64B_sectors": sectors,
+        "with_nucleus_check_ms": mean_c,
+        "with_nucleus_check_tokens_per_s": w.N / (mean_c * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
+                     "traffic": None},
+    }
+
+
 def leg_fused(torch, rlk, synth, steps, warmup):
     """Fused LM-head forward, Qwen3-8B head: hidden [8192, 4096], W [151936, 4096], T=1, p=1."""
     w = synth.workload("fused")
@@ -312,7 +369,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--legs", default="logits,fused,grpo,grpo_train,fused_bwd")
+    ap.add_argument("--legs", default="logits,support,fused,grpo,grpo_train,fused_bwd")
     ap.add_argument("--cpu-sample", type=int, default=1024,
                     help="rows of the logits workload the CPU oracle is timed on (0 = skip)")
     args = ap.parse_args()
@@ -330,6 +387,8 @@ def main():
     if "logits" in legs:
         out_legs["logits"] = leg_logits(torch, rlk, synth, args.steps, args.warmup,
                                         args.cpu_sample)
+    if "support" in legs:
+        out_legs["support"] = leg_support(torch, rlk, synth, args.steps, args.warmup)
     if "fused" in legs:
         out_legs["fused"] = leg_fused(torch, rlk, synth, min(20, max(3, args.steps // 4)), 1)
     if "copy" in legs:

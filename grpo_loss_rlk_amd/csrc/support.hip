@@ -13,10 +13,14 @@
 // |S| equals the nucleus size and every logit of S is >= the threshold
 // (S has distinct ids, and the nucleus is {z >= tau}).
 //
-// One 256-thread block per row, two passes over the support (ids read
-// coalesced, logits gathered): validation, max, min, target; then the sums in
-// fp64 with a fixed per-thread order and a fixed block tree, so a row's
-// outputs are bitwise independent of the batch.
+// Work split by the size of the set only (so a row's outputs never depend on
+// the batch): a block of 256 threads takes 4 rows; a row of at most 512 ids
+// is scored by one wave, a larger one by the whole block afterwards. Two
+// passes over the set (ids read coalesced, logits gathered, 4 loads in flight
+// per thread): validation, max, min and the target; then the sums in fp64,
+// each thread in index order and a fixed reduction tree. The first 8 logits
+// of every thread stay in registers between the passes (all of a wave's set),
+// so only sets beyond 2048 ids gather anything twice.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -52,14 +56,40 @@ RLK_DEV float support_mass(float z, double m, double c, double invT, double* d) 
   return fmaf(e, r * 0.69314718f, e);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kST) void support_rows(SupportArgs a) {
-  __shared__ double sd[kST / kWave];
-  __shared__ float sf[kST / kWave];
-  __shared__ int si[kST / kWave];
-  __shared__ float zy_s;
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+constexpr int kRowsPerBlock = kST / kWave;
+constexpr int64_t kWaveMaxIds = 512;   // sets up to this size are scored by one wave
+constexpr int kU = 4;                  // ids per thread per round
+constexpr int kCached = 2;             // rounds whose logits stay in registers
+
+// Reductions over a group of G threads (a wave or the block), result in
+// every thread; fixed trees.
+template <int G>
+struct Group;
+template <>
+struct Group<kWave> {
+  static RLK_DEV float max(float v, float*) { return __shfl(wave_max(v), 0, kWave); }
+  static RLK_DEV float min(float v, float*) { return __shfl(wave_min(v), 0, kWave); }
+  static RLK_DEV int any(int v, int*) { return __any(v) ? 1 : 0; }
+  static RLK_DEV double sum(double v, double*) { return __shfl(wave_sum(v), 0, kWave); }
+};
+template <>
+struct Group<kST> {
+  static RLK_DEV float max(float v, float* s) { return block_max(v, s); }
+  static RLK_DEV float min(float v, float* s) { return block_min(v, s); }
+  static RLK_DEV int any(int v, int* s) { return block_max(v, s); }
+  static RLK_DEV double sum(double v, double* s) { return block_sum(v, s); }
+};
+
+struct Scratch {
+  double d[kST / kWave];
+  float f[kST / kWave];
+  int i[kST / kWave];
+};
+
+// Score one row with the G threads whose index in the group is g.
+template <typename T, int G>
+RLK_DEV void score_row(const SupportArgs& a, int64_t row, int g, Scratch& sc) {
+  using R = Group<G>;
   const int64_t V = a.vocab;
   const T* zrow = reinterpret_cast<const T*>(a.logits) + row * a.row_stride;
   const int64_t y = a.targets[row];
@@ -67,39 +97,55 @@ __global__ __launch_bounds__(kST) void support_rows(SupportArgs a) {
   uint8_t flags = 0;
   if (y < 0 || y >= V) flags |= kBadTarget;
   const bool range_ok = o0 >= 0 && o1 > o0 && o1 <= a.n_support;
-  if (tid == 0) zy_s = 0.f;
-  __syncthreads();
 
   // ---- pass 1: ids valid and increasing, logits finite, max, min, target ----
+  // The first kCached rounds keep their logits in registers for pass 2.
   int bad = range_ok ? 0 : 1, nonfin = 0, found = 0;
-  float mx = -INFINITY, mn = INFINITY;
-  if (range_ok) {
-    for (int64_t k = o0 + tid; k < o1; k += kST) {
-      const int32_t id = a.ids[k];
-      if (id < 0 || id >= V || (k > o0 && a.ids[k - 1] >= id)) {
-        bad = 1;
-        continue;
-      }
-      const float z = value_at<T>(zrow, id);
-      if (!(fabsf(z) <= 3.402823466e38f)) nonfin = 1;
-      mx = fmaxf(mx, z);
-      mn = fminf(mn, z);
-      if (id == y) {
-        found = 1;
-        zy_s = z;
+  float mx = -INFINITY, mn = INFINITY, zy = -INFINITY;
+  float zc[kCached][kU];
+  auto round1 = [&](int64_t k0, float (&z)[kU]) __attribute__((always_inline)) {
+    int32_t id[kU], prev[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t k = k0 + int64_t(u) * G;
+      id[u] = k < o1 ? a.ids[k] : 0;
+      prev[u] = (k < o1 && k > o0) ? a.ids[k - 1] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t k = k0 + int64_t(u) * G;
+      const bool live = k < o1;
+      const bool ok = id[u] >= 0 && id[u] < V && prev[u] < id[u];
+      if (live && !ok) bad = 1;
+      z[u] = (live && ok) ? value_at<T>(zrow, id[u]) : -INFINITY;
+      if (live && ok) {
+        if (!(fabsf(z[u]) <= 3.402823466e38f)) nonfin = 1;
+        mx = fmaxf(mx, z[u]);
+        mn = fminf(mn, z[u]);
+        if (id[u] == y) {
+          found = 1;
+          zy = z[u];
+        }
       }
     }
+  };
+  if (range_ok) {
+#pragma unroll
+    for (int r = 0; r < kCached; ++r) round1(o0 + g + int64_t(r) * G * kU, zc[r]);
+    for (int64_t k0 = o0 + g + int64_t(kCached) * G * kU; k0 < o1; k0 += int64_t(G) * kU) {
+      float z[kU];
+      round1(k0, z);
+    }
   }
-  __syncthreads();
-  bad = block_max(bad, si);
-  nonfin = block_max(nonfin, si);
-  found = block_max(found, si);
-  mx = block_max(mx, sf);
-  mn = block_min(mn, sf);
-  const float zy = zy_s;
+  bad = R::any(bad, sc.i);
+  nonfin = R::any(nonfin, sc.i);
+  found = R::any(found, sc.i);
+  mx = R::max(mx, sc.f);
+  mn = R::min(mn, sc.f);
+  zy = R::max(zy, sc.f);   // the only candidate is the thread that found y
   const float nan = __builtin_nanf("");
   if (bad || nonfin) {
-    if (tid == 0) {
+    if (g == 0) {
       a.lp[row] = nan;
       a.ent[row] = nan;
       if (a.flags) a.flags[row] = flags | (bad ? kBadSupport : kNonFinite);
@@ -111,15 +157,31 @@ __global__ __launch_bounds__(kST) void support_rows(SupportArgs a) {
   const double m = double(mx), invT = 1.0 / double(a.temperature);
   const double c = 1.4426950408889634 * invT;
   double zs = 0.0, ss = 0.0;
-  for (int64_t k = o0 + tid; k < o1; k += kST) {
-    double d;
-    const double e = double(support_mass(value_at<T>(zrow, a.ids[k]), m, c, invT, &d));
-    zs += e;
-    ss = fma(e, d, ss);
+  auto round2 = [&](int64_t k0, const float (&z)[kU]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (k0 + int64_t(u) * G < o1) {
+        double d;
+        const double e = double(support_mass(z[u], m, c, invT, &d));
+        zs += e;
+        ss = fma(e, d, ss);
+      }
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < kCached; ++r) round2(o0 + g + int64_t(r) * G * kU, zc[r]);
+  for (int64_t k0 = o0 + g + int64_t(kCached) * G * kU; k0 < o1; k0 += int64_t(G) * kU) {
+    float z[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t k = k0 + int64_t(u) * G;
+      z[u] = k < o1 ? value_at<T>(zrow, a.ids[k]) : mx;
+    }
+    round2(k0, z);
   }
-  const double Zs = block_sum(zs, sd);
-  const double Ss = block_sum(ss, sd);
-  if (tid != 0) return;
+  const double Zs = R::sum(zs, sc.d);
+  const double Ss = R::sum(ss, sc.d);
+  if (g != 0) return;
   const double logZs = log(Zs);
   float lp = nan;
   if (!(flags & kBadTarget)) {
@@ -142,11 +204,34 @@ __global__ __launch_bounds__(kST) void support_rows(SupportArgs a) {
   if (a.flags) a.flags[row] = flags;
 }
 
+// A set is "large" when its offsets are valid and it holds more than
+// kWaveMaxIds ids; everything else (including invalid ranges) is a wave's.
+RLK_DEV bool large_set(const SupportArgs& a, int64_t row) {
+  const int64_t o0 = a.offsets[row], o1 = a.offsets[row + 1];
+  return o0 >= 0 && o1 > o0 && o1 <= a.n_support && o1 - o0 > kWaveMaxIds;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kST) void support_rows(SupportArgs a) {
+  __shared__ Scratch sc[kRowsPerBlock + 1];
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int64_t row0 = int64_t(blockIdx.x) * kRowsPerBlock;
+  {   // small sets: one wave each
+    const int64_t row = row0 + w;
+    if (row < a.n_rows && !large_set(a, row)) score_row<T, kWave>(a, row, lane, sc[w]);
+  }
+  // large sets: the whole block, one row after another
+  for (int q = 0; q < kRowsPerBlock; ++q) {
+    const int64_t row = row0 + q;
+    if (row < a.n_rows && large_set(a, row)) score_row<T, kST>(a, row, tid, sc[kRowsPerBlock]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_support_rows(const SupportArgs& a, int dtype, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
-  const dim3 grid(unsigned(a.n_rows));
+  const dim3 grid(unsigned((a.n_rows + kRowsPerBlock - 1) / kRowsPerBlock));
   if (dtype == 0)
     hipLaunchKernelGGL(support_rows<float>, grid, dim3(kST), 0, stream, a);
   else
