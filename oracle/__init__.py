@@ -11,8 +11,10 @@ computes, written in fp64 numpy from the definitions:
   keep-all-ties), truncated/renormalised log-probability and entropy
   (pages: Qwen3-8B VIME train-rollout consistency, "ROCm MI300X and gfx942";
   RL-Kernel ROCm sparse performance page, quick-start command paragraph).
-* ``sampling`` -- seeded Gumbel-max draw of a target from the nucleus (used
-  only to prepare inputs; the GPU path never samples).
+* ``sampling`` -- seeded Gumbel-max draw of a target from the nucleus (test
+  inputs), and the definition the GPU sampler follows (``sample_row``).
+* ``philox``   -- the Philox-4x32-10 counter-based generator the sampler draws
+  its uniforms from (published definition, Salmon et al., SC 2011).
 * ``fused``    -- the LM-head forms: logits = hidden . W^T in fp64, then the
   same statistics; the backward through them (prime-rl v0.10.0 release notes,
   "1. Trainer Performance": chunked loss; consistency page, "Canonical
@@ -28,4 +30,4 @@ It shares no code with the HIP path. Inputs come from ``synth`` (seeded
 random numbers only). Every function is pinned by CPU tests against closed
 forms, library routines, brute force and finite differences (tests/test_oracle_*.py).
 """
-from . import logprob, sampling, fused, grpo, support  # noqa: F401
+from . import logprob, philox, sampling, fused, grpo, support  # noqa: F401

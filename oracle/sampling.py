@@ -1,7 +1,8 @@
 """fp64 oracle: seeded Gumbel-max draw of a target token from the nucleus.
 
-TEST INFRASTRUCTURE ONLY (see the package docstring). It prepares inputs: the
-HIP path never samples, it scores the target it is given.
+TEST INFRASTRUCTURE ONLY (see the package docstring). ``gumbel_max_target``
+prepares test inputs from given uniforms; ``sample_row`` is the definition the
+GPU sampler (rlk_sample_top_p) is checked against.
 
 The rollout side samples from the same truncated distribution the trainer
 scores (prime-rl v0.10.0 release notes, "2. RL Algorithms": top-p sampling is
@@ -13,7 +14,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import logprob
+from . import logprob, philox
 
 
 def gumbel_max_target(z, T: float, p: float, u) -> int:
@@ -23,4 +24,20 @@ def gumbel_max_target(z, T: float, p: float, u) -> int:
     m = z[keep].max()
     score = np.full(z.size, -np.inf)
     score[keep] = (z[keep] - m) / T - np.log(-np.log(np.asarray(u, dtype=np.float64)[keep]))
+    return int(np.argmax(score))
+
+
+def sample_row(z, T: float, p: float, seed: int, offset: int, row_key: int) -> int:
+    """The GPU sampler's definition: Gumbel-max over the top-p nucleus of the
+    tempered row with Philox uniforms (``philox.row_uniforms``):
+    y = argmax_{i in S} (z_i / T - log(-log u_i)), the lowest id on an exact
+    tie; -1 for a row with a NaN / +inf logit or no finite logit. The score
+    drops the row max the other form subtracts: the same argmax and law."""
+    z = np.asarray(z, dtype=np.float64)
+    if np.isnan(z).any() or np.isposinf(z).any() or not (z > -np.inf).any():
+        return -1
+    keep, *_ = logprob.nucleus(z, T, p)
+    u = philox.row_uniforms(seed, offset, row_key, z.size)
+    score = np.full(z.size, -np.inf)
+    score[keep] = z[keep] / T - np.log(-np.log(u[keep]))
     return int(np.argmax(score))
