@@ -184,6 +184,36 @@ def leg_support(torch, rlk, synth, steps, warmup):
     }
 
 
+def leg_sample(torch, rlk, synth, steps, warmup):
+    """Rollout-side top-p sampler on the config-2 logits (4096 x 151936 bf16,
+    T=0.7, p=0.95): nucleus (row kernel), seeded Gumbel-max draw, and the
+    drawn token scored by the row kernel (bitwise the training-side value).
+    The call reads each row three times (nucleus, draw, score): 3 x 2V bytes
+    per row plus outputs."""
+    w = synth.workload("qwen")
+    arr = synth.logits_rows(w, range(w.N))
+    x = torch.from_numpy(arr.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    state = {"offset": 0}
+
+    def fn():
+        state["offset"] += 1
+        return rlk.sample_top_p(x, w.temperature, w.top_p, 1234, state["offset"])
+
+    mean_ms, total_ms, min_ms = _events_time(torch, fn, steps, warmup)
+    bytes_per_row = 3 * 2 * w.V + 8 + 4 + 4 + 4 + 1
+    achieved = w.N * bytes_per_row / (mean_ms * 1e-3) / 1e9
+    return {
+        "workload": f"top-p sampler + score, {w.N} rows x V={w.V} bf16, T={w.temperature}, "
+                    f"top-p={w.top_p}, Philox-4x32-10 Gumbel-max",
+        "tokens_per_s": w.N * steps / (total_ms * 1e-3),
+        "ms_per_step": total_ms / steps,
+        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "bytes_per_row": bytes_per_row,
+    }
+
+
 def leg_fused(torch, rlk, synth, steps, warmup):
     """Fused LM-head forward, Qwen3-8B head: hidden [8192, 4096], W [151936, 4096], T=1, p=1."""
     w = synth.workload("fused")
@@ -369,7 +399,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--legs", default="logits,support,fused,grpo,grpo_train,fused_bwd")
+    ap.add_argument("--legs", default="logits,support,sample,fused,grpo,grpo_train,fused_bwd")
     ap.add_argument("--cpu-sample", type=int, default=1024,
                     help="rows of the logits workload the CPU oracle is timed on (0 = skip)")
     args = ap.parse_args()
@@ -389,6 +419,8 @@ def main():
                                         args.cpu_sample)
     if "support" in legs:
         out_legs["support"] = leg_support(torch, rlk, synth, args.steps, args.warmup)
+    if "sample" in legs:
+        out_legs["sample"] = leg_sample(torch, rlk, synth, max(3, args.steps // 4), args.warmup)
     if "fused" in legs:
         out_legs["fused"] = leg_fused(torch, rlk, synth, min(20, max(3, args.steps // 4)), 1)
     if "copy" in legs:

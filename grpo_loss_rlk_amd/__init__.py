@@ -129,6 +129,45 @@ def logprob_from_support(logits: torch.Tensor, targets: torch.Tensor, temperatur
     return out
 
 
+def sample_top_p(logits: torch.Tensor, temperature: float, top_p: float, seed: int,
+                 offset: int = 0, *, row_keys=None, vocab: int | None = None) -> dict:
+    """Draw one token per row from the tempered top-p nucleus (seeded
+    Gumbel-max, Philox-4x32-10 uniforms) and score it with the logits-in
+    kernel. Returns samples (int64, -1 for a row without a finite logit),
+    logprob, entropy, nucleus_size, flags."""
+    if logits.dtype == torch.float32:
+        dtype = DTYPE_F32
+    elif logits.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+    else:
+        raise TypeError(f"logits dtype {logits.dtype} is not float32 or bfloat16")
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D tensor with unit column stride")
+    N, width = logits.shape
+    V = width if vocab is None else int(vocab)
+    dev = logits.device
+    keys = None
+    if row_keys is not None:
+        keys = torch.as_tensor(row_keys).to(device=dev, dtype=torch.int64).contiguous()
+        if keys.numel() != N:
+            raise ValueError("row_keys must hold one key per row")
+    f = dict(device=dev, dtype=torch.float32)
+    out = {"samples": torch.empty(N, device=dev, dtype=torch.int64),
+           "logprob": torch.empty(N, **f), "entropy": torch.empty(N, **f),
+           "nucleus_size": torch.empty(N, device=dev, dtype=torch.int32),
+           "flags": torch.empty(N, device=dev, dtype=torch.uint8)}
+    L = lib()
+    ws_n = L.rlk_sample_top_p_workspace_size(N, V, dtype)
+    ws = _workspace(ws_n, dev)
+    st = L.rlk_sample_top_p(
+        _ptr(logits), dtype, N, V, logits.stride(0) if N > 0 else V, float(temperature),
+        float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, _ptr(keys),
+        _ptr(out["samples"]), _ptr(out["logprob"]), _ptr(out["entropy"]),
+        _ptr(out["nucleus_size"]), _ptr(out["flags"]), _ptr(ws), ws_n, _stream(dev))
+    _native.check(st, "rlk_sample_top_p")
+    return out
+
+
 def logprob_fused_linear(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
                          temperature: float = 1.0, top_p: float = 1.0, *, top_k: int = 0,
                          want_saved: bool = True) -> dict:

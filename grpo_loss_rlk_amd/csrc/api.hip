@@ -11,6 +11,7 @@
 #include "../../include/rlk.h"
 #include "fused_kernels.h"
 #include "kernels.h"
+#include "sampler_kernels.h"
 #include "support_kernels.h"
 
 namespace {
@@ -233,6 +234,99 @@ rlk_status rlk_logprob_from_support(const void* logits, int32_t dtype, int64_t n
     a.nflags = r.flags;
   }
   return hip_status(rlk::launch_support_rows(a, dtype, st), "rlk_logprob_from_support launch");
+}
+
+// ------------------------------------------------------------------- sampler
+size_t rlk_sample_top_p_workspace_size(int64_t n_rows, int64_t vocab, int32_t dtype) {
+  if (n_rows < 0) return 0;
+  // dummy targets (int64), lp_full, lp_trunc, entropy, threshold (fp32), flags,
+  // then the logits-in workspace
+  return support_slot(n_rows, 8) + 4 * support_slot(n_rows, 4) + support_slot(n_rows, 1) +
+         rlk::logits_rows_workspace(n_rows, vocab, dtype);
+}
+
+rlk_status rlk_sample_top_p(const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab,
+                            int64_t row_stride, float temperature, float top_p, uint64_t seed,
+                            uint32_t offset, const int64_t* row_keys, int64_t* samples,
+                            float* logprob, float* entropy, int32_t* nucleus_size,
+                            uint8_t* flags, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (dtype != RLK_DTYPE_F32 && dtype != RLK_DTYPE_BF16)
+    return fail(RLK_EINVAL, "dtype=%d is not RLK_DTYPE_F32 or RLK_DTYPE_BF16", dtype);
+  rlk_status s = check_sampling(temperature, top_p, 0);
+  if (s != RLK_OK) return s;
+  if (n_rows < 0) return fail(RLK_EINVAL, "n_rows=%lld < 0", (long long)n_rows);
+  if (n_rows >= (int64_t(1) << 31))
+    return fail(RLK_EINVAL, "n_rows=%lld must be below 2^31", (long long)n_rows);
+  if (vocab < 1 || vocab > kMaxVocab)
+    return fail(RLK_EINVAL, "vocab=%lld outside [1, 2^24]", (long long)vocab);
+  if (row_stride < vocab)
+    return fail(RLK_EINVAL, "row_stride=%lld < vocab=%lld", (long long)row_stride,
+                (long long)vocab);
+  if (n_rows == 0) return ok();
+  const size_t esz = dtype == RLK_DTYPE_F32 ? 4 : 2;
+  if (!logits || !samples) return fail(RLK_EINVAL, "logits and samples are required");
+  if (!aligned(logits, esz) || !aligned(samples, 8) || !aligned(row_keys, 8) ||
+      !aligned(logprob, 4) || !aligned(entropy, 4) || !aligned(nucleus_size, 4))
+    return fail(RLK_EINVAL, "an array is not naturally aligned");
+  s = check_workspace(workspace, workspace_bytes,
+                      rlk_sample_top_p_workspace_size(n_rows, vocab, dtype));
+  if (s != RLK_OK) return s;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  const size_t f4 = support_slot(n_rows, 4);
+  int64_t* zero_t = reinterpret_cast<int64_t*>(w);
+  w += support_slot(n_rows, 8);
+  float* lp_full = reinterpret_cast<float*>(w);
+  float* lp_tr = reinterpret_cast<float*>(w + f4);
+  float* ent = reinterpret_cast<float*>(w + 2 * f4);
+  float* thr = reinterpret_cast<float*>(w + 3 * f4);
+  uint8_t* nfl = reinterpret_cast<uint8_t*>(w + 4 * f4);
+  void* rows_ws = w + 4 * f4 + support_slot(n_rows, 1);
+
+  rlk::RowArgs r{};
+  r.logits = logits;
+  r.n_rows = n_rows;
+  r.vocab = vocab;
+  r.row_stride = row_stride;
+  r.temperature = temperature;
+  r.top_p = top_p;
+  // 1. each row's nucleus threshold (the target is a placeholder)
+  s = hip_status(rlk::launch_fill_i64(zero_t, n_rows, 0, st), "rlk_sample_top_p fill");
+  if (s != RLK_OK) return s;
+  r.targets = zero_t;
+  r.lp_full = lp_full;
+  r.lp_trunc = lp_tr;
+  r.ent_trunc = ent;
+  r.thresh = thr;
+  r.flags = nfl;
+  s = hip_status(rlk::launch_logits_rows(r, dtype, rows_ws, st), "rlk_sample_top_p nucleus");
+  if (s != RLK_OK) return s;
+  // 2. the draw
+  rlk::SampleArgs a{};
+  a.logits = logits;
+  a.n_rows = n_rows;
+  a.vocab = vocab;
+  a.row_stride = row_stride;
+  a.temperature = temperature;
+  a.seed = seed;
+  a.offset = offset;
+  a.row_keys = row_keys;
+  a.thresh = thr;
+  a.nflags = nfl;
+  a.samples = samples;
+  s = hip_status(rlk::launch_sample_rows(a, dtype, st), "rlk_sample_top_p draw");
+  if (s != RLK_OK) return s;
+  // 3. the drawn tokens scored by the logits-in kernel itself, so the
+  // rollout's logprobs are bitwise those of a training-side call
+  if (!logprob && !entropy && !nucleus_size && !flags) return ok();
+  r.targets = samples;
+  r.lp_trunc = logprob ? logprob : lp_tr;
+  r.ent_trunc = entropy ? entropy : ent;
+  r.thresh = nullptr;
+  r.nsize = nucleus_size;
+  r.flags = flags;
+  return hip_status(rlk::launch_logits_rows(r, dtype, rows_ws, st), "rlk_sample_top_p score");
 }
 
 // ------------------------------------------------------------------ fused LM head

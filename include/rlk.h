@@ -167,6 +167,34 @@ rlk_status rlk_logprob_from_support(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------------------
+ * Top-p sampler on the same row kernel (rollout side of the replay).
+ *
+ * prime-rl v0.10.0 release notes, "2. RL Algorithms": top-p sampling is
+ * replayed exactly in the trainer; consistency page: rollout and training
+ * logprobs must agree bitwise. Per row: the nucleus S at (temperature, top_p)
+ * as rlk_logprob_from_logits finds it, then
+ *   samples[n] = argmax_{i in S} z_i / T - log(-log u_i)   (fp64; the lowest
+ *                id on an exact tie; -1 for a row without a finite logit or
+ *                with a NaN / +inf one)
+ * with u_i = (w + 1/2) 2^-32, w = word i % 4 of Philox-4x32-10 (Salmon et
+ * al., SC 2011) on counter (i / 4, key_n low 32 bits, key_n high 32 bits,
+ * offset) and key (seed low 32 bits, seed high 32 bits); key_n = row_keys[n]
+ * (nullable: n). A draw depends on its row, seed, offset and key only.
+ * logprob, entropy, nucleus_size, flags (nullable): the drawn token scored by
+ * rlk_logprob_from_logits' kernel (its lp_trunc, entropy_trunc, nucleus size
+ * and flags), so they equal bitwise what a training-side call with
+ * targets = samples returns.
+ * Limits: as rlk_logprob_from_logits; n_rows < 2^31.
+ * -------------------------------------------------------------------------- */
+size_t rlk_sample_top_p_workspace_size(int64_t n_rows, int64_t vocab, int32_t dtype);
+
+rlk_status rlk_sample_top_p(
+    const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab, int64_t row_stride,
+    float temperature, float top_p, uint64_t seed, uint32_t offset, const int64_t* row_keys,
+    int64_t* samples, float* logprob, float* entropy, int32_t* nucleus_size, uint8_t* flags,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
  * Fused LM head, forward: logprob and entropy of targets under softmax(h W^T / T)
  * without materialising the [N, V] logits (prime-rl v0.10.0 release notes,
  * "1. Trainer Performance": the loss is chunked torchtitan-style).

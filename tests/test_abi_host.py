@@ -238,3 +238,40 @@ def test_support_empty_batch_and_workspace(L):
     assert L.rlk_logprob_from_support_workspace_size(4096, 151936, 1, 0.0) == 0
     need = L.rlk_logprob_from_support_workspace_size(4096, 151936, 1, 0.95)
     assert need >= 4096 * (5 * 4 + 1) + L.rlk_logprob_from_logits_workspace_size(4096, 151936, 1)
+
+
+def _sample(L, **kw):
+    a = dict(logits=FAKE, dtype=1, n=4, V=1000, stride=1000, T=1.0, p=0.9, seed=1, off=0,
+             keys=None, out=FAKE, lp=None, ent=None, ns=None, fl=None, ws=WS, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.rlk_sample_top_p(a["logits"], a["dtype"], a["n"], a["V"], a["stride"], a["T"],
+                              a["p"], a["seed"], a["off"], a["keys"], a["out"], a["lp"], a["ent"],
+                              a["ns"], a["fl"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), _native.RLK_EINVAL),
+    (dict(T=0.0), _native.RLK_EINVAL),
+    (dict(T=math.nan), _native.RLK_EINVAL),
+    (dict(p=0.0), _native.RLK_EINVAL),
+    (dict(p=1.01), _native.RLK_EINVAL),
+    (dict(n=-2), _native.RLK_EINVAL),
+    (dict(V=0), _native.RLK_EINVAL),
+    (dict(V=(1 << 24) + 1, stride=(1 << 24) + 1), _native.RLK_EINVAL),
+    (dict(stride=10), _native.RLK_EINVAL),
+    (dict(out=None), _native.RLK_EINVAL),
+    (dict(logits=None), _native.RLK_EINVAL),
+    (dict(out=P(0x100004)), _native.RLK_EINVAL),
+    (dict(keys=P(0x100004)), _native.RLK_EINVAL),
+    (dict(ws=None), _native.RLK_EWORKSPACE),
+    (dict(ws_bytes=8), _native.RLK_EWORKSPACE),
+])
+def test_sample_validation(L, kw, status):
+    assert _sample(L, **kw) == status
+    assert len(L.rlk_last_error()) > 0
+
+
+def test_sample_empty_batch_and_workspace(L):
+    assert _sample(L, n=0, logits=None, out=None) == _native.RLK_OK
+    need = L.rlk_sample_top_p_workspace_size(4096, 151936, 1)
+    assert need >= 4096 * (8 + 4 * 4 + 1) + L.rlk_logprob_from_logits_workspace_size(4096, 151936, 1)
