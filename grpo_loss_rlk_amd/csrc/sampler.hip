@@ -56,10 +56,26 @@ RLK_DEV bool better(double s, int64_t i, double s2, int64_t i2) {
   return s > s2 || (s == s2 && i < i2);
 }
 
-template <typename T>
+constexpr int kRound = kSmT * 8;   // ids of one round at most (one 16-byte vector per thread)
+constexpr int kAhead = 4;          // 16-byte vectors in flight per thread
+
+// One row per block, in rounds of one 16-byte vector per thread. A round
+// lists (id, logit) of its nucleus members (logit >= tau) in LDS, one atomic
+// per wave (a wave prefix sum places each thread's entries); then every
+// thread scores list entries densely (so the Philox and fp64 work is not
+// spread thin over diverged lanes) while the next kAhead vectors are in
+// flight.
+// Rounds alternate between two lists with their own running counters, so one
+// barrier per round separates a round's appends from its scoring and the
+// scoring from the list's reuse two rounds later. The draw is an argmax, so
+// the order of a list does not matter.
+template <typename T, bool kVec>
 __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
   __shared__ double ss[kSmT / kWave];
   __shared__ int64_t si[kSmT / kWave];
+  __shared__ int32_t list_i[2][kRound];
+  __shared__ float list_z[2][kRound];
+  __shared__ int cnt[2];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int64_t row = blockIdx.x;
   if (a.nflags[row] & (kNonFinite | kBadParam)) {
@@ -74,29 +90,109 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
   double best = -INFINITY;
   int64_t best_i = INT64_MAX;
-  // thread t takes groups of 4 consecutive ids t, t + 256, ... (one Philox call each)
-  for (int64_t g = tid; 4 * g < V; g += kSmT) {
-    float z[4];
-    bool in[4], any = false;
+  if (tid < 2) cnt[tid] = 0;
+  __syncthreads();
+  int last[2] = {0, 0};   // each list's counter at its previous scoring
+  int par = 0;
+  constexpr int kEV = 16 / int(sizeof(T));   // values per 16-byte vector (8 bf16, 4 fp32)
+
+  // list this thread's ids i0 .. i0 + kEV - 1 that are in the nucleus; the
+  // whole wave calls this together
+  auto offer = [&](int64_t i0, const float (&z)[kEV]) __attribute__((always_inline)) {
+    uint32_t m = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t i = 4 * g + e;
-      z[e] = i < V ? val<T>(zrow, i) : -INFINITY;
-      in[e] = z[e] >= tau && z[e] > -INFINITY;
-      any |= in[e];
+    for (int e = 0; e < kEV; ++e)
+      if (i0 + e < V && z[e] >= tau && z[e] > -INFINITY) m |= 1u << e;
+    const int n = __popc(m);
+    const int incl = wave_scan_incl(n);
+    const int total = __shfl(incl, kWave - 1, kWave);
+    if (total == 0) return;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&cnt[par], total);
+    base = __shfl(base, 0, kWave) - last[par] + incl - n;
+    while (m) {
+      const int e = __ffs(m) - 1;
+      m &= m - 1;
+      list_i[par][base] = int32_t(i0 + e);
+      list_z[par][base] = z[e];
+      ++base;
     }
-    if (!any) continue;
-    uint32_t c[4] = {uint32_t(g), uint32_t(rk), uint32_t(rk >> 32), a.offset};
-    philox4x32_10(c, k0, k1);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (!in[e]) continue;
-      const double u = (double(c[e]) + 0.5) * 0x1p-32;
-      const double s = double(z[e]) / T64 - log(-log(u));
-      if (better(s, 4 * g + e, best, best_i)) {
+  };
+  auto score_listed = [&]() __attribute__((always_inline)) {
+    __syncthreads();
+    const int end = cnt[par];
+    for (int c = tid; c < end - last[par]; c += kSmT) {
+      const int64_t i = list_i[par][c];
+      uint32_t w[4] = {uint32_t(i >> 2), uint32_t(rk), uint32_t(rk >> 32), a.offset};
+      philox4x32_10(w, k0, k1);
+      const uint32_t word = (i & 3) == 0 ? w[0] : (i & 3) == 1 ? w[1] : (i & 3) == 2 ? w[2] : w[3];
+      const double u = (double(word) + 0.5) * 0x1p-32;
+      const double s = double(list_z[par][c]) / T64 - log(-log(u));
+      if (better(s, i, best, best_i)) {
         best = s;
-        best_i = 4 * g + e;
+        best_i = i;
       }
+    }
+    last[par] = end;
+    par ^= 1;
+  };
+  auto unpack = [&](const uint4& q, float (&z)[kEV]) __attribute__((always_inline)) {
+    const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
+    if (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[2 * e] = __uint_as_float(wv[e] << 16);
+        z[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = __uint_as_float(wv[e]);
+    }
+  };
+
+  if (kVec) {
+    const uint4* v4 = reinterpret_cast<const uint4*>(zrow);
+    const int64_t nvec = (V + kEV - 1) / kEV;   // the last vector may run past V (row padding)
+    const int64_t full = V / kEV;
+    // kAhead vectors per thread in flight: round r consumes slot r % kAhead
+    // and refills it with round r + kAhead's vector
+    uint4 q[kAhead];
+#pragma unroll
+    for (int s = 0; s < kAhead; ++s) {
+      const int64_t j = int64_t(s) * kSmT + tid;
+      q[s] = j < full ? v4[j] : make_uint4(0, 0, 0, 0);
+    }
+    for (int64_t r0 = 0; r0 < nvec; r0 += int64_t(kSmT) * kAhead) {
+#pragma unroll
+      for (int s = 0; s < kAhead; ++s) {
+        const int64_t rs = r0 + int64_t(s) * kSmT;
+        if (rs >= nvec) break;   // uniform
+        const int64_t j = rs + tid;
+        float z[kEV];
+        unpack(q[s], z);
+        const int64_t jn = j + int64_t(kSmT) * kAhead;
+        q[s] = jn < full ? v4[jn] : make_uint4(0, 0, 0, 0);
+        if (j >= full) {   // the partial last vector, element by element
+#pragma unroll
+          for (int e = 0; e < kEV; ++e) {
+            const int64_t i = j * kEV + e;
+            z[e] = (j < nvec && i < V) ? val<T>(zrow, i) : -INFINITY;
+          }
+        }
+        offer(j * kEV, z);
+        score_listed();
+      }
+    }
+  } else {
+    for (int64_t r0 = 0; r0 < V; r0 += int64_t(kSmT) * kEV) {
+      float z[kEV];
+#pragma unroll
+      for (int e = 0; e < kEV; ++e) {
+        const int64_t i = r0 + int64_t(tid) * kEV + e;
+        z[e] = i < V ? val<T>(zrow, i) : -INFINITY;
+      }
+      offer(r0 + int64_t(tid) * kEV, z);
+      score_listed();
     }
   }
   // block argmax: a fixed butterfly in each wave, then the waves in order
@@ -135,10 +231,19 @@ __global__ void fill_i64(int64_t* p, int64_t n, int64_t v) {
 hipError_t launch_sample_rows(const SampleArgs& a, int dtype, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
   const dim3 grid(unsigned(a.n_rows));
-  if (dtype == 0)
-    hipLaunchKernelGGL(sample_rows<float>, grid, dim3(kSmT), 0, stream, a);
-  else
-    hipLaunchKernelGGL(sample_rows<uint16_t>, grid, dim3(kSmT), 0, stream, a);
+  const size_t esz = dtype == 0 ? 4 : 2;
+  const bool vec = reinterpret_cast<uintptr_t>(a.logits) % 16 == 0 && (a.row_stride * esz) % 16 == 0;
+  if (dtype == 0) {
+    if (vec)
+      hipLaunchKernelGGL((sample_rows<float, true>), grid, dim3(kSmT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((sample_rows<float, false>), grid, dim3(kSmT), 0, stream, a);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((sample_rows<uint16_t, true>), grid, dim3(kSmT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((sample_rows<uint16_t, false>), grid, dim3(kSmT), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
