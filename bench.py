@@ -180,7 +180,7 @@ def leg_support(torch, rlk, synth, steps, warmup):
         "with_nucleus_check_tokens_per_s": w.N / (mean_c * 1e-3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
-                     "traffic": None},
+                     "traffic": _profile_traffic("support_rows_qwen3_logits_4096x151936")},
     }
 
 
