@@ -312,7 +312,7 @@ constexpr int kStreamers = kStreamWaves * kWave; // streaming threads
 constexpr int kHWords = 16384;                   // 64 KB of 16-bit counter pairs per buffer
 constexpr int kMagLo = 0x2000, kMagHi = 0x6000;  // counted magnitudes: |z| in [2^-63, 2^64)
 constexpr int kKeyLo = 0x7fff - (kMagHi - 1);    // lowest merged key of a counted value
-constexpr int kUnroll = 6;                       // 16-byte vectors in flight per streamer
+constexpr int kUnroll = 4;                       // 16-byte vectors in flight per streamer
 
 // Counter index of a counted magnitude (a rotation of the window onto 0..16383).
 RLK_DEV int widx(int mag) { return mag & 0x3fff; }
