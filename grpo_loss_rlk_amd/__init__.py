@@ -231,11 +231,17 @@ def grpo_token_loss(lp_new: torch.Tensor, lp_old: torch.Tensor, lp_ref, cu_seqle
                     *, rewards=None, advantages=None, group_size: int = 8,
                     tis_cap: float = 2.0, eps_low: float = 0.2, eps_high: float = 0.28,
                     kl_coef: float = 0.01, adv_eps: float = 1e-6, std_ddof: int = 1,
-                    normalize_std: bool = True) -> dict:
-    """GRPO/DAPO token-mean loss over packed responses (``cu_seqlens`` on the host).
+                    normalize_std: bool = True, loss_type: str = "dapo",
+                    correction: str = "tis", aggregation: str = "token_mean",
+                    filter_zero_adv: bool = False, baseline: str = "mean",
+                    ipo_eps: float = 0.3, icepop_lo: float = 0.5,
+                    icepop_hi: float = 2.0) -> dict:
+    """GRPO/DAPO token loss over packed responses (``cu_seqlens`` on the host).
 
+    loss_type: dapo | ipo | icepop | cispo; correction: tis | mis;
+    aggregation: token_mean | prompt_mean; baseline: mean | length.
     Returns loss (device scalar), grad (dL/dlp_new), token_loss, token_flags,
-    metrics [clip frac, TIS frac, mean k3, mean ratio], advantages.
+    metrics [clipped/masked frac, TIS frac, mean k3, mean ratio], advantages.
     """
     cu = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if torch.is_tensor(cu_seqlens)
                                          else cu_seqlens, dtype=np.int64))
@@ -253,7 +259,10 @@ def grpo_token_loss(lp_new: torch.Tensor, lp_old: torch.Tensor, lp_ref, cu_seqle
            "token_flags": torch.empty(T, device=dev, dtype=torch.uint8),
            "metrics": torch.empty(4, **f), "advantages": torch.empty(B, **f)}
     prm = _native.GrpoParams(ctypes.sizeof(_native.GrpoParams), tis_cap, eps_low, eps_high,
-                             kl_coef, adv_eps, std_ddof, int(bool(normalize_std)))
+                             kl_coef, adv_eps, std_ddof, int(bool(normalize_std)),
+                             _native.LOSS_TYPES[loss_type], _native.CORRECTIONS[correction],
+                             _native.AGGREGATIONS[aggregation], int(bool(filter_zero_adv)),
+                             _native.BASELINES[baseline], ipo_eps, icepop_lo, icepop_hi)
     L = lib()
     ws_n = L.rlk_grpo_token_loss_workspace_size(T, B)
     ws = _workspace(ws_n, dev)

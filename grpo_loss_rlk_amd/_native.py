@@ -23,7 +23,16 @@ FLAG_BAD_SUPPORT, FLAG_MISMATCH = 32, 64
 class GrpoParams(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("tis_cap", c_f32), ("eps_low", c_f32),
                 ("eps_high", c_f32), ("kl_coef", c_f32), ("adv_eps", c_f32),
-                ("std_ddof", c_i32), ("normalize_std", c_i32)]
+                ("std_ddof", c_i32), ("normalize_std", c_i32), ("loss_type", c_i32),
+                ("correction", c_i32), ("aggregation", c_i32), ("filter_zero_adv", c_i32),
+                ("baseline", c_i32), ("ipo_eps", c_f32), ("icepop_lo", c_f32),
+                ("icepop_hi", c_f32)]
+
+
+LOSS_TYPES = {"dapo": 0, "ipo": 1, "icepop": 2, "cispo": 3}
+CORRECTIONS = {"tis": 0, "mis": 1}
+AGGREGATIONS = {"token_mean": 0, "prompt_mean": 1}
+BASELINES = {"mean": 0, "length": 1}
 
 
 # name -> (restype, argtypes); every symbol include/rlk.h declares

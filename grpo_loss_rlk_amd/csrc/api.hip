@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstddef>
 #include <cstdio>
 #include <cstring>
 
@@ -466,10 +467,34 @@ rlk_status rlk_grpo_token_loss(const float* lp_new, const float* lp_old, const f
                                float* adv_out, void* workspace, size_t workspace_bytes,
                                void* stream) {
   if (!params) return fail(RLK_EINVAL, "params is NULL");
-  if (params->struct_size < sizeof(rlk_grpo_params))
-    return fail(RLK_EINVAL, "params->struct_size=%u < %zu", params->struct_size,
-                sizeof(rlk_grpo_params));
-  const rlk_grpo_params& p = *params;
+  // the first layout ends after normalize_std; later fields take their defaults
+  constexpr uint32_t kFirstLayout = offsetof(rlk_grpo_params, loss_type);
+  if (params->struct_size < kFirstLayout)
+    return fail(RLK_EINVAL, "params->struct_size=%u < %u", params->struct_size, kFirstLayout);
+  rlk_grpo_params p{};
+  p.loss_type = RLK_LOSS_DAPO;
+  p.correction = RLK_CORRECTION_TIS;
+  p.aggregation = RLK_AGG_TOKEN_MEAN;
+  p.filter_zero_adv = 0;
+  p.baseline = RLK_BASELINE_MEAN;
+  p.ipo_eps = 0.3f;
+  p.icepop_lo = 0.5f;
+  p.icepop_hi = 2.0f;
+  std::memcpy(&p, params, params->struct_size < sizeof(p) ? params->struct_size : sizeof(p));
+  if (p.loss_type < RLK_LOSS_DAPO || p.loss_type > RLK_LOSS_CISPO)
+    return fail(RLK_EINVAL, "loss_type=%d is not an RLK_LOSS_* value", p.loss_type);
+  if (p.correction != RLK_CORRECTION_TIS && p.correction != RLK_CORRECTION_MIS)
+    return fail(RLK_EINVAL, "correction=%d is not an RLK_CORRECTION_* value", p.correction);
+  if (p.aggregation != RLK_AGG_TOKEN_MEAN && p.aggregation != RLK_AGG_PROMPT_MEAN)
+    return fail(RLK_EINVAL, "aggregation=%d is not an RLK_AGG_* value", p.aggregation);
+  if (p.filter_zero_adv != 0 && p.filter_zero_adv != 1)
+    return fail(RLK_EINVAL, "filter_zero_adv must be 0 or 1");
+  if (p.baseline != RLK_BASELINE_MEAN && p.baseline != RLK_BASELINE_LENGTH)
+    return fail(RLK_EINVAL, "baseline=%d is not an RLK_BASELINE_* value", p.baseline);
+  if (!(p.ipo_eps > 0.f) || !std::isfinite(p.ipo_eps))
+    return fail(RLK_EINVAL, "ipo_eps must be finite and > 0");
+  if (!(p.icepop_lo > 0.f) || !(p.icepop_hi >= p.icepop_lo) || !std::isfinite(p.icepop_hi))
+    return fail(RLK_EINVAL, "the IcePop band must satisfy 0 < icepop_lo <= icepop_hi < inf");
   if (!(p.tis_cap > 0.f) || !std::isfinite(p.tis_cap))
     return fail(RLK_EINVAL, "tis_cap must be finite and > 0");
   if (!(p.eps_low >= 0.f && p.eps_low < 1.f)) return fail(RLK_EINVAL, "eps_low must lie in [0, 1)");
@@ -490,10 +515,12 @@ rlk_status rlk_grpo_token_loss(const float* lp_new, const float* lp_old, const f
   if (n_tokens > (int64_t(1) << 40)) return fail(RLK_EINVAL, "too many tokens");
   if ((rewards == nullptr) == (advantages == nullptr))
     return fail(RLK_EINVAL, "exactly one of rewards / advantages must be given");
-  if (rewards) {
+  if (rewards || p.aggregation == RLK_AGG_PROMPT_MEAN) {
     if (group_size < 1 || n_seqs % group_size != 0)
       return fail(RLK_EINVAL, "group_size=%d must be >= 1 and divide n_seqs=%lld", group_size,
                   (long long)n_seqs);
+  }
+  if (rewards) {
     if (p.normalize_std && group_size - p.std_ddof < 1)
       return fail(RLK_EINVAL, "group_size=%d too small for a std with ddof=%d", group_size,
                   p.std_ddof);
@@ -527,6 +554,14 @@ rlk_status rlk_grpo_token_loss(const float* lp_new, const float* lp_old, const f
   a.adv_eps = p.adv_eps;
   a.std_ddof = p.std_ddof;
   a.normalize_std = p.normalize_std;
+  a.loss_type = p.loss_type;
+  a.correction = p.correction;
+  a.aggregation = p.aggregation;
+  a.filter_zero_adv = p.filter_zero_adv;
+  a.baseline = p.baseline;
+  a.ipo_eps = p.ipo_eps;
+  a.icepop_lo = p.icepop_lo;
+  a.icepop_hi = p.icepop_hi;
   a.loss = loss;
   a.grad = grad_lp_new;
   a.token_loss = token_loss;

@@ -46,6 +46,8 @@ struct GrpoArgs {
   int32_t group_size;
   float tis_cap, eps_low, eps_high, kl_coef, adv_eps;
   int32_t std_ddof, normalize_std;
+  int32_t loss_type, correction, aggregation, filter_zero_adv, baseline;
+  float ipo_eps, icepop_lo, icepop_hi;
   float* loss;
   float* grad;
   float* token_loss;          // nullable

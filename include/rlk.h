@@ -286,6 +286,8 @@ rlk_status rlk_logprob_fused_linear_bwd(
  *               T_tot = cu_seqlens[n_seqs]. Copied into the workspace.
  * rewards / advantages    [n_seqs] fp32: exactly one must be non-NULL.
  * group_size    responses per prompt; must divide n_seqs (rewards mode).
+ * (The variants of rlk_grpo_params below change s, rho~, the baseline and the
+ * token weights; the defaults are the formulas above.)
  * loss          device fp32 scalar (required).  grad_lp_new [T_tot] fp32 (required).
  * token_loss    [T_tot] fp32 (nullable).  token_flags [T_tot] uint8 (nullable):
  *               bit0 TIS cap binds (rho > C), bit1 clipped branch taken.
@@ -293,8 +295,44 @@ rlk_status rlk_logprob_fused_linear_bwd(
  * adv_out       [n_seqs] fp32 (nullable): the advantages used.
  * T_tot == 0 gives loss 0.
  * -------------------------------------------------------------------------- */
+/* Loss variants (prime-rl v0.10.0 release notes, "2. RL Algorithms": IPO
+ * masks a token when |pi_train - pi_infer| > eps (eps 0.3, no KL term);
+ * IcePop masks it when pi_train / pi_infer leaves a fixed band; CISPO stays an
+ * opt-in loss; GRPO gains a length-weighted baseline and exact prompt-mean
+ * aggregation. "Breaking changes": zero-advantage samples are filtered.
+ * LumenRL README, "Rollout Correction": MIS normalises the ratios.)
+ * pi_infer = exp(lp_old), pi_train = exp(lp_new); rho~ per `correction`:
+ *   TIS: rho~ = min(rho, tis_cap);  MIS: rho~ = rho / mean(rho) over the
+ *   tokens entering the loss (the mean held constant).
+ *   DAPO:   s = min(rho~ A, clip(rho~, 1 - eps_low, 1 + eps_high) A)   (above)
+ *   IPO:    s = [|exp(lp_new) - exp(lp_old)| <= ipo_eps] rho~ A
+ *   ICEPOP: s = [icepop_lo <= rho <= icepop_hi] rho~ A
+ *   CISPO:  s = w A lp_new, w = clip(rho~, 1 - eps_low, 1 + eps_high) held
+ *           constant (gradient -w A)
+ * Token flag bit1 marks the clipped branch (DAPO), a masked token (IPO,
+ * ICEPOP) or a binding clip on w (CISPO); metrics[0] is its token mean.
+ * baseline LENGTH (rewards mode): the group baseline is sum_j L_j r_j /
+ * sum_j L_j with L_j the response's token count. filter_zero_adv: a response
+ * with A_j == 0 is left out of the loss and of the counts. aggregation
+ * PROMPT_MEAN: a kept token of group g (group_size consecutive responses,
+ * in both modes) weighs 1 / (G_kept T_g), T_g the kept tokens of group g and
+ * G_kept the groups with T_g > 0; TOKEN_MEAN: 1 / T_kept. The loss is the
+ * weighted sum of l_t and dL/dlp_new carries the same weight. */
+#define RLK_LOSS_DAPO 0
+#define RLK_LOSS_IPO 1
+#define RLK_LOSS_ICEPOP 2
+#define RLK_LOSS_CISPO 3
+#define RLK_CORRECTION_TIS 0
+#define RLK_CORRECTION_MIS 1
+#define RLK_AGG_TOKEN_MEAN 0
+#define RLK_AGG_PROMPT_MEAN 1
+#define RLK_BASELINE_MEAN 0
+#define RLK_BASELINE_LENGTH 1
+
 typedef struct rlk_grpo_params {
-    uint32_t struct_size;   /* sizeof(rlk_grpo_params) */
+    uint32_t struct_size;   /* sizeof(rlk_grpo_params); the first layout (up to
+                               normalize_std, 32 bytes) is accepted and takes the
+                               defaults for the fields after it */
     float tis_cap;          /* C > 0, e.g. 2.0 */
     float eps_low;          /* in [0, 1), e.g. 0.2 */
     float eps_high;         /* >= 0, e.g. 0.28 */
@@ -302,6 +340,14 @@ typedef struct rlk_grpo_params {
     float adv_eps;          /* >= 0, e.g. 1e-6 */
     int32_t std_ddof;       /* 0 or 1 */
     int32_t normalize_std;  /* 1 = divide by the group std */
+    int32_t loss_type;      /* RLK_LOSS_* (default DAPO) */
+    int32_t correction;     /* RLK_CORRECTION_* (default TIS) */
+    int32_t aggregation;    /* RLK_AGG_* (default TOKEN_MEAN) */
+    int32_t filter_zero_adv;/* 0 or 1 (default 0) */
+    int32_t baseline;       /* RLK_BASELINE_* (default MEAN) */
+    float ipo_eps;          /* > 0 (default 0.3) */
+    float icepop_lo;        /* 0 < icepop_lo <= icepop_hi (defaults 0.5, 2.0) */
+    float icepop_hi;
 } rlk_grpo_params;
 
 size_t rlk_grpo_token_loss_workspace_size(int64_t n_tokens, int64_t n_seqs);

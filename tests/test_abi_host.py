@@ -89,7 +89,8 @@ def test_workspace_queries(L):
 
 
 def _grpo(L, cu=(0, 3, 5), **kw):
-    prm = _native.GrpoParams(ctypes.sizeof(_native.GrpoParams), 2.0, 0.2, 0.28, 0.01, 1e-6, 1, 1)
+    prm = _native.GrpoParams(ctypes.sizeof(_native.GrpoParams), 2.0, 0.2, 0.28, 0.01, 1e-6, 1, 1,
+                             0, 0, 0, 0, 0, 0.3, 0.5, 2.0)
     for k, v in kw.pop("prm", {}).items():
         setattr(prm, k, v)
     cu_arr = None if cu is None else (ctypes.c_int64 * len(cu))(*cu)
@@ -121,6 +122,19 @@ def _grpo(L, cu=(0, 3, 5), **kw):
     (dict(grad=None), _native.RLK_EINVAL),
     (dict(loss=None), _native.RLK_EINVAL),
     (dict(ws_bytes=8), _native.RLK_EWORKSPACE),
+    # the first params layout (32 bytes) is accepted: defaults for the rest
+    (dict(prm=dict(struct_size=32, ipo_eps=-1.0), ws_bytes=8), _native.RLK_EWORKSPACE),
+    (dict(prm=dict(struct_size=31)), _native.RLK_EINVAL),
+    (dict(prm=dict(loss_type=4)), _native.RLK_EINVAL),
+    (dict(prm=dict(loss_type=-1)), _native.RLK_EINVAL),
+    (dict(prm=dict(correction=2)), _native.RLK_EINVAL),
+    (dict(prm=dict(aggregation=2)), _native.RLK_EINVAL),
+    (dict(prm=dict(filter_zero_adv=2)), _native.RLK_EINVAL),
+    (dict(prm=dict(baseline=2)), _native.RLK_EINVAL),
+    (dict(prm=dict(ipo_eps=0.0)), _native.RLK_EINVAL),
+    (dict(prm=dict(icepop_lo=0.0)), _native.RLK_EINVAL),
+    (dict(prm=dict(icepop_lo=2.0, icepop_hi=1.0)), _native.RLK_EINVAL),
+    (dict(prm=dict(aggregation=1), rewards=None, adv=FAKE, G=3), _native.RLK_EINVAL),
 ])
 def test_grpo_validation(L, kw, status):
     assert _grpo(L, **kw) == status

@@ -91,3 +91,51 @@ def test_bitwise_deterministic():
     b = rlk.grpo_token_loss(*args, cu, rewards=r, group_size=8)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("loss_type,correction,aggregation,filt,baseline", [
+    ("ipo", "tis", "token_mean", False, "mean"),
+    ("icepop", "tis", "prompt_mean", True, "mean"),
+    ("cispo", "mis", "token_mean", True, "length"),
+    ("dapo", "mis", "prompt_mean", False, "length"),
+    ("dapo", "tis", "prompt_mean", True, "length"),
+])
+def test_loss_variants(loss_type, correction, aggregation, filt, baseline):
+    """The loss variants on the config-4 lengths with noisy ratios (every mask
+    and clip branch taken), Bernoulli rewards (zero-advantage groups occur)."""
+    w = synth.workload("grpo")
+    lengths = synth.response_lengths(w)
+    cu, lp_new, lp_old, lp_ref = _inputs(6, lengths, sd_old=0.6, sd_ref=0.5)
+    r = synth.rewards(w)
+    r[8:16] = 1.0                                  # one group with equal rewards: A = 0
+    kw = dict(loss_type=loss_type, correction=correction, aggregation=aggregation,
+              filter_zero_adv=filt, baseline=baseline, ipo_eps=0.1, icepop_lo=0.6,
+              icepop_hi=1.5)
+    prm = OG.Params(**kw)
+    A = OG.advantages(r, 8, prm, lengths=lengths)
+    assert np.any(A == 0.0)
+    o = OG.token_loss(lp_new, lp_old, lp_ref, cu, A, prm, group_size=8)
+    assert (o.flags & OG.FLAG_CLIP).any()
+    print(f"  rlk_grpo_token_loss T_tot={cu[-1]} {kw}", flush=True)
+    out = rlk.grpo_token_loss(f32_to_device(lp_new), f32_to_device(lp_old), f32_to_device(lp_ref),
+                              cu, rewards=r, group_size=8, **kw)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(out["advantages"]), A, rtol=1e-6, atol=1e-7)
+    _compare(out, o, o.near_branch)
+    if filt:                                       # filtered responses get no gradient
+        Atok = np.repeat(A, np.diff(cu))
+        assert not host(out["grad"])[Atok == 0.0].any()
+
+
+def test_variants_with_advantages_given():
+    """Advantages mode with prompt-mean aggregation (groups of 4) and IPO."""
+    lengths = np.array([3, 0, 5, 2, 7, 1, 4, 4])
+    cu, lp_new, lp_old, lp_ref = _inputs(7, lengths, sd_old=0.8)
+    A = np.array([0.5, -0.5, 0.0, 1.0, 0.0, 0.0, 0.0, 0.0], dtype=np.float32)
+    kw = dict(loss_type="ipo", aggregation="prompt_mean", filter_zero_adv=True, ipo_eps=0.05)
+    prm = OG.Params(**kw)
+    o = OG.token_loss(lp_new, lp_old, lp_ref, cu, A.astype(np.float64), prm, group_size=4)
+    out = rlk.grpo_token_loss(f32_to_device(lp_new), f32_to_device(lp_old), f32_to_device(lp_ref),
+                              cu, advantages=A, group_size=4, **kw)
+    torch.cuda.synchronize()
+    _compare(out, o, o.near_branch)
