@@ -238,7 +238,7 @@ def grpo_token_loss(lp_new: torch.Tensor, lp_old: torch.Tensor, lp_ref, cu_seqle
                     icepop_hi: float = 2.0) -> dict:
     """GRPO/DAPO token loss over packed responses (``cu_seqlens`` on the host).
 
-    loss_type: dapo | ipo | icepop | cispo; correction: tis | mis;
+    loss_type: dapo | ipo | icepop | cispo | tis_pg; correction: tis | mis;
     aggregation: token_mean | prompt_mean; baseline: mean | length.
     Returns loss (device scalar), grad (dL/dlp_new), token_loss, token_flags,
     metrics [clipped/masked frac, TIS frac, mean k3, mean ratio], advantages.

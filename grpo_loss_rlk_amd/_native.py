@@ -29,7 +29,7 @@ class GrpoParams(ctypes.Structure):
                 ("icepop_hi", c_f32)]
 
 
-LOSS_TYPES = {"dapo": 0, "ipo": 1, "icepop": 2, "cispo": 3}
+LOSS_TYPES = {"dapo": 0, "ipo": 1, "icepop": 2, "cispo": 3, "tis_pg": 4}
 CORRECTIONS = {"tis": 0, "mis": 1}
 AGGREGATIONS = {"token_mean": 0, "prompt_mean": 1}
 BASELINES = {"mean": 0, "length": 1}

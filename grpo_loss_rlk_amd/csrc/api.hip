@@ -481,7 +481,7 @@ rlk_status rlk_grpo_token_loss(const float* lp_new, const float* lp_old, const f
   p.icepop_lo = 0.5f;
   p.icepop_hi = 2.0f;
   std::memcpy(&p, params, params->struct_size < sizeof(p) ? params->struct_size : sizeof(p));
-  if (p.loss_type < RLK_LOSS_DAPO || p.loss_type > RLK_LOSS_CISPO)
+  if (p.loss_type < RLK_LOSS_DAPO || p.loss_type > RLK_LOSS_TIS_PG)
     return fail(RLK_EINVAL, "loss_type=%d is not an RLK_LOSS_* value", p.loss_type);
   if (p.correction != RLK_CORRECTION_TIS && p.correction != RLK_CORRECTION_MIS)
     return fail(RLK_EINVAL, "correction=%d is not an RLK_CORRECTION_* value", p.correction);

@@ -200,6 +200,10 @@ __global__ __launch_bounds__(kTB) void grpo_tokens(GrpoArgs a, Ws w) {
       s = s1 < s2 ? s1 : s2;
       flag2 = (A > 0.0 && rt > hi_b) || (A < 0.0 && rt < lo_b);
       g_ratio = (ratio_live && !flag2) ? -A * rt : 0.0;
+    } else if (a.loss_type == 4) {   // detached TIS weight on an on-policy surrogate
+      s = rt * A;
+      flag2 = false;
+      g_ratio = -A * rt;
     } else if (a.loss_type == 3) {   // CISPO: constant clipped weight on lp_new
       const double wc = rt < lo_b ? lo_b : (rt > hi_b ? hi_b : rt);
       s = wc * A * lpn;

@@ -309,6 +309,9 @@ rlk_status rlk_logprob_fused_linear_bwd(
  *   ICEPOP: s = [icepop_lo <= rho <= icepop_hi] rho~ A
  *   CISPO:  s = w A lp_new, w = clip(rho~, 1 - eps_low, 1 + eps_high) held
  *           constant (gradient -w A)
+ *   TIS_PG: the detached-TIS form: rho~ a constant weight on an on-policy
+ *           surrogate (its ratio is 1 at the evaluation point): s = rho~ A,
+ *           gradient -rho~ A, no clip
  * Token flag bit1 marks the clipped branch (DAPO), a masked token (IPO,
  * ICEPOP) or a binding clip on w (CISPO); metrics[0] is its token mean.
  * baseline LENGTH (rewards mode): the group baseline is sum_j L_j r_j /
@@ -322,6 +325,7 @@ rlk_status rlk_logprob_fused_linear_bwd(
 #define RLK_LOSS_IPO 1
 #define RLK_LOSS_ICEPOP 2
 #define RLK_LOSS_CISPO 3
+#define RLK_LOSS_TIS_PG 4
 #define RLK_CORRECTION_TIS 0
 #define RLK_CORRECTION_MIS 1
 #define RLK_AGG_TOKEN_MEAN 0

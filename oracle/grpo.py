@@ -48,6 +48,10 @@ GRPO gains a length-weighted baseline and exact prompt-mean aggregation;
   icepop       m = [band_lo <= rho <= band_hi];              s = m rho~ A
   cispo        w = clip(rho~, 1 - eps_low, 1 + eps_high) held constant;
                s = w A lp_new (its gradient is w A)
+  tis_pg       the detached-TIS form: rho~ a constant weight on an on-policy
+               surrogate whose proximal policy is lp_new itself, so the
+               surrogate's ratio is 1 at the evaluation point: s = rho~ A,
+               gradient rho~ A (no clip can bind)
   baseline     mean: mean_g r;  length: sum_j L_j r_j / sum_j L_j (L_j tokens)
   filter       a response with A_j == 0 is left out of the loss and its count
   aggregation  token_mean: every kept token weighs 1 / T_kept;
@@ -79,7 +83,7 @@ class Params:
     adv_eps: float = 1e-6
     std_ddof: int = 1
     normalize_std: bool = True
-    loss_type: str = "dapo"        # dapo | ipo | icepop | cispo
+    loss_type: str = "dapo"        # dapo | ipo | icepop | cispo | tis_pg
     correction: str = "tis"        # tis | mis
     aggregation: str = "token_mean"   # token_mean | prompt_mean
     filter_zero_adv: bool = False
@@ -176,6 +180,10 @@ def token_loss(lp_new, lp_old, lp_ref, cu_seqlens, adv, prm: Params = Params(),
         s = m * rt * A
         flag2 = ~m
         g_ratio = -A * rt * (m & ratio_live)
+    elif prm.loss_type == "tis_pg":
+        s = rt * A
+        flag2 = np.zeros(T_tot, bool)
+        g_ratio = -A * rt
     elif prm.loss_type == "cispo":
         w = np.clip(rt, lo, hi)
         s = w * A * lp_new

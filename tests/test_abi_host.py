@@ -125,7 +125,7 @@ def _grpo(L, cu=(0, 3, 5), **kw):
     # the first params layout (32 bytes) is accepted: defaults for the rest
     (dict(prm=dict(struct_size=32, ipo_eps=-1.0), ws_bytes=8), _native.RLK_EWORKSPACE),
     (dict(prm=dict(struct_size=31)), _native.RLK_EINVAL),
-    (dict(prm=dict(loss_type=4)), _native.RLK_EINVAL),
+    (dict(prm=dict(loss_type=5)), _native.RLK_EINVAL),
     (dict(prm=dict(loss_type=-1)), _native.RLK_EINVAL),
     (dict(prm=dict(correction=2)), _native.RLK_EINVAL),
     (dict(prm=dict(aggregation=2)), _native.RLK_EINVAL),

@@ -99,6 +99,8 @@ def test_bitwise_deterministic():
     ("cispo", "mis", "token_mean", True, "length"),
     ("dapo", "mis", "prompt_mean", False, "length"),
     ("dapo", "tis", "prompt_mean", True, "length"),
+    ("tis_pg", "tis", "token_mean", False, "mean"),
+    ("tis_pg", "mis", "prompt_mean", True, "mean"),
 ])
 def test_loss_variants(loss_type, correction, aggregation, filt, baseline):
     """The loss variants on the config-4 lengths with noisy ratios (every mask
@@ -115,7 +117,7 @@ def test_loss_variants(loss_type, correction, aggregation, filt, baseline):
     A = OG.advantages(r, 8, prm, lengths=lengths)
     assert np.any(A == 0.0)
     o = OG.token_loss(lp_new, lp_old, lp_ref, cu, A, prm, group_size=8)
-    assert (o.flags & OG.FLAG_CLIP).any()
+    assert (o.flags & OG.FLAG_CLIP).any() or loss_type == "tis_pg"
     print(f"  rlk_grpo_token_loss T_tot={cu[-1]} {kw}", flush=True)
     out = rlk.grpo_token_loss(f32_to_device(lp_new), f32_to_device(lp_old), f32_to_device(lp_ref),
                               cu, rewards=r, group_size=8, **kw)

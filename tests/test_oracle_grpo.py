@@ -200,3 +200,13 @@ def test_variant_gradients_by_finite_differences(loss_type, agg, filt):
         num = (G.token_loss(up, lpo, lpr, cu, A, prm, 2).loss -
                G.token_loss(dn, lpo, lpr, cu, A, prm, 2).loss) / (2 * eps)
         assert r.grad[t] == pytest.approx(num, rel=1e-5, abs=1e-9), t
+
+
+def test_detached_tis_form_closed_form():
+    # the weight min(rho, C) is a constant and the surrogate's own ratio is 1:
+    # loss -w A and gradient -w A, whether or not the cap binds
+    for rho, w in ((0.7, 0.7), (1.9, 1.9), (3.0, 2.0)):
+        r = _one(np.log(rho) - 1.0, -1.0, -1.5, loss_type="tis_pg", tis_cap=2.0)
+        assert r.loss == pytest.approx(w * 1.5, rel=1e-12)
+        assert r.grad[0] == pytest.approx(w * 1.5, rel=1e-12)
+        assert r.flags[0] == (G.FLAG_TIS if rho > 2.0 else 0)
