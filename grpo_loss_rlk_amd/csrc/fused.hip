@@ -45,6 +45,7 @@ struct Part {
 };
 
 RLK_DEV Part merge_part(Part p, Part q, float c2) {
+  if (p.m != p.m || q.m != q.m) return Part{p.m + q.m, 0.f, 0.f};   // a non-finite logit: NaN
   if (q.m == -INFINITY) return p;   // an empty partial (no valid vocabulary rows)
   if (p.m == -INFINITY) return q;
   const float m = fmaxf(p.m, q.m);
@@ -59,15 +60,21 @@ RLK_DEV Part merge_part(Part p, Part q, float c2) {
 
 // This lane's 64 logits of token column j folded into (max, sum 2^x, sum 2^x x).
 // kFull: every vocabulary row of the tile exists; else rows from `rem` on
-// (relative to this lane's first row) are past the vocabulary.
+// (relative to this lane's first row) are past the vocabulary. A NaN or
+// infinite logit makes the partial's max NaN, which every merge propagates.
 template <bool kFull>
 RLK_DEV Part fold_lane(const f32x16 (&acc)[4][4], int j, int rem, float c2) {
   float mx = -INFINITY;
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (kFull || 32 * i + 8 * (r >> 2) + (r & 3) < rem) mx = fmaxf(mx, acc[i][j][r]);
+      if (kFull || 32 * i + 8 * (r >> 2) + (r & 3) < rem) {
+        mx = fmaxf(mx, acc[i][j][r]);
+        bad |= !(fabsf(acc[i][j][r]) <= 3.402823466e38f);
+      }
+  if (bad) return Part{__builtin_nanf(""), 0.f, 0.f};
   float A = 0.f, B = 0.f;
   if (mx > -INFINITY) {
 #pragma unroll
@@ -243,15 +250,22 @@ __global__ __launch_bounds__(kMergeTok * kMergeSlices) void fwd_merge(FusedFwdAr
 
   float mx = -INFINITY;
   if (live)
-    for (int vt = sl; vt < nvt; vt += kMergeSlices) mx = fmaxf(mx, a.part[int64_t(vt) * a.N + n].x);
+    for (int vt = sl; vt < nvt; vt += kMergeSlices) {
+      const float px = a.part[int64_t(vt) * a.N + n].x;
+      mx = (px != px || mx != mx) ? __builtin_nanf("") : fmaxf(mx, px);   // NaN: non-finite logit
+    }
   sh[0][sl][tok] = double(mx);
   __syncthreads();
   double m = -INFINITY;
-  for (int k = 0; k < kMergeSlices; ++k) m = sh[0][k][tok] > m ? sh[0][k][tok] : m;
+  bool bad = false;   // a tile saw a NaN or infinite logit
+  for (int k = 0; k < kMergeSlices; ++k) {
+    m = sh[0][k][tok] > m ? sh[0][k][tok] : m;
+    bad |= sh[0][k][tok] != sh[0][k][tok];
+  }
   __syncthreads();
 
   double A = 0.0, B = 0.0;   // B in log2 units
-  if (live && m > -INFINITY)
+  if (live && !bad && m > -INFINITY)
     for (int vt = sl; vt < nvt; vt += kMergeSlices) {
       const float4 p = a.part[int64_t(vt) * a.N + n];
       if (!(p.x > -INFINITY)) continue;   // a tile with no valid vocabulary row
@@ -283,13 +297,15 @@ __global__ __launch_bounds__(kMergeTok * kMergeSlices) void fwd_merge(FusedFwdAr
   } else {
     lp = float((double(a.zy[n]) - m) * invT - lnA);
   }
-  a.logprob[n] = lp;
-  a.entropy[n] = float(H);
+  const float nan = __builtin_nanf("");
+  if (bad || !(m > -INFINITY)) flags |= 4;   // a NaN / infinite logit, or no finite one
+  a.logprob[n] = (flags & 4) ? nan : lp;
+  a.entropy[n] = (flags & 4) ? nan : float(H);
   if (a.saved) {
-    a.saved[4 * n + 0] = float(m * invT + lnA);   // log Z of the scaled logits z/T
-    a.saved[4 * n + 1] = float(m * invT + Ed);    // E_q[z/T]
+    a.saved[4 * n + 0] = (flags & 4) ? nan : float(m * invT + lnA);   // log Z of z/T
+    a.saved[4 * n + 1] = (flags & 4) ? nan : float(m * invT + Ed);    // E_q[z/T]
     a.saved[4 * n + 2] = -INFINITY;              // no cut at top-p = 1
-    a.saved[4 * n + 3] = (flags & 2) ? 0.f : 1.f;  // the lp term is live (target in range)
+    a.saved[4 * n + 3] = (flags & 6) ? 0.f : 1.f;  // the lp term is live (target in range)
   }
   if (a.nsize) a.nsize[n] = int32_t(a.V);
   if (a.flags) a.flags[n] = flags;

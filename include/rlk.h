@@ -213,7 +213,9 @@ rlk_status rlk_sample_top_p(
  *               -inf at top_p = 1; 1 when the row's logprob term is live -- target
  *               in range and kept -- else 0), consumed by
  *               rlk_logprob_fused_linear_bwd.
- * nucleus_size  [n_rows] int32 (nullable).  flags [n_rows] uint8 (nullable).
+ * nucleus_size  [n_rows] int32 (nullable).  flags [n_rows] uint8 (nullable):
+ *               RLK_FLAG_NONFINITE with NaN outputs for a row with a NaN or
+ *               infinite logit (e.g. from a non-finite hidden or weight value).
  * Limits: hidden_size % 64 == 0, 1 <= vocab <= 2^24, 0 <= n_rows < 2^23,
  * strides >= hidden_size, multiples of 8 and < 2^23, hidden/weight 16-byte
  * aligned.

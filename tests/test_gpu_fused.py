@@ -121,3 +121,38 @@ def test_qwen_head_full_size_sampled_rows():
     assert_close_rows(host(out["entropy"])[rows], o.h_trunc, H_ATOL, H_RTOL, what="entropy")
     assert np.all(np.isfinite(host(out["logprob"])))
 
+
+
+@pytest.mark.parametrize("p", [1.0, 0.9])
+def test_nonfinite_hidden_rows_are_flagged(p):
+    """A NaN or an infinity in a hidden row makes that token's logits
+    non-finite: its outputs are NaN with the non-finite flag, at top-p 1 and
+    below; every other row is bitwise the clean run's. Also a whole W tile of
+    NaN (256 vocabulary rows) flags every row."""
+    w, hb, wb, y = _inputs("fused", 300, 256, 1000)
+    h = bf16_to_device(hb)
+    W = bf16_to_device(wb)
+    yt = torch.as_tensor(y)
+    clean = rlk.logprob_fused_linear(h, W, yt, 0.7, p)
+    hbad = hb.copy()
+    hbad[5, 17] = 0x7fc0          # NaN
+    hbad[9, 3] = 0x7f80           # +inf
+    hbad[11, 200] = 0xff80        # -inf
+    out = rlk.logprob_fused_linear(bf16_to_device(hbad), W, yt, 0.7, p)
+    torch.cuda.synchronize()
+    fl = host(out["flags"])
+    bad = np.zeros(w.N, bool)
+    bad[[5, 9, 11]] = True
+    assert np.all(fl[bad] & rlk.FLAG_NONFINITE), fl[bad]
+    assert np.all(np.isnan(host(out["logprob"])[bad]))
+    assert np.all(np.isnan(host(out["entropy"])[bad]))
+    assert not np.any(fl[~bad] & rlk.FLAG_NONFINITE)
+    good = torch.from_numpy(np.flatnonzero(~bad)).to(DEV)
+    for k in ("logprob", "entropy"):
+        assert bits_equal(clean[k][good], out[k][good]), k
+    wbad = wb.copy()
+    wbad[256:512, :] = 0x7fc0     # the second vocabulary tile entirely NaN
+    out = rlk.logprob_fused_linear(h, bf16_to_device(wbad), yt, 0.7, p)
+    torch.cuda.synchronize()
+    assert np.all(host(out["flags"]) & rlk.FLAG_NONFINITE)
+    assert np.all(np.isnan(host(out["logprob"])))
