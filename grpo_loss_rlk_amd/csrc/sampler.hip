@@ -57,14 +57,14 @@ RLK_DEV bool better(double s, int64_t i, double s2, int64_t i2) {
 }
 
 constexpr int kRound = kSmT * 8;   // ids of one round at most (one 16-byte vector per thread)
-constexpr int kAhead = 4;          // 16-byte vectors in flight per thread
+constexpr int kAhead = 8;          // 16-byte vectors in flight per thread
 
 // One row per block, in rounds of one 16-byte vector per thread. A round
-// lists (id, logit) of its nucleus members (logit >= tau) in LDS, one atomic
+// lists the ids of its nucleus members (logit >= tau) in LDS, one atomic
 // per wave (a wave prefix sum places each thread's entries); then every
 // thread scores list entries densely (so the Philox and fp64 work is not
-// spread thin over diverged lanes) while the next kAhead vectors are in
-// flight.
+// spread thin over diverged lanes; the logit is read again, from cache)
+// while the next kAhead vectors are in flight.
 // Rounds alternate between two lists with their own running counters, so one
 // barrier per round separates a round's appends from its scoring and the
 // scoring from the list's reuse two rounds later. The draw is an argmax, so
@@ -74,7 +74,6 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
   __shared__ double ss[kSmT / kWave];
   __shared__ int64_t si[kSmT / kWave];
   __shared__ int32_t list_i[2][kRound];
-  __shared__ float list_z[2][kRound];
   __shared__ int cnt[2];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int64_t row = blockIdx.x;
@@ -114,7 +113,6 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
       const int e = __ffs(m) - 1;
       m &= m - 1;
       list_i[par][base] = int32_t(i0 + e);
-      list_z[par][base] = z[e];
       ++base;
     }
   };
@@ -127,7 +125,7 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
       philox4x32_10(w, k0, k1);
       const uint32_t word = (i & 3) == 0 ? w[0] : (i & 3) == 1 ? w[1] : (i & 3) == 2 ? w[2] : w[3];
       const double u = (double(word) + 0.5) * 0x1p-32;
-      const double s = double(list_z[par][c]) / T64 - log(-log(u));
+      const double s = double(val<T>(zrow, i)) / T64 - log(-log(u));
       if (better(s, i, best, best_i)) {
         best = s;
         best_i = i;
