@@ -171,12 +171,16 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats(FusedFwdArgs a) {
   tile_epilogue(a, acc, v0, n0, vt, reinterpret_cast<float*>(&smem[0][0][0]));
 }
 
-// Logits of a row block: A = h (tokens), B = W (vocabulary), so that the
-// lanes of an accumulator register hold consecutive vocabulary ids of one
-// token and each store writes 128 contiguous bytes of a scratch row.
-// Also per token: the max logit over the tile (as an order key, merged with
-// atomicMax, which is order-free) and whether a non-finite logit appeared,
-// so that the row kernel can skip its max pass.
+// Logits of a row block: A = h (tokens), B = W (vocabulary). Each wave
+// passes its 128 x 128 block through LDS one 32-id slab at a time (16 KB per
+// wave) and writes each token's 32 logits (128 contiguous bytes of a scratch
+// row) as eight 16-byte stores, 4x fewer store instructions than writing the
+// accumulators lane by lane. From the same staged values, per token: the max
+// logit over the tile (as an order key, merged with atomicMax, which is
+// order-free) and whether a non-finite logit appeared, so that the row kernel
+// can skip its max pass; the max is folded in registers over the 16 values a
+// lane stores per token and then over the 8 lanes of that token, one atomic
+// per token and wave.
 __global__ __launch_bounds__(kT) void fwd_logits_tile(FusedFwdArgs a, int64_t r0, int64_t rows,
                                                       float* z, int64_t zs, uint32_t* zmax_key,
                                                       uint32_t* zbad) {
@@ -187,44 +191,57 @@ __global__ __launch_bounds__(kT) void fwd_logits_tile(FusedFwdArgs a, int64_t r0
   const int64_t n0 = int64_t(nt) * kBN, v0 = int64_t(vt) * kBM;
   f32x16 acc[4][4];
   gemm::gemm_nt_tile(acc, smem, a.h + r0 * a.hs, n0, rows, a.hs, a.w, v0, a.V, a.ws, a.H);
+
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  // the GEMM's LDS is free: this wave's [128 tokens][32 ids] fp32 slab
+  float* stg = reinterpret_cast<float*>(&smem[0][0][0]) + wid * (128 * 32);
+  float tmax[16];      // token 8 q + lane / 8 of this wave's 128
+  uint32_t badq = 0;   // bit q: a non-finite logit of that token
+#pragma unroll
+  for (int q = 0; q < 16; ++q) tmax[q] = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t v = v0 + gemm::acc_b_row(j);
-    if (v >= a.V) continue;
+    // acc[i][j][r] is token 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, id 32 j + lane % 32
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t n = n0 + gemm::acc_a_row(i, r);
-        if (n < rows) z[n * zs + v] = acc[i][j][r];
-      }
-  }
-  // lanes l and l ^ k (k < 32) hold the same tokens and different vocabulary ids
-  const int lane = threadIdx.x & 63;
+      for (int r = 0; r < 16; ++r)
+        stg[(32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * 32 + (lane & 31)] =
+            acc[i][j][r];
+    __syncthreads();
+    // lane: ids col .. col + 3 of tokens 8 q + lane / 8
+    const int64_t col = v0 + 128 * wn + 32 * j + 4 * (lane & 7);
+    const int64_t nv = a.V - col;   // ids of the chunk inside the vocabulary, if < 4
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 16; ++q) {
+      const int tl = 8 * q + (lane >> 3);
+      const int64_t n = n0 + 128 * wm + tl;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stg + tl * 32 + 4 * (lane & 7));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float m = -INFINITY;
-      bool nonfinite = false;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t v = v0 + gemm::acc_b_row(j);
-        if (v < a.V) {
-          const float x = acc[i][j][r];
-          m = fmaxf(m, x);
-          nonfinite |= !(fabsf(x) <= 3.402823466e38f);
+      for (int e = 0; e < 4; ++e)
+        if (e < nv) {
+          tmax[q] = fmaxf(tmax[q], v[e]);
+          badq |= (fabsf(v[e]) <= 3.402823466e38f) ? 0u : (1u << q);
         }
-      }
-#pragma unroll
-      for (int k = 1; k < 32; k <<= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
-      const uint64_t nf = __ballot(nonfinite);
-      const int64_t n = n0 + gemm::acc_a_row(i, r);
-      if ((lane & 31) == 0 && n < rows) {
-        if (m > -INFINITY) atomicMax(&zmax_key[n], f32_key(m));
-        if ((nf >> (lane & 32)) & 0xffffffffull) atomicOr(&zbad[n], 1u);
-      }
+      // zs is a multiple of 4, so a chunk that starts inside the row ends inside it
+      if (n < rows && col < zs) *reinterpret_cast<f32x4*>(z + n * zs + col) = v;
     }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 1; k < 8; k <<= 1) badq |= __shfl_xor(badq, k, 64);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+#pragma unroll
+    for (int k = 1; k < 8; k <<= 1) tmax[q] = fmaxf(tmax[q], __shfl_xor(tmax[q], k, 64));
+    const int64_t n = n0 + 128 * wm + 8 * q + (lane >> 3);
+    if ((lane & 7) == 0 && n < rows) {
+      if (tmax[q] > -INFINITY) atomicMax(&zmax_key[n], f32_key(tmax[q]));
+      if ((badq >> q) & 1u) atomicOr(&zbad[n], 1u);
+    }
+  }
 }
 
 __global__ void clear_u32(uint32_t* p, int64_t n) {
