@@ -779,7 +779,7 @@ __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
 }
 
 // ===========================================================================
-// fp32 rows: three streaming passes with float4 loads (one 1024-thread block
+// fp32 rows: three streaming passes with float4 loads (one 512-thread block
 // per row). Pass 1: max and finite count. Pass 2: Z, sum e d and a histogram
 // of fixed-point masses over bins of equal width in d = (z - max)/T (64 bins
 // per nat; a bin index never increases with z, so every bin above the
@@ -789,7 +789,12 @@ __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
 // crossing bin holds more than kCand elements is redone by the generic
 // algorithm in the same block.
 // ===========================================================================
-constexpr int kF32T = 1024;           // threads per block
+// threads per block: 512, so that two blocks share a CU (66 KB of LDS and at
+// most 128 VGPRs each) and one row's barrier-bound phases (the bin walk, the
+// sort of the crossing bin, the block reductions) overlap the other row's
+// streaming passes; a 1024-thread block held its CU alone
+constexpr int kF32T = 512;
+constexpr int kF32WavesPerSimd = 4;   // two blocks of 8 waves per CU
 constexpr int kFBins = 4096;          // bins of d: [b / 64, (b + 1) / 64) nats below the max
 constexpr float kFBinPerNat = 64.f;
 constexpr int kCand = 8192;           // crossing-bin elements resolved in LDS
@@ -886,7 +891,7 @@ RLK_DEV void for_each_f32(const float* rowp, int64_t V, F&& f) {
 }
 
 template <bool kVec>
-__global__ __launch_bounds__(kF32T) void f32_rows(RowArgs a) {
+__global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
   __shared__ union {
     struct {
       uint64_t hist[kFBins];
