@@ -191,7 +191,26 @@ __global__ __launch_bounds__(kT) void bwd_g_tile(FusedBwdArgs a, ChunkArgs c) {
 
 enum DhMode { kDhOnly = 0, kDhFirst = 1, kDhMiddle = 2, kDhLast = 3 };
 
+// Four dh values (consecutive columns) to bf16, as one 8-byte store when the
+// output is 8-byte aligned, else one 2-byte store each.
+RLK_DEV void store_bf16x4(uint16_t* p, float x, float y, float z, float w, bool vec) {
+  const uint16_t b0 = to_bf16(x), b1 = to_bf16(y), b2 = to_bf16(z), b3 = to_bf16(w);
+  if (vec) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(uint32_t(b0) | (uint32_t(b1) << 16),
+                                              uint32_t(b2) | (uint32_t(b3) << 16));
+  } else {
+    p[0] = b0;
+    p[1] = b1;
+    p[2] = b2;
+    p[3] = b3;
+  }
+}
+
 // dh tile (tokens x hidden columns) += G_c W_c over the chunk's vocabulary.
+// Each wave passes its 128 x 128 block through LDS one 32-column slab at a
+// time (16 KB per wave), so a lane reads and writes four consecutive columns
+// of a dh row at once: 16-byte fp32 partial sums (all 16 of a slab's loads
+// issued before the adds) and 8-byte bf16 outputs.
 template <int kMode>
 __global__ __launch_bounds__(kT) void bwd_dh_tile(FusedBwdArgs a, ChunkArgs c) {
   __shared__ gemm::Smem smem;
@@ -201,23 +220,49 @@ __global__ __launch_bounds__(kT) void bwd_dh_tile(FusedBwdArgs a, ChunkArgs c) {
   const int64_t n0 = int64_t(nt) * kTile, k0 = int64_t(ht) * kTile;
   f32x16 acc[4][4];
   gemm::gemm_nt_tile(acc, smem, c.g_nc, n0, a.N, c.cap, c.wt + c.c0, k0, a.H, c.vpad, c.cpad);
+
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  float* stg = reinterpret_cast<float*>(&smem[0][0][0]) + wid * (128 * 32);
+  const bool vec_out = (reinterpret_cast<uintptr_t>(a.dh) & 7u) == 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t col = k0 + gemm::acc_b_row(j);
-    if (col >= a.H) continue;
+    // acc[i][j][r] is token 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, column 32 j + lane % 32
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t n = n0 + gemm::acc_a_row(i, r);
-        if (n >= a.N) continue;
-        const int64_t o = n * a.H + col;
-        const float v = acc[i][j][r];
-        if (kMode == kDhOnly) a.dh[o] = to_bf16(v);
-        if (kMode == kDhFirst) c.dh_acc[o] = v;
-        if (kMode == kDhMiddle) c.dh_acc[o] += v;
-        if (kMode == kDhLast) a.dh[o] = to_bf16(c.dh_acc[o] + v);
+      for (int r = 0; r < 16; ++r)
+        stg[(32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * 32 + (lane & 31)] =
+            acc[i][j][r];
+    __syncthreads();
+    // lane: columns col .. col + 3 (H is a multiple of 64, so all or none
+    // exist) of tokens n0 + 128 wm + 8 q + lane / 8
+    const int64_t col = k0 + 128 * wn + 32 * j + 4 * (lane & 7);
+    f32x4 prev[16];
+    if (kMode == kDhMiddle || kMode == kDhLast) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t n = n0 + 128 * wm + 8 * q + (lane >> 3);
+        prev[q] = (n < a.N && col < a.H)
+                      ? *reinterpret_cast<const f32x4*>(c.dh_acc + n * a.H + col)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int tl = 8 * q + (lane >> 3);
+      const int64_t n = n0 + 128 * wm + tl;
+      f32x4 v = *reinterpret_cast<const f32x4*>(stg + tl * 32 + 4 * (lane & 7));
+      if (n >= a.N || col >= a.H) continue;
+      const int64_t o = n * a.H + col;
+      if (kMode == kDhMiddle || kMode == kDhLast) v = prev[q] + v;
+      if (kMode == kDhFirst || kMode == kDhMiddle)
+        *reinterpret_cast<f32x4*>(c.dh_acc + o) = v;
+      else
+        store_bf16x4(a.dh + o, v[0], v[1], v[2], v[3], vec_out);
+    }
+    __syncthreads();
   }
 }
 
