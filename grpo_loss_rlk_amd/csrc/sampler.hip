@@ -56,25 +56,27 @@ RLK_DEV bool better(double s, int64_t i, double s2, int64_t i2) {
   return s > s2 || (s == s2 && i < i2);
 }
 
-constexpr int kRound = kSmT * 8;   // ids of one round at most (one 16-byte vector per thread)
-constexpr int kAhead = 8;          // 16-byte vectors in flight per thread
+constexpr int kAhead = 8;   // 16-byte vectors in flight per thread
 
-// One row per block, in rounds of one 16-byte vector per thread. A round
-// lists the ids of its nucleus members (logit >= tau) in LDS, one atomic
-// per wave (a wave prefix sum places each thread's entries); then every
-// thread scores list entries densely (so the Philox and fp64 work is not
-// spread thin over diverged lanes; the logit is read again, from cache)
-// while the next kAhead vectors are in flight.
-// Rounds alternate between two lists with their own running counters, so one
-// barrier per round separates a round's appends from its scoring and the
-// scoring from the list's reuse two rounds later. The draw is an argmax, so
-// the order of a list does not matter.
+// One row per block. Each round, a wave reads 64 consecutive 16-byte vectors
+// (one per lane; kAhead rounds in flight) and appends the ids of its nucleus
+// members (logit >= tau) to its own list in LDS (a wave prefix sum places
+// each lane's entries). The list is scored densely across the wave's lanes
+// (so the Philox and fp64 work is not spread thin over diverged lanes; the
+// logit is read again, from cache) only when the next round might overflow
+// it and at the end of the row, so a sparse nucleus costs a few scoring
+// passes per row rather than one per round. The waves never wait for one
+// another until the final argmax: a wave's LDS accesses are performed in
+// order, so its list needs no block barrier. The draw is an argmax under a total order (higher
+// score, then lower id), so neither the order of a list nor the split of the
+// row over waves changes it.
 template <typename T, bool kVec>
 __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
+  constexpr int kEV = 16 / int(sizeof(T));   // values per 16-byte vector (8 bf16, 4 fp32)
   __shared__ double ss[kSmT / kWave];
   __shared__ int64_t si[kSmT / kWave];
-  __shared__ int32_t list_i[2][kRound];
-  __shared__ int cnt[2];
+  constexpr int kCap = 2 * kWave * kEV;   // a wave's list: two rounds' worth of ids
+  __shared__ int32_t list_i[kSmT / kWave][kCap];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int64_t row = blockIdx.x;
   if (a.nflags[row] & (kNonFinite | kBadParam)) {
@@ -89,38 +91,17 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
   double best = -INFINITY;
   int64_t best_i = INT64_MAX;
-  if (tid < 2) cnt[tid] = 0;
-  __syncthreads();
-  int last[2] = {0, 0};   // each list's counter at its previous scoring
-  int par = 0;
-  constexpr int kEV = 16 / int(sizeof(T));   // values per 16-byte vector (8 bf16, 4 fp32)
+  int32_t* lst = list_i[wid];
 
-  // list this thread's ids i0 .. i0 + kEV - 1 that are in the nucleus; the
-  // whole wave calls this together
-  auto offer = [&](int64_t i0, const float (&z)[kEV]) __attribute__((always_inline)) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int e = 0; e < kEV; ++e)
-      if (i0 + e < V && z[e] >= tau && z[e] > -INFINITY) m |= 1u << e;
-    const int n = __popc(m);
-    const int incl = wave_scan_incl(n);
-    const int total = __shfl(incl, kWave - 1, kWave);
-    if (total == 0) return;
-    int base = 0;
-    if (lane == 0) base = atomicAdd(&cnt[par], total);
-    base = __shfl(base, 0, kWave) - last[par] + incl - n;
-    while (m) {
-      const int e = __ffs(m) - 1;
-      m &= m - 1;
-      list_i[par][base] = int32_t(i0 + e);
-      ++base;
-    }
-  };
-  auto score_listed = [&]() __attribute__((always_inline)) {
-    __syncthreads();
-    const int end = cnt[par];
-    for (int c = tid; c < end - last[par]; c += kSmT) {
-      const int64_t i = list_i[par][c];
+  int listed = 0;   // entries in this wave's list (wave-uniform)
+
+  // score this wave's listed ids densely across its lanes and empty the list
+  auto score = [&]() __attribute__((always_inline)) {
+    // the wave's list writes before its reads (compiler order; the hardware
+    // performs one wave's LDS accesses in order)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (int c = lane; c < listed; c += kWave) {
+      const int64_t i = lst[c];
       uint32_t w[4] = {uint32_t(i >> 2), uint32_t(rk), uint32_t(rk >> 32), a.offset};
       philox4x32_10(w, k0, k1);
       const uint32_t word = (i & 3) == 0 ? w[0] : (i & 3) == 1 ? w[1] : (i & 3) == 2 ? w[2] : w[3];
@@ -131,8 +112,31 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
         best_i = i;
       }
     }
-    last[par] = end;
-    par ^= 1;
+    // the reads before later writes
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    listed = 0;
+  };
+  // append this lane's ids i0 .. i0 + kEV - 1 that are in the nucleus to the
+  // wave's list, scoring the list first if this round might not fit; the
+  // whole wave calls this together
+  auto offer = [&](int64_t i0, const float (&z)[kEV]) __attribute__((always_inline)) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < kEV; ++e)
+      if (i0 + e < V && z[e] >= tau && z[e] > -INFINITY) m |= 1u << e;
+    const int n = __popc(m);
+    const int incl = wave_scan_incl(n);
+    const int total = __shfl(incl, kWave - 1, kWave);
+    if (total == 0) return;
+    if (listed + total > kCap) score();
+    int base = listed + incl - n;
+    while (m) {
+      const int e = __ffs(m) - 1;
+      m &= m - 1;
+      lst[base] = int32_t(i0 + e);
+      ++base;
+    }
+    listed += total;
   };
   auto unpack = [&](const uint4& q, float (&z)[kEV]) __attribute__((always_inline)) {
     const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
@@ -178,7 +182,6 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
           }
         }
         offer(j * kEV, z);
-        score_listed();
       }
     }
   } else {
@@ -190,9 +193,9 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
         z[e] = i < V ? val<T>(zrow, i) : -INFINITY;
       }
       offer(r0 + int64_t(tid) * kEV, z);
-      score_listed();
     }
   }
+  if (listed > 0) score();
   // block argmax: a fixed butterfly in each wave, then the waves in order
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) {
