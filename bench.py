@@ -87,6 +87,52 @@ def _events_time(torch, fn, steps, warmup):
     return float(np.mean(per)), float(t0.elapsed_time(t1)), float(np.min(per))
 
 
+def _outs(torch, o):
+    """The tensors of a call's result (dict, tuple or tensor), in a fixed order."""
+    if isinstance(o, dict):
+        return [o[k] for k in sorted(o) if torch.is_tensor(o[k])]
+    if isinstance(o, (tuple, list)):
+        return [t for t in o if torch.is_tensor(t)]
+    return [o]
+
+
+def _same(torch, a, b):
+    """Bitwise equality (NaN-safe: the raw bytes are compared)."""
+    if a.shape != b.shape or a.dtype != b.dtype:
+        return False
+    return torch.equal(a.contiguous().view(-1).view(torch.uint8),
+                       b.contiguous().view(-1).view(torch.uint8))
+
+
+def _determinism(torch, run_full, run_rows=None, n=0, seed=0):
+    """Outside the timed region: three calls on the same inputs must agree
+    bitwise; with `run_rows(idx)` (the per-row outputs for the rows idx, in
+    that order), the full batch's per-row outputs must equal, bitwise, those
+    of 4 random contiguous splits of the rows (each piece its own call) and
+    of one random permutation."""
+    ref = [t.clone() for t in _outs(torch, run_full())]
+    ok = True
+    for _ in range(2):
+        ok = all(_same(torch, a, b) for a, b in zip(ref, _outs(torch, run_full()))) and ok
+    res = {"run_to_run_x3": "pass" if ok else "FAIL"}
+    if run_rows is not None:
+        g = torch.Generator().manual_seed(seed)
+        full_rows = [t.clone() for t in run_rows(torch.arange(n, device="cuda:0"))]
+        ok = True
+        for _ in range(4):
+            cuts = sorted(set(torch.randint(1, n, (3,), generator=g).tolist()))
+            bounds = [0] + cuts + [n]
+            for a, b in zip(bounds[:-1], bounds[1:]):
+                part = run_rows(torch.arange(a, b, device="cuda:0"))
+                ok = all(_same(torch, p, r[a:b]) for p, r in zip(part, full_rows)) and ok
+        perm = torch.randperm(n, generator=g).to("cuda:0")
+        part = run_rows(perm)
+        ok = all(_same(torch, p, r[perm]) for p, r in zip(part, full_rows)) and ok
+        res["batch_invariance_4splits_1perm"] = "pass" if ok else "FAIL"
+    torch.cuda.synchronize()
+    return res
+
+
 def leg_logits(torch, rlk, synth, steps, warmup, cpu_sample):
     w = synth.workload("qwen")
     t_gen = time.perf_counter()
@@ -99,6 +145,9 @@ def leg_logits(torch, rlk, synth, steps, warmup, cpu_sample):
           file=sys.stderr, flush=True)
     fn = lambda: rlk.logprob_from_logits(x, yt, w.temperature, w.top_p)  # noqa: E731
     mean_ms, total_ms, min_ms = _events_time(torch, fn, steps, warmup)
+    det = _determinism(
+        torch, fn, lambda idx: _outs(torch, rlk.logprob_from_logits(
+            x[idx], yt[idx], w.temperature, w.top_p)), w.N, seed=2)
     rows = w.N
     bytes_per_row = 2 * w.V + 8 + 25     # logits + target id + 5 fp32, 1 int32, 1 flag out
     achieved = rows * bytes_per_row / (mean_ms * 1e-3) / 1e9
@@ -112,6 +161,7 @@ def leg_logits(torch, rlk, synth, steps, warmup, cpu_sample):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _profile_traffic("bf16_hist_rows_qwen3_logits_4096x151936")},
         "bytes_per_row": bytes_per_row,
+        "determinism": det,
     }
     if cpu_sample > 0:
         from oracle import logprob as OL
@@ -158,6 +208,7 @@ def leg_support(torch, rlk, synth, steps, warmup):
     fnc = lambda: rlk.logprob_from_support(x, yt, w.temperature, offsets, ids,  # noqa: E731
                                            check_top_p=w.top_p)
     mean_c, total_c, min_c = _events_time(torch, fnc, max(3, steps // 4), warmup)
+    det = _determinism(torch, fnc)
     # A gather moves whole 64-byte sectors: the bytes a perfect kernel must
     # move are the ids (4 B each), every distinct 64-byte sector of logits the
     # sets touch (32 bf16 ids per sector; a row's ids are sorted), and per row
@@ -181,6 +232,7 @@ def leg_support(torch, rlk, synth, steps, warmup):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
                      "traffic": _profile_traffic("support_rows_qwen3_logits_4096x151936")},
+        "determinism": det,
     }
 
 
@@ -200,6 +252,11 @@ def leg_sample(torch, rlk, synth, steps, warmup):
         return rlk.sample_top_p(x, w.temperature, w.top_p, 1234, state["offset"])
 
     mean_ms, total_ms, min_ms = _events_time(torch, fn, steps, warmup)
+    # with row keys = original row ids, a draw is a function of its row alone
+    det = _determinism(
+        torch, lambda: rlk.sample_top_p(x, w.temperature, w.top_p, 1234, 7),
+        lambda idx: _outs(torch, rlk.sample_top_p(x[idx], w.temperature, w.top_p, 1234, 7,
+                                                  row_keys=idx)), w.N, seed=3)
     bytes_per_row = 3 * 2 * w.V + 8 + 4 + 4 + 4 + 1
     achieved = w.N * bytes_per_row / (mean_ms * 1e-3) / 1e9
     return {
@@ -211,6 +268,7 @@ def leg_sample(torch, rlk, synth, steps, warmup):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "bytes_per_row": bytes_per_row,
+        "determinism": det,
     }
 
 
@@ -228,6 +286,9 @@ def leg_fused(torch, rlk, synth, steps, warmup):
           f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     fn = lambda: rlk.logprob_fused_linear(h, W, yt, w.temperature, 1.0)  # noqa: E731
     mean_ms, total_ms, min_ms = _events_time(torch, fn, steps, warmup)
+    det = _determinism(
+        torch, fn, lambda idx: _outs(torch, rlk.logprob_fused_linear(
+            h[idx], W, yt[idx], w.temperature, 1.0)), w.N, seed=3)
     flops = 2.0 * w.N * w.V * w.H
     achieved = flops / (mean_ms * 1e-3) / 1e12
     return {
@@ -240,6 +301,7 @@ def leg_fused(torch, rlk, synth, steps, warmup):
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": _profile_traffic("fwd_tile_stats_qwen3_head_8192x4096x151936")},
         "flops_per_token": 2.0 * w.V * w.H,
+        "determinism": det,
     }
 
 
@@ -266,6 +328,14 @@ def leg_fused_bwd(torch, rlk, synth, steps, warmup):
         return rlk.logprob_fused_linear_bwd(h, W, yt, out["saved"], g_lp, g_h, w.temperature, 1.0)
 
     mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
+
+    def dh_rows(idx):   # dh of the rows idx (a row's dh depends on that row only; dW sums rows)
+        hi, yi = h[idx], yt[idx]
+        out = rlk.logprob_fused_linear(hi, W, yi, w.temperature, 1.0)
+        return [rlk.logprob_fused_linear_bwd(hi, W, yi, out["saved"], g_lp[idx], g_h[idx],
+                                             w.temperature, 1.0)[0]]
+
+    det = _determinism(torch, step, dh_rows, w.N, seed=5)
     flops = 8.0 * w.N * w.V * w.H      # forward 2VH + recompute 2VH + dh 2VH + dW 2VH per token
     achieved = flops / (mean_ms * 1e-3) / 1e12
     return {
@@ -279,6 +349,7 @@ def leg_fused_bwd(torch, rlk, synth, steps, warmup):
                      "traffic": None},
         "flops_per_token_executed": 8.0 * w.V * w.H,
         "frac_useful_6vh": round(0.75 * achieved / BF16_PEAK_TFLOPS, 4),
+        "determinism": det,
     }
 
 
@@ -331,6 +402,14 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
                                    rewards=g["rw"], group_size=w.group_size)
 
     mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
+    # the loss and its per-token outputs run to run; the top-p forward's
+    # per-token outputs under splits and a permutation of the tokens
+    det = _determinism(torch, step)
+    det.update({k: v for k, v in _determinism(
+        torch, lambda: rlk.logprob_fused_linear(g["h"], g["W"], g["yt"], w.temperature, w.top_p),
+        lambda idx: _outs(torch, rlk.logprob_fused_linear(g["h"][idx], g["W"], g["yt"][idx],
+                                                          w.temperature, w.top_p)),
+        T_tot, seed=4).items() if k != "run_to_run_x3"})
     flops = 2.0 * T_tot * w.V * w.H
     achieved = flops / (mean_ms * 1e-3) / 1e12
     return {
@@ -343,6 +422,7 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": None},
         "flops_per_token": 2.0 * w.V * w.H,
+        "determinism": det,
     }
 
 
@@ -361,6 +441,7 @@ def leg_grpo_train(torch, rlk, synth, steps, warmup):
                                             None, w.temperature, w.top_p)
 
     mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
+    det = _determinism(torch, step)   # dh and dW, three steps bitwise
     flops = 8.0 * T_tot * w.V * w.H    # forward 2VH + recompute 2VH + dh 2VH + dW 2VH per token
     achieved = flops / (mean_ms * 1e-3) / 1e12
     return {
@@ -374,6 +455,7 @@ def leg_grpo_train(torch, rlk, synth, steps, warmup):
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": None},
         "flops_per_token_executed": 8.0 * w.V * w.H,
+        "determinism": det,
     }
 
 

@@ -108,6 +108,21 @@ RLK_DEV void g_epilogue(const FusedBwdArgs& a, const ChunkArgs& c, const f32x16 
   const int rbase = gemm::acc_a_row(0, 0);   // 128 wm + 4 (lane / 32): this lane's first row
   const float inv_t = a.inv_t, c1 = inv_t * kLog2e;
   const int vrem = int(c.csz - v0 < 2 * kTile ? c.csz - v0 : 2 * kTile) - rbase;
+  // the four token columns' inputs, loaded together (a token past N reads
+  // row N - 1 and is then ignored) so that one memory latency is exposed
+  // instead of a chain of dependent ones per column
+  float sv[4][4], ghv[4], glv[4];
+  int64_t yv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + gemm::acc_b_row(j);
+    const int64_t nc = n < a.N ? n : a.N - 1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sv[j][k] = a.saved[4 * nc + k];
+    ghv[j] = a.g_H ? a.g_H[nc] : 0.f;
+    glv[j] = a.g_lp ? a.g_lp[nc] : 0.f;
+    yv[j] = a.targets[nc];
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int nl = gemm::acc_b_row(j);
@@ -115,15 +130,15 @@ RLK_DEV void g_epilogue(const FusedBwdArgs& a, const ChunkArgs& c, const f32x16 
     float lse2 = 1e30f, eq = 0.f, glp = 0.f, gh = 0.f, tau = -INFINITY;
     int ty = -1;   // target row relative to this lane's first row (-1: none here)
     if (n < a.N) {
-      lse2 = a.saved[4 * n + 0] * kLog2e;
-      eq = a.saved[4 * n + 1];
-      tau = a.saved[4 * n + 2];
-      gh = a.g_H ? a.g_H[n] : 0.f;
-      const int64_t y = a.targets[n];
+      lse2 = sv[j][0] * kLog2e;
+      eq = sv[j][1];
+      tau = sv[j][2];
+      gh = ghv[j];
+      const int64_t y = yv[j];
       // a row whose target is out of range or outside the nucleus keeps only
       // its entropy term
-      if (y >= 0 && y < a.V && a.saved[4 * n + 3] != 0.f) {
-        glp = a.g_lp ? a.g_lp[n] : 0.f;
+      if (y >= 0 && y < a.V && sv[j][3] != 0.f) {
+        glp = glv[j];
         const int64_t rel = y - c.c0 - v0 - rbase;
         ty = rel >= 0 && rel < kTile ? int(rel) : -1;
       }
