@@ -204,7 +204,7 @@ rlk_status rlk_sample_top_p(
  * targets       [n_rows] int64.
  * Logits are accumulated in fp32 over the hidden dimension and never rounded
  * to bf16. With top_p < 1 the outputs are the truncated ones of the
- * logits-in entry point (same nucleus rule; the fp32 logits of up to 4096
+ * logits-in entry point (same nucleus rule; the fp32 logits of up to 16384
  * rows at a time are formed in the workspace and cut by the logits-in row
  * kernel); with top_p = 1 they are full and no logits are stored.
  * logprob, entropy   [n_rows] fp32 outputs (required).

@@ -224,3 +224,39 @@ def test_bwd_grpo_full_size_sampled():
         want = _oracle_dh_row(OL.widen_bf16(hb[n]), W64, int(y[n]), float(g_lp[n]), 0.0, Tf, pf)
         got = host(dh[n].float()).astype(np.float64)
         assert _rel(got, want) <= ROW_TOL, (n, _rel(got, want))
+
+
+def test_bwd_grad_hidden_only_2_byte_aligned():
+    """grad_hidden needs only 2-byte alignment: the dh epilogue writes four
+    bf16 values as one 8-byte store when the output is 8-byte aligned and as
+    four 2-byte stores otherwise. Through the C ABI with grad_hidden at an
+    offset of 2 bytes (one and several vocabulary chunks, so the first,
+    middle and last dh modes all store), dh must equal the aligned call's
+    bitwise, and dW too."""
+    from grpo_loss_rlk_amd import _native
+    L = _native.lib()
+    for N, H, V in [(300, 128, 5000), (197, 64, 70001)]:
+        w, hb, wb, y = _inputs("fused", N, H, V)
+        h, W = bf16_to_device(hb), bf16_to_device(wb)
+        yt = torch.as_tensor(y).to(DEV)
+        g_lp, g_h = _upstream(N, 11)
+        glp, gh = torch.as_tensor(g_lp).to(DEV), torch.as_tensor(g_h).to(DEV)
+        fwd = rlk.logprob_fused_linear(h, W, yt, 0.7, 0.95)
+        dh_ref, dw_ref = rlk.logprob_fused_linear_bwd(h, W, yt, fwd["saved"], glp, gh, 0.7, 0.95)
+        buf = torch.full((N * H + 4,), float("nan"), device=DEV, dtype=torch.bfloat16)
+        dw = torch.empty(V, H, device=DEV, dtype=torch.float32)
+        ws_n = L.rlk_logprob_fused_linear_bwd_workspace_size(N, H, V, 0.95)
+        ws = torch.empty(ws_n, device=DEV, dtype=torch.uint8)
+        print(f"  rlk bwd with grad_hidden at +2 bytes N={N} H={H} V={V}", flush=True)
+        st = L.rlk_logprob_fused_linear_bwd(
+            h.data_ptr(), W.data_ptr(), N, H, V, h.stride(0), W.stride(0), yt.data_ptr(),
+            fwd["saved"].data_ptr(), glp.data_ptr(), gh.data_ptr(), 0.7, 0.95, 0,
+            buf.data_ptr() + 2, dw.data_ptr(), ws.data_ptr(), ws_n,
+            torch.cuda.current_stream().cuda_stream)
+        assert st == _native.RLK_OK, L.rlk_last_error()
+        torch.cuda.synchronize()
+        dh = buf[1:1 + N * H].view(N, H)
+        assert bits_equal(dh, dh_ref)
+        assert bits_equal(dw, dw_ref)
+        # nothing written outside [ptr, ptr + 2 N H)
+        assert torch.isnan(buf[0].float()) and torch.isnan(buf[1 + N * H:].float()).all()
