@@ -244,10 +244,10 @@ def leg_support(torch, rlk, synth, steps, warmup):
 
 def leg_sample(torch, rlk, synth, steps, warmup):
     """Rollout-side top-p sampler on the config-2 logits (4096 x 151936 bf16,
-    T=0.7, p=0.95): nucleus (row kernel), seeded Gumbel-max draw, and the
-    drawn token scored by the row kernel (bitwise the training-side value).
-    The call reads each row three times (nucleus, draw, score): 3 x 2V bytes
-    per row plus outputs."""
+    T=0.7, p=0.95): nucleus (row kernel), then the seeded Gumbel-max draw,
+    which scores the drawn token with the row kernel's own statistics
+    (bitwise the training-side value). The call reads each row twice
+    (nucleus, draw): 2 x 2V bytes per row plus outputs."""
     w = synth.workload("qwen")
     arr = synth.logits_rows(w, range(w.N))
     x = torch.from_numpy(arr.view(np.int16)).to("cuda:0").view(torch.bfloat16)
@@ -263,7 +263,7 @@ def leg_sample(torch, rlk, synth, steps, warmup):
         torch, lambda: rlk.sample_top_p(x, w.temperature, w.top_p, 1234, 7),
         lambda idx: _outs(torch, rlk.sample_top_p(x[idx], w.temperature, w.top_p, 1234, 7,
                                                   row_keys=idx)), w.N, seed=3)
-    bytes_per_row = 3 * 2 * w.V + 8 + 4 + 4 + 4 + 1
+    bytes_per_row = 2 * 2 * w.V + 8 + 4 + 4 + 4 + 1
     achieved = w.N * bytes_per_row / (mean_ms * 1e-3) / 1e9
     return {
         "workload": f"top-p sampler + score, {w.N} rows x V={w.V} bf16, T={w.temperature}, "

@@ -241,9 +241,9 @@ rlk_status rlk_logprob_from_support(const void* logits, int32_t dtype, int64_t n
 size_t rlk_sample_top_p_workspace_size(int64_t n_rows, int64_t vocab, int32_t dtype) {
   if (n_rows < 0) return 0;
   // dummy targets (int64), lp_full, lp_trunc, entropy, threshold (fp32), flags,
-  // then the logits-in workspace
+  // the row max and log Z_S (fp64 pairs), then the logits-in workspace
   return support_slot(n_rows, 8) + 4 * support_slot(n_rows, 4) + support_slot(n_rows, 1) +
-         rlk::logits_rows_workspace(n_rows, vocab, dtype);
+         support_slot(n_rows, 16) + rlk::logits_rows_workspace(n_rows, vocab, dtype);
 }
 
 rlk_status rlk_sample_top_p(const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab,
@@ -283,7 +283,8 @@ rlk_status rlk_sample_top_p(const void* logits, int32_t dtype, int64_t n_rows, i
   float* ent = reinterpret_cast<float*>(w + 2 * f4);
   float* thr = reinterpret_cast<float*>(w + 3 * f4);
   uint8_t* nfl = reinterpret_cast<uint8_t*>(w + 4 * f4);
-  void* rows_ws = w + 4 * f4 + support_slot(n_rows, 1);
+  double* stats = reinterpret_cast<double*>(w + 4 * f4 + support_slot(n_rows, 1));
+  void* rows_ws = w + 4 * f4 + support_slot(n_rows, 1) + support_slot(n_rows, 16);
 
   rlk::RowArgs r{};
   r.logits = logits;
@@ -292,15 +293,18 @@ rlk_status rlk_sample_top_p(const void* logits, int32_t dtype, int64_t n_rows, i
   r.row_stride = row_stride;
   r.temperature = temperature;
   r.top_p = top_p;
-  // 1. each row's nucleus threshold (the target is a placeholder)
+  // 1. each row's nucleus: threshold, entropy, size, flags, and the row max
+  // and log Z_S its tokens are scored with (the target is a placeholder)
   s = hip_status(rlk::launch_fill_i64(zero_t, n_rows, 0, st), "rlk_sample_top_p fill");
   if (s != RLK_OK) return s;
   r.targets = zero_t;
   r.lp_full = lp_full;
   r.lp_trunc = lp_tr;
-  r.ent_trunc = ent;
+  r.ent_trunc = entropy ? entropy : ent;
+  r.nsize = nucleus_size;
   r.thresh = thr;
   r.flags = nfl;
+  r.score_stats = stats;
   s = hip_status(rlk::launch_logits_rows(r, dtype, rows_ws, st), "rlk_sample_top_p nucleus");
   if (s != RLK_OK) return s;
   // 2. the draw
@@ -315,19 +319,14 @@ rlk_status rlk_sample_top_p(const void* logits, int32_t dtype, int64_t n_rows, i
   a.row_keys = row_keys;
   a.thresh = thr;
   a.nflags = nfl;
+  a.score_stats = stats;
   a.samples = samples;
-  s = hip_status(rlk::launch_sample_rows(a, dtype, st), "rlk_sample_top_p draw");
-  if (s != RLK_OK) return s;
-  // 3. the drawn tokens scored by the logits-in kernel itself, so the
-  // rollout's logprobs are bitwise those of a training-side call
-  if (!logprob && !entropy && !nucleus_size && !flags) return ok();
-  r.targets = samples;
-  r.lp_trunc = logprob ? logprob : lp_tr;
-  r.ent_trunc = entropy ? entropy : ent;
-  r.thresh = nullptr;
-  r.nsize = nucleus_size;
-  r.flags = flags;
-  return hip_status(rlk::launch_logits_rows(r, dtype, rows_ws, st), "rlk_sample_top_p score");
+  // 2'. the drawn token scored in the same kernel with the row kernel's own
+  // (row max, log Z_S) and token_logprob, so the rollout's logprobs are
+  // bitwise those of a training-side call with targets = samples
+  a.logprob = logprob;
+  a.flags = flags;
+  return hip_status(rlk::launch_sample_rows(a, dtype, st), "rlk_sample_top_p draw");
 }
 
 // ------------------------------------------------------------------ fused LM head

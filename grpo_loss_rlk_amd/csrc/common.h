@@ -13,6 +13,18 @@ namespace rlk {
 
 constexpr int kWave = 64;
 
+// Log-probability of a token with logit zy in a row whose max is m and whose
+// log-normaliser (over the nucleus, or the whole row) is logZ, on the scale
+// z/T after subtracting m: (zy - m) / T - logZ in fp64, rounded to fp32. The
+// fp64 operations are rounded one by one (no contraction into a fused
+// multiply-add), so every kernel that scores a token from the same (m, logZ)
+// returns the same bits.
+RLK_DEV float token_logprob(float zy, double m, double invT, double logZ) {
+#pragma clang fp contract(off)
+  const double d = (double(zy) - m) * invT;
+  return float(d - logZ);
+}
+
 // Order-preserving 32-bit key of an fp32 value: a < b  <=>  key(a) < key(b)
 // for non-NaN values, with -0 folded onto +0 so that equal values share a key.
 RLK_DEV uint32_t f32_key(float f) {

@@ -29,6 +29,8 @@ struct RowArgs {
   // by the producer; read and cleared to 0 here
   uint32_t* zmax_key;
   uint32_t* zbad;
+  double* score_stats;    // nullable [n_rows, 2]: the row max m and log Z_S with which
+                          // the row's tokens are scored (token_logprob), for live rows
   uint8_t* fallback;      // workspace [n_rows]: rows the histogram path hands on
 };
 

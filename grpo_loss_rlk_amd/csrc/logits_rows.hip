@@ -279,10 +279,9 @@ RLK_DEV void generic_row(const RowArgs& a, int64_t row, GenScratch& g) {
         lpt = -INFINITY;
         flags |= kOutside;
       } else {
-        const double dy = (double(zy) - m) * invT;
-        lpf = float(dy - logZ);
+        lpf = token_logprob(zy, m, invT, logZ);
         if (!cut || f32_key(zy) >= tau_key) {
-          lpt = float(dy - logZs);
+          lpt = token_logprob(zy, m, invT, logZs);
         } else {
           lpt = -INFINITY;
           flags |= kOutside;
@@ -290,6 +289,10 @@ RLK_DEV void generic_row(const RowArgs& a, int64_t row, GenScratch& g) {
       }
     }
     const float tau = cut ? key_f32(tau_key) : -INFINITY;
+    if (a.score_stats) {
+      a.score_stats[2 * row] = m;
+      a.score_stats[2 * row + 1] = logZs;
+    }
     store_row(a, row, lpf, lpt, float(logZ - S / Z), float(logZs - Ss / Zs), int32_t(size), tau,
               flags, float(m * invT + logZs), float(m * invT + Ss / Zs));
   }
@@ -661,10 +664,9 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
           lpt = -INFINITY;
           flags |= kOutside;
         } else {
-          const double dy = double(vy - mval) * invT;
-          lpf = float(dy - logZ);
+          lpf = token_logprob(vy, double(mval), invT, logZ);
           if (!cut || bf16_key_merged(cy) >= tau_key) {
-            lpt = float(dy - logZs);
+            lpt = token_logprob(vy, double(mval), invT, logZs);
           } else {
             lpt = -INFINITY;
             flags |= kOutside;
@@ -679,6 +681,10 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
           flags |= kBoundary;
       }
       const double mT = double(mval) * invT;
+      if (a.score_stats) {
+        a.score_stats[2 * row] = double(mval);
+        a.score_stats[2 * row + 1] = logZs;
+      }
       store_row(a, row, lpf, lpt, h_full, h_trunc, size, tau, flags, float(mT + logZs),
                 float(mT + Ss / Zs));
     }
@@ -1121,10 +1127,9 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
         lpt = -INFINITY;
         flags |= kOutside;
       } else {
-        const double dy = (double(zy) - m) * invT;
-        lpf = float(dy - logZ);
+        lpf = token_logprob(zy, m, invT, logZ);
         if (!cut || f32_key(zy) >= tau_key) {
-          lpt = float(dy - logZs);
+          lpt = token_logprob(zy, m, invT, logZs);
         } else {
           lpt = -INFINITY;
           flags |= kOutside;
@@ -1132,6 +1137,10 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
       }
     }
     const float tau = cut ? key_f32(tau_key) : -INFINITY;
+    if (a.score_stats) {
+      a.score_stats[2 * row] = m;
+      a.score_stats[2 * row + 1] = logZs;
+    }
     store_row(a, row, lpf, lpt, float(logZ - S / Z), float(logZs - Ss / Zs), int32_t(size), tau,
               flags, float(m * invT + logZs), float(m * invT + Ss / Zs));
   }

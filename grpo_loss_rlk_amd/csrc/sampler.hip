@@ -22,7 +22,7 @@ namespace rlk {
 namespace {
 
 constexpr int kSmT = 256;
-constexpr uint8_t kNonFinite = 4, kBadParam = 16;
+constexpr uint8_t kOutside = 1, kBadTarget = 2, kNonFinite = 4, kBadParam = 16;
 
 // Ten Philox-4x32 rounds on counter c with key (k0, k1).
 RLK_DEV void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
@@ -50,6 +50,21 @@ template <>
 RLK_DEV float val<float>(const float* row, int64_t i) { return row[i]; }
 template <>
 RLK_DEV float val<uint16_t>(const uint16_t* row, int64_t i) { return bf16_to_f32(row[i]); }
+
+// The drawn token y scored as the logits-in kernel scores a target (the same
+// token_logprob from the nucleus pass's row max and log Z_S): the nucleus
+// pass's flags without its placeholder target's bits, and for y < 0 (no
+// draw) the out-of-range bit and a NaN logprob.
+template <typename T>
+RLK_DEV void score_draw(const SampleArgs& a, int64_t row, const T* zrow, int64_t y) {
+  const uint8_t f = a.nflags[row] & uint8_t(~(kOutside | kBadTarget));
+  float lp = __builtin_nanf("");
+  if (y >= 0)
+    lp = token_logprob(val<T>(zrow, y), a.score_stats[2 * row], 1.0 / double(a.temperature),
+                       a.score_stats[2 * row + 1]);
+  if (a.logprob) a.logprob[row] = lp;
+  if (a.flags) a.flags[row] = y >= 0 ? f : uint8_t(f | kBadTarget);
+}
 
 // (score, id) order: higher score first, then the lower id
 RLK_DEV bool better(double s, int64_t i, double s2, int64_t i2) {
@@ -79,11 +94,14 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
   __shared__ int32_t list_i[kSmT / kWave][kCap];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int64_t row = blockIdx.x;
+  const T* zrow = reinterpret_cast<const T*>(a.logits) + row * a.row_stride;
   if (a.nflags[row] & (kNonFinite | kBadParam)) {
-    if (tid == 0) a.samples[row] = -1;
+    if (tid == 0) {
+      a.samples[row] = -1;
+      score_draw<T>(a, row, zrow, -1);
+    }
     return;
   }
-  const T* zrow = reinterpret_cast<const T*>(a.logits) + row * a.row_stride;
   const int64_t V = a.vocab;
   const float tau = a.thresh[row];
   const double T64 = double(a.temperature);
@@ -217,7 +235,9 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
         best = ss[w];
         best_i = si[w];
       }
-    a.samples[row] = best_i == INT64_MAX ? -1 : best_i;
+    const int64_t y = best_i == INT64_MAX ? -1 : best_i;
+    a.samples[row] = y;
+    score_draw<T>(a, row, zrow, y);
   }
 }
 

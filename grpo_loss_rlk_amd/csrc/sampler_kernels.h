@@ -15,7 +15,10 @@ struct SampleArgs {
   const int64_t* row_keys;    // nullable: the row index
   const float* thresh;        // [n_rows] nucleus threshold of each row (logit value)
   const uint8_t* nflags;      // [n_rows] flags of the nucleus pass
+  const double* score_stats;  // [n_rows, 2] the nucleus pass's row max and log Z_S
   int64_t* samples;           // [n_rows] out
+  float* logprob;             // nullable [n_rows] out: the drawn token's truncated logprob
+  uint8_t* flags;             // nullable [n_rows] out: the row's flags for the drawn token
 };
 
 // dtype: 0 = fp32, 1 = bf16

@@ -180,9 +180,10 @@ rlk_status rlk_logprob_from_support(
  * al., SC 2011) on counter (i / 4, key_n low 32 bits, key_n high 32 bits,
  * offset) and key (seed low 32 bits, seed high 32 bits); key_n = row_keys[n]
  * (nullable: n). A draw depends on its row, seed, offset and key only.
- * logprob, entropy, nucleus_size, flags (nullable): the drawn token scored by
- * rlk_logprob_from_logits' kernel (its lp_trunc, entropy_trunc, nucleus size
- * and flags), so they equal bitwise what a training-side call with
+ * logprob, entropy, nucleus_size, flags (nullable): the drawn token scored as
+ * rlk_logprob_from_logits scores a target (the row kernel's own row max and
+ * log Z_S, the same fp64 arithmetic; entropy, size and flags from the same
+ * pass), so they equal bitwise what a training-side call with
  * targets = samples returns.
  * Limits: as rlk_logprob_from_logits; n_rows < 2^31.
  * -------------------------------------------------------------------------- */

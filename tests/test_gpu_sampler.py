@@ -105,6 +105,14 @@ def test_edge_rows():
         assert ids[3] % 2 == 1
         if p < 1e-3:
             assert ids[0] == int(np.argmax(z[0])) and ids[2] in (5, 9)
+        # every row, the NaN and all -inf ones included, scored bitwise as the
+        # logits-in entry point scores targets = samples
+        ref = rlk.logprob_from_logits(x, out["samples"], T, p)
+        torch.cuda.synchronize()
+        assert bits_equal(out["logprob"], ref["lp_trunc"])
+        assert bits_equal(out["entropy"], ref["entropy_trunc"])
+        assert bits_equal(out["nucleus_size"], ref["nucleus_size"])
+        assert torch.equal(out["flags"], ref["flags"])
 
 
 def test_law_of_the_draws():
