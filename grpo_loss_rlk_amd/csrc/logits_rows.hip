@@ -716,6 +716,9 @@ RLK_DEV void stream_row(const RowArgs& a, int64_t row, int64_t nvec, uint32_t* h
       uint4 q[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) q[u] = stream_load(v4 + i + u * NS);
+      // all kUnroll loads issued before the first is used (the scheduler
+      // would otherwise wait for the first before issuing the rest)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) count8(h, sp, q[u]);
     }
@@ -874,6 +877,7 @@ RLK_DEV void for_each_f32(const float* rowp, int64_t V, F&& f) {
       float4 q[kF32Unroll];
 #pragma unroll
       for (int u = 0; u < kF32Unroll; ++u) q[u] = p4[i + u * kF32T];
+      __builtin_amdgcn_sched_barrier(0);   // all loads issued before the first use
 #pragma unroll
       for (int u = 0; u < kF32Unroll; ++u) {
         const int64_t e = 4 * (i + u * kF32T);
