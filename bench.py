@@ -139,6 +139,32 @@ def _determinism(torch, run_full, run_rows=None, n=0, seed=0):
     return res
 
 
+_CPU_ORACLE = [True]
+
+
+def _cpu_oracle(fn, units, sample):
+    """The fp64 oracle timed on a bounded sample of the leg's workload, on one
+    host thread (BLAS pinned to one), as a baseline beside the GPU figure;
+    input widening and other preparation stay outside the timing."""
+    if not _CPU_ORACLE[0]:
+        return None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            fn()
+            dt = time.perf_counter() - t0
+        return {"value": units / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{sample}, fp64 numpy, one thread, {dt:.2f}s"}
+    except Exception as e:  # noqa: BLE001 -- the GPU figure stands without it
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
+def _host_bits(torch, t):
+    """bf16 device tensor -> its uint16 bit patterns on the host."""
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
 def leg_logits(torch, rlk, synth, steps, warmup, cpu_sample):
     w = synth.workload("qwen")
     t_gen = time.perf_counter()
@@ -215,6 +241,14 @@ def leg_support(torch, rlk, synth, steps, warmup):
                                            check_top_p=w.top_p)
     mean_c, total_c, min_c = _events_time(torch, fnc, max(3, steps // 4), warmup)
     det = _determinism(torch, fnc)
+    from oracle import logprob as OL
+    from oracle import support as OSup
+    ns = w.N
+    off_h = offsets[:ns + 1].cpu().numpy()
+    ids_h, y_h = ids[:int(off_h[-1])].cpu().numpy(), yt[:ns].cpu().numpy()
+    z_h = OL.widen_bf16(arr[:ns])
+    cpu = _cpu_oracle(lambda: OSup.logprob_from_support(z_h, y_h, OL.f32(w.temperature), off_h,
+                                                        ids_h), ns, f"all {ns} rows")
     # A gather moves whole 64-byte sectors: the bytes a perfect kernel must
     # move are the ids (4 B each), every distinct 64-byte sector of logits the
     # sets touch (32 bf16 ids per sector; a row's ids are sorted), and per row
@@ -239,6 +273,7 @@ def leg_support(torch, rlk, synth, steps, warmup):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
                      "traffic": _profile_traffic("support_rows_qwen3_logits_4096x151936")},
         "determinism": det,
+        "cpu_oracle": cpu,
     }
 
 
@@ -263,6 +298,17 @@ def leg_sample(torch, rlk, synth, steps, warmup):
         torch, lambda: rlk.sample_top_p(x, w.temperature, w.top_p, 1234, 7),
         lambda idx: _outs(torch, rlk.sample_top_p(x[idx], w.temperature, w.top_p, 1234, 7,
                                                   row_keys=idx)), w.N, seed=3)
+    from oracle import logprob as OL
+    from oracle import sampling as OS
+    ns = 64
+    z_h = OL.widen_bf16(arr[:ns])
+    Tf, pf = OL.f32(w.temperature), OL.f32(w.top_p)
+
+    def oracle_draws():
+        yd = np.array([OS.sample_row(z_h[n], Tf, pf, 1234, 7, n) for n in range(ns)])
+        OL.logprob_from_logits(z_h, yd, Tf, pf)
+
+    cpu = _cpu_oracle(oracle_draws, ns, f"first {ns} rows (draw and score)")
     bytes_per_row = 2 * 2 * w.V + 8 + 4 + 4 + 4 + 1
     achieved = w.N * bytes_per_row / (mean_ms * 1e-3) / 1e9
     return {
@@ -275,6 +321,7 @@ def leg_sample(torch, rlk, synth, steps, warmup):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "bytes_per_row": bytes_per_row,
         "determinism": det,
+        "cpu_oracle": cpu,
     }
 
 
@@ -295,6 +342,14 @@ def leg_fused(torch, rlk, synth, steps, warmup):
     det = _determinism(
         torch, fn, lambda idx: _outs(torch, rlk.logprob_fused_linear(
             h[idx], W, yt[idx], w.temperature, 1.0)), w.N, seed=3)
+    from oracle import fused as OF
+    from oracle import logprob as OL
+    ns = 64
+    W64 = OL.widen_bf16(wb)
+    h64 = OL.widen_bf16(hb[:ns])
+    cpu = _cpu_oracle(lambda: OF.forward(h64, W64, y[:ns], OL.f32(w.temperature), 1.0), ns,
+                      f"first {ns} tokens")
+    del W64
     flops = 2.0 * w.N * w.V * w.H
     achieved = flops / (mean_ms * 1e-3) / 1e12
     return {
@@ -308,6 +363,7 @@ def leg_fused(torch, rlk, synth, steps, warmup):
                      "traffic": _profile_traffic("fwd_tile_stats_qwen3_head_8192x4096x151936")},
         "flops_per_token": 2.0 * w.V * w.H,
         "determinism": det,
+        "cpu_oracle": cpu,
     }
 
 
@@ -342,6 +398,20 @@ def leg_fused_bwd(torch, rlk, synth, steps, warmup):
                                              w.temperature, 1.0)[0]]
 
     det = _determinism(torch, step, dh_rows, w.N, seed=5)
+    from oracle import fused as OF
+    from oracle import logprob as OL
+    ns = 8
+    W64 = OL.widen_bf16(_host_bits(torch, W))
+    h64 = OL.widen_bf16(_host_bits(torch, h[:ns]))
+    gl, gh = np.full(ns, -1.0 / w.N), np.full(ns, -0.001 / w.N)
+
+    def oracle_step():
+        OF.forward(h64, W64, y[:ns], 1.0, 1.0)
+        OF.backward(h64, W64, y[:ns], gl, gh, 1.0, 1.0)
+
+    cpu = _cpu_oracle(oracle_step, ns, f"first {ns} tokens, forward and backward "
+                                       "(dW: their contribution)")
+    del W64
     flops = 8.0 * w.N * w.V * w.H      # forward 2VH + recompute 2VH + dh 2VH + dW 2VH per token
     achieved = flops / (mean_ms * 1e-3) / 1e12
     return {
@@ -356,6 +426,7 @@ def leg_fused_bwd(torch, rlk, synth, steps, warmup):
         "flops_per_token_executed": 8.0 * w.V * w.H,
         "frac_useful_6vh": round(0.75 * achieved / BF16_PEAK_TFLOPS, 4),
         "determinism": det,
+        "cpu_oracle": cpu,
     }
 
 
@@ -416,6 +487,24 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
         lambda idx: _outs(torch, rlk.logprob_fused_linear(g["h"][idx], g["W"], g["yt"][idx],
                                                           w.temperature, w.top_p)),
         T_tot, seed=4).items() if k != "run_to_run_x3"})
+    from oracle import fused as OF
+    from oracle import grpo as OG
+    from oracle import logprob as OL
+    ns = 64
+    W64 = OL.widen_bf16(_host_bits(torch, g["W"]))
+    h64 = OL.widen_bf16(_host_bits(torch, g["h"][:ns]))
+    y_h = g["yt"][:ns].cpu().numpy()
+    lp_o, lp_r = g["lp_old"].cpu().numpy(), g["lp_ref"].cpu().numpy()
+    r_h = g["rw"].cpu().numpy()
+    Tf, pf = OL.f32(w.temperature), OL.f32(w.top_p)
+
+    def oracle_grpo():   # forward on the sample; the loss stage over every token
+        OF.forward(h64, W64, y_h, Tf, pf)
+        OG.token_loss(lp_o, lp_o, lp_r, g["cu"], OG.advantages(r_h, w.group_size))
+
+    cpu = _cpu_oracle(oracle_grpo, ns, f"first {ns} tokens of the top-p forward, plus the "
+                                       f"loss stage over all {T_tot} tokens")
+    del W64
     flops = 2.0 * T_tot * w.V * w.H
     achieved = flops / (mean_ms * 1e-3) / 1e12
     return {
@@ -429,6 +518,7 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
                      "traffic": None},
         "flops_per_token": 2.0 * w.V * w.H,
         "determinism": det,
+        "cpu_oracle": cpu,
     }
 
 
@@ -448,6 +538,22 @@ def leg_grpo_train(torch, rlk, synth, steps, warmup):
 
     mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
     det = _determinism(torch, step)   # dh and dW, three steps bitwise
+    from oracle import fused as OF
+    from oracle import logprob as OL
+    ns = 16
+    W64 = OL.widen_bf16(_host_bits(torch, g["W"]))
+    h64 = OL.widen_bf16(_host_bits(torch, g["h"][:ns]))
+    y_h = g["yt"][:ns].cpu().numpy()
+    Tf, pf = OL.f32(w.temperature), OL.f32(w.top_p)
+    gl = np.full(ns, 1.0 / T_tot)
+
+    def oracle_step():
+        OF.forward(h64, W64, y_h, Tf, pf)
+        OF.backward(h64, W64, y_h, gl, np.zeros(ns), Tf, pf)
+
+    cpu = _cpu_oracle(oracle_step, ns, f"first {ns} tokens, top-p forward and backward "
+                                       "(dW: their contribution)")
+    del W64
     flops = 8.0 * T_tot * w.V * w.H    # forward 2VH + recompute 2VH + dh 2VH + dW 2VH per token
     achieved = flops / (mean_ms * 1e-3) / 1e12
     return {
@@ -462,6 +568,7 @@ def leg_grpo_train(torch, rlk, synth, steps, warmup):
                      "traffic": None},
         "flops_per_token_executed": 8.0 * w.V * w.H,
         "determinism": det,
+        "cpu_oracle": cpu,
     }
 
 
@@ -494,6 +601,7 @@ def main():
                     help="skip the bitwise determinism checks (profiler runs)")
     args = ap.parse_args()
     _CHECK_DETERMINISM[0] = not args.no_determinism
+    _CPU_ORACLE[0] = args.cpu_sample > 0
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
                                    "(multi-GPU sharding is a design note only)"}))
