@@ -107,7 +107,7 @@ def _same(torch, a, b):
 _CHECK_DETERMINISM = [True]
 
 
-def _determinism(torch, run_full, run_rows=None, n=0, seed=0):
+def _determinism(torch, run_full, run_rows=None, n=0, seed=0, device="cuda:0"):
     """Outside the timed region: three calls on the same inputs must agree
     bitwise; with `run_rows(idx)` (the per-row outputs for the rows idx, in
     that order), the full batch's per-row outputs must equal, bitwise, those
@@ -123,19 +123,20 @@ def _determinism(torch, run_full, run_rows=None, n=0, seed=0):
     res = {"run_to_run_x3": "pass" if ok else "FAIL"}
     if run_rows is not None:
         g = torch.Generator().manual_seed(seed)
-        full_rows = [t.clone() for t in run_rows(torch.arange(n, device="cuda:0"))]
+        full_rows = [t.clone() for t in run_rows(torch.arange(n, device=device))]
         ok = True
         for _ in range(4):
             cuts = sorted(set(torch.randint(1, n, (3,), generator=g).tolist()))
             bounds = [0] + cuts + [n]
             for a, b in zip(bounds[:-1], bounds[1:]):
-                part = run_rows(torch.arange(a, b, device="cuda:0"))
+                part = run_rows(torch.arange(a, b, device=device))
                 ok = all(_same(torch, p, r[a:b]) for p, r in zip(part, full_rows)) and ok
-        perm = torch.randperm(n, generator=g).to("cuda:0")
+        perm = torch.randperm(n, generator=g).to(device)
         part = run_rows(perm)
         ok = all(_same(torch, p, r[perm]) for p, r in zip(part, full_rows)) and ok
         res["batch_invariance_4splits_1perm"] = "pass" if ok else "FAIL"
-    torch.cuda.synchronize()
+    if torch.device(device).type == "cuda":
+        torch.cuda.synchronize()
     return res
 
 
