@@ -2,9 +2,6 @@
 must pass deterministic per-row functions and catch run-to-run noise and
 batch dependence) and the traffic figure read from a counter summary (null
 once the kernel's sources no longer hash to the recorded value)."""
-import os
-import shutil
-
 import pytest
 import torch
 
@@ -50,21 +47,21 @@ def test_determinism_can_be_skipped():
 
 
 def test_profile_traffic_follows_the_source_hash(tmp_path, monkeypatch):
-    name = "bf16_hist_rows_qwen3_logits_4096x151936"
-    assert isinstance(bench._profile_traffic(name), int)    # committed summary matches
+    import hashlib
     root = tmp_path / "repo"
     (root / "profiles").mkdir(parents=True)
-    shutil.copy(os.path.join(bench.ROOT, "profiles", name + ".md"), root / "profiles")
-    text = (root / "profiles" / (name + ".md")).read_text()
-    files = [ln.split(":", 1)[1].split() for ln in text.splitlines()
-             if ln.startswith("source_files:")][0]
-    for f in files:
-        (root / f).parent.mkdir(parents=True, exist_ok=True)
-        shutil.copy(os.path.join(bench.ROOT, f), root / f)
+    (root / "src").mkdir()
+    (root / "src" / "k.hip").write_text("kernel source\n")
+    (root / "src" / "k.h").write_text("header\n")
+    h = hashlib.sha256()
+    for f in ("src/k.hip", "src/k.h"):
+        h.update((root / f).read_bytes())
+    (root / "profiles" / "k_w.md").write_text(
+        "# k on w\n\nkernel: k\nsource_files: src/k.hip src/k.h\n"
+        f"source_sha256_16: {h.hexdigest()[:16]}\ntraffic_bytes_per_launch: 12345\n")
     monkeypatch.setattr(bench, "ROOT", str(root))
-    assert bench._profile_traffic(name) == int(
-        [ln.split(":")[1] for ln in text.splitlines() if ln.startswith("traffic_bytes")][0])
-    with open(root / files[0], "a") as fh:     # the kernel's source changes
-        fh.write("\n// edited\n")
-    assert bench._profile_traffic(name) is None
+    assert bench._profile_traffic("k_w") == 12345
+    with open(root / "src" / "k.h", "a") as fh:    # the kernel's source changes
+        fh.write("edited\n")
+    assert bench._profile_traffic("k_w") is None
     assert bench._profile_traffic("no_such_summary") is None
