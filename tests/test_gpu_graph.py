@@ -82,3 +82,25 @@ def test_sampler_graph_replay():
     x = sets[0][0].clone()
     print(f"  rlk_sample_top_p in a graph N={N} V={V}", flush=True)
     _replay_matches_eager([x], sets, lambda: rlk.sample_top_p(x, 0.7, 0.95, 99, 5))
+
+
+def test_fused_backward_graph_replay():
+    """Forward and backward (two vocabulary chunks, so the first and last dh
+    modes both run) captured together; dh and dW on every replay."""
+    N, H, V = 200, 64, 40000
+    w = synth.workload("fused", N=N, H=H, V=V)
+    r = np.random.default_rng(11)
+    W = bf16_to_device(synth.weight_rows(w, range(V)))
+    glp = torch.full((N,), -1.0 / N, device=DEV)
+    gh = torch.full((N,), -0.001 / N, device=DEV)
+    sets = [(bf16_to_device(synth.bf16_bits_from_f32(r.normal(0, 1, (N, H)))),
+             torch.as_tensor(r.integers(0, V, N)).to(DEV)) for _ in range(3)]
+    h, y = sets[0][0].clone(), sets[0][1].clone()
+
+    def step():
+        f = rlk.logprob_fused_linear(h, W, y, 0.7, 0.95)
+        dh, dw = rlk.logprob_fused_linear_bwd(h, W, y, f["saved"], glp, gh, 0.7, 0.95)
+        return {"dh": dh, "dw": dw, "lp": f["logprob"]}
+
+    print(f"  rlk fused forward + backward in a graph N={N} H={H} V={V}", flush=True)
+    _replay_matches_eager([h, y], sets, step)
