@@ -614,24 +614,33 @@ def main():
 
     legs = [s for s in args.legs.split(",") if s]
     out_legs = {}
-    if "logits" in legs:
+    if "logits" in legs:   # the headline: a failure here fails the run
         out_legs["logits"] = leg_logits(torch, rlk, synth, args.steps, args.warmup,
                                         args.cpu_sample)
-    if "support" in legs:
-        out_legs["support"] = leg_support(torch, rlk, synth, args.steps, args.warmup)
-    if "sample" in legs:
-        out_legs["sample"] = leg_sample(torch, rlk, synth, max(3, args.steps // 4), args.warmup)
-    if "fused" in legs:
-        out_legs["fused"] = leg_fused(torch, rlk, synth, min(20, max(3, args.steps // 4)), 1)
-    if "copy" in legs:
-        out_legs["copy"] = leg_copy(torch, args.steps, args.warmup)
-    if "grpo" in legs:
-        out_legs["grpo"] = leg_grpo(torch, rlk, synth, 3, 1)
-    if "grpo_train" in legs:
-        out_legs["grpo_train"] = leg_grpo_train(torch, rlk, synth, 3, 1)
-    if "fused_bwd" in legs:
-        out_legs["fused_bwd"] = leg_fused_bwd(torch, rlk, synth, 3, 1)
-    main_leg = out_legs.get("logits") or next(iter(out_legs.values()))
+    others = {
+        "support": lambda: leg_support(torch, rlk, synth, args.steps, args.warmup),
+        "sample": lambda: leg_sample(torch, rlk, synth, max(3, args.steps // 4), args.warmup),
+        "fused": lambda: leg_fused(torch, rlk, synth, min(20, max(3, args.steps // 4)), 1),
+        "copy": lambda: leg_copy(torch, args.steps, args.warmup),
+        "grpo": lambda: leg_grpo(torch, rlk, synth, 3, 1),
+        "grpo_train": lambda: leg_grpo_train(torch, rlk, synth, 3, 1),
+        "fused_bwd": lambda: leg_fused_bwd(torch, rlk, synth, 3, 1),
+    }
+    for name, run in others.items():
+        if name not in legs:
+            continue
+        try:
+            out_legs[name] = run()
+        except Exception as e:  # noqa: BLE001 -- the other legs and the headline still report
+            print(f"[bench] leg {name} failed: {type(e).__name__}: {e}", file=sys.stderr,
+                  flush=True)
+            out_legs[name] = {"error": f"{type(e).__name__}: {e}"}
+        torch.cuda.empty_cache()
+    ok_legs = [v for v in out_legs.values() if "error" not in v]
+    if not ok_legs:
+        print(json.dumps({"error": "no leg completed", "legs": out_legs}))
+        sys.exit(1)
+    main_leg = out_legs.get("logits") or ok_legs[0]
     line = {
         "metric": METRIC,
         "value": round(main_leg["tokens_per_s"], 1),
