@@ -334,20 +334,30 @@ RLK_DEV void count_code(uint32_t* hist, uint32_t* special, uint32_t c) {
 
 // Eight bf16 patterns (16 bytes). The counter pair at index magnitude & 0x3fff
 // holds the positive pattern in its low half and the negative one in its
-// high half. Bit 14 ^ bit 13 of a magnitude is 1 exactly inside the window;
-// when all eight pass that test (the normal case) they are counted directly.
+// high half. A pattern's magnitude is inside the window exactly when bit 14
+// of (pattern + 0x2000), added in 16 bits, is set; when all eight pass that
+// test (the normal case) they are counted directly, at a few operations per
+// pattern: the counter's byte offset is a mask and a shift, and the
+// increment, 1 or 0x10000 by the sign bit, is the pattern's sign spread over
+// its half (one packed shift for both patterns of a word) plus 1.
+RLK_DEV uint32_t window_bits(uint32_t w) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 t = __builtin_bit_cast(u16x2, w) + u16x2{0x2000, 0x2000};
+  return __builtin_bit_cast(uint32_t, t);
+}
+
 RLK_DEV void count8(uint32_t* hist, uint32_t* special, const uint4& q) {
-  const uint32_t t = (q.x ^ (q.x << 1)) & (q.y ^ (q.y << 1)) & (q.z ^ (q.z << 1)) &
-                     (q.w ^ (q.w << 1));
+  const uint32_t t = window_bits(q.x) & window_bits(q.y) & window_bits(q.z) & window_bits(q.w);
   if ((t & 0x40004000u) == 0x40004000u) {
     char* base = reinterpret_cast<char*>(hist);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    typedef short i16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      atomicAdd(reinterpret_cast<uint32_t*>(base + ((w[k] << 2) & 0xfffcu)),
-                (w[k] & 0x8000u) ? 0x10000u : 1u);
-      atomicAdd(reinterpret_cast<uint32_t*>(base + ((w[k] >> 14) & 0xfffcu)),
-                (w[k] & 0x80000000u) ? 0x10000u : 1u);
+      // both patterns' signs at once: 0 or 0xffff per half
+      const uint32_t sg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, w[k]) >> 15);
+      atomicAdd(reinterpret_cast<uint32_t*>(base + ((w[k] & 0x3fffu) << 2)), (sg & 0xffffu) + 1u);
+      atomicAdd(reinterpret_cast<uint32_t*>(base + (((w[k] >> 16) & 0x3fffu) << 2)), (sg >> 16) + 1u);
     }
   } else {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -403,10 +413,12 @@ RLK_DEV MassScale mass_scale(double invT) {
   return k;
 }
 
+// The hardware exp2 is used as is: below 2^-126 a mass is far under the
+// resolution of the fp64 sums it enters (each row's max contributes 1).
 RLK_DEV float code_mass(float dv, MassScale k) {
   const float xh = dv * k.c_hi;
   const float r = fmaf(dv, k.c_hi, -xh) + dv * k.c_lo;
-  const float e = exp2f(xh);
+  const float e = __builtin_amdgcn_exp2f(xh);
   return fmaf(e, r * 0.69314718f, e);
 }
 
@@ -427,6 +439,10 @@ struct FinScratch {
 
 template <int FW>
 RLK_DEV void fsync(unsigned int* bar, unsigned int& epoch) {
+  if constexpr (FW == kHT / kWave) {   // the whole block: the hardware barrier
+    __syncthreads();
+    return;
+  }
   epoch += FW;
   if ((threadIdx.x & (kWave - 1)) == 0)
     __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -441,7 +457,10 @@ template <int FW>
 RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t* special,
                         FinScratch& fs, unsigned int& epoch) {
   constexpr int FT = FW * kWave;                  // finisher threads: the last FT of the block
-  const int ft = int(threadIdx.x) - (kHT - FT);    // 0 .. FT-1
+  int ft = int(threadIdx.x) - (kHT - FT);          // 0 .. FT-1
+  // an opaque copy per row: otherwise the compiler hoists every per-thread
+  // counter address and magnitude out of the row loop into registers
+  asm volatile("" : "+v"(ft));
   const int lane = ft & (kWave - 1), fw = ft / kWave;
   const int64_t V = a.vocab;
   const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.logits) + row * a.row_stride;
@@ -452,38 +471,140 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
   const float p = a.p_row ? a.p_row[row] : a.top_p;
   const int n_zero = int(special[0]), n_neginf = int(special[1]), n_other = int(special[2]);
 
-  // ---- checksum and occupied magnitude range, 4 counters at a time ----
+  // ---- one sweep over the counters in 16-byte groups (4 magnitudes), a
+  //      batch of reads in flight, with a few operations per group (this
+  //      wave shares its SIMD's issue with three streaming waves): occupied
+  //      range, and the groups holding the largest positive and the
+  //      smallest negative magnitude ----
   {
+    constexpr int kPer = kHWords / 4 / FT;            // groups per finisher thread
+    constexpr int kBatch = kPer < 8 ? kPer : 8;
+    // group q = ft + k*FT covers counters 4q..4q+3; counters below 0x2000
+    // hold magnitudes 0x4000 above their index (the window's rotation), and
+    // 0x2000 is a multiple of 4*FT, so the shift depends on k alone
+    static_assert(0x2000 % (4 * FT) == 0, "rotation boundary on a k boundary");
     const uint4* h4 = reinterpret_cast<const uint4*>(hist);
-    uint32_t t_acc = 0;
-    int tmin = 0x7fff, tmax = -1;
-#pragma unroll 4
-    for (int k = 0; k < kHWords / 4 / FT; ++k) {
-      const int q = ft + k * FT;
-      const uint4 x = h4[q];
-      t_acc = __builtin_amdgcn_sad_u16(x.x, 0u, t_acc);
-      t_acc = __builtin_amdgcn_sad_u16(x.y, 0u, t_acc);
-      t_acc = __builtin_amdgcn_sad_u16(x.z, 0u, t_acc);
-      t_acc = __builtin_amdgcn_sad_u16(x.w, 0u, t_acc);
-      if (x.x | x.y | x.z | x.w) {
-        const int m0 = wmag(4 * q);
-        tmin = min(tmin, m0);
-        tmax = max(tmax, m0 + 3);
+    int tmin = 0x7fff, tmax = -1, pg = -1, ng_ = 0x8000;
+#pragma unroll
+    for (int k0 = 0; k0 < kPer; k0 += kBatch) {
+      uint4 x[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) x[u] = h4[ft + (k0 + u) * FT];
+      __builtin_amdgcn_sched_barrier(0);   // every read issued before the first use
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int k = k0 + u;
+        const int m0 = 4 * ft + 4 * k * FT + (4 * k * FT < 0x2000 ? 0x4000 : 0);
+        const uint32_t o = x[u].x | x[u].y | x[u].z | x[u].w;
+        tmin = min(tmin, o ? m0 : 0x7fff);
+        tmax = max(tmax, o ? m0 + 3 : -1);
+        pg = max(pg, (o & 0xffffu) ? m0 : -1);
+        ng_ = min(ng_, (o >> 16) ? m0 : 0x8000);
       }
     }
-    const int t_w = wave_total(int(t_acc));
-    const int mn_w = wave_min_i32(tmin);
-    const int mx_w = wave_max_i32(tmax);
+    // the exact magnitudes inside this thread's two groups
+    int pmax = -1, nmin = 0x8000;
+    {
+      const uint4 xp = h4[widx(pg >= 0 ? pg : 0x4000) >> 2];
+      const uint4 xn = h4[widx(ng_ < 0x8000 ? ng_ : 0x4000) >> 2];
+      if (pg >= 0)
+        pmax = pg + ((xp.w & 0xffffu) ? 3 : (xp.z & 0xffffu) ? 2 : (xp.y & 0xffffu) ? 1 : 0);
+      if (ng_ < 0x8000)
+        nmin = ng_ + ((xn.x >> 16) ? 0 : (xn.y >> 16) ? 1 : (xn.z >> 16) ? 2 : 3);
+    }
+    const int mn_w = wave_min_i32(tmin), mx_w = wave_max_i32(tmax);
+    const int pm_w = wave_max_i32(pmax), nm_w = wave_min_i32(nmin);
     if (lane == 0) {
-      fs.i[0][fw] = t_w;
       fs.i[1][fw] = mn_w;
       fs.i[2][fw] = mx_w;
+      fs.i[3][fw] = pm_w;
+      fs.i[4][fw] = nm_w;
+    }
+  }
+  fsync<FW>(&fs.bar, epoch);
+  const int wmin = wave_min_i32(lane < FW ? fs.i[1][lane] : 0x7fff);
+  const int wmax = wave_max_i32(lane < FW ? fs.i[2][lane] : -1);
+  const int maxpos = wave_max_i32(lane < FW ? fs.i[3][lane] : -1);
+  const int minneg = wave_min_i32(lane < FW ? fs.i[4][lane] : 0x8000);
+  // the occupied range as 4-aligned groups of magnitudes: group g holds
+  // magnitudes g0 + 4g .. g0 + 4g + 3, one 16-byte read (the rotation keeps
+  // such a group contiguous)
+  const int g0 = wmin & ~3;
+  const int ng = ((wmax | 3) - g0 + 1) >> 2;   // <= 0 when nothing was counted
+
+  // largest value: highest magnitude with a positive pattern; else zero;
+  // else the negative pattern of smallest magnitude
+  float mval;
+  int kmax;
+  if (maxpos >= 0) {
+    mval = bf16_to_f32(uint16_t(maxpos));
+    kmax = 0x8000 + maxpos;
+  } else if (n_zero > 0) {
+    mval = 0.f;
+    kmax = 0x8000;
+  } else {
+    mval = bf16_to_f32(uint16_t(0x8000 | minneg));
+    kmax = 0x7fff - minneg;
+  }
+  const double invT = 1.0 / double(T);
+  const float invTf = float(invT);
+  const MassScale ks = mass_scale(invT);
+
+  // ---- over the occupied groups, 2 in flight (more would spill): the
+  //      checksum of all counts, and Z and sum e*d over the distinct values
+  //      (formed for every row; used only when the row is live) ----
+  {
+    uint32_t t_acc = 0;
+    double zt = 0.0, st = 0.0;
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist);
+    for (int gb = 0; gb < ng; gb += 2 * FT) {
+      uint4 x[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int g = gb + ft + u * FT;
+        x[u] = g < ng ? h4[widx(g0 + 4 * g) >> 2] : make_uint4(0u, 0u, 0u, 0u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int m0 = g0 + 4 * (gb + ft + u * FT);
+        const uint32_t c[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          t_acc = __builtin_amdgcn_sad_u16(c[j], 0u, t_acc);
+          const float v = __uint_as_float(uint32_t(m0 + j) << 16);   // the positive value
+#pragma unroll
+          for (int sgn = 0; sgn < 2; ++sgn) {
+            const uint32_t n = sgn ? (c[j] >> 16) : (c[j] & 0xffffu);
+            // v - max, clamped to <= 0: a value above the max is absent from
+            // the row (n = 0), and the clamp keeps its mass finite so that it
+            // contributes exactly 0; present values are unchanged
+            const float dv = fminf((sgn ? -v : v) - mval, 0.f);
+            const float e = code_mass(dv, ks) * float(n);
+            zt += double(e);
+            st += double(e) * double(dv * invTf);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one group's arithmetic at a time
+      }
+    }
+    if (ft == 0 && n_zero > 0) {   // the +-0 group
+      const float dv = -mval;
+      const float e = code_mass(dv, ks) * float(n_zero);
+      zt += double(e);
+      st += double(e) * double(dv * invTf);
+    }
+    const int t_w = wave_total(int(t_acc));
+    zt = wave_total(zt);
+    st = wave_total(st);
+    if (lane == 0) {
+      fs.i[0][fw] = t_w;
+      fs.d[0][fw] = zt;
+      fs.d[1][fw] = st;
     }
   }
   fsync<FW>(&fs.bar, epoch);
   const int tot = fold_partials(fs.i[0], FW);
-  const int wmin = wave_min_i32(lane < FW ? fs.i[1][lane] : 0x7fff);
-  const int wmax = wave_max_i32(lane < FW ? fs.i[2][lane] : -1);
 
   uint8_t flags = 0;
   if (!y_ok) flags |= kBadTarget;
@@ -499,75 +620,6 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
   }
 
   if (live) {
-    // largest value: highest magnitude with a positive pattern; else zero;
-    // else the negative pattern of smallest magnitude
-    int maxpos = -1, minneg = 0x8000;
-    for (int m0 = wmax; m0 >= wmin && maxpos < 0; m0 -= FT) {
-      const int m = m0 - ft;
-      const bool hit = m >= wmin && (hist[widx(m >= wmin ? m : wmin)] & 0xffffu);
-      const uint64_t bal = __ballot(hit);
-      if (lane == 0) fs.i[3][fw] = bal ? m0 - fw * kWave - (__ffsll((unsigned long long)bal) - 1) : -1;
-      fsync<FW>(&fs.bar, epoch);
-      maxpos = wave_max_i32(lane < FW ? fs.i[3][lane] : -1);
-      fsync<FW>(&fs.bar, epoch);
-    }
-    for (int m0 = wmin; m0 <= wmax && maxpos < 0 && n_zero == 0 && minneg == 0x8000; m0 += FT) {
-      const int m = m0 + ft;
-      const bool hit = m <= wmax && (hist[widx(m <= wmax ? m : wmax)] >> 16);
-      const uint64_t bal = __ballot(hit);
-      if (lane == 0) fs.i[4][fw] = bal ? m0 + fw * kWave + (__ffsll((unsigned long long)bal) - 1) : 0x8000;
-      fsync<FW>(&fs.bar, epoch);
-      minneg = wave_min_i32(lane < FW ? fs.i[4][lane] : 0x8000);
-      fsync<FW>(&fs.bar, epoch);
-    }
-    float mval;
-    int kmax;
-    if (maxpos >= 0) {
-      mval = bf16_to_f32(uint16_t(maxpos));
-      kmax = 0x8000 + maxpos;
-    } else if (n_zero > 0) {
-      mval = 0.f;
-      kmax = 0x8000;
-    } else {
-      mval = bf16_to_f32(uint16_t(0x8000 | minneg));
-      kmax = 0x7fff - minneg;
-    }
-    const double invT = 1.0 / double(T);
-    const float invTf = float(invT);
-    const MassScale ks = mass_scale(invT);
-
-    // ---- Z and sum e*d over the distinct values ----
-    {
-      double zt = 0.0, st = 0.0;
-      for (int m = wmin + ft; m <= wmax; m += FT) {
-        const uint32_t x = hist[widx(m)];
-        if (x & 0xffffu) {
-          const float dv = bf16_to_f32(uint16_t(m)) - mval;
-          const float e = code_mass(dv, ks) * float(x & 0xffffu);
-          zt += double(e);
-          st += double(e) * double(dv * invTf);
-        }
-        if (x >> 16) {
-          const float dv = bf16_to_f32(uint16_t(0x8000 | m)) - mval;
-          const float e = code_mass(dv, ks) * float(x >> 16);
-          zt += double(e);
-          st += double(e) * double(dv * invTf);
-        }
-      }
-      if (ft == 0 && n_zero > 0) {   // the +-0 group
-        const float dv = -mval;
-        const float e = code_mass(dv, ks) * float(n_zero);
-        zt += double(e);
-        st += double(e) * double(dv * invTf);
-      }
-      zt = wave_total(zt);
-      st = wave_total(st);
-      if (lane == 0) {
-        fs.d[0][fw] = zt;
-        fs.d[1][fw] = st;
-      }
-    }
-    fsync<FW>(&fs.bar, epoch);
     const double Z = fold_partials(fs.d[0], FW);
     const double S = fold_partials(fs.d[1], FW);
 
@@ -652,10 +704,21 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
       }
     }
 
+    // the two logarithms and quotients on lanes 0 and 1 of the first
+    // finisher wave at once, then the outputs from its lane 0
+    double logZ = 0.0, logZs = 0.0, eZ = 0.0, eZs = 0.0;
+    if (fw == 0) {
+      const bool second = lane == 1;
+      const double lg = log(second ? Zs : Z);
+      const double q = (second ? Ss : S) / (second ? Zs : Z);
+      logZ = readlane_f64(lg, 0);
+      logZs = readlane_f64(lg, 1);
+      eZ = readlane_f64(q, 0);
+      eZs = readlane_f64(q, 1);
+    }
     if (ft == 0) {
-      const double logZ = log(Z), logZs = log(Zs);
-      const float h_full = float(logZ - S / Z);
-      const float h_trunc = float(logZs - Ss / Zs);
+      const float h_full = float(logZ - eZ);
+      const float h_trunc = float(logZs - eZs);
       float lpf = __builtin_nanf(""), lpt = __builtin_nanf("");
       if (y_ok) {
         const float vy = bf16_to_f32(cy);
@@ -686,12 +749,15 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
         a.score_stats[2 * row + 1] = logZs;
       }
       store_row(a, row, lpf, lpt, h_full, h_trunc, size, tau, flags, float(mT + logZs),
-                float(mT + Ss / Zs));
+                float(mT + eZs));
     }
   }
 
   // ---- release the buffer: every nonzero counter lies in [wmin, wmax] ----
-  for (int m = wmin + ft; m <= wmax; m += FT) hist[widx(m)] = 0;
+  {
+    uint4* h4 = reinterpret_cast<uint4*>(hist);
+    for (int g = ft; g < ng; g += FT) h4[widx(g0 + 4 * g) >> 2] = make_uint4(0u, 0u, 0u, 0u);
+  }
   if (ft == 0) special[0] = special[1] = special[2] = 0;
 }
 
@@ -730,10 +796,10 @@ RLK_DEV void stream_row(const RowArgs& a, int64_t row, int64_t nvec, uint32_t* h
 }
 
 // One persistent block per CU; block b takes rows b, b + G, b + 2G, ...
-// (G = gridDim.x). The first row is streamed by all 16 waves. Then, step s:
-// waves 0..kStreamWaves-1 stream row R_s into counter buffer s & 1 while the
-// finisher waves post-process row R_{s-1} from the other buffer, one block
-// barrier between steps; the last row is post-processed by all 16 waves.
+// (G = gridDim.x). Step s: waves 0..kStreamWaves-1 stream row R_s into
+// counter buffer s & 1 while (from step 1 on) the finisher waves
+// post-process row R_{s-1} from the other buffer, one block barrier between
+// steps; the last row is post-processed by all 16 waves.
 // Rows the finishers hand on (see finish_row) are then redone by the whole
 // block with the generic algorithm, in the same launch.
 template <bool kVec>
@@ -759,15 +825,21 @@ __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
   __syncthreads();
 
   int64_t prev = blockIdx.x;   // the row in the buffer the finishers read next
-  if (prev < N) stream_row<kVec, kHT>(a, prev, nvec, hist[0], special[0]);
+  // the first row by the streaming waves alone (all 16 waves measured slower)
+  if (prev < N && wid < kStreamWaves) stream_row<kVec, kStreamers>(a, prev, nvec, hist[0], special[0]);
   __syncthreads();
   int s = 1;
   for (int64_t cur = prev + G; cur < N; cur += G, ++s) {
     const int b = s & 1;
-    if (wid < kStreamWaves)
-      stream_row<kVec, kStreamers>(a, cur, nvec, hist[b], special[b]);
-    else
+    if (wid < kStreamWaves) {
+      // one copy per buffer, so that its LDS base is a constant
+      if (b)
+        stream_row<kVec, kStreamers>(a, cur, nvec, hist[1], special[1]);
+      else
+        stream_row<kVec, kStreamers>(a, cur, nvec, hist[0], special[0]);
+    } else {
       finish_row<kFW>(a, prev, hist[b ^ 1], special[b ^ 1], fs, epoch);
+    }
     __syncthreads();
     prev = cur;
   }
