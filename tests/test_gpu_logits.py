@@ -156,6 +156,42 @@ def test_edge_rows(dtype, V, T, p):
     check(g, o, **(F32_TOL if dtype == "f32" else BF16_TOL))
 
 
+def _window_edge_rows(V):
+    """bf16 rows (as 16-bit codes) aimed at the counting kernel's index
+    arithmetic: the counters hold magnitudes 0x2000..0x5fff, stored rotated
+    (0x4000..0x5fff first), and the row max is located per 16-byte group of
+    four magnitudes before the exact one is picked inside the group."""
+    rng = np.random.default_rng(2024)
+    base = synth.bf16_bits_from_f32(rng.normal(0, 2.5, V).astype(np.float32))
+    rows, tg = [], []
+    # all negative, no zero: the max is the negative value of smallest magnitude
+    r = base | np.uint16(0x8000); r[r == 0x8000] = 0xBF80; rows.append(r); tg.append(int(np.argmin(r & 0x7FFF)))
+    # only magnitudes around the rotation seam (|z| near 2), both signs
+    r = rng.choice(np.arange(0x3FFC, 0x4004, dtype=np.uint16), V); r[rng.random(V) < 0.5] |= 0x8000
+    rows.append(r); tg.append(int(np.argmax(np.where(r & 0x8000, 0, r))))
+    # the largest counted magnitude present (|z| about 3.7e19), once and negated
+    r = base.copy(); r[[10, 11]] = [0x5FFF, 0xDFFE]; rows.append(r); tg.append(10)
+    # the smallest counted magnitudes (|z| about 1e-19) mixed in
+    r = base.copy(); r[rng.choice(V, 64, replace=False)] = rng.choice(
+        np.array([0x2000, 0x2001, 0x2003, 0xA000, 0xA002], dtype=np.uint16), 64); rows.append(r); tg.append(5)
+    # max group holding several present magnitudes: 1.0 .. 1.0234375 (codes 0x3F80..0x3F83)
+    r = np.full(V, 0xBF80, np.uint16); r[:8] = [0x3F80, 0x3F81, 0x3F82, 0x3F83, 0x3F81, 0x3F80, 0x3F7F, 0x3F7C]
+    rows.append(r); tg.append(3)
+    # negatives only, smallest magnitudes inside one group: -0.5 .. -0.50390625 (0xBF00..0xBF01)
+    r = np.full(V, 0xC000, np.uint16); r[[3, 4, 5]] = [0xBF01, 0xBF00, 0xBF02]; rows.append(r); tg.append(4)
+    return np.stack(rows), np.array(tg, dtype=np.int64)
+
+
+@pytest.mark.parametrize("V", [151936, 20000])
+@pytest.mark.parametrize("T,p", [(0.7, 0.95), (1.0, 1.0), (1.3, 0.5)])
+def test_bf16_counter_window_edges(V, T, p):
+    arr, y = _window_edge_rows(V)
+    zz = widen(arr, "bf16")
+    o = OL.logprob_from_logits(zz, y, OL.f32(T), OL.f32(p))
+    g = run(arr, "bf16", y, T, p)
+    check(g, o, **BF16_TOL)
+
+
 @pytest.mark.parametrize("T,p", [(0.7, 0.95), (1.0, 1.0), (0.7, 0.3)])
 def test_special_values_in_realistic_rows(T, p):
     """Zeros, -0, -inf (vocabulary masking), tiny and huge magnitudes mixed
