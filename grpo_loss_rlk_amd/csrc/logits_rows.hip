@@ -435,6 +435,7 @@ struct FinScratch {
   double bd[3];
   int bi[2];
   unsigned int bar;
+  unsigned int handed_on;   // nonzero once any row of the block is handed on
 };
 
 template <int FW>
@@ -616,6 +617,7 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
   const bool live = !handoff && !(flags & (kBadParam | kNonFinite));
   if (ft == 0) {
     a.fallback[row] = handoff ? 1 : 0;
+    if (handoff) fs.handed_on = 1u;
     if (!handoff && !live) store_nan_row(a, row, flags);
   }
 
@@ -820,7 +822,10 @@ __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
     for (int i = tid; i < 2 * kHWords / 4; i += kHT) h4[i] = make_uint4(0, 0, 0, 0);
   }
   if (tid < 8) special[tid >> 2][tid & 3] = 0;
-  if (tid == 0) fs.bar = 0;
+  if (tid == 0) {
+    fs.bar = 0;
+    fs.handed_on = 0;
+  }
   unsigned int epoch = 0;
   __syncthreads();
 
@@ -849,7 +854,10 @@ __global__ __launch_bounds__(kHT) void bf16_hist_rows(RowArgs a) {
     __syncthreads();
   }
   // rows handed on by this block's finishers (flags written before the last
-  // barrier), redone with the counters' LDS as scratch
+  // barrier), redone with the counters' LDS as scratch; the block-local mark
+  // skips the scan of the flags (one dependent global read per row) in the
+  // normal case, where none was handed on
+  if (fs.handed_on == 0u) return;
   GenScratch& gs = *reinterpret_cast<GenScratch*>(&hist[0][0]);
   for (int64_t row = blockIdx.x; row < N; row += gridDim.x) {
     if (a.fallback[row]) {
