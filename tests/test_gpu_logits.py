@@ -222,6 +222,32 @@ def test_special_values_in_realistic_rows(T, p):
     check(g, o, **BF16_TOL)
 
 
+def test_hand_off_from_every_finisher_path():
+    """More rows than blocks, so a block post-processes rows both with its
+    finisher waves (while the next row streams) and with the whole block
+    (its last row). Rows the counting kernel must hand to the generic
+    algorithm — a NaN, a +inf, a magnitude above the counted window, and a
+    value present more than 65535 times (its 16-bit counter wraps, caught by
+    the checksum of all counts) — sit on both paths and on a block's only
+    row; every row must match the oracle."""
+    w = synth.workload("qwen")
+    N, G = 300, 256                       # blocks 0..43 take two rows: b and b + 256
+    rows = synth.logits_rows(w, range(N))
+    y = synth.peak_targets(w, range(N))
+    rows[3, 17] = 0x7FC0                  # NaN, finisher waves (block 3, first of two rows)
+    rows[259, 5] = 0x7F80                 # +inf, whole block (block 3, last row)
+    rows[100, 9] = 0x6010                 # above the window, a block's only row
+    rows[10, :70000] = 0x3F80             # 70000 copies of 1.0, finisher waves (block 10)
+    rows[266, :66000] = 0xBF80            # 66000 copies of -1.0, whole block (block 10)
+    y[10] = 3
+    y[266] = 70000
+    zz = widen(rows, "bf16")
+    o = OL.logprob_from_logits(zz, y, OL.f32(0.7), OL.f32(0.95))
+    g = run(rows, "bf16", y, 0.7, 0.95)
+    check(g, o, **BF16_TOL)
+    assert G < N < 2 * G
+
+
 def test_per_row_temperature_and_top_p():
     w = synth.workload("qwen", V=32768)
     N = 16
