@@ -11,7 +11,9 @@ plain reading used here, for response j in group g (consecutive blocks of
 ``group_size`` responses) and token t of response j:
 
   advantages   A_j  = (r_j - mean_g r) / (std_g r + adv_eps)   (std with ``ddof``;
-                      without std normalisation A_j = r_j - mean_g r)
+                      without std normalisation A_j = r_j - mean_g r);
+                      A_j = 0 for every response of a group whose rewards
+                      are all equal (a constant group gives A = 0)
   ratio        rho_t = exp(lp_new_t - lp_old_t)
   TIS          rho~_t = min(rho_t, C)
   surrogate    s_t  = min(rho~_t A_j, clip(rho~_t, 1 - eps_low, 1 + eps_high) A_j)
@@ -108,7 +110,13 @@ def advantages(rewards, group_size: int, prm: Params = Params(), lengths=None) -
     a = r - b
     if prm.normalize_std:
         sd = np.sqrt(((r - mu) ** 2).sum(axis=1, keepdims=True) / (group_size - prm.std_ddof))
-        a = a / (sd + prm.adv_eps)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            a = a / (sd + prm.adv_eps)
+    # a group whose rewards are all equal carries no signal: its advantages are
+    # exactly 0 (its std and every r_j - baseline vanish), also with adv_eps = 0
+    # where the quotient above would be 0/0
+    const = (r == r[:, :1]).all(axis=1, keepdims=True)
+    a = np.where(const, 0.0, a)
     return a.reshape(-1)
 
 

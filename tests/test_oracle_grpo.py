@@ -25,6 +25,27 @@ def test_bernoulli_group_closed_form():
         assert np.all(grpo.advantages(np.full(8, c), 8) == 0.0)
 
 
+@pytest.mark.parametrize("c", [0.0, 1.0, 0.1, -3.7])
+@pytest.mark.parametrize("prm", [grpo.Params(adv_eps=0.0), grpo.Params(),
+                                 grpo.Params(adv_eps=0.0, std_ddof=0),
+                                 grpo.Params(normalize_std=False),
+                                 grpo.Params(adv_eps=0.0, baseline="length")])
+def test_constant_group_is_zero_in_every_mode(c, prm):
+    """A constant group's advantages are exactly 0, also with adv_eps = 0
+    (no 0/0), with a length-weighted baseline (no rounding residue) and beside
+    a group that does vary; the loss of such a batch stays finite."""
+    r = np.concatenate([np.full(8, c), [1, 0, 0, 1, 1, 0, 1, 1]]).astype(np.float32)
+    lengths = np.arange(3, 19)
+    A = grpo.advantages(r, 8, prm, lengths=lengths)
+    assert np.all(A[:8] == 0.0) and np.all(np.isfinite(A))
+    assert np.all(A[8:] != 0.0)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    lp = np.linspace(-3, -0.1, cu[-1])
+    out = grpo.token_loss(lp, lp - 0.01, lp, cu, A, prm)
+    assert np.isfinite(out.loss) and np.all(np.isfinite(out.grad))
+    assert np.all(out.grad[:cu[8]] == 0.0)     # rho != 1 but A = 0 and k3' = 0 at ref = new
+
+
 def test_on_policy_identity():
     rng = np.random.default_rng(1)
     lengths = rng.integers(1, 30, size=16)

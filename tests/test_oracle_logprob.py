@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import scipy.special
 import scipy.stats
+import torch
 
 from oracle import logprob as L
 from oracle import sampling
@@ -252,3 +253,94 @@ def test_gumbel_target_in_nucleus_and_distribution():
         counts[y] += 1
     sd = np.sqrt(draws * q * (1 - q)) + 1e-9
     assert np.all(np.abs(counts - draws * q) <= 5 * sd)
+
+
+# ------------------------------------------------- input widening (bf16 -> fp64)
+
+def test_widen_bf16_all_patterns_match_torch():
+    """Every one of the 65536 bf16 bit patterns widens to the value torch's own
+    bf16 -> fp32 conversion gives (fp32 -> fp64 is exact), NaNs to NaNs."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = L.widen_bf16(bits)
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32)
+    theirs = t.numpy().astype(np.float64)
+    nan = np.isnan(theirs)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert nan.sum() == 2 * 127                       # exponent all ones, mantissa != 0
+    np.testing.assert_array_equal(ours[~nan], theirs[~nan])
+    # the sign of zero survives
+    assert math.copysign(1.0, ours[0x8000]) == -1.0 and math.copysign(1.0, ours[0]) == 1.0
+
+
+@pytest.mark.parametrize("bits,value", [
+    (0x3F80, 1.0), (0xBF80, -1.0), (0x4000, 2.0), (0x3F00, 0.5),
+    (0x4049, 3.140625),                       # sign 0, exponent 128, mantissa 0x49
+    (0x3F81, 1.0 + 2.0 ** -7),                # one unit of the 7-bit mantissa
+    (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127),  # the largest finite bf16
+    (0x0080, 2.0 ** -126),                    # the smallest normal
+    (0x0001, 2.0 ** -133),                    # the smallest subnormal
+    (0x7F80, math.inf), (0xFF80, -math.inf),
+])
+def test_widen_bf16_known_values(bits, value):
+    # the values follow from the format alone: 1 sign, 8 exponent (bias 127)
+    # and 7 mantissa bits, subnormals at exponent 0
+    assert L.widen_bf16(np.array([bits], dtype=np.uint16))[0] == value
+
+
+# ------------------------------------------------------ the batch wrapper
+
+def test_batch_per_row_parameters_match_single_rows():
+    """Per-row T and p arrays reach each row: the batch equals the rows one by
+    one, and a row with (T, p) = (1, 1) gives scipy's log-softmax."""
+    rng = np.random.default_rng(21)
+    N, V = 12, 300
+    z = rng.normal(0, 2, (N, V))
+    z[3] = np.round(z[3] * 4) / 4                      # a tie-heavy row
+    y = rng.integers(0, V, N)
+    Ts = rng.choice(TEMPS, N)
+    ps = rng.choice([0.3, 0.9, 0.95, 1.0], N)
+    Ts[5], ps[5] = 1.0, 1.0
+    b = L.logprob_from_logits(z, y, Ts, ps)
+    for n in range(N):
+        r = L.row(z[n], int(y[n]), float(Ts[n]), float(ps[n]))
+        for got, want in ((b.lp_full[n], r.lp_full), (b.h_full[n], r.h_full),
+                          (b.lp_trunc[n], r.lp_trunc), (b.h_trunc[n], r.h_trunc),
+                          (b.tau[n], r.tau)):
+            assert got == want or (math.isnan(got) and math.isnan(want))
+        assert b.size[n] == r.size and b.flags[n] == r.flags
+    ls = scipy.special.log_softmax(z[5])
+    assert b.lp_full[5] == pytest.approx(ls[y[5]], rel=1e-12, abs=1e-12)
+    assert b.lp_trunc[5] == pytest.approx(ls[y[5]], rel=1e-12, abs=1e-12)
+    # scalar parameters broadcast to every row
+    s = L.logprob_from_logits(z, y, 0.7, 0.95)
+    assert np.array_equal(s.size, [L.row(z[n], int(y[n]), 0.7, 0.95).size for n in range(N)])
+
+
+def test_batch_boundary_alternatives_are_the_other_valid_sets():
+    """A boundary row's alternative tuples hold the statistics of the other
+    valid nucleus, checked against closed forms of an equal-logit group."""
+    # masses (T = 1): a group of 2 equal tokens with 0.25 each, then 5 equal
+    # tokens with 0.1 each. p = 0.5 exactly equals the top group's mass, so
+    # keeping the top group (|S| = 2) and keeping everything (|S| = 7) are
+    # both valid within the boundary tolerance.
+    z = np.log(np.array([0.25, 0.25, 0.1, 0.1, 0.1, 0.1, 0.1]))
+    y = np.array([0, 4])
+    b = L.logprob_from_logits(np.stack([z, z]), y, 1.0, 0.5)
+    for n in range(2):
+        assert b.flags[n] & L.FLAG_BOUNDARY
+        sets = {b.size[n]: (b.lp_trunc[n], b.h_trunc[n])}
+        for alt in b.alts[n]:
+            sets[alt[0]] = alt[1:]
+        assert sorted(sets) == [2, 7]
+        # |S| = 2: uniform over the top pair; token 4 is outside it
+        lp2, h2 = sets[2]
+        assert h2 == pytest.approx(math.log(2), abs=1e-14)
+        assert (lp2 == pytest.approx(-math.log(2), abs=1e-14)) if n == 0 else lp2 == -math.inf
+        # |S| = 7: the whole row, masses 0.25 x2 and 0.1 x5
+        lp7, h7 = sets[7]
+        assert lp7 == pytest.approx(math.log(0.25 if n == 0 else 0.1), abs=1e-14)
+        assert h7 == pytest.approx(-(2 * 0.25 * math.log(0.25) + 5 * 0.1 * math.log(0.1)),
+                                   abs=1e-14)
+    # a row away from the boundary has no alternatives
+    far = L.logprob_from_logits(z[None, :], y[:1], 1.0, 0.6)
+    assert far.alts[0] == [] and not far.flags[0] & L.FLAG_BOUNDARY
