@@ -461,7 +461,7 @@ def _grpo_inputs(torch, rlk, synth):
     lp0 = rlk.logprob_fused_linear(h, W, yt, w.temperature, w.top_p)["logprob"]
     n_old, n_ref = synth.logprob_noise(w, T_tot)
     _GRPO_INPUTS.update(
-        w=w, cu=cu, T_tot=T_tot, h=h, W=W, yt=yt,
+        w=w, cu=cu, cu_dev=torch.from_numpy(cu).to("cuda:0"), T_tot=T_tot, h=h, W=W, yt=yt,
         lp_old=(lp0 + torch.from_numpy(n_old).to(lp0)).contiguous(),
         lp_ref=(lp0 + torch.from_numpy(n_ref).to(lp0)).contiguous(),
         rw=torch.from_numpy(synth.rewards(w)).to("cuda:0"))
@@ -476,7 +476,7 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
 
     def step():
         out = rlk.logprob_fused_linear(g["h"], g["W"], g["yt"], w.temperature, w.top_p)
-        return rlk.grpo_token_loss(out["logprob"], g["lp_old"], g["lp_ref"], g["cu"],
+        return rlk.grpo_token_loss(out["logprob"], g["lp_old"], g["lp_ref"], g["cu_dev"],
                                    rewards=g["rw"], group_size=w.group_size)
 
     mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
@@ -532,7 +532,7 @@ def leg_grpo_train(torch, rlk, synth, steps, warmup):
 
     def step():
         out = rlk.logprob_fused_linear(g["h"], g["W"], g["yt"], w.temperature, w.top_p)
-        loss = rlk.grpo_token_loss(out["logprob"], g["lp_old"], g["lp_ref"], g["cu"],
+        loss = rlk.grpo_token_loss(out["logprob"], g["lp_old"], g["lp_ref"], g["cu_dev"],
                                    rewards=g["rw"], group_size=w.group_size)
         return rlk.logprob_fused_linear_bwd(g["h"], g["W"], g["yt"], out["saved"], loss["grad"],
                                             None, w.temperature, w.top_p)

@@ -236,18 +236,29 @@ def grpo_token_loss(lp_new: torch.Tensor, lp_old: torch.Tensor, lp_ref, cu_seqle
                     filter_zero_adv: bool = False, baseline: str = "mean",
                     ipo_eps: float = 0.3, icepop_lo: float = 0.5,
                     icepop_hi: float = 2.0) -> dict:
-    """GRPO/DAPO token loss over packed responses (``cu_seqlens`` on the host).
+    """GRPO/DAPO token loss over packed responses.
 
+    ``cu_seqlens`` [B + 1] int64 offsets: a device tensor is passed as it is
+    (nothing is read on the host, so the call can be captured in a graph);
+    a host array or tensor is copied to the device first. The token count is
+    ``lp_new.numel()``; offsets that do not run from 0 to it, non-decreasing,
+    give NaN outputs and ``status`` = 1 (checked on the device).
     loss_type: dapo | ipo | icepop | cispo | tis_pg; correction: tis | mis;
     aggregation: token_mean | prompt_mean; baseline: mean | length.
     Returns loss (device scalar), grad (dL/dlp_new), token_loss, token_flags,
-    metrics [clipped/masked frac, TIS frac, mean k3, mean ratio], advantages.
+    metrics [clipped/masked frac, TIS frac, mean k3, mean ratio], advantages,
+    status (device int32).
     """
-    cu = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if torch.is_tensor(cu_seqlens)
-                                         else cu_seqlens, dtype=np.int64))
-    B = cu.size - 1
-    T = int(cu[-1]) if B >= 0 else 0
     dev = lp_new.device
+    if torch.is_tensor(cu_seqlens) and cu_seqlens.device == dev:
+        cu = cu_seqlens
+        if cu.dtype != torch.int64 or not cu.is_contiguous():
+            raise ValueError("a device cu_seqlens must be a contiguous int64 tensor")
+    else:
+        host = cu_seqlens.cpu() if torch.is_tensor(cu_seqlens) else cu_seqlens
+        cu = torch.from_numpy(np.ascontiguousarray(np.asarray(host, dtype=np.int64))).to(dev)
+    B = cu.numel() - 1
+    T = lp_new.numel()
     lp_new = lp_new.to(torch.float32).contiguous()
     lp_old = lp_old.to(torch.float32).contiguous()
     lp_ref = None if lp_ref is None else lp_ref.to(torch.float32).contiguous()
@@ -257,7 +268,8 @@ def grpo_token_loss(lp_new: torch.Tensor, lp_old: torch.Tensor, lp_ref, cu_seqle
     out = {"loss": torch.empty((), **f), "grad": torch.empty(T, **f),
            "token_loss": torch.empty(T, **f),
            "token_flags": torch.empty(T, device=dev, dtype=torch.uint8),
-           "metrics": torch.empty(4, **f), "advantages": torch.empty(B, **f)}
+           "metrics": torch.empty(4, **f), "advantages": torch.empty(max(B, 0), **f),
+           "status": torch.empty((), device=dev, dtype=torch.int32)}
     prm = _native.GrpoParams(ctypes.sizeof(_native.GrpoParams), tis_cap, eps_low, eps_high,
                              kl_coef, adv_eps, std_ddof, int(bool(normalize_std)),
                              _native.LOSS_TYPES[loss_type], _native.CORRECTIONS[correction],
@@ -267,9 +279,9 @@ def grpo_token_loss(lp_new: torch.Tensor, lp_old: torch.Tensor, lp_ref, cu_seqle
     ws_n = L.rlk_grpo_token_loss_workspace_size(T, B)
     ws = _workspace(ws_n, dev)
     st = L.rlk_grpo_token_loss(
-        _ptr(lp_new), _ptr(lp_old), _ptr(lp_ref), cu.ctypes.data_as(ctypes.c_void_p), B,
+        _ptr(lp_new), _ptr(lp_old), _ptr(lp_ref), _ptr(cu), B, T,
         _ptr(rw), _ptr(ad), int(group_size), ctypes.byref(prm), _ptr(out["loss"]),
         _ptr(out["grad"]), _ptr(out["token_loss"]), _ptr(out["token_flags"]), _ptr(out["metrics"]),
-        _ptr(out["advantages"]), _ptr(ws), ws_n, _stream(dev))
+        _ptr(out["advantages"]), _ptr(out["status"]), _ptr(ws), ws_n, _stream(dev))
     _native.check(st, "rlk_grpo_token_loss")
     return out

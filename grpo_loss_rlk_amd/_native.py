@@ -62,8 +62,8 @@ SIGNATURES = {
         c_f32, c_f32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "rlk_grpo_token_loss_workspace_size": (c_sz, [c_i64, c_i64]),
     "rlk_grpo_token_loss": (c_i32, [
-        c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, ctypes.POINTER(GrpoParams),
-        c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+        c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i32, ctypes.POINTER(GrpoParams),
+        c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
 }
 
 _lib = None

@@ -68,7 +68,7 @@ constexpr int64_t kMaxFusedRows = int64_t(1) << 23;
 
 extern "C" {
 
-int32_t rlk_abi_version(void) { return 1; }
+int32_t rlk_abi_version(void) { return 2; }
 
 const char* rlk_status_str(rlk_status s) {
   switch (s) {
@@ -459,12 +459,12 @@ size_t rlk_grpo_token_loss_workspace_size(int64_t n_tokens, int64_t n_seqs) {
 }
 
 rlk_status rlk_grpo_token_loss(const float* lp_new, const float* lp_old, const float* lp_ref,
-                               const int64_t* cu_seqlens_host, int64_t n_seqs,
+                               const int64_t* cu_seqlens, int64_t n_seqs, int64_t n_tokens,
                                const float* rewards, const float* advantages, int32_t group_size,
                                const rlk_grpo_params* params, float* loss, float* grad_lp_new,
                                float* token_loss, uint8_t* token_flags, float* metrics,
-                               float* adv_out, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               float* adv_out, int32_t* status, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (!params) return fail(RLK_EINVAL, "params is NULL");
   // the first layout ends after normalize_std; later fields take their defaults
   constexpr uint32_t kFirstLayout = offsetof(rlk_grpo_params, loss_type);
@@ -505,13 +505,12 @@ rlk_status rlk_grpo_token_loss(const float* lp_new, const float* lp_old, const f
     return fail(RLK_EINVAL, "adv_eps must be finite and >= 0");
   if (p.std_ddof != 0 && p.std_ddof != 1) return fail(RLK_EINVAL, "std_ddof must be 0 or 1");
   if (n_seqs < 1) return fail(RLK_EINVAL, "n_seqs=%lld < 1", (long long)n_seqs);
-  if (!cu_seqlens_host) return fail(RLK_EINVAL, "cu_seqlens_host is NULL");
-  if (cu_seqlens_host[0] != 0) return fail(RLK_EINVAL, "cu_seqlens[0] must be 0");
-  for (int64_t j = 0; j < n_seqs; ++j)
-    if (cu_seqlens_host[j + 1] < cu_seqlens_host[j])
-      return fail(RLK_EINVAL, "cu_seqlens is not non-decreasing at %lld", (long long)j);
-  const int64_t n_tokens = cu_seqlens_host[n_seqs];
-  if (n_tokens > (int64_t(1) << 40)) return fail(RLK_EINVAL, "too many tokens");
+  if (n_seqs > (int64_t(1) << 31)) return fail(RLK_EINVAL, "n_seqs=%lld too large", (long long)n_seqs);
+  if (!cu_seqlens) return fail(RLK_EINVAL, "cu_seqlens is NULL");
+  if (!aligned(cu_seqlens, 8)) return fail(RLK_EINVAL, "cu_seqlens is not 8-byte aligned");
+  if (n_tokens < 0 || n_tokens > (int64_t(1) << 40))
+    return fail(RLK_EINVAL, "n_tokens=%lld outside [0, 2^40]", (long long)n_tokens);
+  if (!aligned(status, 4)) return fail(RLK_EINVAL, "status is not 4-byte aligned");
   if ((rewards == nullptr) == (advantages == nullptr))
     return fail(RLK_EINVAL, "exactly one of rewards / advantages must be given");
   if (rewards || p.aggregation == RLK_AGG_PROMPT_MEAN) {
@@ -541,6 +540,7 @@ rlk_status rlk_grpo_token_loss(const float* lp_new, const float* lp_old, const f
   a.lp_new = lp_new;
   a.lp_old = lp_old;
   a.lp_ref = p.kl_coef != 0.f ? lp_ref : nullptr;
+  a.cu = cu_seqlens;
   a.n_seqs = n_seqs;
   a.n_tokens = n_tokens;
   a.rewards = rewards;
@@ -567,8 +567,8 @@ rlk_status rlk_grpo_token_loss(const float* lp_new, const float* lp_old, const f
   a.token_flags = token_flags;
   a.metrics = metrics;
   a.adv_out = adv_out;
-  return hip_status(rlk::launch_grpo(a, cu_seqlens_host, workspace,
-                                     reinterpret_cast<hipStream_t>(stream)),
+  a.status = status;
+  return hip_status(rlk::launch_grpo(a, workspace, reinterpret_cast<hipStream_t>(stream)),
                     "rlk_grpo_token_loss launch");
 }
 

@@ -18,11 +18,15 @@
 // baseline, zero-advantage filtering and prompt-mean aggregation; the token
 // weights replace 1 / T_tot.
 //
-// Launches: advantages (one thread per group), token weights (one block,
-// fixed order), for MIS the ratio mean (fixed 256-token blocks, then one
-// block), per-token terms (one thread per token, fixed 256-token blocks,
-// per-block fp64 partial sums), and a single-block fixed-order fold. Every
-// split depends only on the sizes, so the loss is bitwise reproducible.
+// Launches: advantages (one thread per group), token weights and the check of
+// cu_seqlens (one block, fixed order), for MIS the ratio mean (fixed
+// 256-token blocks, then one block), per-token terms (one thread per token,
+// fixed 256-token blocks, per-block fp64 partial sums), and a single-block
+// fixed-order fold. Every split depends only on the sizes, so the loss is
+// bitwise reproducible. cu_seqlens is read in device memory only (no host
+// copy), so a call can be captured in a graph; offsets that are not
+// non-decreasing from 0 to n_tokens make every float output NaN and set the
+// status word.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,22 +38,22 @@ constexpr int kTB = 256;
 constexpr int kNMetric = 5;   // sum l, clip count, TIS count, sum k3, sum rho
 
 struct Ws {
-  int64_t* cu;
+  const int64_t* cu;   // the caller's device offsets
   double* adv;
   double* resp_w;    // [n_seqs] token weight of each response
-  double* scal;      // [0] MIS ratio mean, [1] tokens entering the loss
+  double* scal;      // [0] MIS ratio mean, [1] tokens entering the loss,
+                     // [2] 1 when cu_seqlens is valid, else 0
   double* rho_part;  // [n_blocks] MIS partial sums
   double* partial;   // [n_blocks][kNMetric]
 };
 
 size_t slot(size_t bytes) { return (bytes + 255) / 256 * 256; }
 
-Ws carve(void* workspace, int64_t n_tokens, int64_t n_seqs) {
+Ws carve(void* workspace, const int64_t* cu, int64_t n_tokens, int64_t n_seqs) {
   char* p = reinterpret_cast<char*>(workspace);
   const size_t nb = size_t((n_tokens + kTB - 1) / kTB);
   Ws w;
-  w.cu = reinterpret_cast<int64_t*>(p);
-  p += slot(size_t(n_seqs + 1) * 8);
+  w.cu = cu;
   w.adv = reinterpret_cast<double*>(p);
   p += slot(size_t(n_seqs) * 8);
   w.resp_w = reinterpret_cast<double*>(p);
@@ -65,15 +69,20 @@ Ws carve(void* workspace, int64_t n_tokens, int64_t n_seqs) {
 __global__ __launch_bounds__(kTB) void grpo_advantages(GrpoArgs a, Ws w) {
   const int64_t g = int64_t(blockIdx.x) * kTB + threadIdx.x;
   if (a.advantages) {
-    if (g < a.n_seqs) {
-      w.adv[g] = double(a.advantages[g]);
-      if (a.adv_out) a.adv_out[g] = a.advantages[g];
-    }
+    if (g < a.n_seqs) w.adv[g] = double(a.advantages[g]);
     return;
   }
   const int G = a.group_size;
   if (g >= a.n_seqs / G) return;
   const float* r = a.rewards + g * G;
+  // a group whose rewards are all equal carries no signal: A = 0 exactly
+  // (also with adv_eps = 0, where the quotient below would be 0/0)
+  bool constant = true;
+  for (int j = 1; j < G; ++j) constant = constant && r[j] == r[0];
+  if (constant) {
+    for (int j = 0; j < G; ++j) w.adv[g * G + j] = 0.0;
+    return;
+  }
   double mu = 0.0;
   for (int j = 0; j < G; ++j) mu += double(r[j]);
   mu /= double(G);
@@ -97,15 +106,24 @@ __global__ __launch_bounds__(kTB) void grpo_advantages(GrpoArgs a, Ws w) {
     double A = double(r[j]) - b;
     if (a.normalize_std) A /= (sd + double(a.adv_eps));
     w.adv[g * G + j] = A;
-    if (a.adv_out) a.adv_out[g * G + j] = float(A);
   }
 }
 
 // Token weight of each response (one block, fixed order): token mean 1 /
-// T_kept; prompt mean 1 / (G_kept T_g); 0 for a filtered response.
+// T_kept; prompt mean 1 / (G_kept T_g); 0 for a filtered response. The same
+// block checks cu_seqlens (cu[0] = 0, non-decreasing, cu[n_seqs] = n_tokens)
+// and writes the advantages out (NaN when the offsets are invalid).
 __global__ __launch_bounds__(kTB) void grpo_weights(GrpoArgs a, Ws w) {
   __shared__ double sd[kTB / kWave];
   const int tid = threadIdx.x;
+  double bad = 0.0;
+  for (int64_t j = tid; j < a.n_seqs; j += kTB) bad += w.cu[j + 1] < w.cu[j] ? 1.0 : 0.0;
+  if (tid == 0) bad += (w.cu[0] != 0 || w.cu[a.n_seqs] != a.n_tokens) ? 1.0 : 0.0;
+  const bool valid = block_sum(bad, sd) == 0.0;
+  if (a.adv_out)
+    for (int64_t j = tid; j < a.n_seqs; j += kTB)
+      a.adv_out[j] = valid ? float(w.adv[j]) : __builtin_nanf("");
+  if (tid == 0) w.scal[2] = valid ? 1.0 : 0.0;
   auto kept = [&](int64_t j) { return !(a.filter_zero_adv && w.adv[j] == 0.0); };
   auto len = [&](int64_t j) { return double(w.cu[j + 1] - w.cu[j]); };
   if (a.aggregation == 0) {
@@ -174,7 +192,12 @@ __global__ __launch_bounds__(kTB) void grpo_tokens(GrpoArgs a, Ws w) {
   __shared__ double sd[kTB / kWave];
   const int64_t t = int64_t(blockIdx.x) * kTB + threadIdx.x;
   double acc[kNMetric] = {0, 0, 0, 0, 0};
-  if (t < a.n_tokens) {
+  if (t < a.n_tokens && w.scal[2] == 0.0) {   // invalid offsets: NaN outputs
+    const float nan = __builtin_nanf("");
+    a.grad[t] = nan;
+    if (a.token_loss) a.token_loss[t] = nan;
+    if (a.token_flags) a.token_flags[t] = 0;
+  } else if (t < a.n_tokens) {
     const int64_t j = owner(w, a.n_seqs, t);
     const double A = w.adv[j], wt = w.resp_w[j];
     const double C = a.tis_cap, lo_b = 1.0 - double(a.eps_low), hi_b = 1.0 + double(a.eps_high);
@@ -250,13 +273,16 @@ __global__ __launch_bounds__(kTB) void grpo_final(GrpoArgs a, Ws w, int64_t n_bl
 #pragma unroll
   for (int k = 0; k < kNMetric; ++k) acc[k] = block_sum(acc[k], sd);
   if (threadIdx.x == 0) {
-    a.loss[0] = float(acc[0]);   // the token weights are folded in
+    const bool valid = w.scal[2] != 0.0;
+    const float nan = __builtin_nanf("");
+    a.loss[0] = valid ? float(acc[0]) : nan;   // the token weights are folded in
     if (a.metrics) {
-      a.metrics[0] = float(acc[1] * inv_tot);
-      a.metrics[1] = float(acc[2] * inv_tot);
-      a.metrics[2] = float(acc[3] * inv_tot);
-      a.metrics[3] = float(acc[4] * inv_tot);
+      a.metrics[0] = valid ? float(acc[1] * inv_tot) : nan;
+      a.metrics[1] = valid ? float(acc[2] * inv_tot) : nan;
+      a.metrics[2] = valid ? float(acc[3] * inv_tot) : nan;
+      a.metrics[3] = valid ? float(acc[4] * inv_tot) : nan;
     }
+    if (a.status) a.status[0] = valid ? 0 : 1;
   }
 }
 
@@ -264,16 +290,13 @@ __global__ __launch_bounds__(kTB) void grpo_final(GrpoArgs a, Ws w, int64_t n_bl
 
 size_t grpo_workspace(int64_t n_tokens, int64_t n_seqs) {
   const size_t nb = size_t((n_tokens + kTB - 1) / kTB);
-  return slot(size_t(n_seqs + 1) * 8) + 2 * slot(size_t(n_seqs) * 8) + slot(4 * 8) +
-         slot(nb * 8) + slot(nb * kNMetric * 8) + 256;
+  return 2 * slot(size_t(n_seqs) * 8) + slot(4 * 8) + slot(nb * 8) +
+         slot(nb * kNMetric * 8) + 256;
 }
 
-hipError_t launch_grpo(const GrpoArgs& a, const int64_t* cu_host, void* workspace,
-                       hipStream_t stream) {
-  const Ws w = carve(workspace, a.n_tokens, a.n_seqs);
-  hipError_t e = hipMemcpyAsync(w.cu, cu_host, size_t(a.n_seqs + 1) * 8, hipMemcpyHostToDevice,
-                                stream);
-  if (e != hipSuccess) return e;
+hipError_t launch_grpo(const GrpoArgs& a, void* workspace, hipStream_t stream) {
+  const Ws w = carve(workspace, a.cu, a.n_tokens, a.n_seqs);
+  hipError_t e = hipSuccess;
   const int64_t n_adv = a.advantages ? a.n_seqs : a.n_seqs / a.group_size;
   if (n_adv > 0) {
     hipLaunchKernelGGL(grpo_advantages, dim3(unsigned((n_adv + kTB - 1) / kTB)), dim3(kTB), 0,

@@ -42,6 +42,7 @@ struct GrpoArgs {
   const float* lp_new;
   const float* lp_old;
   const float* lp_ref;        // nullable when kl_coef == 0
+  const int64_t* cu;          // device [n_seqs + 1] packed offsets (checked by the kernels)
   int64_t n_seqs, n_tokens;
   const float* rewards;       // one of rewards / advantages
   const float* advantages;
@@ -56,11 +57,10 @@ struct GrpoArgs {
   uint8_t* token_flags;       // nullable
   float* metrics;             // nullable
   float* adv_out;             // nullable
+  int32_t* status;            // nullable device word: 0 offsets valid, 1 invalid
 };
 
 size_t grpo_workspace(int64_t n_tokens, int64_t n_seqs);
-// cu_host: host copy of the packed offsets [n_seqs + 1]
-hipError_t launch_grpo(const GrpoArgs& a, const int64_t* cu_host, void* workspace,
-                       hipStream_t stream);
+hipError_t launch_grpo(const GrpoArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace rlk

@@ -149,15 +149,8 @@ RLK_DEV void read_frag(Frags& f, int r, const char* stage, const FragAddr& fa) {
 // stage's 4 copy units after MFMAs copy_slot(u), so that LDS reads and LDS
 // copies are spread over the stage and the last read lands before the
 // barrier that ends it.
-#ifndef RLK_GEMM_SCHED
-#define RLK_GEMM_SCHED 0
-#endif
-constexpr int read_slot(int r) {
-  return RLK_GEMM_SCHED == 0 ? r : (r / 2) * 3 + (r % 2);
-}
-constexpr int copy_slot(int u) {
-  return RLK_GEMM_SCHED == 0 ? 16 + 4 * u : 2 + 6 * u;
-}
+constexpr int read_slot(int r) { return r; }
+constexpr int copy_slot(int u) { return 16 + 4 * u; }
 
 // The 32 MFMAs of one stage, the next stage's fragment reads and (with
 // kCopyOp = 0 or 1) the copy units of operand A or B of two later stages.

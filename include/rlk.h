@@ -67,7 +67,7 @@ typedef int32_t rlk_status;
 #define RLK_FLAG_MISMATCH 64u   /* retained-support scoring with a top-p check: the set is not
                                     the nucleus recomputed from the logits */
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int32_t rlk_abi_version(void);
 
 /* Static text for a status code. */
@@ -271,6 +271,7 @@ rlk_status rlk_logprob_fused_linear_bwd(
 
 /* --------------------------------------------------------------------------
  * GRPO / DAPO token loss over a packed ragged batch.
+ * (Every input lives in device memory, so a call can be captured in a HIP graph.)
  *
  * LumenRL README, "Key Features" (GRPO, DAPO, PPO) and "Rollout Correction"
  * (TIS clips large ratios); RL-Kernel ROCm sparse performance page: KL
@@ -285,8 +286,11 @@ rlk_status rlk_logprob_fused_linear_bwd(
  *   l_t    = -s + kl_coef k3;   loss = sum_t l_t / T_tot  (token mean)
  *   dL/dlp_new = (-A rho [rho <= C, clip not binding] + kl_coef (1 - exp(lp_ref - lp_new))) / T_tot
  * lp_new, lp_old, lp_ref  [T_tot] fp32 (lp_ref nullable when kl_coef == 0).
- * cu_seqlens    HOST [n_seqs + 1] int64 packed offsets, non-decreasing from 0;
- *               T_tot = cu_seqlens[n_seqs]. Copied into the workspace.
+ * cu_seqlens    [n_seqs + 1] int64 packed offsets (device), which must be
+ *               non-decreasing from 0 to n_tokens. They are checked on the
+ *               device: invalid offsets make loss, grad_lp_new, token_loss,
+ *               metrics and adv_out NaN (token_flags 0) and set *status = 1.
+ * n_tokens      T_tot, the packed token count (by value).
  * rewards / advantages    [n_seqs] fp32: exactly one must be non-NULL.
  * group_size    responses per prompt; must divide n_seqs (rewards mode).
  * (The variants of rlk_grpo_params below change s, rho~, the baseline and the
@@ -295,8 +299,10 @@ rlk_status rlk_logprob_fused_linear_bwd(
  * token_loss    [T_tot] fp32 (nullable).  token_flags [T_tot] uint8 (nullable):
  *               bit0 TIS cap binds (rho > C), bit1 clipped branch taken.
  * metrics       [4] fp32 (nullable): token means of clip flag, TIS flag, k3, rho.
- * adv_out       [n_seqs] fp32 (nullable): the advantages used.
- * T_tot == 0 gives loss 0.
+ * adv_out       [n_seqs] fp32 (nullable): the advantages used. A group whose
+ *               rewards are all equal gets A = 0 exactly in every mode.
+ * status        device int32 (nullable): 0 when cu_seqlens was valid, else 1.
+ * T_tot == 0 gives loss 0. Limits: 1 <= n_seqs <= 2^31, 0 <= n_tokens <= 2^40.
  * -------------------------------------------------------------------------- */
 /* Loss variants (prime-rl v0.10.0 release notes, "2. RL Algorithms": IPO
  * masks a token when |pi_train - pi_infer| > eps (eps 0.3, no KL term);
@@ -361,11 +367,11 @@ size_t rlk_grpo_token_loss_workspace_size(int64_t n_tokens, int64_t n_seqs);
 
 rlk_status rlk_grpo_token_loss(
     const float* lp_new, const float* lp_old, const float* lp_ref,
-    const int64_t* cu_seqlens_host, int64_t n_seqs,
+    const int64_t* cu_seqlens, int64_t n_seqs, int64_t n_tokens,
     const float* rewards, const float* advantages, int32_t group_size,
     const rlk_grpo_params* params,
     float* loss, float* grad_lp_new, float* token_loss, uint8_t* token_flags,
-    float* metrics, float* adv_out,
+    float* metrics, float* adv_out, int32_t* status,
     void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

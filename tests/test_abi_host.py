@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_text(L):
-    assert L.rlk_abi_version() == 1
+    assert L.rlk_abi_version() == 2
     assert L.rlk_status_str(0) == b"ok"
     assert b"workspace" in L.rlk_status_str(3)
 
@@ -88,19 +88,21 @@ def test_workspace_queries(L):
     assert L.rlk_grpo_token_loss_workspace_size(1000, 32) > 0
 
 
-def _grpo(L, cu=(0, 3, 5), **kw):
+def _grpo(L, **kw):
     prm = _native.GrpoParams(ctypes.sizeof(_native.GrpoParams), 2.0, 0.2, 0.28, 0.01, 1e-6, 1, 1,
                              0, 0, 0, 0, 0, 0.3, 0.5, 2.0)
     for k, v in kw.pop("prm", {}).items():
         setattr(prm, k, v)
-    cu_arr = None if cu is None else (ctypes.c_int64 * len(cu))(*cu)
-    a = dict(lp_new=FAKE, lp_old=FAKE, lp_ref=FAKE, n=2, rewards=FAKE, adv=None,
-             G=2, params=ctypes.byref(prm), loss=FAKE, grad=FAKE, ws=WS, ws_bytes=1 << 20,
-             cu=None if cu_arr is None else ctypes.cast(cu_arr, P))
+    # cu_seqlens is a device array: its values are checked by the kernels, so
+    # the host checks only its pointer and the sizes passed by value
+    a = dict(lp_new=FAKE, lp_old=FAKE, lp_ref=FAKE, cu=FAKE, n=2, T=5, rewards=FAKE, adv=None,
+             G=2, params=ctypes.byref(prm), loss=FAKE, grad=FAKE, status=None, ws=WS,
+             ws_bytes=1 << 20)
     a.update(kw)
-    return L.rlk_grpo_token_loss(a["lp_new"], a["lp_old"], a["lp_ref"], a["cu"], a["n"],
+    return L.rlk_grpo_token_loss(a["lp_new"], a["lp_old"], a["lp_ref"], a["cu"], a["n"], a["T"],
                                  a["rewards"], a["adv"], a["G"], a["params"], a["loss"],
-                                 a["grad"], None, None, None, None, a["ws"], a["ws_bytes"], None)
+                                 a["grad"], None, None, None, None, a["status"], a["ws"],
+                                 a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -111,9 +113,12 @@ def _grpo(L, cu=(0, 3, 5), **kw):
     (dict(prm=dict(eps_high=-0.1)), _native.RLK_EINVAL),
     (dict(prm=dict(kl_coef=-1.0)), _native.RLK_EINVAL),
     (dict(prm=dict(std_ddof=2)), _native.RLK_EINVAL),
-    (dict(cu=(1, 3, 5)), _native.RLK_EINVAL),
-    (dict(cu=(0, 3, 2)), _native.RLK_EINVAL),
+    (dict(T=-1), _native.RLK_EINVAL),
+    (dict(T=(1 << 40) + 1), _native.RLK_EINVAL),
+    (dict(n=0), _native.RLK_EINVAL),
     (dict(cu=None), _native.RLK_EINVAL),
+    (dict(cu=P(0x100004)), _native.RLK_EINVAL),          # not 8-byte aligned
+    (dict(status=P(0x100002)), _native.RLK_EINVAL),      # not 4-byte aligned
     (dict(adv=FAKE), _native.RLK_EINVAL),
     (dict(rewards=None), _native.RLK_EINVAL),
     (dict(G=3), _native.RLK_EINVAL),

@@ -2,9 +2,8 @@
 an entry point captured once into a HIP graph (torch.cuda.graph) and
 replayed with new inputs copied into the same buffers must give, on every
 replay, bitwise the outputs of an eager call on those inputs. The program's
-own eager work and a synchronisation come between replays. The GRPO loss is
-left out: it copies cu_seqlens from host memory, which a capture would
-freeze."""
+own eager work and a synchronisation come between replays. Every entry
+point reads its inputs from device memory only, so each is captured as it is."""
 import numpy as np
 import pytest
 import torch
@@ -104,3 +103,29 @@ def test_fused_backward_graph_replay():
 
     print(f"  rlk fused forward + backward in a graph N={N} H={H} V={V}", flush=True)
     _replay_matches_eager([h, y], sets, step)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(loss_type="cispo", correction="mis",
+                                             aggregation="prompt_mean", filter_zero_adv=True,
+                                             baseline="length")])
+def test_grpo_loss_graph_replay(kw):
+    """The loss with device offsets: new log-probabilities, new response
+    lengths (same token count) and new rewards on every replay."""
+    B, T = 32, 4000
+    r = np.random.default_rng(5)
+
+    def one():
+        cut = np.sort(r.choice(np.arange(1, T), B - 1, replace=False))
+        cu = torch.as_tensor(np.concatenate([[0], cut, [T]]).astype(np.int64)).to(DEV)
+        lp = r.normal(-2, 1, T)
+        mk = lambda a: torch.as_tensor(a.astype(np.float32)).to(DEV)
+        rew = r.integers(0, 2, B).astype(np.float32)
+        rew[:8] = 1.0                              # a constant group
+        return (mk(lp), mk(lp + r.normal(0, 0.4, T)), mk(lp + r.normal(0, 0.3, T)), cu, mk(rew))
+
+    sets = [one() for _ in range(3)]
+    lpn, lpo, lpr, cu, rew = (t.clone() for t in sets[0])
+    print(f"  rlk_grpo_token_loss in a graph B={B} T={T} {kw}", flush=True)
+    _replay_matches_eager([lpn, lpo, lpr, cu, rew], sets,
+                          lambda: rlk.grpo_token_loss(lpn, lpo, lpr, cu, rewards=rew,
+                                                      group_size=8, **kw))

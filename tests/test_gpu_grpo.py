@@ -141,3 +141,59 @@ def test_variants_with_advantages_given():
                               cu, advantages=A, group_size=4, **kw)
     torch.cuda.synchronize()
     _compare(out, o, o.near_branch)
+
+
+@pytest.mark.parametrize("kw", [dict(adv_eps=0.0), dict(adv_eps=0.0, baseline="length"),
+                                dict(adv_eps=0.0, std_ddof=0), dict(normalize_std=False)])
+def test_constant_reward_groups_give_zero_advantages(kw):
+    """Groups whose rewards are all equal (all-correct / all-wrong, or any
+    constant) get A = 0 exactly, with adv_eps = 0 too: no NaN reaches the loss,
+    and zero-advantage filtering drops them."""
+    lengths = np.arange(5, 37)
+    cu, lp_new, lp_old, lp_ref = _inputs(11, lengths, sd_old=0.3)
+    r = synth.rewards(synth.workload("grpo"))
+    r[0:8], r[8:16], r[24:32] = 1.0, 0.0, 0.3
+    prm = OG.Params(filter_zero_adv=True, **kw)
+    A = OG.advantages(r, 8, prm, lengths=lengths)
+    assert np.all(A[:16] == 0.0) and np.all(A[24:] == 0.0) and np.all(np.isfinite(A))
+    o = OG.token_loss(lp_new, lp_old, lp_ref, cu, A, prm, group_size=8)
+    print(f"  rlk_grpo_token_loss constant groups {kw}", flush=True)
+    out = rlk.grpo_token_loss(f32_to_device(lp_new), f32_to_device(lp_old), f32_to_device(lp_ref),
+                              cu, rewards=r, group_size=8, filter_zero_adv=True, **kw)
+    torch.cuda.synchronize()
+    adv = host(out["advantages"])
+    assert np.all(adv[:16] == 0.0) and np.all(adv[24:] == 0.0)
+    np.testing.assert_allclose(adv, A, rtol=1e-6, atol=1e-7)
+    _compare(out, o, o.near_branch)
+    assert int(host(out["status"])) == 0
+
+
+def test_device_offsets_and_their_device_check():
+    """cu_seqlens given as a device tensor is used in place; offsets that are
+    not non-decreasing from 0 to the token count give NaN outputs and status 1
+    (nothing is read on the host), and a valid call afterwards is unaffected."""
+    lengths = np.array([4, 0, 9, 3, 6, 1, 2, 5])
+    cu, lp_new, lp_old, lp_ref = _inputs(12, lengths, sd_old=0.3)
+    args = [f32_to_device(a) for a in (lp_new, lp_old, lp_ref)]
+    r = np.array([1, 0, 1, 1, 0, 0, 1, 0], dtype=np.float32)
+    cu_dev = torch.from_numpy(cu).to("cuda:0")
+    good = rlk.grpo_token_loss(*args, cu_dev, rewards=r, group_size=4)
+    o = OG.token_loss(lp_new, lp_old, lp_ref, cu, OG.advantages(r, 4))
+    torch.cuda.synchronize()
+    _compare(good, o, o.near_branch)
+    assert int(host(good["status"])) == 0
+    T = int(cu[-1])
+    for bad in ([1, 4, 4, 13, 16, 22, 23, 25, T], [0, 4, 3, 13, 16, 22, 23, 25, T],
+                [0, 4, 4, 13, 16, 22, 23, 25, T - 1], [0, 4, 4, 13, 16, 22, 23, 25, T + 1]):
+        cb = torch.tensor(bad, dtype=torch.int64, device="cuda:0")
+        print(f"  rlk_grpo_token_loss invalid offsets {bad}", flush=True)
+        out = rlk.grpo_token_loss(*args, cb, rewards=r, group_size=4)
+        torch.cuda.synchronize()
+        assert int(host(out["status"])) == 1
+        assert np.isnan(float(host(out["loss"])))
+        assert np.isnan(host(out["grad"])).all() and np.isnan(host(out["token_loss"])).all()
+        assert np.isnan(host(out["metrics"])).all() and np.isnan(host(out["advantages"])).all()
+        assert not host(out["token_flags"]).any()
+    again = rlk.grpo_token_loss(*args, cu_dev, rewards=r, group_size=4)
+    for k in good:
+        assert torch.equal(good[k], again[k]), k
