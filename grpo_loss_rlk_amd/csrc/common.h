@@ -156,6 +156,13 @@ RLK_DEV double dpp_f64(double fill, double v) {
 }
 
 template <int kCtrl, int kRowMask = 0xf, int kBankMask = 0xf>
+RLK_DEV uint64_t dpp_u64(uint64_t fill, uint64_t v) {
+  const uint32_t lo = dpp_u32<kCtrl, kRowMask, kBankMask>(uint32_t(fill), uint32_t(v));
+  const uint32_t hi = dpp_u32<kCtrl, kRowMask, kBankMask>(uint32_t(fill >> 32), uint32_t(v >> 32));
+  return (uint64_t(hi) << 32) | lo;
+}
+
+template <int kCtrl, int kRowMask = 0xf, int kBankMask = 0xf>
 RLK_DEV float dpp_f32(float fill, float v) {
   return __uint_as_float(dpp_u32<kCtrl, kRowMask, kBankMask>(__float_as_uint(fill), __float_as_uint(v)));
 }
@@ -179,6 +186,7 @@ RLK_DEV int dpp_i32(int fill, int v) {
 RLK_DPP_SCAN(double, dpp_f64)
 RLK_DPP_SCAN(float, dpp_f32)
 RLK_DPP_SCAN(int, dpp_i32)
+RLK_DPP_SCAN(uint64_t, dpp_u64)
 #undef RLK_DPP_SCAN
 
 RLK_DEV uint32_t readlane_u32(uint32_t v, int lane) {
@@ -190,13 +198,20 @@ RLK_DEV double readlane_f64(double v, int lane) {
   return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
 }
 
+RLK_DEV uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = readlane_u32(uint32_t(v), lane), hi = readlane_u32(uint32_t(v >> 32), lane);
+  return (uint64_t(hi) << 32) | lo;
+}
+
 // Wave totals via the inclusive scan's last lane (uniform result).
 RLK_DEV double wave_total(double v) { return readlane_f64(wave_scan_incl(v), kWave - 1); }
 RLK_DEV int wave_total(int v) { return int(readlane_u32(uint32_t(wave_scan_incl(v)), kWave - 1)); }
+RLK_DEV uint64_t wave_total(uint64_t v) { return readlane_u64(wave_scan_incl(v), kWave - 1); }
 
 // Exclusive scan from an inclusive one: lane i gets lane i-1's value (lane 0: 0).
 RLK_DEV double wave_shift_up(double v) { return dpp_f64<0x138>(0.0, v); }   // wave_shr:1
 RLK_DEV int wave_shift_up(int v) { return dpp_i32<0x138>(0, v); }
+RLK_DEV uint64_t wave_shift_up(uint64_t v) { return dpp_u64<0x138>(uint64_t(0), v); }
 
 // Fold of per-wave partials p[0..n) (n <= 64) held in LDS: lane w loads p[w]
 // and the wave reduces with DPP. Uniform result, fixed order.
@@ -207,6 +222,10 @@ RLK_DEV double fold_partials(const double* p, int n) {
 RLK_DEV int fold_partials(const int* p, int n) {
   const int lane = threadIdx.x & (kWave - 1);
   return wave_total(lane < n ? p[lane] : 0);
+}
+RLK_DEV uint64_t fold_partials(const uint64_t* p, int n) {
+  const int lane = threadIdx.x & (kWave - 1);
+  return wave_total(lane < n ? p[lane] : uint64_t(0));
 }
 
 // Wave max / min of ints (uniform result).

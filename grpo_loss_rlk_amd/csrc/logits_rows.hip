@@ -431,8 +431,8 @@ RLK_DEV float code_mass(float dv, MassScale k) {
 constexpr int kMaxFW = kHT / kWave;              // every wave finishes the block's last row
 struct FinScratch {
   int i[8][kMaxFW];
-  double d[6][kMaxFW];
-  double bd[3];
+  uint64_t d[6][kMaxFW];   // fixed-point partial sums
+  uint64_t bd[3];
   int bi[2];
   unsigned int bar;
   unsigned int handed_on;   // nonzero once any row of the block is handed on
@@ -450,6 +450,19 @@ RLK_DEV void fsync(unsigned int* bar, unsigned int& epoch) {
   while (__hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < epoch)
     __builtin_amdgcn_s_sleep(1);
 }
+
+// The finisher's sums are exact: masses (and mass times d) enter them as
+// unsigned fixed-point integers in units of 2^-kFxBits, so integer addition
+// makes every total independent of how the terms are split across threads
+// and waves. That keeps a row's outputs bitwise the same whether 4 waves
+// finish it (while the others stream) or all 16 do (a block's last row),
+// i.e. independent of the number of rows and of which rows share a block.
+// A value below the unit is truncated; a row holds at most 2^24 values of
+// mass <= 1 each, so 2^24 2^38 < 2^63 never overflows, and the truncation
+// costs at most 2^-38 per term (Z >= 1: the max contributes 1).
+constexpr int kFxBits = 38;
+RLK_DEV uint64_t to_fx(double x) { return uint64_t(x * 0x1p38); }   // x in [0, 2^24)
+RLK_DEV double from_fx(uint64_t u) { return double(u) * 0x1p-38; }
 
 // Everything after counting, for one row: checksum and occupied range, max,
 // Z and entropy, the top-p walk, outputs (or the hand-off flag), and zeroing
@@ -552,11 +565,13 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
   const MassScale ks = mass_scale(invT);
 
   // ---- over the occupied groups, 2 in flight (more would spill): the
-  //      checksum of all counts, and Z and sum e*d over the distinct values
-  //      (formed for every row; used only when the row is live) ----
+  //      checksum of all counts, and Z and -sum e*d over the distinct
+  //      values (formed for every row; used only when the row is live): a
+  //      16-byte group's 8 terms summed in fp64 in a fixed order, the group
+  //      sum converted to fixed point ----
   {
     uint32_t t_acc = 0;
-    double zt = 0.0, st = 0.0;
+    uint64_t zt = 0, st = 0;
     const uint4* h4 = reinterpret_cast<const uint4*>(hist);
     for (int gb = 0; gb < ng; gb += 2 * FT) {
       uint4 x[2];
@@ -570,6 +585,7 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
       for (int u = 0; u < 2; ++u) {
         const int m0 = g0 + 4 * (gb + ft + u * FT);
         const uint32_t c[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+        double zg = 0.0, sg = 0.0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           t_acc = __builtin_amdgcn_sad_u16(c[j], 0u, t_acc);
@@ -582,18 +598,20 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
             // contributes exactly 0; present values are unchanged
             const float dv = fminf((sgn ? -v : v) - mval, 0.f);
             const float e = code_mass(dv, ks) * float(n);
-            zt += double(e);
-            st += double(e) * double(dv * invTf);
+            zg += double(e);
+            sg -= double(e) * double(dv * invTf);
           }
         }
+        zt += to_fx(zg);
+        st += to_fx(sg);
         __builtin_amdgcn_sched_barrier(0);   // one group's arithmetic at a time
       }
     }
     if (ft == 0 && n_zero > 0) {   // the +-0 group
       const float dv = -mval;
       const float e = code_mass(dv, ks) * float(n_zero);
-      zt += double(e);
-      st += double(e) * double(dv * invTf);
+      zt += to_fx(double(e));
+      st += to_fx(-(double(e) * double(dv * invTf)));
     }
     const int t_w = wave_total(int(t_acc));
     zt = wave_total(zt);
@@ -622,23 +640,26 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
   }
 
   if (live) {
-    const double Z = fold_partials(fs.d[0], FW);
-    const double S = fold_partials(fs.d[1], FW);
+    const uint64_t Zu = fold_partials(fs.d[0], FW);
+    const uint64_t Su = fold_partials(fs.d[1], FW);
+    const double Z = from_fx(Zu);
+    const double S = -from_fx(Su);
 
-    // ---- top-p cut: walk merged keys down from the max, FT at a time ----
+    // ---- top-p cut: walk merged keys down from the max, FT at a time; the
+    //      masses per key in fixed point, so every cumulative sum is exact ----
     double Zs = Z, Ss = S, Mgt = 0.0;
     uint32_t tau_key = 0;
     int size = int(V) - n_neginf;
     const bool cut = p < 1.f;
     if (cut) {
       const double thr = double(p) * Z;
-      double cz = 0.0, cs = 0.0;
+      uint64_t cz = 0, cs = 0;
       int cn = 0;
       bool found = false;
       int par = 0;
       for (int k0 = kmax; !found && k0 >= kKeyLo; k0 -= FT, par ^= 1) {
         const int key = k0 - ft;
-        double mass = 0.0, ms = 0.0;
+        uint64_t mass = 0, ms = 0;
         int n = 0;
         if (key >= kKeyLo) {
           float v;
@@ -646,11 +667,11 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
           if (n) {
             const float dv = v - mval;
             const float e = code_mass(dv, ks) * float(n);
-            mass = double(e);
-            ms = mass * double(dv * invTf);
+            mass = to_fx(double(e));
+            ms = to_fx(-(double(e) * double(dv * invTf)));
           }
         }
-        const double iz = wave_scan_incl(mass), is = wave_scan_incl(ms);
+        const uint64_t iz = wave_scan_incl(mass), is = wave_scan_incl(ms);
         const int in = wave_scan_incl(n);
         if (lane == kWave - 1) {
           fs.d[2 + 2 * par][fw] = iz;
@@ -658,49 +679,50 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
           fs.i[5 + par][fw] = in;
         }
         fsync<FW>(&fs.bar, epoch);
-        // wave partials in lanes 0..FW-1: exclusive prefixes, and the
-        // inclusive value exactly as the crossing wave's last lane forms it
-        const double pz = lane < FW ? fs.d[2 + 2 * par][lane] : 0.0;
-        const double ps = lane < FW ? fs.d[3 + 2 * par][lane] : 0.0;
+        // wave partials in lanes 0..FW-1: exclusive prefixes; the inclusive
+        // cumulative mass of a key, compared with p Z as a double (the
+        // conversion of an exact integer: the same whoever forms it)
+        const uint64_t pz = lane < FW ? fs.d[2 + 2 * par][lane] : uint64_t(0);
+        const uint64_t ps = lane < FW ? fs.d[3 + 2 * par][lane] : uint64_t(0);
         const int pn = lane < FW ? fs.i[5 + par][lane] : 0;
-        const double ez = wave_shift_up(wave_scan_incl(pz));
-        const double es = wave_shift_up(wave_scan_incl(ps));
+        const uint64_t ez = wave_shift_up(wave_scan_incl(pz));
+        const uint64_t es = wave_shift_up(wave_scan_incl(ps));
         const int en = wave_shift_up(wave_scan_incl(pn));
-        const uint64_t wcross = __ballot(lane < FW && cz + (ez + pz) >= thr);
+        const uint64_t wcross = __ballot(lane < FW && from_fx(cz + ez + pz) >= thr);
         const int cross_wave = wcross ? __ffsll((unsigned long long)wcross) - 1 : -1;
         if (cross_wave >= 0) {
           if (fw == cross_wave) {
-            const double wbz = readlane_f64(ez, cross_wave);
-            const double wbs = readlane_f64(es, cross_wave);
+            const uint64_t wbz = readlane_u64(ez, cross_wave);
+            const uint64_t wbs = readlane_u64(es, cross_wave);
             const int wbn = int(readlane_u32(uint32_t(en), cross_wave));
-            const double incl = cz + (wbz + iz);
-            const uint64_t bal = __ballot(incl >= thr);
+            const uint64_t incl = cz + wbz + iz;
+            const uint64_t bal = __ballot(from_fx(incl) >= thr);
             const int first = __ffsll((unsigned long long)bal) - 1;
             if (lane == first) {
               fs.bd[0] = incl;
-              fs.bd[1] = cs + (wbs + is);
+              fs.bd[1] = cs + wbs + is;
               fs.bd[2] = incl - mass;
               fs.bi[0] = key;
               fs.bi[1] = cn + wbn + in;
             }
           }
           fsync<FW>(&fs.bar, epoch);
-          Zs = fs.bd[0];
-          Ss = fs.bd[1];
-          Mgt = fs.bd[2];
+          Zs = from_fx(fs.bd[0]);
+          Ss = -from_fx(fs.bd[1]);
+          Mgt = from_fx(fs.bd[2]);
           tau_key = uint32_t(fs.bi[0]);
           size = fs.bi[1];
           found = true;
         } else {
-          cz += readlane_f64(ez, FW - 1) + readlane_f64(pz, FW - 1);
-          cs += readlane_f64(es, FW - 1) + readlane_f64(ps, FW - 1);
+          cz += readlane_u64(ez, FW - 1) + readlane_u64(pz, FW - 1);
+          cs += readlane_u64(es, FW - 1) + readlane_u64(ps, FW - 1);
           cn += int(readlane_u32(uint32_t(en), FW - 1)) + int(readlane_u32(uint32_t(pn), FW - 1));
         }
       }
-      if (!found) {   // rounding left the mass just short of p: keep every value
-        Zs = cz;
-        Ss = cs;
-        Mgt = cz;
+      if (!found) {   // truncation left the mass just short of p: keep every value
+        Zs = from_fx(cz);
+        Ss = -from_fx(cs);
+        Mgt = Zs;
         tau_key = uint32_t(kKeyLo);
         size = cn;
       }

@@ -4,10 +4,12 @@ top-p = 1 and through the top-p cut (nucleus held fixed).
 The GPU forward supplies `saved` to the GPU backward; the oracle recomputes
 everything from the same bf16 inputs. Tolerance (bf16 G and bf16 dh, fp32
 accumulation): normwise relative ||d||_F / ||ref||_F <= 5e-3 for dh and dW,
-and <= 1e-2 for every single row of dh (relative to the larger of the row's
-norm and 1e-3 of the rms row norm). dh rows are bitwise independent of
-how the rows are batched (fixed vocabulary chunks, fixed summation order);
-dW sums over all rows and is only checked for run-to-run determinism.
+and <= 1e-2 for every single row of dh and every single vocabulary row of dW
+(relative to the larger of the row's norm and 1e-3 of the rms row norm; the
+expected per-row error is about 1e-3, the bf16 rounding of G). dh rows are
+bitwise independent of how the rows are batched (fixed vocabulary chunks,
+fixed summation order); dW sums over all rows and is checked for run-to-run
+determinism.
 """
 import numpy as np
 import pytest
@@ -19,7 +21,7 @@ from oracle import fused as OF
 from oracle import logprob as OL
 from oracle import sampling as OS
 
-from gpu_util import DEV, bf16_to_device, bits_equal, host
+from gpu_util import DEV, assert_close_rows, bf16_to_device, bits_equal, host
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +62,19 @@ def _rel(got, want):
     return np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)
 
 
+def _rows_ok(got, want, what, floor_rms=None):
+    """Every row of ``got`` within ROW_TOL of ``want`` relative to the larger
+    of the row's norm and 1e-3 of the rms row norm (a row whose exact value
+    vanishes -- a one-token nucleus: q = 1 and d = E_q d -- keeps fp32
+    rounding of q around 1). ``floor_rms``: the rms row norm to use when
+    ``want`` holds only a sample of the rows."""
+    ref_rows = np.linalg.norm(want, axis=1)
+    rms = np.sqrt(np.mean(ref_rows ** 2)) if floor_rms is None else floor_rms
+    floor = 1e-3 * rms + 1e-300
+    rows = np.linalg.norm(got - want, axis=1) / np.maximum(ref_rows, floor)
+    assert np.all(rows <= ROW_TOL), (what, np.flatnonzero(rows > ROW_TOL)[:8], rows.max())
+
+
 def _check(dh, dw, hb, wb, y, g_lp, g_h, T, p=1.0):
     dh_ref, dw_ref = OF.backward(OL.widen_bf16(hb), OL.widen_bf16(wb), y, g_lp.astype(np.float64),
                                  g_h.astype(np.float64), OL.f32(T), OL.f32(p))
@@ -67,13 +82,10 @@ def _check(dh, dw, hb, wb, y, g_lp, g_h, T, p=1.0):
     dw_got = host(dw).astype(np.float64)
     assert _rel(dh_got, dh_ref) <= NORM_TOL, ("dh", _rel(dh_got, dh_ref))
     assert _rel(dw_got, dw_ref) <= NORM_TOL, ("dW", _rel(dw_got, dw_ref))
-    # per row, relative to the row's norm with a floor of 1e-3 of the rms row
-    # norm: a row whose exact gradient vanishes (a one-token nucleus: q = 1
-    # and d = E_q d) is left with fp32 rounding of q around 1
-    ref_rows = np.linalg.norm(dh_ref, axis=1)
-    floor = 1e-3 * np.sqrt(np.mean(ref_rows ** 2)) + 1e-300
-    rows = np.linalg.norm(dh_got - dh_ref, axis=1) / np.maximum(ref_rows, floor)
-    assert np.all(rows <= ROW_TOL), ("dh rows", np.flatnonzero(rows > ROW_TOL)[:8], rows.max())
+    _rows_ok(dh_got, dh_ref, "dh rows")
+    # every vocabulary row of dW: the last partial vocabulary tile, the
+    # 32768-row chunk seams of a large V and rows no target names included
+    _rows_ok(dw_got, dw_ref, "dW rows")
 
 
 @pytest.mark.parametrize("N,H,V,T", [(300, 256, 1000, 1.0), (77, 128, 515, 0.7),
@@ -171,10 +183,58 @@ def _oracle_dh_row(h_row64, W64, y, g_lp, g_h, T, p=1.0):
     return G @ W64
 
 
+def _seam_rows(V, chunk=32768, tile=256):
+    """Vocabulary rows at every chunk seam, the first and last rows and the
+    first row of the last (possibly partial) tile."""
+    rows = {0, 1, V - 1, V - 2, (V - 1) // tile * tile}
+    for c in range(chunk, V, chunk):
+        rows |= {c - 1, c}
+    return np.array(sorted(r for r in rows if 0 <= r < V))
+
+
+def test_bwd_llama_width_sampled():
+    """Llama-3-70B head width (H = 8192, V = 128256: four vocabulary chunks)
+    on 1024 tokens, the loss form -mean lp - 0.001 mean H: the forward's lp
+    and H of every token, and sampled rows of dh and of dW (every chunk seam,
+    the ends, every target row sampled and random rows) against the oracle
+    computed from the full fp64 logits."""
+    w = synth.workload("llama70b", N=1024)
+    hb = synth.hidden_rows(w, range(w.N))
+    wb = synth.weight_rows(w, range(w.V))
+    y = synth.uniform_targets(w, w.N)
+    N, V = w.N, w.V
+    g_lp = np.full(N, -1.0 / N, dtype=np.float32)
+    g_h = np.full(N, -0.001 / N, dtype=np.float32)
+    h, W, yt = bf16_to_device(hb), bf16_to_device(wb), torch.as_tensor(y)
+    print(f"  rlk fused fwd+bwd N={N} H={w.H} V={V}", flush=True)
+    fwd = rlk.logprob_fused_linear(h, W, yt, 1.0, 1.0)
+    dh, dw = rlk.logprob_fused_linear_bwd(h, W, yt, fwd["saved"], torch.as_tensor(g_lp).to(DEV),
+                                          torch.as_tensor(g_h).to(DEV), 1.0, 1.0)
+    torch.cuda.synchronize()
+    h64, W64 = OL.widen_bf16(hb), OL.widen_bf16(wb)
+    z = OF.logits(h64, W64)
+    o = OL.logprob_from_logits(z, y, 1.0, 1.0)
+    assert_close_rows(host(fwd["logprob"]), o.lp_trunc, 2e-3, what="logprob")
+    assert_close_rows(host(fwd["entropy"]), o.h_trunc, 1e-5, 1e-3, what="entropy")
+    G = OF.grad_logits(z, y, g_lp.astype(np.float64), g_h.astype(np.float64), 1.0, 1.0)
+    del z
+    rng = np.random.default_rng(2)
+    vs = np.unique(np.concatenate([_seam_rows(V), y[:16], rng.choice(V, 48, replace=False)]))
+    ns = np.unique(np.concatenate([[0, 1, N - 1], rng.choice(N, 13, replace=False)]))
+    # the floor of the per-row checks: the rms row norm of all of dW, from
+    # ||G^T h||_F^2 = sum(G * (h h^T) G) without forming the [V, H] product
+    dw_rms = np.sqrt(np.sum(G * ((h64 @ h64.T) @ G)) / V)
+    _rows_ok(host(dw[vs]).astype(np.float64), G[:, vs].T @ h64, "dW rows", dw_rms)
+    dh_ref = G[ns] @ W64
+    _rows_ok(host(dh[ns].float()).astype(np.float64), dh_ref, "dh rows")
+
+
 def test_bwd_llama70b_full_size_sampled():
-    """Full Llama-3-70B head (16384 x 8192 . 128256 x 8192): two dh rows against
-    the oracle computed row by row, and the zero-sum property of dW rows
-    (rows of G sum to zero, so sum_v dW[v, :] = 0 up to rounding)."""
+    """Full Llama-3-70B head (16384 x 8192 . 128256 x 8192): the forward's lp
+    and H on 8 rows, two dh rows against the oracle computed row by row, and
+    the zero-sum property of dW rows (rows of G sum to zero, so
+    sum_v dW[v, :] = 0 up to rounding). Sampled dW rows need every token's
+    logits and are checked at this width on 1024 tokens (above)."""
     w = synth.workload("llama70b")
     hb = synth.hidden_rows(w, range(w.N))
     wb = synth.weight_rows(w, range(w.V))
@@ -182,10 +242,19 @@ def test_bwd_llama70b_full_size_sampled():
     N = w.N
     g_lp = np.full(N, -1.0 / N, dtype=np.float32)
     g_h = np.full(N, -0.001 / N, dtype=np.float32)
-    dh, dw = _gpu_bwd(bf16_to_device(hb), bf16_to_device(wb), torch.as_tensor(y), g_lp, g_h, 1.0)
+    h, W, yt = bf16_to_device(hb), bf16_to_device(wb), torch.as_tensor(y)
+    print(f"  rlk fused fwd+bwd N={N} H={w.H} V={w.V}", flush=True)
+    fwd = rlk.logprob_fused_linear(h, W, yt, 1.0, 1.0)
+    dh, dw = rlk.logprob_fused_linear_bwd(h, W, yt, fwd["saved"], torch.as_tensor(g_lp).to(DEV),
+                                          torch.as_tensor(g_h).to(DEV), 1.0, 1.0)
+    torch.cuda.synchronize()
     colsum = host(torch.sum(dw, dim=0, dtype=torch.float64))
     assert np.abs(colsum).max() <= 3e-4, np.abs(colsum).max()
     W64 = OL.widen_bf16(wb)
+    rows = np.array([0, 1, 4097, 8191, 8192, 12345, N - 2, N - 1])
+    o = OL.logprob_from_logits(OL.widen_bf16(hb[rows]) @ W64.T, y[rows], 1.0, 1.0)
+    assert_close_rows(host(fwd["logprob"])[rows], o.lp_trunc, 2e-3, what="logprob")
+    assert_close_rows(host(fwd["entropy"])[rows], o.h_trunc, 1e-5, 1e-3, what="entropy")
     for n in (0, N - 1):
         want = _oracle_dh_row(OL.widen_bf16(hb[n]), W64, int(y[n]), -1.0 / N, -0.001 / N, 1.0)
         got = host(dh[n].float()).astype(np.float64)

@@ -8,8 +8,9 @@ bf16 operands. Tolerances as for bf16 inputs: |d lp| <= 2e-3, |d H| <= 1e-3
 the oracle flags as within 1e-6 of the top-p boundary, where either valid set
 passes, and on rows where fp64 logits at the cut lie within fp32
 accumulation error of one another (the GPU may see them tied or reordered),
-where the GPU's set down to any of them passes; the saved threshold within
-1e-4 of the oracle's (fp32 vs fp64 logits).
+where the GPU's set down to any of them passes (at most 8 tokens apart, on at
+most 0.1 % of the rows); the saved threshold within 1e-4 of the oracle's
+(fp32 vs fp64 logits).
 """
 import numpy as np
 import pytest
@@ -42,31 +43,42 @@ def _run(h, W, y, T, p):
     return {k: host(v) for k, v in out.items()}
 
 
+MAX_TIE_SPAN = 8          # at most this many tokens between the two cut points
+MAX_TIE_ROWS = 1e-3       # and at most this share of the rows (2 rows at least)
+
+
 def _accept_fp32_ties(g, size, lpt, ht, z64, y, T, h64, W64):
     """The GPU cuts its own fp32-accumulated logits, the oracle fp64 ones of
     the same bf16 operands. Where fp64 logits at the cut differ by less than
     fp32 accumulation can resolve, the GPU may see them tied (and keep the
     whole tie group) or reordered, so its nucleus may hold the tokens down
-    to another of them. Such a row passes with the GPU's size when every
-    fp64 logit between the two cut points lies within the worst-case error
-    of an fp32 dot product of length H, H 2^-24 sum_k |h_k w_k|, of both
-    ends; its logprob and entropy are then the oracle's over that set."""
+    to another of them. Such a row passes with the GPU's size when the two
+    cut points are at most MAX_TIE_SPAN tokens apart and the fp64 gap between
+    them is within twice the smallest worst-case error bound of an fp32 dot
+    product of length H, H 2^-24 sum_k |h_k w_k|, over every token from one
+    cut point to the other (so every such token could sit on either side);
+    its logprob and entropy are then the oracle's over that set. Returns the
+    number of rows so accepted (the caller caps it)."""
     H = h64.shape[1]
+    accepted = 0
     for n in np.flatnonzero(g["nucleus_size"] != size):
         k, k2 = int(size[n]), int(g["nucleus_size"][n])
-        if k2 < 1 or k2 > z64.shape[1]:
+        if k2 < 1 or k2 > z64.shape[1] or abs(k2 - k) > MAX_TIE_SPAN:
             continue
         order = np.argsort(-z64[n], kind="stable")
         zs = z64[n][order]
         lo, hi = min(k, k2), max(k, k2)
-        err = H * 2.0 ** -24 * (np.abs(W64[order[[lo - 1, hi - 1]]]) @ np.abs(h64[n]))
-        if zs[lo - 1] - zs[hi - 1] <= err.sum():
+        errs = H * 2.0 ** -24 * (np.abs(W64[order[lo - 1:hi]]) @ np.abs(h64[n]))
+        gap = zs[lo - 1] - zs[hi - 1]
+        if gap <= 2.0 * errs.min():
             keep = np.zeros(z64.shape[1], dtype=bool)
             keep[order[:k2]] = True
             l2, h2 = OL.truncated(z64[n], int(y[n]), OL.f32(T), keep)
-            print(f"  row {n}: fp32 near-tie at the cut (fp64 gap {zs[lo - 1] - zs[hi - 1]:.3g} "
-                  f"<= {err.sum():.3g}), GPU size {k2} vs oracle {k}", flush=True)
+            print(f"  row {n}: fp32 near-tie at the cut (fp64 gap {gap:.3g} <= "
+                  f"{2.0 * errs.min():.3g}), GPU size {k2} vs oracle {k}", flush=True)
             size[n], lpt[n], ht[n] = k2, l2, h2
+            accepted += 1
+    return accepted
 
 
 def _check(g, o, z64, y, T, hw=None):
@@ -79,7 +91,8 @@ def _check(g, o, z64, y, T, hw=None):
             if g["nucleus_size"][n] == s2:
                 size[n], lpt[n], ht[n] = s2, l2, h2
     if hw is not None:
-        _accept_fp32_ties(g, size, lpt, ht, z64, y, T, *hw)
+        n_tie = _accept_fp32_ties(g, size, lpt, ht, z64, y, T, *hw)
+        assert n_tie <= max(2, MAX_TIE_ROWS * len(y)), ("fp32 near-tie rows", n_tie, len(y))
     np.testing.assert_array_equal(g["nucleus_size"], size, err_msg="nucleus size")
     assert_close_rows(g["logprob"], lpt, LP_TOL, what="logprob")
     assert_close_rows(g["entropy"], ht, H_ATOL, H_RTOL, what="entropy")

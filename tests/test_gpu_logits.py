@@ -307,3 +307,43 @@ def test_bitwise_run_to_run_and_batch_invariance(dtype, V):
     for k in ref:
         if ref[k] is not None:
             assert torch.equal(ref[k][perm.to(DEV)], pr[k]), k
+
+
+@pytest.mark.parametrize("p", [0.95, 1.0])
+def test_bf16_row_as_last_and_middle_row_of_a_block(p):
+    """The bf16 kernel runs one block per CU over rows b, b + G, b + 2G, ...
+    (G = min(N, CUs)); a block's last row is finished by all of its waves,
+    every other row by four while the rest stream. With N = 2G + 3 rows
+    holding 7 distinct rows in turn, each distinct row is scored both as a
+    block's last row and as a middle row (and alone, N = 1): every output must
+    be bitwise the same in every position."""
+    G = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K = 2 * G + 3, 7
+    w = synth.workload("qwen")
+    base = synth.logits_rows(w, range(K))
+    yb = synth.peak_targets(w, range(K))
+    idx = np.arange(N) % K
+    x = bf16_to_device(base[idx])
+    y = torch.as_tensor(yb[idx])
+    print(f"  rlk_logprob_from_logits N={N} G={G} V={w.V} p={p}", flush=True)
+    out = rlk.logprob_from_logits(x, y, 0.7, p)
+    torch.cuda.synchronize()
+    last = np.arange(N) + G >= N
+    for k, v in out.items():
+        if v is None:
+            continue
+        v = host(v)
+        for c in range(K):
+            pos = np.flatnonzero(idx == c)
+            assert last[pos].any() and (~last[pos]).any()
+            ref = v[pos[0]]
+            for q in pos[1:]:
+                assert v[q].tobytes() == ref.tobytes(), (k, c, q, v[q], ref)
+    for c in range(K):
+        one = rlk.logprob_from_logits(bf16_to_device(base[c:c + 1]), torch.as_tensor(yb[c:c + 1]),
+                                      0.7, p)
+        for k, v in one.items():
+            if v is not None:
+                assert host(v)[0].tobytes() == host(out[k])[c].tobytes(), (k, c)
+    o = OL.logprob_from_logits(OL.widen_bf16(base), yb, OL.f32(0.7), OL.f32(p))
+    check({k: (None if v is None else host(v)[:K]) for k, v in out.items()}, o, **BF16_TOL)
