@@ -44,6 +44,9 @@ SIGNATURES = {
     "rlk_logprob_from_logits": (c_i32, [
         c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_f32, c_vp, c_vp, c_i32,
         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "rlk_logprob_from_logits_noalloc": (c_i32, [
+        c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_f32, c_vp, c_vp, c_i32,
+        c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "rlk_logprob_from_support_workspace_size": (c_sz, [c_i64, c_i64, c_i32, c_f32]),
     "rlk_logprob_from_support": (c_i32, [
         c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_vp, c_vp, c_i64, c_f32,

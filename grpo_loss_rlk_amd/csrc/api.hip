@@ -89,14 +89,19 @@ size_t rlk_logprob_from_logits_workspace_size(int64_t n_rows, int64_t vocab, int
   return rlk::logits_rows_workspace(n_rows, vocab, dtype);
 }
 
-rlk_status rlk_logprob_from_logits(const void* logits, int32_t dtype, int64_t n_rows,
-                                   int64_t vocab, int64_t row_stride, const int64_t* targets,
-                                   float temperature, float top_p,
-                                   const float* temperature_per_row, const float* top_p_per_row,
-                                   int32_t top_k, float* lp_full, float* lp_trunc,
-                                   float* entropy_trunc, float* entropy_full,
-                                   int32_t* nucleus_size, float* threshold, uint8_t* flags,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of rlk_logprob_from_logits' arguments other than the workspace, and
+// the kernel arguments they describe.
+rlk_status logits_args(const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab,
+                       int64_t row_stride, const int64_t* targets, float temperature,
+                       float top_p, const float* temperature_per_row,
+                       const float* top_p_per_row, int32_t top_k, float* lp_full,
+                       float* lp_trunc, float* entropy_trunc, float* entropy_full,
+                       int32_t* nucleus_size, float* threshold, uint8_t* flags,
+                       rlk::RowArgs* a) {
   if (dtype != RLK_DTYPE_F32 && dtype != RLK_DTYPE_BF16)
     return fail(RLK_EINVAL, "dtype=%d is not RLK_DTYPE_F32 or RLK_DTYPE_BF16", dtype);
   rlk_status s = check_sampling(temperature, top_p, top_k);
@@ -116,30 +121,81 @@ rlk_status rlk_logprob_from_logits(const void* logits, int32_t dtype, int64_t n_
       !aligned(nucleus_size, 4) || !aligned(threshold, 4) || !aligned(temperature_per_row, 4) ||
       !aligned(top_p_per_row, 4))
     return fail(RLK_EINVAL, "an array is not naturally aligned");
+  *a = rlk::RowArgs{};
+  a->logits = logits;
+  a->n_rows = n_rows;
+  a->vocab = vocab;
+  a->row_stride = row_stride;
+  a->targets = targets;
+  a->temperature = temperature;
+  a->top_p = top_p;
+  a->t_row = temperature_per_row;
+  a->p_row = top_p_per_row;
+  a->lp_full = lp_full;
+  a->lp_trunc = lp_trunc;
+  a->ent_trunc = entropy_trunc;
+  a->ent_full = entropy_full;
+  a->nsize = nucleus_size;
+  a->thresh = threshold;
+  a->flags = flags;
+  return RLK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rlk_status rlk_logprob_from_logits(const void* logits, int32_t dtype, int64_t n_rows,
+                                   int64_t vocab, int64_t row_stride, const int64_t* targets,
+                                   float temperature, float top_p,
+                                   const float* temperature_per_row, const float* top_p_per_row,
+                                   int32_t top_k, float* lp_full, float* lp_trunc,
+                                   float* entropy_trunc, float* entropy_full,
+                                   int32_t* nucleus_size, float* threshold, uint8_t* flags,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  rlk::RowArgs a;
+  rlk_status s = logits_args(logits, dtype, n_rows, vocab, row_stride, targets, temperature,
+                             top_p, temperature_per_row, top_p_per_row, top_k, lp_full,
+                             lp_trunc, entropy_trunc, entropy_full, nucleus_size, threshold,
+                             flags, &a);
+  if (s != RLK_OK || n_rows == 0) return s;
   s = check_workspace(workspace, workspace_bytes,
                       rlk_logprob_from_logits_workspace_size(n_rows, vocab, dtype));
   if (s != RLK_OK) return s;
-
-  rlk::RowArgs a{};
-  a.logits = logits;
-  a.n_rows = n_rows;
-  a.vocab = vocab;
-  a.row_stride = row_stride;
-  a.targets = targets;
-  a.temperature = temperature;
-  a.top_p = top_p;
-  a.t_row = temperature_per_row;
-  a.p_row = top_p_per_row;
-  a.lp_full = lp_full;
-  a.lp_trunc = lp_trunc;
-  a.ent_trunc = entropy_trunc;
-  a.ent_full = entropy_full;
-  a.nsize = nucleus_size;
-  a.thresh = threshold;
-  a.flags = flags;
   return hip_status(rlk::launch_logits_rows(a, dtype, workspace,
                                             reinterpret_cast<hipStream_t>(stream)),
                     "rlk_logprob_from_logits launch");
+}
+
+rlk_status rlk_logprob_from_logits_noalloc(const void* logits, int32_t dtype, int64_t n_rows,
+                                           int64_t vocab, int64_t row_stride,
+                                           const int64_t* targets, float temperature,
+                                           float top_p, const float* temperature_per_row,
+                                           const float* top_p_per_row, int32_t top_k,
+                                           float* lp_full, float* lp_trunc,
+                                           float* entropy_trunc, float* entropy_full,
+                                           int32_t* nucleus_size, float* threshold,
+                                           uint8_t* flags, void* stream) {
+  rlk::RowArgs a;
+  rlk_status s = logits_args(logits, dtype, n_rows, vocab, row_stride, targets, temperature,
+                             top_p, temperature_per_row, top_p_per_row, top_k, lp_full,
+                             lp_trunc, entropy_trunc, entropy_full, nucleus_size, threshold,
+                             flags, &a);
+  if (s != RLK_OK) return s;
+  if (n_rows > rlk::kNoAllocMaxRows)
+    return fail(RLK_EINVAL, "n_rows=%lld exceeds the no-allocation limit of %lld rows",
+                (long long)n_rows, (long long)rlk::kNoAllocMaxRows);
+  if (n_rows == 0) return s;
+  const size_t need = rlk::logits_rows_workspace(n_rows, vocab, dtype);
+  if (need > rlk::kNoAllocScratchBytes)
+    return fail(RLK_EINVAL, "n_rows=%lld needs %zu bytes of scratch, more than %zu",
+                (long long)n_rows, need, rlk::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = rlk::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "rlk_logprob_from_logits_noalloc scratch lookup");
+  return hip_status(rlk::launch_logits_rows(a, dtype, scratch,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                    "rlk_logprob_from_logits_noalloc launch");
 }
 
 // ------------------------------------------------------------ retained support

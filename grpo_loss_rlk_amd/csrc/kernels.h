@@ -37,6 +37,13 @@ struct RowArgs {
 size_t logits_rows_workspace(int64_t n_rows, int64_t vocab, int dtype);
 hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipStream_t stream);
 
+// The no-allocation entry point's scratch: one static device array per GPU
+// (noalloc.hip), large enough for the logits-in workspace of this many rows.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+constexpr int64_t kNoAllocMaxRows = int64_t(kNoAllocScratchBytes);
+// This GPU's (the current device's) scratch address, looked up on first use.
+hipError_t noalloc_scratch(void** out);
+
 // ------------------------------------------------------------------ GRPO loss
 struct GrpoArgs {
   const float* lp_new;

@@ -124,6 +124,32 @@ rlk_status rlk_logprob_from_logits(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------------------
+ * Logits in, without allocating: rlk_logprob_from_logits for callers that
+ * cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, outputs and results as rlk_logprob_from_logits (bitwise),
+ * without workspace and workspace_bytes. Its scratch (the per-row hand-off
+ * flags of the bf16 row kernel, written for every row before they are read,
+ * so nothing needs clearing) is a static 1 MiB device array in the library:
+ * each GPU the library runs on holds its own copy until the process ends,
+ * its address looked up once per device on the first call there. This call
+ * allocates nothing and calls no allocating routine.
+ * Limits: n_rows <= 2^20 (RLK_EINVAL above that, before anything is launched),
+ * otherwise as rlk_logprob_from_logits.
+ * Concurrency: every call on one GPU shares that GPU's array, so calls that
+ * overlap on one GPU (e.g. on two streams) race and must be serialised by the
+ * caller; calls on different GPUs are independent.
+ * -------------------------------------------------------------------------- */
+rlk_status rlk_logprob_from_logits_noalloc(
+    const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab, int64_t row_stride,
+    const int64_t* targets, float temperature, float top_p,
+    const float* temperature_per_row, const float* top_p_per_row, int32_t top_k,
+    float* lp_full, float* lp_trunc, float* entropy_trunc,
+    float* entropy_full, int32_t* nucleus_size, float* threshold, uint8_t* flags,
+    void* stream);
+
+/* --------------------------------------------------------------------------
  * Logits in, retained support: log-probability and entropy over a
  * caller-supplied token set per row.
  *

@@ -79,6 +79,38 @@ def test_logits_validation(L, kw, status):
     assert len(L.rlk_last_error()) > 0
 
 
+def _noalloc_call(L, **kw):
+    a = dict(logits=FAKE, dtype=1, n=4, V=1000, stride=1000, targets=FAKE, T=0.7, p=0.95,
+             t_row=None, p_row=None, top_k=0, lpf=FAKE, lpt=FAKE, ht=FAKE)
+    a.update(kw)
+    return L.rlk_logprob_from_logits_noalloc(a["logits"], a["dtype"], a["n"], a["V"], a["stride"],
+                                             a["targets"], a["T"], a["p"], a["t_row"],
+                                             a["p_row"], a["top_k"], a["lpf"], a["lpt"], a["ht"],
+                                             None, None, None, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=(1 << 20) + 1), _native.RLK_EINVAL),      # beyond the static scratch
+    (dict(n=1 << 40), _native.RLK_EINVAL),
+    (dict(top_k=5), _native.RLK_EUNSUPPORTED),
+    (dict(T=0.0), _native.RLK_EINVAL),
+    (dict(stride=999), _native.RLK_EINVAL),
+    (dict(lpt=None), _native.RLK_EINVAL),
+    (dict(n=-1), _native.RLK_EINVAL),
+])
+def test_noalloc_validation(L, kw, status):
+    """The no-allocation entry point checks its arguments (and its row limit)
+    on the host before it touches the GPU."""
+    assert _noalloc_call(L, **kw) == status
+    assert len(L.rlk_last_error()) > 0
+    if kw.get("n", 0) > (1 << 20):
+        assert b"no-allocation limit" in L.rlk_last_error()
+
+
+def test_noalloc_empty_batch_is_a_noop(L):
+    assert _noalloc_call(L, n=0, logits=None, targets=None) == 0
+
+
 def test_logits_empty_batch_is_a_noop(L):
     assert _logits_call(L, n=0, logits=None, targets=None, ws=None) == 0
 
