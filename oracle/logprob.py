@@ -25,6 +25,13 @@ Nucleus S (top-p, keep-all-ties reading):
   Equivalently: walk groups from the top, stop at the first group whose
   inclusive cumulative mass reaches p, keep that whole group.
 
+Top-k (opt-in, k > 0; the consistency page's strict contract rejects it, the
+prime-rl release notes replay it in the trainer): first S_k = {z >= v_k}
+with v_k the k-th largest finite value (ties with it kept, so |S_k| >= k; k
+at or above the number of finite values keeps them all), then the top-p rule
+above on the distribution renormalised over S_k (masses relative to
+Z_k = sum_{i in S_k} exp(d_i)); p = 1 keeps S_k and reports tau = v_k.
+
 Truncated, renormalised distribution over S:
   Z_S      = sum_{i in S} exp(d_i)
   lp_trunc = d_y - log Z_S   if y in S, else -inf (flag bit 0)
@@ -81,20 +88,35 @@ def _nan_row(V: int, flags: int) -> RowResult:
                      np.zeros(V, dtype=bool), [])
 
 
-def nucleus(z: np.ndarray, T: float, p: float):
-    """Top-p nucleus of one row by sorting (the plain definition).
+def top_k_floor(z, top_k: int) -> float:
+    """v_k, the k-th largest finite value of the row (ties counted one by
+    one), or -inf when top-k is off (k = 0) or keeps every finite value."""
+    z = np.asarray(z, dtype=np.float64)
+    fin = np.sort(z[z > -np.inf])[::-1]
+    if top_k <= 0 or top_k >= fin.size:
+        return -np.inf
+    return float(fin[top_k - 1])
+
+
+def nucleus(z, T: float, p: float, top_k: int = 0):
+    """Top-k then top-p nucleus of one row by sorting (the plain definition).
 
     Returns (keep mask, tau, M_>(tau), M_>=(tau), alt masks). Masses are
-    probabilities of the tempered distribution. ``z`` must hold no NaN/+inf
-    and at least one finite value.
+    probabilities of the tempered distribution renormalised over the top-k
+    set (the whole row without top-k). ``z`` must hold no NaN/+inf and at
+    least one finite value.
     """
     z = np.asarray(z, dtype=np.float64)
     finite = z > -np.inf
+    vk = top_k_floor(z, top_k)
+    if vk > -np.inf:
+        finite = z >= vk                  # S_k: the top-k set, ties with v_k kept
     if p >= 1.0:
-        return finite.copy(), -np.inf, 0.0, 1.0, []
+        return finite.copy(), vk, 0.0, 1.0, []
     m = z[finite].max()
     e = np.where(finite, np.exp((z - m) / T), 0.0)
     order = np.argsort(-z, kind="stable")
+    order = order[finite[order]]          # the candidates, largest first
     zs = z[order]
     c = np.cumsum(e[order])
     Z = c[-1]
@@ -132,8 +154,8 @@ def truncated(z, y: int, T: float, keep: np.ndarray) -> tuple[float, float]:
     return float((z[y] - m) / T - logZs), float(h_trunc)
 
 
-def row(z, y: int, T: float, p: float) -> RowResult:
-    """All outputs for one row (fp64)."""
+def row(z, y: int, T: float, p: float, top_k: int = 0) -> RowResult:
+    """All outputs for one row (fp64); ``top_k`` = 0: no top-k."""
     z = np.asarray(z, dtype=np.float64)
     V = z.size
     flags = 0
@@ -150,7 +172,7 @@ def row(z, y: int, T: float, p: float) -> RowResult:
     Z = e.sum()
     logZ = np.log(Z)
     h_full = logZ - ed.sum() / Z
-    keep, tau, m_gt, m_ge, alts = nucleus(z, T, p)
+    keep, tau, m_gt, m_ge, alts = nucleus(z, T, p, top_k)
     if alts:
         flags |= FLAG_BOUNDARY
     lp_trunc, h_trunc = truncated(z, y, T, keep)
@@ -176,20 +198,21 @@ class BatchResult:
     alts: list           # per row: [(|S'|, lp_trunc', H_trunc') for each other valid nucleus]
 
 
-def logprob_from_logits(logits, targets, T, p) -> BatchResult:
+def logprob_from_logits(logits, targets, T, p, top_k=0) -> BatchResult:
     """Row-wise outputs for a [N, V] array of fp64-widened logits.
 
     ``T`` and ``p`` are scalars or per-row arrays (already the fp32 values the
-    ABI receives, widened).
+    ABI receives, widened); ``top_k`` a scalar or per-row array (0: off).
     """
     logits = np.asarray(logits, dtype=np.float64)
     N = logits.shape[0]
     Ts = np.broadcast_to(np.asarray(T, dtype=np.float64), (N,))
     ps = np.broadcast_to(np.asarray(p, dtype=np.float64), (N,))
+    ks = np.broadcast_to(np.asarray(top_k, dtype=np.int64), (N,))
     out = BatchResult(*(np.empty(N) for _ in range(4)), np.empty(N, dtype=np.int64),
                       np.empty(N), np.empty(N, dtype=np.uint8), [])
     for n in range(N):
-        r = row(logits[n], int(targets[n]), float(Ts[n]), float(ps[n]))
+        r = row(logits[n], int(targets[n]), float(Ts[n]), float(ps[n]), int(ks[n]))
         out.lp_full[n], out.h_full[n] = r.lp_full, r.h_full
         out.lp_trunc[n], out.h_trunc[n] = r.lp_trunc, r.h_trunc
         out.size[n], out.tau[n], out.flags[n] = r.size, r.tau, r.flags

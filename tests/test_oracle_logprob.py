@@ -344,3 +344,106 @@ def test_batch_boundary_alternatives_are_the_other_valid_sets():
     # a row away from the boundary has no alternatives
     far = L.logprob_from_logits(z[None, :], y[:1], 1.0, 0.6)
     assert far.alts[0] == [] and not far.flags[0] & L.FLAG_BOUNDARY
+
+
+# ------------------------------------------------------------------ top-k
+
+def _kth_by_count(z, k):
+    """v_k by counting: the largest row value v with #{z_i >= v} >= k."""
+    vals = sorted(set(z.tolist()), reverse=True)
+    for v in vals:
+        if sum(1 for x in z if x >= v) >= k:
+            return v
+    return vals[-1]
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_top_k_then_top_p_bruteforce(ties):
+    """S = the smallest value-closed set inside the top-k set S_k (ties with the
+    k-th value kept) whose mass, renormalised over S_k, reaches p: checked by
+    enumerating subsets of S_k on tiny rows."""
+    rng = np.random.default_rng(31 + ties)
+    checked = 0
+    for _ in range(200):
+        V = int(rng.integers(1, 10))
+        z = rng.integers(-3, 3, V).astype(float) if ties else rng.normal(0, 2, V)
+        k = int(rng.integers(1, V + 2))
+        T = float(rng.choice(TEMPS))
+        p = float(rng.choice([rng.uniform(0.05, 0.999), 1.0]))
+        vk = _kth_by_count(z, k)
+        Sk = z >= vk
+        keep, tau, _, _, alts = L.nucleus(z, T, p, top_k=k)
+        assert np.all(keep <= Sk)                                  # inside the top-k set
+        if p >= 1.0:
+            np.testing.assert_array_equal(keep, Sk)
+            continue
+        if alts:
+            continue
+        idx = np.flatnonzero(Sk)
+        prob = scipy.special.softmax(z[idx] / T)                   # renormalised over S_k
+        kmin = _min_card(prob, p)
+        kth = np.sort(z[idx])[::-1][kmin - 1]
+        np.testing.assert_array_equal(keep, Sk & (z >= kth))
+        checked += 1
+    assert checked > 50
+
+
+def test_top_k_closed_forms():
+    rng = np.random.default_rng(41)
+    z = rng.normal(0, 2, 50)
+    y = int(np.argmax(z))
+    r = L.row(z, y, 0.7, 1.0, top_k=1)                 # k = 1, distinct values: the argmax
+    assert r.size == 1 and r.lp_trunc == 0.0 and r.h_trunc == 0.0 and r.tau == z.max()
+    r = L.row(z, (y + 1) % 50, 0.7, 1.0, top_k=1)
+    assert r.lp_trunc == -math.inf and r.flags & L.FLAG_OUTSIDE
+    # k levels: k tokens at a, the rest at b < a; top-k = k keeps exactly the k
+    for k in (1, 3, 7):
+        zz = np.array([2.5] * k + [-1.0] * (20 - k))
+        r = L.row(zz, 0, 0.9, 1.0, top_k=k)
+        assert r.size == k and r.tau == 2.5
+        assert r.lp_trunc == pytest.approx(-math.log(k), abs=1e-14)
+        assert r.h_trunc == pytest.approx(math.log(k), abs=1e-14)
+        # the full statistics stay those of the whole row
+        full = scipy.special.log_softmax(zz / 0.9)
+        assert r.lp_full == pytest.approx(full[0], rel=1e-13)
+    # ties at the k-th value are all kept: 4 equal values, k = 2
+    zz = np.array([3.0, 1.0, 1.0, 1.0, 1.0, -2.0])
+    r = L.row(zz, 4, 1.0, 1.0, top_k=2)
+    assert r.size == 5 and r.tau == 1.0
+    # k at or above the finite count: no filtering
+    zz = np.array([1.0, -np.inf, 0.5, 0.25])
+    for k in (3, 4, 100):
+        a, b = L.row(zz, 0, 0.8, 0.9, top_k=k), L.row(zz, 0, 0.8, 0.9)
+        assert (a.size, a.lp_trunc, a.h_trunc) == (b.size, b.lp_trunc, b.h_trunc)
+    # uniform row: every k keeps the whole tie group
+    r = L.row(np.full(16, 0.5), 3, 0.7, 0.3, top_k=5)
+    assert r.size == 16 and r.lp_trunc == pytest.approx(-math.log(16), abs=1e-14)
+
+
+def test_top_k_invariants():
+    """Renormalising over S_k only raises relative masses, so the top-k/top-p
+    set lies inside both S_k and the plain top-p set; the full statistics do
+    not depend on k; k = 0 is the plain rule."""
+    for z, T, p in _rows(17, n=40):
+        for k in (1, 2, 5, 17, 60):
+            keep, tau, *_ = L.nucleus(z, T, p, top_k=k)
+            keep0, *_ = L.nucleus(z, T, p)
+            vk = L.top_k_floor(z, k)
+            assert np.all(keep <= (z >= vk)) and np.all(keep <= keep0)
+            assert keep[np.argmax(z)]
+            assert np.all(keep[z >= z[keep].min()])             # value-closed
+            a, b = L.row(z, 0, T, p, top_k=k), L.row(z, 0, T, p)
+            assert a.lp_full == b.lp_full and a.h_full == b.h_full
+        np.testing.assert_array_equal(L.nucleus(z, T, p, top_k=0)[0], L.nucleus(z, T, p)[0])
+
+
+def test_top_k_per_row_batch():
+    rng = np.random.default_rng(43)
+    z = rng.normal(0, 2, (6, 40))
+    y = rng.integers(0, 40, 6)
+    ks = np.array([0, 1, 3, 40, 7, 2])
+    b = L.logprob_from_logits(z, y, 0.7, 0.95, top_k=ks)
+    for n in range(6):
+        r = L.row(z[n], int(y[n]), 0.7, 0.95, top_k=int(ks[n]))
+        assert b.size[n] == r.size and b.tau[n] == r.tau
+        assert b.lp_trunc[n] == r.lp_trunc or (math.isnan(b.lp_trunc[n]) and math.isnan(r.lp_trunc))

@@ -73,3 +73,22 @@ def test_sample_row_limits():
     zm = z.copy()
     zm[::2] = -np.inf                              # -inf tokens are never drawn
     assert all(sampling.sample_row(zm, 1.0, 1.0, 2, off, 0) % 2 == 1 for off in range(200))
+
+
+def test_sample_row_law_with_top_k():
+    """With top-k the draws follow the tempered softmax renormalised over the
+    top-k/top-p set, and never leave it."""
+    from oracle import logprob as L
+    z = np.array([2.0, 1.6, 1.5, 1.5, 0.3, -0.2, -1.0, 0.9])
+    T, p, k = 0.8, 0.97, 4
+    keep, *_ = L.nucleus(z, T, p, top_k=k)
+    assert keep.sum() == 4
+    q = np.zeros(z.size)
+    q[keep] = np.exp(z[keep] / T) / np.exp(z[keep] / T).sum()
+    draws = 20000
+    counts = np.zeros(z.size)
+    for off in range(draws):
+        counts[sampling.sample_row(z, T, p, 7, off, 0, top_k=k)] += 1
+    assert counts[~keep].sum() == 0
+    sd = np.sqrt(draws * q * (1 - q)) + 1e-9
+    assert np.all(np.abs(counts - draws * q) <= 5 * sd)
