@@ -43,16 +43,25 @@ def _f32_opt(x, n, device):
     return x
 
 
+def _i32_opt(x, n, device):
+    if x is None:
+        return None
+    x = torch.as_tensor(x, dtype=torch.int32, device=device).contiguous()
+    assert x.numel() == n
+    return x
+
+
 def logprob_from_logits(logits: torch.Tensor, targets: torch.Tensor, temperature: float,
                         top_p: float = 1.0, *, vocab: int | None = None,
                         temperature_per_row=None, top_p_per_row=None, top_k: int = 0,
-                        want_entropy_full: bool = True, want_nucleus: bool = True) -> dict:
-    """Full and top-p truncated logprob / entropy for each row of ``logits``.
+                        top_k_per_row=None, want_entropy_full: bool = True,
+                        want_nucleus: bool = True) -> dict:
+    """Full and top-k/top-p truncated logprob / entropy for each row of ``logits``.
 
     ``logits`` is [N, row_stride] fp32 or bf16 on the GPU (row-major, rows may
-    be padded: only the first ``vocab`` entries are scored). Returns a dict of
-    tensors: lp_full, lp_trunc, entropy_trunc, entropy_full, nucleus_size,
-    threshold, flags.
+    be padded: only the first ``vocab`` entries are scored). ``top_k`` = 0 is
+    no top-k. Returns a dict of tensors: lp_full, lp_trunc, entropy_trunc,
+    entropy_full, nucleus_size, threshold, flags.
     """
     if logits.dtype == torch.float32:
         dtype = DTYPE_F32
@@ -75,12 +84,13 @@ def logprob_from_logits(logits: torch.Tensor, targets: torch.Tensor, temperature
            "flags": torch.empty(N, device=dev, dtype=torch.uint8)}
     t_row = _f32_opt(temperature_per_row, N, dev)
     p_row = _f32_opt(top_p_per_row, N, dev)
+    k_row = _i32_opt(top_k_per_row, N, dev)
     L = lib()
     ws_n = L.rlk_logprob_from_logits_workspace_size(N, V, dtype)
     ws = _workspace(ws_n, dev)
     st = L.rlk_logprob_from_logits(
         _ptr(logits), dtype, N, V, logits.stride(0) if N > 0 else V, _ptr(targets),
-        float(temperature), float(top_p), _ptr(t_row), _ptr(p_row), int(top_k),
+        float(temperature), float(top_p), _ptr(t_row), _ptr(p_row), int(top_k), _ptr(k_row),
         _ptr(out["lp_full"]), _ptr(out["lp_trunc"]), _ptr(out["entropy_trunc"]),
         _ptr(out["entropy_full"]), _ptr(out["nucleus_size"]), _ptr(out["threshold"]),
         _ptr(out["flags"]), _ptr(ws), ws_n, _stream(dev))
@@ -90,13 +100,14 @@ def logprob_from_logits(logits: torch.Tensor, targets: torch.Tensor, temperature
 
 def logprob_from_support(logits: torch.Tensor, targets: torch.Tensor, temperature: float,
                          support_offsets: torch.Tensor, support_ids: torch.Tensor, *,
-                         vocab: int | None = None, check_top_p: float = 0.0) -> dict:
+                         vocab: int | None = None, check_top_p: float = 0.0,
+                         check_top_k: int = 0) -> dict:
     """Logprob / entropy of each row over a caller-supplied retained set (CSR).
 
     ``support_offsets`` [N + 1] int64 and ``support_ids`` int32 (strictly
     increasing ids per row) on the GPU. ``check_top_p`` in (0, 1] also
-    recomputes each row's nucleus and flags a set that differs from it.
-    Returns logprob, entropy, flags.
+    recomputes each row's nucleus (with top-k ``check_top_k``, 0 = none) and
+    flags a set that differs from it. Returns logprob, entropy, flags.
     """
     if logits.dtype == torch.float32:
         dtype = DTYPE_F32
@@ -123,18 +134,21 @@ def logprob_from_support(logits: torch.Tensor, targets: torch.Tensor, temperatur
     st = L.rlk_logprob_from_support(
         _ptr(logits), dtype, N, V, logits.stride(0) if N > 0 else V, _ptr(targets),
         float(temperature), _ptr(offsets), _ptr(ids) if ids.numel() else None, ids.numel(),
-        float(check_top_p), _ptr(out["logprob"]), _ptr(out["entropy"]), _ptr(out["flags"]),
+        float(check_top_p), int(check_top_k), _ptr(out["logprob"]), _ptr(out["entropy"]),
+        _ptr(out["flags"]),
         _ptr(ws), ws_n, _stream(dev))
     _native.check(st, "rlk_logprob_from_support")
     return out
 
 
 def sample_top_p(logits: torch.Tensor, temperature: float, top_p: float, seed: int,
-                 offset: int = 0, *, row_keys=None, vocab: int | None = None) -> dict:
-    """Draw one token per row from the tempered top-p nucleus (seeded
+                 offset: int = 0, *, row_keys=None, vocab: int | None = None, top_k: int = 0,
+                 temperature_per_row=None, top_p_per_row=None, top_k_per_row=None) -> dict:
+    """Draw one token per row from the tempered top-k/top-p nucleus (seeded
     Gumbel-max, Philox-4x32-10 uniforms) and score it with the logits-in
-    kernel. Returns samples (int64, -1 for a row without a finite logit),
-    logprob, entropy, nucleus_size, flags."""
+    kernel. Parameters are scalars or per-row arrays (``top_k`` 0: none).
+    Returns samples (int64, -1 for a row without a finite logit or with an
+    out-of-range parameter), logprob, entropy, nucleus_size, flags."""
     if logits.dtype == torch.float32:
         dtype = DTYPE_F32
     elif logits.dtype == torch.bfloat16:
@@ -156,12 +170,16 @@ def sample_top_p(logits: torch.Tensor, temperature: float, top_p: float, seed: i
            "logprob": torch.empty(N, **f), "entropy": torch.empty(N, **f),
            "nucleus_size": torch.empty(N, device=dev, dtype=torch.int32),
            "flags": torch.empty(N, device=dev, dtype=torch.uint8)}
+    t_row = _f32_opt(temperature_per_row, N, dev)
+    p_row = _f32_opt(top_p_per_row, N, dev)
+    k_row = _i32_opt(top_k_per_row, N, dev)
     L = lib()
     ws_n = L.rlk_sample_top_p_workspace_size(N, V, dtype)
     ws = _workspace(ws_n, dev)
     st = L.rlk_sample_top_p(
         _ptr(logits), dtype, N, V, logits.stride(0) if N > 0 else V, float(temperature),
-        float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, _ptr(keys),
+        float(top_p), int(top_k), _ptr(t_row), _ptr(p_row), _ptr(k_row),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, _ptr(keys),
         _ptr(out["samples"]), _ptr(out["logprob"]), _ptr(out["entropy"]),
         _ptr(out["nucleus_size"]), _ptr(out["flags"]), _ptr(ws), ws_n, _stream(dev))
     _native.check(st, "rlk_sample_top_p")
@@ -192,7 +210,7 @@ def logprob_fused_linear(hidden: torch.Tensor, weight: torch.Tensor, targets: to
            "nucleus_size": torch.empty(N, device=dev, dtype=torch.int32),
            "flags": torch.empty(N, device=dev, dtype=torch.uint8)}
     L = lib()
-    ws_n = L.rlk_logprob_fused_linear_workspace_size(N, H, V, float(top_p))
+    ws_n = L.rlk_logprob_fused_linear_workspace_size(N, H, V, float(top_p), int(top_k))
     ws = _workspace(ws_n, dev)
     st = L.rlk_logprob_fused_linear(
         _ptr(hidden), _ptr(weight), N, H, V, hidden.stride(0), weight.stride(0), _ptr(targets),

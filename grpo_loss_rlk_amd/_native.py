@@ -42,20 +42,21 @@ SIGNATURES = {
     "rlk_last_error": (ctypes.c_char_p, []),
     "rlk_logprob_from_logits_workspace_size": (c_sz, [c_i64, c_i64, c_i32]),
     "rlk_logprob_from_logits": (c_i32, [
-        c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_f32, c_vp, c_vp, c_i32,
+        c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_f32, c_vp, c_vp, c_i32, c_vp,
         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "rlk_logprob_from_logits_noalloc": (c_i32, [
-        c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_f32, c_vp, c_vp, c_i32,
+        c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_f32, c_vp, c_vp, c_i32, c_vp,
         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "rlk_logprob_from_support_workspace_size": (c_sz, [c_i64, c_i64, c_i32, c_f32]),
     "rlk_logprob_from_support": (c_i32, [
-        c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_vp, c_vp, c_i64, c_f32,
+        c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_f32, c_vp, c_vp, c_i64, c_f32, c_i32,
         c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "rlk_sample_top_p_workspace_size": (c_sz, [c_i64, c_i64, c_i32]),
     "rlk_sample_top_p": (c_i32, [
-        c_vp, c_i32, c_i64, c_i64, c_i64, c_f32, c_f32, ctypes.c_uint64, ctypes.c_uint32, c_vp,
+        c_vp, c_i32, c_i64, c_i64, c_i64, c_f32, c_f32, c_i32, c_vp, c_vp, c_vp,
+        ctypes.c_uint64, ctypes.c_uint32, c_vp,
         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
-    "rlk_logprob_fused_linear_workspace_size": (c_sz, [c_i64, c_i64, c_i64, c_f32]),
+    "rlk_logprob_fused_linear_workspace_size": (c_sz, [c_i64, c_i64, c_i64, c_f32, c_i32]),
     "rlk_logprob_fused_linear": (c_i32, [
         c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_f32, c_f32, c_i32,
         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),

@@ -40,8 +40,7 @@ rlk_status hip_status(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 rlk_status check_sampling(float temperature, float top_p, int32_t top_k) {
-  if (top_k != 0)
-    return fail(RLK_EUNSUPPORTED, "top_k=%d: top-k filtering is rejected, not ignored", top_k);
+  if (top_k < 0) return fail(RLK_EINVAL, "top_k=%d must be >= 0 (0: no top-k)", top_k);
   if (!(temperature > 0.f) || !std::isfinite(temperature))
     return fail(RLK_EINVAL, "temperature=%g must be finite and > 0", double(temperature));
   if (!(top_p > 0.f) || !(top_p <= 1.f))
@@ -98,7 +97,8 @@ namespace {
 rlk_status logits_args(const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab,
                        int64_t row_stride, const int64_t* targets, float temperature,
                        float top_p, const float* temperature_per_row,
-                       const float* top_p_per_row, int32_t top_k, float* lp_full,
+                       const float* top_p_per_row, int32_t top_k,
+                       const int32_t* top_k_per_row, float* lp_full,
                        float* lp_trunc, float* entropy_trunc, float* entropy_full,
                        int32_t* nucleus_size, float* threshold, uint8_t* flags,
                        rlk::RowArgs* a) {
@@ -119,7 +119,7 @@ rlk_status logits_args(const void* logits, int32_t dtype, int64_t n_rows, int64_
   if (!aligned(logits, esz) || !aligned(targets, 8) || !aligned(lp_full, 4) ||
       !aligned(lp_trunc, 4) || !aligned(entropy_trunc, 4) || !aligned(entropy_full, 4) ||
       !aligned(nucleus_size, 4) || !aligned(threshold, 4) || !aligned(temperature_per_row, 4) ||
-      !aligned(top_p_per_row, 4))
+      !aligned(top_p_per_row, 4) || !aligned(top_k_per_row, 4))
     return fail(RLK_EINVAL, "an array is not naturally aligned");
   *a = rlk::RowArgs{};
   a->logits = logits;
@@ -131,6 +131,8 @@ rlk_status logits_args(const void* logits, int32_t dtype, int64_t n_rows, int64_
   a->top_p = top_p;
   a->t_row = temperature_per_row;
   a->p_row = top_p_per_row;
+  a->top_k = top_k;
+  a->k_row = top_k_per_row;
   a->lp_full = lp_full;
   a->lp_trunc = lp_trunc;
   a->ent_trunc = entropy_trunc;
@@ -149,15 +151,15 @@ rlk_status rlk_logprob_from_logits(const void* logits, int32_t dtype, int64_t n_
                                    int64_t vocab, int64_t row_stride, const int64_t* targets,
                                    float temperature, float top_p,
                                    const float* temperature_per_row, const float* top_p_per_row,
-                                   int32_t top_k, float* lp_full, float* lp_trunc,
-                                   float* entropy_trunc, float* entropy_full,
+                                   int32_t top_k, const int32_t* top_k_per_row, float* lp_full,
+                                   float* lp_trunc, float* entropy_trunc, float* entropy_full,
                                    int32_t* nucleus_size, float* threshold, uint8_t* flags,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   rlk::RowArgs a;
   rlk_status s = logits_args(logits, dtype, n_rows, vocab, row_stride, targets, temperature,
-                             top_p, temperature_per_row, top_p_per_row, top_k, lp_full,
-                             lp_trunc, entropy_trunc, entropy_full, nucleus_size, threshold,
-                             flags, &a);
+                             top_p, temperature_per_row, top_p_per_row, top_k, top_k_per_row,
+                             lp_full, lp_trunc, entropy_trunc, entropy_full, nucleus_size,
+                             threshold, flags, &a);
   if (s != RLK_OK || n_rows == 0) return s;
   s = check_workspace(workspace, workspace_bytes,
                       rlk_logprob_from_logits_workspace_size(n_rows, vocab, dtype));
@@ -172,15 +174,15 @@ rlk_status rlk_logprob_from_logits_noalloc(const void* logits, int32_t dtype, in
                                            const int64_t* targets, float temperature,
                                            float top_p, const float* temperature_per_row,
                                            const float* top_p_per_row, int32_t top_k,
-                                           float* lp_full, float* lp_trunc,
-                                           float* entropy_trunc, float* entropy_full,
-                                           int32_t* nucleus_size, float* threshold,
-                                           uint8_t* flags, void* stream) {
+                                           const int32_t* top_k_per_row, float* lp_full,
+                                           float* lp_trunc, float* entropy_trunc,
+                                           float* entropy_full, int32_t* nucleus_size,
+                                           float* threshold, uint8_t* flags, void* stream) {
   rlk::RowArgs a;
   rlk_status s = logits_args(logits, dtype, n_rows, vocab, row_stride, targets, temperature,
-                             top_p, temperature_per_row, top_p_per_row, top_k, lp_full,
-                             lp_trunc, entropy_trunc, entropy_full, nucleus_size, threshold,
-                             flags, &a);
+                             top_p, temperature_per_row, top_p_per_row, top_k, top_k_per_row,
+                             lp_full, lp_trunc, entropy_trunc, entropy_full, nucleus_size,
+                             threshold, flags, &a);
   if (s != RLK_OK) return s;
   if (n_rows > rlk::kNoAllocMaxRows)
     return fail(RLK_EINVAL, "n_rows=%lld exceeds the no-allocation limit of %lld rows",
@@ -219,9 +221,9 @@ rlk_status rlk_logprob_from_support(const void* logits, int32_t dtype, int64_t n
                                     int64_t vocab, int64_t row_stride, const int64_t* targets,
                                     float temperature, const int64_t* support_offsets,
                                     const int32_t* support_ids, int64_t n_support,
-                                    float check_top_p, float* logprob, float* entropy,
-                                    uint8_t* flags, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+                                    float check_top_p, int32_t check_top_k, float* logprob,
+                                    float* entropy, uint8_t* flags, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   if (dtype != RLK_DTYPE_F32 && dtype != RLK_DTYPE_BF16)
     return fail(RLK_EINVAL, "dtype=%d is not RLK_DTYPE_F32 or RLK_DTYPE_BF16", dtype);
   if (!(temperature > 0.f) || !std::isfinite(temperature))
@@ -229,6 +231,9 @@ rlk_status rlk_logprob_from_support(const void* logits, int32_t dtype, int64_t n
   const bool check = check_top_p != 0.f;
   if (check && !(check_top_p > 0.f && check_top_p <= 1.f))
     return fail(RLK_EINVAL, "check_top_p=%g must be 0 or lie in (0, 1]", double(check_top_p));
+  if (check_top_k < 0 || (check_top_k > 0 && !check))
+    return fail(RLK_EINVAL, "check_top_k=%d must be >= 0, and 0 without a check_top_p",
+                check_top_k);
   if (n_rows < 0) return fail(RLK_EINVAL, "n_rows=%lld < 0", (long long)n_rows);
   if (n_rows >= (int64_t(1) << 31))
     return fail(RLK_EINVAL, "n_rows=%lld must be below 2^31", (long long)n_rows);
@@ -277,6 +282,7 @@ rlk_status rlk_logprob_from_support(const void* logits, int32_t dtype, int64_t n
     r.targets = targets;
     r.temperature = temperature;
     r.top_p = check_top_p;
+    r.top_k = check_top_k;
     r.lp_full = reinterpret_cast<float*>(w);
     r.lp_trunc = reinterpret_cast<float*>(w + f4);
     r.ent_trunc = reinterpret_cast<float*>(w + 2 * f4);
@@ -303,14 +309,15 @@ size_t rlk_sample_top_p_workspace_size(int64_t n_rows, int64_t vocab, int32_t dt
 }
 
 rlk_status rlk_sample_top_p(const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab,
-                            int64_t row_stride, float temperature, float top_p, uint64_t seed,
-                            uint32_t offset, const int64_t* row_keys, int64_t* samples,
-                            float* logprob, float* entropy, int32_t* nucleus_size,
-                            uint8_t* flags, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            int64_t row_stride, float temperature, float top_p, int32_t top_k,
+                            const float* temperature_per_row, const float* top_p_per_row,
+                            const int32_t* top_k_per_row, uint64_t seed, uint32_t offset,
+                            const int64_t* row_keys, int64_t* samples, float* logprob,
+                            float* entropy, int32_t* nucleus_size, uint8_t* flags,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != RLK_DTYPE_F32 && dtype != RLK_DTYPE_BF16)
     return fail(RLK_EINVAL, "dtype=%d is not RLK_DTYPE_F32 or RLK_DTYPE_BF16", dtype);
-  rlk_status s = check_sampling(temperature, top_p, 0);
+  rlk_status s = check_sampling(temperature, top_p, top_k);
   if (s != RLK_OK) return s;
   if (n_rows < 0) return fail(RLK_EINVAL, "n_rows=%lld < 0", (long long)n_rows);
   if (n_rows >= (int64_t(1) << 31))
@@ -324,7 +331,9 @@ rlk_status rlk_sample_top_p(const void* logits, int32_t dtype, int64_t n_rows, i
   const size_t esz = dtype == RLK_DTYPE_F32 ? 4 : 2;
   if (!logits || !samples) return fail(RLK_EINVAL, "logits and samples are required");
   if (!aligned(logits, esz) || !aligned(samples, 8) || !aligned(row_keys, 8) ||
-      !aligned(logprob, 4) || !aligned(entropy, 4) || !aligned(nucleus_size, 4))
+      !aligned(logprob, 4) || !aligned(entropy, 4) || !aligned(nucleus_size, 4) ||
+      !aligned(temperature_per_row, 4) || !aligned(top_p_per_row, 4) ||
+      !aligned(top_k_per_row, 4))
     return fail(RLK_EINVAL, "an array is not naturally aligned");
   s = check_workspace(workspace, workspace_bytes,
                       rlk_sample_top_p_workspace_size(n_rows, vocab, dtype));
@@ -349,6 +358,10 @@ rlk_status rlk_sample_top_p(const void* logits, int32_t dtype, int64_t n_rows, i
   r.row_stride = row_stride;
   r.temperature = temperature;
   r.top_p = top_p;
+  r.t_row = temperature_per_row;
+  r.p_row = top_p_per_row;
+  r.top_k = top_k;
+  r.k_row = top_k_per_row;
   // 1. each row's nucleus: threshold, entropy, size, flags, and the row max
   // and log Z_S its tokens are scored with (the target is a placeholder)
   s = hip_status(rlk::launch_fill_i64(zero_t, n_rows, 0, st), "rlk_sample_top_p fill");
@@ -370,6 +383,7 @@ rlk_status rlk_sample_top_p(const void* logits, int32_t dtype, int64_t n_rows, i
   a.vocab = vocab;
   a.row_stride = row_stride;
   a.temperature = temperature;
+  a.t_row = temperature_per_row;
   a.seed = seed;
   a.offset = offset;
   a.row_keys = row_keys;
@@ -412,10 +426,9 @@ rlk_status check_fused_shapes(const void* hidden, const void* weight, int64_t N,
 }  // namespace
 
 size_t rlk_logprob_fused_linear_workspace_size(int64_t n_rows, int64_t hidden_size, int64_t vocab,
-                                               float top_p) {
-  (void)top_p;
+                                               float top_p, int32_t top_k) {
   if (n_rows < 0 || vocab < 1) return 0;
-  return rlk::fused_fwd_workspace(n_rows, hidden_size, vocab, top_p);
+  return rlk::fused_fwd_workspace(n_rows, hidden_size, vocab, top_p, top_k);
 }
 
 rlk_status rlk_logprob_fused_linear(const void* hidden, const void* weight, int64_t n_rows,
@@ -433,8 +446,9 @@ rlk_status rlk_logprob_fused_linear(const void* hidden, const void* weight, int6
   if (!aligned(logprob, 4) || !aligned(entropy, 4) || !aligned(saved, 4) ||
       !aligned(nucleus_size, 4))
     return fail(RLK_EINVAL, "an output array is not naturally aligned");
-  s = check_workspace(workspace, workspace_bytes,
-                      rlk_logprob_fused_linear_workspace_size(n_rows, hidden_size, vocab, top_p));
+  s = check_workspace(
+      workspace, workspace_bytes,
+      rlk_logprob_fused_linear_workspace_size(n_rows, hidden_size, vocab, top_p, top_k));
   if (s != RLK_OK) return s;
   rlk::FusedFwdArgs a{};
   a.h = reinterpret_cast<const uint16_t*>(hidden);
@@ -448,6 +462,7 @@ rlk_status rlk_logprob_fused_linear(const void* hidden, const void* weight, int6
   a.c2 = float(1.4426950408889634 / double(temperature));
   a.temperature = temperature;
   a.top_p = top_p;
+  a.top_k = top_k;
   a.logprob = logprob;
   a.entropy = entropy;
   a.saved = saved;

@@ -14,7 +14,7 @@
 //     "Canonical topology strategy", combines vocabulary shards in one fixed
 //     order).
 //
-// Forward at top-p < 1 (the cut needs the whole row's distribution): per
+// Forward at top-p < 1 or with top-k (the cut needs the whole row): per
 // block of kTopPRowBlock tokens, fwd_logits_tile writes the block's fp32
 // logits z = h W^T to a workspace scratch [rows, Vs] and the logits-in row
 // kernel (max, nucleus by value histogram, truncated statistics) cuts each
@@ -337,9 +337,9 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V, float top_p) {
+size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V, float top_p, int32_t top_k) {
   (void)H;
-  if (top_p < 1.f) {
+  if (top_p < 1.f || top_k > 0) {
     const int64_t R = N < kTopPRowBlock ? N : kTopPRowBlock;
     return align256(size_t(R) * size_t(logits_ld(V)) * 4) + align256(size_t(N) * 4) +
            2 * align256(size_t(R) * 4) + logits_rows_workspace(R, V, 0);
@@ -351,7 +351,7 @@ size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V, float top_p) {
 hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream) {
   if (a.N == 0) return hipSuccess;
   char* ws = reinterpret_cast<char*>(workspace);
-  if (a.top_p < 1.f) {
+  if (a.top_p < 1.f || a.top_k > 0) {
     const int64_t R = a.N < kTopPRowBlock ? a.N : kTopPRowBlock, zs = logits_ld(a.V);
     float* z = reinterpret_cast<float*>(ws);
     size_t off = align256(size_t(R) * size_t(zs) * 4);
@@ -378,6 +378,7 @@ hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream)
       ra.targets = a.targets + r0;
       ra.temperature = a.temperature;
       ra.top_p = a.top_p;
+      ra.top_k = a.top_k;
       ra.lp_full = lp_full + r0;
       ra.lp_trunc = a.logprob + r0;
       ra.ent_trunc = a.entropy + r0;

@@ -21,6 +21,7 @@ struct FusedFwdArgs {
   float4* part;            // workspace: [ceil(V/256), N] tile partials
   float* zy;               // workspace: [N] target logits
   float temperature, top_p;
+  int32_t top_k;           // 0: off; > 0 takes the stored-logits path at any top-p
 };
 
 // Tokens per row block of the top-p < 1 path: the block's fp32 logits are
@@ -32,7 +33,7 @@ struct FusedFwdArgs {
 // 46.0 ms with 16384).
 constexpr int64_t kTopPRowBlock = 16384;
 
-size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V, float top_p);
+size_t fused_fwd_workspace(int64_t N, int64_t H, int64_t V, float top_p, int32_t top_k);
 hipError_t launch_fused_fwd(FusedFwdArgs a, void* workspace, hipStream_t stream);
 
 struct FusedBwdArgs {

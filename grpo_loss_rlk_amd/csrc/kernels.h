@@ -15,6 +15,10 @@ struct RowArgs {
   float temperature, top_p;
   const float* t_row;     // nullable per-row temperature
   const float* p_row;     // nullable per-row top-p
+  int32_t top_k;          // top-k for every row (0: off), unless k_row is given
+  const int32_t* k_row;   // nullable per-row top-k (0: off; < 0 flags the row)
+  const float* kfloor;    // nullable [n_rows]: each row's top-k floor v_k (-inf: none),
+                          // set by the launcher when top-k is requested
   float* lp_full;
   float* lp_trunc;
   float* ent_trunc;
@@ -39,8 +43,8 @@ hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipS
 
 // The no-allocation entry point's scratch: one static device array per GPU
 // (noalloc.hip), large enough for the logits-in workspace of this many rows.
-constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
-constexpr int64_t kNoAllocMaxRows = int64_t(kNoAllocScratchBytes);
+constexpr int64_t kNoAllocMaxRows = int64_t(1) << 20;
+constexpr size_t kNoAllocScratchBytes = 5 * size_t(kNoAllocMaxRows);   // flags + fp32 floors
 // This GPU's (the current device's) scratch address, looked up on first use.
 hipError_t noalloc_scratch(void** out);
 

@@ -6,16 +6,20 @@
 // with the logprob): for a row z, d_i = (z_i - max z)/T, the full softmax
 // statistics, the nucleus S = {z >= tau} with tau the lowest row value whose
 // strictly-higher mass is below p (all ties kept), and the statistics of the
-// distribution renormalised over S.
+// distribution renormalised over S. With the opt-in top-k, a first kernel
+// (topk_floor_rows) finds each row's k-th largest value v_k and the cut then
+// runs on the values >= v_k only, its masses relative to their sum (the
+// prime-rl v0.10.0 release notes, "2. RL Algorithms", replay top-k in the
+// trainer); at top-p 1 the nucleus is {z >= v_k}.
 //
-// Two kernels, chosen per call by dtype and vocabulary size only (never by the
-// number of rows, so a row's result does not depend on its batch):
+// Row kernels, chosen per call by dtype and vocabulary size only (never by
+// the number of rows, so a row's result does not depend on its batch):
 //
 //  * bf16_hist_rows: bf16 rows with V >= 16384. A bf16 value has only 65536
 //    bit patterns, so one streaming pass that counts each pattern in LDS
 //    captures the whole row. Everything after that -- max, Z, entropy, the
 //    top-p cut, the truncated sums -- is arithmetic over the distinct values
-//    (fp32 masses, fp64 sums in a fixed order), so HBM is read once at a few
+//    (fp32 masses, exact fixed-point sums), so HBM is read once at a few
 //    VALU ops per element. The counters (16-bit, a positive and a negative
 //    pattern per 32-bit word) cover the magnitudes with bf16 exponent field
 //    0x40..0xbf, |z| in [2^-63, 2^64): 64 KB per buffer. Two buffers let 12
@@ -23,6 +27,8 @@
 //    one. Zeros and -inf are tallied on the side; a row holding +inf, NaN,
 //    extreme magnitudes or one value more than 65535 times is handed to the
 //    generic kernel.
+//
+//  * f32_rows: fp32 rows (below).
 //
 //  * generic_rows: any dtype and size. Multi-pass over the row: max, then
 //    exp / Z / entropy with a 12-bit radix histogram of fixed-point masses,
@@ -44,6 +50,14 @@ constexpr double kBoundaryEps = 1e-6;
 
 RLK_DEV bool param_ok(float T, float p) {
   return T > 0.f && T <= 3.4e38f && p > 0.f && p <= 1.f;  // NaN fails every compare
+}
+
+// The row's top-k (0: off) and its floor v_k (-inf: no top-k cut).
+RLK_DEV int32_t row_top_k(const RowArgs& a, int64_t row) {
+  return a.k_row ? a.k_row[row] : a.top_k;
+}
+RLK_DEV float row_floor(const RowArgs& a, int64_t row) {
+  return a.kfloor ? a.kfloor[row] : -INFINITY;
 }
 
 // lse_s, eq_s: log Z_S and E_q[z/T] over the nucleus, in units of z/T;
@@ -147,10 +161,14 @@ RLK_DEV void generic_row(const RowArgs& a, int64_t row, GenScratch& g) {
   const int64_t y = a.targets[row];
   uint8_t flags = 0;
   if (y < 0 || y >= V) flags |= kBadTarget;
-  if (!param_ok(Tv, p)) {
+  if (!param_ok(Tv, p) || row_top_k(a, row) < 0) {
     if (tid == 0) store_nan_row(a, row, flags | kBadParam);
     return;
   }
+  // top-k: only values >= the floor take part in the cut (fk = 0: all)
+  const float floor_v = row_floor(a, row);
+  const bool has_floor = floor_v > -INFINITY;
+  const uint32_t fk = has_floor ? f32_key(floor_v) : 0u;
 
   // ---- pass 1: max, finite count, non-finite detection ----
   float mx = -INFINITY;
@@ -173,9 +191,11 @@ RLK_DEV void generic_row(const RowArgs& a, int64_t row, GenScratch& g) {
   }
   const double m = double(mx);
   const double invT = 1.0 / double(Tv);
-  const bool cut = p < 1.f;
+  const bool cut_p = p < 1.f;
+  const bool cut = cut_p || has_floor;
 
-  // ---- pass 2: Z, sum e*d, round-1 histogram of fixed-point masses ----
+  // ---- pass 2: Z, sum e*d, round-1 histogram of fixed-point masses (of
+  //      the values at or above the top-k floor) ----
   for (int i = tid; i < kBins1; i += NT) hist[i] = 0ull;
   __syncthreads();
   double zt = 0.0, st = 0.0;
@@ -187,7 +207,7 @@ RLK_DEV void generic_row(const RowArgs& a, int64_t row, GenScratch& g) {
     const float e = mass_of(z, m, invT, &d);
     zt += double(e);
     st += double(e) * d;
-    if (cut) {
+    if (cut_p && f32_key(z) >= fk) {
       const uint64_t w = fixed_mass(e);
       if (w) {
         wt += w;
@@ -203,54 +223,59 @@ RLK_DEV void generic_row(const RowArgs& a, int64_t row, GenScratch& g) {
   uint32_t tau_key = 0;
   uint32_t size = nfin;
   if (cut) {
-    const uint64_t W = block_sum(wt, su64);
-    const uint64_t thr = uint64_t(ceil(double(p) * double(W)));
-    // round 1
-    uint64_t above = 0;
-    int d1 = walk_down<NT>(hist, kBins1 - 1, thr, 0ull, &above, su64, si, &bslot);
-    if (d1 < 0) d1 = 0;   // unreachable: the total mass reaches thr
-    // round 2
-    __syncthreads();
-    for (int i = tid; i < kBins2; i += NT) hist[i] = 0ull;
-    __syncthreads();
-    for (int64_t i = tid; i < V; i += NT) {
-      const float z = load_val(rowp, i);
-      if (!(z > -INFINITY)) continue;
-      const uint32_t k = f32_key(z);
-      if (int(k >> 20) != d1) continue;
-      double d;
-      const uint64_t w = fixed_mass(mass_of(z, m, invT, &d));
-      if (w) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[(k >> 10) & 0x3ffu]),
-                       (unsigned long long)w);
-    }
-    __syncthreads();
-    int d2 = walk_down<NT>(hist, kBins2 - 1, thr, above, &above, su64, si, &bslot);
-    if (d2 < 0) d2 = 0;
-    // round 3
-    __syncthreads();
-    for (int i = tid; i < kBins2; i += NT) hist[i] = 0ull;
-    __syncthreads();
-    const uint32_t pre = (uint32_t(d1) << 10) | uint32_t(d2);
-    for (int64_t i = tid; i < V; i += NT) {
-      const float z = load_val(rowp, i);
-      if (!(z > -INFINITY)) continue;
-      const uint32_t k = f32_key(z);
-      if ((k >> 10) != pre) continue;
-      double d;
-      const uint64_t w = fixed_mass(mass_of(z, m, invT, &d));
-      if (w) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[k & 0x3ffu]),
-                       (unsigned long long)w);
-    }
-    __syncthreads();
-    int d3 = walk_down<NT>(hist, kBins2 - 1, thr, above, &above, su64, si, &bslot);
-    if (d3 < 0) d3 = 0;
-    tau_key = (pre << 10) | uint32_t(d3);
-    const uint64_t at = hist[d3];
-    if (tid == 0) {
-      const double pp = double(p);
-      if (fabs(double(above) / double(W) - pp) <= kBoundaryEps ||
-          fabs(double(above + at) / double(W) - pp) <= kBoundaryEps)
-        flags |= kBoundary;
+    if (cut_p) {
+      const uint64_t W = block_sum(wt, su64);
+      const uint64_t thr = uint64_t(ceil(double(p) * double(W)));
+      // round 1
+      uint64_t above = 0;
+      int d1 = walk_down<NT>(hist, kBins1 - 1, thr, 0ull, &above, su64, si, &bslot);
+      if (d1 < 0) d1 = 0;   // unreachable: the total mass reaches thr
+      // round 2
+      __syncthreads();
+      for (int i = tid; i < kBins2; i += NT) hist[i] = 0ull;
+      __syncthreads();
+      for (int64_t i = tid; i < V; i += NT) {
+        const float z = load_val(rowp, i);
+        if (!(z > -INFINITY)) continue;
+        const uint32_t k = f32_key(z);
+        if (int(k >> 20) != d1 || k < fk) continue;
+        double d;
+        const uint64_t w = fixed_mass(mass_of(z, m, invT, &d));
+        if (w) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[(k >> 10) & 0x3ffu]),
+                         (unsigned long long)w);
+      }
+      __syncthreads();
+      int d2 = walk_down<NT>(hist, kBins2 - 1, thr, above, &above, su64, si, &bslot);
+      if (d2 < 0) d2 = 0;
+      // round 3
+      __syncthreads();
+      for (int i = tid; i < kBins2; i += NT) hist[i] = 0ull;
+      __syncthreads();
+      const uint32_t pre = (uint32_t(d1) << 10) | uint32_t(d2);
+      for (int64_t i = tid; i < V; i += NT) {
+        const float z = load_val(rowp, i);
+        if (!(z > -INFINITY)) continue;
+        const uint32_t k = f32_key(z);
+        if ((k >> 10) != pre || k < fk) continue;
+        double d;
+        const uint64_t w = fixed_mass(mass_of(z, m, invT, &d));
+        if (w) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[k & 0x3ffu]),
+                         (unsigned long long)w);
+      }
+      __syncthreads();
+      int d3 = walk_down<NT>(hist, kBins2 - 1, thr, above, &above, su64, si, &bslot);
+      if (d3 < 0) d3 = 0;
+      tau_key = (pre << 10) | uint32_t(d3);
+      tau_key = tau_key > fk ? tau_key : fk;
+      const uint64_t at = hist[d3];
+      if (tid == 0) {
+        const double pp = double(p);
+        if (fabs(double(above) / double(W) - pp) <= kBoundaryEps ||
+            fabs(double(above + at) / double(W) - pp) <= kBoundaryEps)
+          flags |= kBoundary;
+      }
+    } else {
+      tau_key = fk;   // top-k at top-p 1: S is the top-k set
     }
     // final pass: truncated sums over S = {key >= tau}
     double zs = 0.0, ss = 0.0;
@@ -431,7 +456,7 @@ RLK_DEV float code_mass(float dv, MassScale k) {
 constexpr int kMaxFW = kHT / kWave;              // every wave finishes the block's last row
 struct FinScratch {
   int i[8][kMaxFW];
-  uint64_t d[6][kMaxFW];   // fixed-point partial sums
+  uint64_t d[7][kMaxFW];   // fixed-point partial sums
   uint64_t bd[3];
   int bi[2];
   unsigned int bar;
@@ -627,7 +652,7 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
 
   uint8_t flags = 0;
   if (!y_ok) flags |= kBadTarget;
-  if (!param_ok(T, p)) flags |= kBadParam;
+  if (!param_ok(T, p) || row_top_k(a, row) < 0) flags |= kBadParam;
   if (n_zero == 0 && n_neginf == int(V)) flags |= kNonFinite;
   // a value held > 65535 times wraps its counter; +inf, NaN and extreme
   // magnitudes are not counted: the generic kernel redoes such rows
@@ -645,23 +670,46 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
     const double Z = from_fx(Zu);
     const double S = -from_fx(Su);
 
+    // ---- top-k: the floor's merged key; the cut below stops there ----
+    const float floor_v = row_floor(a, row);
+    const bool has_floor = floor_v > -INFINITY;
+    const int lo_key =
+        has_floor ? int(bf16_key_merged(uint16_t(__float_as_uint(floor_v) >> 16))) : kKeyLo;
+    // the mass at or above the floor (the top-k set), from the same per-key
+    // terms as the walk below, so that the walk's sums reach it exactly
+    double Zf = Z;
+    if (has_floor && p < 1.f) {
+      uint64_t zf = 0;
+      for (int key = kmax - ft; key >= lo_key; key -= FT) {
+        float v;
+        const int n = int(key_count(hist, key, &v, uint32_t(n_zero)));
+        if (n) zf += to_fx(double(code_mass(v - mval, ks) * float(n)));
+      }
+      zf = wave_total(zf);
+      if (lane == 0) fs.d[6][fw] = zf;
+      fsync<FW>(&fs.bar, epoch);
+      Zf = from_fx(fold_partials(fs.d[6], FW));
+    }
+
     // ---- top-p cut: walk merged keys down from the max, FT at a time; the
-    //      masses per key in fixed point, so every cumulative sum is exact ----
+    //      masses per key in fixed point, so every cumulative sum is exact.
+    //      With top-k at top-p 1 nothing crosses and the walk keeps every
+    //      value down to the floor ----
     double Zs = Z, Ss = S, Mgt = 0.0;
     uint32_t tau_key = 0;
     int size = int(V) - n_neginf;
-    const bool cut = p < 1.f;
+    const bool cut = p < 1.f || has_floor;
     if (cut) {
-      const double thr = double(p) * Z;
+      const double thr = p < 1.f ? double(p) * Zf : INFINITY;
       uint64_t cz = 0, cs = 0;
       int cn = 0;
       bool found = false;
       int par = 0;
-      for (int k0 = kmax; !found && k0 >= kKeyLo; k0 -= FT, par ^= 1) {
+      for (int k0 = kmax; !found && k0 >= lo_key; k0 -= FT, par ^= 1) {
         const int key = k0 - ft;
         uint64_t mass = 0, ms = 0;
         int n = 0;
-        if (key >= kKeyLo) {
+        if (key >= lo_key) {
           float v;
           n = int(key_count(hist, key, &v, uint32_t(n_zero)));
           if (n) {
@@ -719,11 +767,12 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
           cn += int(readlane_u32(uint32_t(en), FW - 1)) + int(readlane_u32(uint32_t(pn), FW - 1));
         }
       }
-      if (!found) {   // truncation left the mass just short of p: keep every value
+      if (!found) {   // top-p 1 with top-k, or truncation left the mass just
+                      // short of p: keep every value down to the floor
         Zs = from_fx(cz);
         Ss = -from_fx(cs);
         Mgt = Zs;
-        tau_key = uint32_t(kKeyLo);
+        tau_key = uint32_t(lo_key);
         size = cn;
       }
     }
@@ -764,7 +813,7 @@ RLK_DEV void finish_row(const RowArgs& a, int64_t row, uint32_t* hist, uint32_t*
       if (cut) {
         tau = merged_key_value(tau_key);
         const double pp = double(p);
-        if (fabs(Mgt / Z - pp) <= kBoundaryEps || fabs(Zs / Z - pp) <= kBoundaryEps)
+        if (p < 1.f && (fabs(Mgt / Zf - pp) <= kBoundaryEps || fabs(Zs / Zf - pp) <= kBoundaryEps))
           flags |= kBoundary;
       }
       const double mT = double(mval) * invT;
@@ -1046,10 +1095,14 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
   const int64_t y = a.targets[row];
   uint8_t flags = 0;
   if (y < 0 || y >= V) flags |= kBadTarget;
-  if (!param_ok(Tv, p)) {
+  if (!param_ok(Tv, p) || row_top_k(a, row) < 0) {
     if (tid == 0) store_nan_row(a, row, flags | kBadParam);
     return;
   }
+  // top-k: only values >= the floor take part in the cut
+  const float floor_v = row_floor(a, row);
+  const bool has_floor = floor_v > -INFINITY;
+  const uint32_t fk = has_floor ? f32_key(floor_v) : 0u;
 
   // ---- pass 1: max, finite count, non-finite detection (or the producer's
   // max when it saw only finite logits) ----
@@ -1085,23 +1138,25 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
   // every element below this has zero mass at fp32 precision; clamping -inf
   // to it keeps the arithmetic free of inf - inf
   const float zfloor = float(m - 1e30);
-  const bool cut = p < 1.f;
+  const bool cut_p = p < 1.f;
+  const bool cut = cut_p || has_floor;
   auto bin_of = [&](double s) {   // s = z - m <= 0
     const double u = s * ks.cneg;
     return u < double(kFBins - 1) ? int(u) : kFBins - 1;
   };
 
-  // ---- pass 2: Z, sum e d, histogram of fixed-point masses over d bins ----
-  if (cut) {
+  // ---- pass 2: Z, sum e d, histogram of fixed-point masses over d bins
+  //      (with top-k, of the values at or above its floor only) ----
+  if (cut_p) {
     for (int i = tid; i < kFBins; i += kF32T) hist[i] = 0ull;
     if (tid == 0) ncand_s = 0;
     __syncthreads();
   }
-  // Per element without branches except the atomic; the top-p histogram is
-  // a compile-time variant.
+  // Per element without branches except the atomic; the top-p histogram and
+  // the top-k floor are compile-time variants.
   double zt = 0.0, st = 0.0;
   uint64_t wt = 0;
-  auto pass2 = [&](auto with_hist) {
+  auto pass2 = [&](auto with_hist, auto with_floor) {
     for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
       double dz;
       const float e = f32_mass(fmaxf(z, zfloor), ks, &dz);
@@ -1109,7 +1164,8 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
       zt += ed;
       st = fma(ed, dz * invT, st);
       if constexpr (decltype(with_hist)::value) {
-        const uint64_t w = f32_fixed(ed);
+        uint64_t w = f32_fixed(ed);
+        if constexpr (decltype(with_floor)::value) w = f32_key(z) >= fk ? w : 0ull;
         wt += w;
         if (w)
           atomicAdd(reinterpret_cast<unsigned long long*>(&hist[bin_of(dz)]),
@@ -1117,15 +1173,33 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
       }
     });
   };
-  if (cut) pass2(std::true_type{});
-  else pass2(std::false_type{});
+  if (!cut_p) pass2(std::false_type{}, std::false_type{});
+  else if (has_floor) pass2(std::true_type{}, std::true_type{});
+  else pass2(std::true_type{}, std::false_type{});
   const double Z = block_sum(zt, sd);
   const double S = block_sum(st, sd);
 
   double Zs = Z, Ss = S;
   uint32_t tau_key = 0;
   uint32_t size = nfin;
-  if (cut) {
+  if (!cut_p && has_floor) {   // top-k at top-p 1: S is the top-k set
+    double zs = 0.0, ss = 0.0;
+    uint32_t cnt = 0;
+    for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
+      const bool in = z > -INFINITY && f32_key(z) >= fk;
+      double dz;
+      const float e = f32_mass(fmaxf(z, zfloor), ks, &dz);
+      const double ed = in ? double(e) : 0.0;
+      zs += ed;
+      ss = fma(ed, dz * invT, ss);
+      cnt += in ? 1u : 0u;
+    });
+    Zs = block_sum(zs, sd);
+    Ss = block_sum(ss, sd);
+    size = uint32_t(block_sum(uint64_t(cnt), su64));
+    tau_key = fk;
+  }
+  if (cut_p) {
     const uint64_t W = block_sum(wt, su64);
     const uint64_t thr = uint64_t(ceil(double(p) * double(W)));
     uint64_t above = 0;
@@ -1148,7 +1222,7 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
       zs += ed;
       ss = fma(ed, dz * invT, ss);
       cnt += in ? 1u : 0u;
-      if (b == bstar) {
+      if (b == bstar && f32_key(z) >= fk) {   // below the top-k floor: not a candidate
         const unsigned int slot = atomicAdd(&ncand_s, 1u);
         if (slot < unsigned(kCand)) cand[slot] = f32_key(z);
       }
@@ -1253,13 +1327,73 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
 }
 
 
+// ===========================================================================
+// Top-k floor of each row (opt-in top-k): v_k, the k-th largest finite
+// logit (ties counted one by one), by an exact radix select on the order
+// keys, 8 bits per round: 4 rounds for fp32 logits, 2 for bf16 ones (their
+// keys have 16 zero low bits). -inf when the row has no top-k (k = 0), when k
+// is at least its number of finite values (the top-k set is then every
+// finite value) or when k < 0 (the row kernel flags that row). NaN and +inf
+// entries are not counted; such a row gets NaN outputs from the row kernel.
+// ===========================================================================
+constexpr int kKT = 256;   // one thread per 8-bit digit
+
+template <typename T>
+__global__ __launch_bounds__(kKT) void topk_floor_rows(RowArgs a, float* floor_out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t su64[kKT / kWave];
+  __shared__ int si[kKT / kWave];
+  __shared__ int64_t above_s;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t V = a.vocab;
+  const T* rowp = reinterpret_cast<const T*>(a.logits) + row * a.row_stride;
+  const int64_t k = row_top_k(a, row);
+  if (k <= 0) {   // uniform across the block
+    if (tid == 0) floor_out[row] = -INFINITY;
+    return;
+  }
+  constexpr int kRounds = sizeof(T) == 2 ? 2 : 4;
+  uint32_t prefix = 0;   // the key bits found so far
+  int64_t need = k;      // rank still to find among the keys with that prefix
+  for (int r = 0; r < kRounds; ++r) {
+    const int shift = 24 - 8 * r;
+    const uint32_t hi_mask = r == 0 ? 0u : (0xffffffffu << (shift + 8));
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int64_t i = tid; i < V; i += kKT) {
+      const float z = load_val(rowp, i);
+      if (!(z > -INFINITY) || !(z < INFINITY)) continue;   // -inf, +inf, NaN
+      const uint32_t key = f32_key(z);
+      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    // digits from the top: the first whose cumulative count reaches `need`
+    const uint32_t c = hist[255 - tid];
+    uint64_t tot;
+    const uint64_t incl = block_inclusive_scan(uint64_t(c), su64, &tot);
+    if (r == 0 && int64_t(tot) <= k) {   // k covers every finite value: no cut
+      if (tid == 0) floor_out[row] = -INFINITY;
+      return;
+    }
+    const int first = block_min((c != 0u && int64_t(incl) >= need) ? tid : kKT, si);
+    if (tid == first) above_s = int64_t(incl) - int64_t(c);
+    __syncthreads();
+    need -= above_s;
+    prefix |= uint32_t(255 - first) << shift;
+    __syncthreads();
+  }
+  if (tid == 0) floor_out[row] = key_f32(prefix);
+}
+
 }  // namespace
 
-// workspace: [0, n_rows) hand-off flags of the bf16 histogram path
+// workspace: [0, n_rows) hand-off flags of the bf16 histogram path, then
+// (256-byte aligned) each row's top-k floor, fp32 [n_rows]
 size_t logits_rows_workspace(int64_t n_rows, int64_t vocab, int dtype) {
   (void)vocab;
   (void)dtype;
-  return size_t((n_rows + 255) / 256 * 256);
+  return size_t((n_rows + 255) / 256 * 256) + size_t((4 * n_rows + 255) / 256 * 256);
 }
 
 hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipStream_t stream) {
@@ -1267,6 +1401,19 @@ hipError_t launch_logits_rows(const RowArgs& a, int dtype, void* workspace, hipS
   RowArgs args = a;
   args.fallback = reinterpret_cast<uint8_t*>(workspace);
   const dim3 grid(unsigned(a.n_rows));
+  if (a.top_k > 0 || a.k_row) {   // top-k: each row's floor first
+    float* fl = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                         (a.n_rows + 255) / 256 * 256);
+    if (dtype == 0)
+      hipLaunchKernelGGL(topk_floor_rows<float>, grid, dim3(kKT), 0, stream, args, fl);
+    else
+      hipLaunchKernelGGL(topk_floor_rows<uint16_t>, grid, dim3(kKT), 0, stream, args, fl);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    args.kfloor = fl;
+  } else {
+    args.kfloor = nullptr;
+  }
   if (dtype == 0) {  // fp32
     const bool vec4 = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.row_stride % 4 == 0);
     if (vec4)

@@ -59,8 +59,9 @@ template <typename T>
 RLK_DEV void score_draw(const SampleArgs& a, int64_t row, const T* zrow, int64_t y) {
   const uint8_t f = a.nflags[row] & uint8_t(~(kOutside | kBadTarget));
   float lp = __builtin_nanf("");
+  const float Tv = a.t_row ? a.t_row[row] : a.temperature;
   if (y >= 0)
-    lp = token_logprob(val<T>(zrow, y), a.score_stats[2 * row], 1.0 / double(a.temperature),
+    lp = token_logprob(val<T>(zrow, y), a.score_stats[2 * row], 1.0 / double(Tv),
                        a.score_stats[2 * row + 1]);
   if (a.logprob) a.logprob[row] = lp;
   if (a.flags) a.flags[row] = y >= 0 ? f : uint8_t(f | kBadTarget);
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kSmT) void sample_rows(SampleArgs a) {
   }
   const int64_t V = a.vocab;
   const float tau = a.thresh[row];
-  const double T64 = double(a.temperature);
+  const double T64 = double(a.t_row ? a.t_row[row] : a.temperature);
   const uint64_t rk = a.row_keys ? uint64_t(a.row_keys[row]) : uint64_t(row);
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
   double best = -INFINITY;

@@ -10,6 +10,7 @@ struct SampleArgs {
   const void* logits;
   int64_t n_rows, vocab, row_stride;
   float temperature;
+  const float* t_row;         // nullable per-row temperature
   uint64_t seed;
   uint32_t offset;
   const int64_t* row_keys;    // nullable: the row index

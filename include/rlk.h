@@ -30,10 +30,19 @@
  *              fixed order so that reduction boundaries never move).
  * Reentrancy.  Concurrent calls on different streams with distinct workspaces
  *              and outputs are safe.
- * Parameters.  Temperature must be finite and > 0; top-p must lie in (0, 1];
- *              top-k must be 0 -- top-k filtering and temperature 0 are
- *              rejected rather than ignored (consistency page, "ROCm MI300X
- *              and gfx942").
+ * Parameters.  Temperature must be finite and > 0 (temperature 0 is
+ *              rejected rather than ignored: consistency page, "ROCm MI300X
+ *              and gfx942"); top-p must lie in (0, 1]; top-k >= 0, where 0
+ *              (the default) means no top-k. Top-k is opt-in: the
+ *              consistency page's strict replay contract rejects it, while the
+ *              prime-rl v0.10.0 release notes ("2. RL Algorithms") replay a
+ *              top-k sampler exactly in the trainer; the sampler and every
+ *              scorer here apply the same rule, so the replay stays exact.
+ * Top-k rule.  Temperature first; then S_k = {i : z_i >= v_k}, v_k the k-th
+ *              largest finite logit (ties with it are all kept, so |S_k| >= k;
+ *              k at or above the number of finite logits keeps them all);
+ *              then the top-p rule on the distribution renormalised over S_k.
+ *              At top-p 1 the nucleus is S_k and its threshold is v_k.
  */
 #ifndef RLK_H
 #define RLK_H
@@ -48,7 +57,7 @@ extern "C" {
 typedef int32_t rlk_status;
 #define RLK_OK 0
 #define RLK_EINVAL 1        /* bad argument value, shape, stride or pointer */
-#define RLK_EUNSUPPORTED 2  /* a valid but unsupported request (e.g. top_k != 0) */
+#define RLK_EUNSUPPORTED 2  /* a valid but unsupported request (reserved) */
 #define RLK_EWORKSPACE 3    /* workspace missing, misaligned or too small */
 #define RLK_EHIP 4          /* a HIP runtime call failed */
 
@@ -101,10 +110,12 @@ const char* rlk_last_error(void);
  *               `vocab` entries of each row are read (padded vocabularies).
  *               -inf entries are allowed (probability 0).
  * targets       [n_rows] int64 target ids.
- * temperature, top_p   scalars used for every row, unless the per-row arrays
- *               temperature_per_row / top_p_per_row ([n_rows] fp32, nullable)
- *               are given; per-row values out of range set RLK_FLAG_BAD_PARAM.
- * top_k         must be 0.
+ * temperature, top_p, top_k   scalars used for every row, unless the per-row
+ *               arrays temperature_per_row / top_p_per_row ([n_rows] fp32) /
+ *               top_k_per_row ([n_rows] int32), each nullable, are given;
+ *               per-row values out of range (a negative k included) set
+ *               RLK_FLAG_BAD_PARAM and NaN outputs. top_k: see "Top-k rule"
+ *               above (0: none); the nucleus S below is then the top-k set's.
  * lp_full, lp_trunc, entropy_trunc   [n_rows] fp32 outputs (required).
  * entropy_full  [n_rows] fp32 (nullable).
  * nucleus_size  [n_rows] int32 |S| (nullable).
@@ -119,6 +130,7 @@ rlk_status rlk_logprob_from_logits(
     const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab, int64_t row_stride,
     const int64_t* targets, float temperature, float top_p,
     const float* temperature_per_row, const float* top_p_per_row, int32_t top_k,
+    const int32_t* top_k_per_row,
     float* lp_full, float* lp_trunc, float* entropy_trunc,
     float* entropy_full, int32_t* nucleus_size, float* threshold, uint8_t* flags,
     void* workspace, size_t workspace_bytes, void* stream);
@@ -130,8 +142,9 @@ rlk_status rlk_logprob_from_logits(
  *
  * Same arguments, outputs and results as rlk_logprob_from_logits (bitwise),
  * without workspace and workspace_bytes. Its scratch (the per-row hand-off
- * flags of the bf16 row kernel, written for every row before they are read,
- * so nothing needs clearing) is a static 1 MiB device array in the library:
+ * flags of the bf16 row kernel and, with top-k, each row's top-k floor, all
+ * written for every row before they are read, so nothing needs clearing) is a
+ * static 5 MiB device array in the library:
  * each GPU the library runs on holds its own copy until the process ends,
  * its address looked up once per device on the first call there. This call
  * allocates nothing and calls no allocating routine.
@@ -145,6 +158,7 @@ rlk_status rlk_logprob_from_logits_noalloc(
     const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab, int64_t row_stride,
     const int64_t* targets, float temperature, float top_p,
     const float* temperature_per_row, const float* top_p_per_row, int32_t top_k,
+    const int32_t* top_k_per_row,
     float* lp_full, float* lp_trunc, float* entropy_trunc,
     float* entropy_full, int32_t* nucleus_size, float* threshold, uint8_t* flags,
     void* stream);
@@ -173,10 +187,11 @@ rlk_status rlk_logprob_from_logits_noalloc(
  *               (or RLK_FLAG_NONFINITE). Offsets outside [0, n_support] make
  *               the row invalid; nothing past n_support is read.
  * check_top_p   0: no check. In (0, 1]: each row's nucleus at (temperature,
- *               check_top_p) is recomputed from the logits as by
+ *               check_top_p, check_top_k) is recomputed from the logits as by
  *               rlk_logprob_from_logits, and RLK_FLAG_MISMATCH marks a set that
  *               differs from it (RLK_FLAG_BOUNDARY: the row lies within 1e-6 of
  *               the top-p boundary, where another set is equally valid).
+ * check_top_k   the top-k of that nucleus (0: none; > 0 needs check_top_p).
  * logprob, entropy [n_rows] fp32 outputs (required); flags [n_rows] uint8
  *               (nullable). Outputs of a row depend on that row only.
  * Workspace: none without the check; with it, the nucleus outputs of every row
@@ -189,7 +204,7 @@ rlk_status rlk_logprob_from_support(
     const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab, int64_t row_stride,
     const int64_t* targets, float temperature,
     const int64_t* support_offsets, const int32_t* support_ids, int64_t n_support,
-    float check_top_p, float* logprob, float* entropy, uint8_t* flags,
+    float check_top_p, int32_t check_top_k, float* logprob, float* entropy, uint8_t* flags,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------------------
@@ -197,8 +212,9 @@ rlk_status rlk_logprob_from_support(
  *
  * prime-rl v0.10.0 release notes, "2. RL Algorithms": top-p sampling is
  * replayed exactly in the trainer; consistency page: rollout and training
- * logprobs must agree bitwise. Per row: the nucleus S at (temperature, top_p)
- * as rlk_logprob_from_logits finds it, then
+ * logprobs must agree bitwise. Per row: the nucleus S at (temperature, top_p,
+ * top_k), scalars or per-row arrays, as rlk_logprob_from_logits finds it
+ * (a row with an out-of-range parameter draws -1 with RLK_FLAG_BAD_PARAM), then
  *   samples[n] = argmax_{i in S} z_i / T - log(-log u_i)   (fp64; the lowest
  *                id on an exact tie; -1 for a row without a finite logit or
  *                with a NaN / +inf one)
@@ -210,14 +226,16 @@ rlk_status rlk_logprob_from_support(
  * rlk_logprob_from_logits scores a target (the row kernel's own row max and
  * log Z_S, the same fp64 arithmetic; entropy, size and flags from the same
  * pass), so they equal bitwise what a training-side call with
- * targets = samples returns.
+ * targets = samples (and the same temperature, top-p and top-k) returns.
  * Limits: as rlk_logprob_from_logits; n_rows < 2^31.
  * -------------------------------------------------------------------------- */
 size_t rlk_sample_top_p_workspace_size(int64_t n_rows, int64_t vocab, int32_t dtype);
 
 rlk_status rlk_sample_top_p(
     const void* logits, int32_t dtype, int64_t n_rows, int64_t vocab, int64_t row_stride,
-    float temperature, float top_p, uint64_t seed, uint32_t offset, const int64_t* row_keys,
+    float temperature, float top_p, int32_t top_k, const float* temperature_per_row,
+    const float* top_p_per_row, const int32_t* top_k_per_row,
+    uint64_t seed, uint32_t offset, const int64_t* row_keys,
     int64_t* samples, float* logprob, float* entropy, int32_t* nucleus_size, uint8_t* flags,
     void* workspace, size_t workspace_bytes, void* stream);
 
@@ -230,14 +248,14 @@ rlk_status rlk_sample_top_p(
  * weight        [vocab, w_stride] bf16 LM-head rows, first hidden_size used.
  * targets       [n_rows] int64.
  * Logits are accumulated in fp32 over the hidden dimension and never rounded
- * to bf16. With top_p < 1 the outputs are the truncated ones of the
- * logits-in entry point (same nucleus rule; the fp32 logits of up to 16384
- * rows at a time are formed in the workspace and cut by the logits-in row
- * kernel); with top_p = 1 they are full and no logits are stored.
+ * to bf16. With top_p < 1 or top_k > 0 the outputs are the truncated ones of
+ * the logits-in entry point (same nucleus rule; the fp32 logits of up to
+ * 16384 rows at a time are formed in the workspace and cut by the logits-in
+ * row kernel); otherwise they are full and no logits are stored.
  * logprob, entropy   [n_rows] fp32 outputs (required).
  * saved         [n_rows, 4] fp32 (nullable): (log Z_S and E_q[z/T] over the
  *               nucleus, both on the scale z/T; tau, the smallest kept logit,
- *               -inf at top_p = 1; 1 when the row's logprob term is live -- target
+ *               -inf without a cut; 1 when the row's logprob term is live -- target
  *               in range and kept -- else 0), consumed by
  *               rlk_logprob_fused_linear_bwd.
  * nucleus_size  [n_rows] int32 (nullable).  flags [n_rows] uint8 (nullable):
@@ -248,7 +266,7 @@ rlk_status rlk_sample_top_p(
  * aligned.
  * -------------------------------------------------------------------------- */
 size_t rlk_logprob_fused_linear_workspace_size(int64_t n_rows, int64_t hidden_size,
-                                                int64_t vocab, float top_p);
+                                                int64_t vocab, float top_p, int32_t top_k);
 
 rlk_status rlk_logprob_fused_linear(
     const void* hidden, const void* weight, int64_t n_rows, int64_t hidden_size, int64_t vocab,
@@ -280,8 +298,8 @@ rlk_status rlk_logprob_fused_linear(
  * W^T and h^T (bf16, padded to multiples of 64), G of one chunk in both
  * orientations (bf16) and, when vocab > 32768, an fp32 [n_rows, hidden_size]
  * partial sum of grad_hidden.
- * temperature and top_p must be the forward call's (top_p is validated; the
- * nucleus itself comes from `saved`).
+ * temperature, top_p and top_k must be the forward call's (top_p and top_k are
+ * validated; the nucleus itself comes from `saved`).
  * Limits: as the forward, and vocab < 2^23.
  * -------------------------------------------------------------------------- */
 size_t rlk_logprob_fused_linear_bwd_workspace_size(int64_t n_rows, int64_t hidden_size,

@@ -36,18 +36,21 @@ def logits(h64: np.ndarray, w64: np.ndarray) -> np.ndarray:
     return np.asarray(h64, dtype=np.float64) @ np.asarray(w64, dtype=np.float64).T
 
 
-def forward(h64, w64, targets, T: float, p: float) -> logprob.BatchResult:
-    """Per-row outputs of the fused form (truncated statistics; full at p = 1)."""
-    return logprob.logprob_from_logits(logits(h64, w64), targets, T, p)
+def forward(h64, w64, targets, T: float, p: float, top_k: int = 0) -> logprob.BatchResult:
+    """Per-row outputs of the fused form (truncated statistics; full at p = 1
+    without top-k)."""
+    return logprob.logprob_from_logits(logits(h64, w64), targets, T, p, top_k)
 
 
-def grad_logits(z: np.ndarray, targets, g_lp, g_H, T: float, p: float) -> np.ndarray:
-    """G = dL/dz [N, V] for per-row upstream gradients g_lp, g_H."""
+def grad_logits(z: np.ndarray, targets, g_lp, g_H, T: float, p: float,
+                top_k: int = 0) -> np.ndarray:
+    """G = dL/dz [N, V] for per-row upstream gradients g_lp, g_H (S the
+    top-k/top-p nucleus, held fixed)."""
     z = np.asarray(z, dtype=np.float64)
     N, V = z.shape
     G = np.zeros((N, V))
     for n in range(N):
-        keep, *_ = logprob.nucleus(z[n], T, p)
+        keep, *_ = logprob.nucleus(z[n], T, p, top_k)
         zk = z[n, keep]
         d = (zk - zk.max()) / T
         e = np.exp(d)
@@ -65,9 +68,9 @@ def grad_logits(z: np.ndarray, targets, g_lp, g_H, T: float, p: float) -> np.nda
     return G
 
 
-def backward(h64, w64, targets, g_lp, g_H, T: float, p: float):
+def backward(h64, w64, targets, g_lp, g_H, T: float, p: float, top_k: int = 0):
     """(dL/dh [N, H], dL/dW [V, H]) in fp64."""
     h64 = np.asarray(h64, dtype=np.float64)
     w64 = np.asarray(w64, dtype=np.float64)
-    G = grad_logits(logits(h64, w64), targets, g_lp, g_H, T, p)
+    G = grad_logits(logits(h64, w64), targets, g_lp, g_H, T, p, top_k)
     return G @ w64, G.T @ h64

@@ -48,8 +48,10 @@ def valid_support(ids, V: int) -> bool:
     return ids.size > 0 and bool(np.all((ids >= 0) & (ids < V))) and bool(np.all(np.diff(ids) > 0))
 
 
-def row(z, y: int, T: float, ids, check_p: float | None = None) -> tuple[float, float, int]:
-    """(lp, H, flags) of one row over the support ``ids``."""
+def row(z, y: int, T: float, ids, check_p: float | None = None,
+        check_k: int = 0) -> tuple[float, float, int]:
+    """(lp, H, flags) of one row over the support ``ids``; with ``check_p``
+    the set is compared with the row's top-k/top-p nucleus (k = ``check_k``)."""
     z = np.asarray(z, dtype=np.float64)
     V = z.size
     ids = np.asarray(ids, dtype=np.int64)
@@ -79,7 +81,7 @@ def row(z, y: int, T: float, ids, check_p: float | None = None) -> tuple[float, 
             lp = -np.inf
             flags |= FLAG_OUTSIDE
     if check_p is not None and not (np.isnan(z).any() or np.isposinf(z).any()):
-        keep, _, _, _, alts = logprob.nucleus(z, T, check_p)
+        keep, _, _, _, alts = logprob.nucleus(z, T, check_p, check_k)
         mask = np.zeros(V, dtype=bool)
         mask[ids] = True
         if alts:
@@ -98,7 +100,7 @@ class SupportResult:
 
 
 def logprob_from_support(logits, targets, T: float, offsets, ids,
-                         check_p: float | None = None) -> SupportResult:
+                         check_p: float | None = None, check_k: int = 0) -> SupportResult:
     """Row-wise outputs for [N, V] logits and a CSR support (offsets [N + 1], ids)."""
     logits = np.asarray(logits, dtype=np.float64)
     offsets = np.asarray(offsets, dtype=np.int64)
@@ -107,7 +109,7 @@ def logprob_from_support(logits, targets, T: float, offsets, ids,
                         np.empty(N, dtype=np.uint8))
     for n in range(N):
         s = ids[offsets[n]:offsets[n + 1]]
-        out.lp[n], out.h[n], out.flags[n] = row(logits[n], int(targets[n]), T, s, check_p)
+        out.lp[n], out.h[n], out.flags[n] = row(logits[n], int(targets[n]), T, s, check_p, check_k)
         out.size[n] = offsets[n + 1] - offsets[n]
     return out
 

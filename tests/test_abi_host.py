@@ -42,17 +42,20 @@ def test_version_and_status_text(L):
 
 def _logits_call(L, **kw):
     a = dict(logits=FAKE, dtype=1, n=4, V=1000, stride=1000, targets=FAKE, T=0.7, p=0.95,
-             t_row=None, p_row=None, top_k=0, lpf=FAKE, lpt=FAKE, ht=FAKE, hf=None, ns=None,
-             th=None, fl=None, ws=WS, ws_bytes=1 << 20)
+             t_row=None, p_row=None, top_k=0, k_row=None, lpf=FAKE, lpt=FAKE, ht=FAKE, hf=None,
+             ns=None, th=None, fl=None, ws=WS, ws_bytes=1 << 20)
     a.update(kw)
     return L.rlk_logprob_from_logits(a["logits"], a["dtype"], a["n"], a["V"], a["stride"],
                                      a["targets"], a["T"], a["p"], a["t_row"], a["p_row"],
-                                     a["top_k"], a["lpf"], a["lpt"], a["ht"], a["hf"], a["ns"],
+                                     a["top_k"], a["k_row"], a["lpf"], a["lpt"], a["ht"], a["hf"],
+                                     a["ns"],
                                      a["th"], a["fl"], a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(top_k=5), _native.RLK_EUNSUPPORTED),
+    (dict(top_k=-1), _native.RLK_EINVAL),
+    (dict(top_k=5, ws=None), _native.RLK_EWORKSPACE),    # top-k is opt-in: accepted
+    (dict(k_row=P(0x100002)), _native.RLK_EINVAL),      # per-row top-k not 4-byte aligned
     (dict(T=0.0), _native.RLK_EINVAL),
     (dict(T=-1.0), _native.RLK_EINVAL),
     (dict(T=math.nan), _native.RLK_EINVAL),
@@ -81,18 +84,19 @@ def test_logits_validation(L, kw, status):
 
 def _noalloc_call(L, **kw):
     a = dict(logits=FAKE, dtype=1, n=4, V=1000, stride=1000, targets=FAKE, T=0.7, p=0.95,
-             t_row=None, p_row=None, top_k=0, lpf=FAKE, lpt=FAKE, ht=FAKE)
+             t_row=None, p_row=None, top_k=0, k_row=None, lpf=FAKE, lpt=FAKE, ht=FAKE)
     a.update(kw)
     return L.rlk_logprob_from_logits_noalloc(a["logits"], a["dtype"], a["n"], a["V"], a["stride"],
                                              a["targets"], a["T"], a["p"], a["t_row"],
-                                             a["p_row"], a["top_k"], a["lpf"], a["lpt"], a["ht"],
+                                             a["p_row"], a["top_k"], a["k_row"], a["lpf"],
+                                             a["lpt"], a["ht"],
                                              None, None, None, None, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(n=(1 << 20) + 1), _native.RLK_EINVAL),      # beyond the static scratch
     (dict(n=1 << 40), _native.RLK_EINVAL),
-    (dict(top_k=5), _native.RLK_EUNSUPPORTED),
+    (dict(top_k=-5), _native.RLK_EINVAL),
     (dict(T=0.0), _native.RLK_EINVAL),
     (dict(stride=999), _native.RLK_EINVAL),
     (dict(lpt=None), _native.RLK_EINVAL),
@@ -189,7 +193,7 @@ def _fused(L, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(top_k=3), _native.RLK_EUNSUPPORTED),
+    (dict(top_k=-3), _native.RLK_EINVAL),
     (dict(T=0.0), _native.RLK_EINVAL),
     (dict(p=1.5), _native.RLK_EINVAL),
     (dict(H=100, hs=128, wsd=128), _native.RLK_EINVAL),
@@ -223,7 +227,7 @@ def _fused_bwd(L, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(p=0.0), _native.RLK_EINVAL),
-    (dict(top_k=1), _native.RLK_EUNSUPPORTED),
+    (dict(top_k=-1), _native.RLK_EINVAL),
     (dict(T=math.inf), _native.RLK_EINVAL),
     (dict(H=96, hs=128, wsd=128), _native.RLK_EINVAL),
     (dict(V=1 << 23), _native.RLK_EINVAL),
@@ -241,8 +245,10 @@ def test_fused_bwd_validation(L, kw, status):
 
 def test_fused_workspace_queries(L):
     # top-p < 1 stores a block of fp32 logits: 4096 rows x V (padded to 64) x 4 bytes
-    assert L.rlk_logprob_fused_linear_workspace_size(8192, 4096, 151936, 0.95) >= 4096 * 151936 * 4
-    assert L.rlk_logprob_fused_linear_workspace_size(8192, 4096, 151936, 1.0) < 4096 * 151936
+    assert L.rlk_logprob_fused_linear_workspace_size(8192, 4096, 151936, 0.95, 0) >= 4096 * 151936 * 4
+    assert L.rlk_logprob_fused_linear_workspace_size(8192, 4096, 151936, 1.0, 0) < 4096 * 151936
+    # top-k needs the stored logits at any top-p
+    assert L.rlk_logprob_fused_linear_workspace_size(8192, 4096, 151936, 1.0, 50) >= 4096 * 151936 * 4
     # backward: W^T and h^T in bf16 plus two bf16 copies of one 32768-row chunk of G
     need = 2 * 4096 * 151936 + 2 * 4096 * 8192 + 2 * 2 * 8192 * 32768
     assert L.rlk_logprob_fused_linear_bwd_workspace_size(8192, 4096, 151936, 1.0) >= need
@@ -250,11 +256,12 @@ def test_fused_workspace_queries(L):
 
 def _support(L, **kw):
     a = dict(logits=FAKE, dtype=1, n=4, V=1000, stride=1000, targets=FAKE, T=1.0, off=FAKE,
-             ids=FAKE, nnz=10, p=0.0, lp=FAKE, ent=FAKE, fl=None, ws=WS, ws_bytes=1 << 30)
+             ids=FAKE, nnz=10, p=0.0, k=0, lp=FAKE, ent=FAKE, fl=None, ws=WS, ws_bytes=1 << 30)
     a.update(kw)
     return L.rlk_logprob_from_support(a["logits"], a["dtype"], a["n"], a["V"], a["stride"],
                                       a["targets"], a["T"], a["off"], a["ids"], a["nnz"], a["p"],
-                                      a["lp"], a["ent"], a["fl"], a["ws"], a["ws_bytes"], None)
+                                      a["k"], a["lp"], a["ent"], a["fl"], a["ws"], a["ws_bytes"],
+                                      None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -277,6 +284,9 @@ def _support(L, **kw):
     (dict(off=P(0x100004)), _native.RLK_EINVAL),
     (dict(p=0.9, ws=None), _native.RLK_EWORKSPACE),
     (dict(p=0.9, ws_bytes=16), _native.RLK_EWORKSPACE),
+    (dict(p=0.9, k=-1), _native.RLK_EINVAL),
+    (dict(k=5), _native.RLK_EINVAL),                     # a top-k check needs check_top_p
+    (dict(p=0.9, k=5, ws=None), _native.RLK_EWORKSPACE),
 ])
 def test_support_validation(L, kw, status):
     assert _support(L, **kw) == status
@@ -292,12 +302,14 @@ def test_support_empty_batch_and_workspace(L):
 
 
 def _sample(L, **kw):
-    a = dict(logits=FAKE, dtype=1, n=4, V=1000, stride=1000, T=1.0, p=0.9, seed=1, off=0,
-             keys=None, out=FAKE, lp=None, ent=None, ns=None, fl=None, ws=WS, ws_bytes=1 << 30)
+    a = dict(logits=FAKE, dtype=1, n=4, V=1000, stride=1000, T=1.0, p=0.9, k=0, t_row=None,
+             p_row=None, k_row=None, seed=1, off=0, keys=None, out=FAKE, lp=None, ent=None,
+             ns=None, fl=None, ws=WS, ws_bytes=1 << 30)
     a.update(kw)
     return L.rlk_sample_top_p(a["logits"], a["dtype"], a["n"], a["V"], a["stride"], a["T"],
-                              a["p"], a["seed"], a["off"], a["keys"], a["out"], a["lp"], a["ent"],
-                              a["ns"], a["fl"], a["ws"], a["ws_bytes"], None)
+                              a["p"], a["k"], a["t_row"], a["p_row"], a["k_row"], a["seed"],
+                              a["off"], a["keys"], a["out"], a["lp"], a["ent"], a["ns"], a["fl"],
+                              a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -316,6 +328,11 @@ def _sample(L, **kw):
     (dict(keys=P(0x100004)), _native.RLK_EINVAL),
     (dict(ws=None), _native.RLK_EWORKSPACE),
     (dict(ws_bytes=8), _native.RLK_EWORKSPACE),
+    (dict(k=-2), _native.RLK_EINVAL),
+    (dict(k=40, ws=None), _native.RLK_EWORKSPACE),      # top-k is opt-in: accepted
+    (dict(t_row=P(0x100002)), _native.RLK_EINVAL),
+    (dict(p_row=P(0x100001)), _native.RLK_EINVAL),
+    (dict(k_row=P(0x100003)), _native.RLK_EINVAL),
 ])
 def test_sample_validation(L, kw, status):
     assert _sample(L, **kw) == status

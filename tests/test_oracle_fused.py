@@ -46,15 +46,16 @@ def test_matches_materialised_logits():
     np.testing.assert_allclose(a.h_trunc, b.h_trunc, rtol=1e-12)
 
 
-def _loss(h, W, y, g_lp, g_H, T, p):
-    r = fused.forward(h, W, y, T, p)
+def _loss(h, W, y, g_lp, g_H, T, p, k=0):
+    r = fused.forward(h, W, y, T, p, k)
     lp = np.where(np.isfinite(r.lp_trunc), r.lp_trunc, 0.0)
     return float(np.dot(g_lp, lp) + np.dot(g_H, r.h_trunc))
 
 
-@pytest.mark.parametrize("T,p", [(1.0, 1.0), (0.7, 1.0), (0.7, 0.9), (1.8, 0.6)])
-def test_backward_finite_differences(T, p):
-    rng = np.random.default_rng(int(T * 10 + p * 100))
+@pytest.mark.parametrize("T,p,k", [(1.0, 1.0, 0), (0.7, 1.0, 0), (0.7, 0.9, 0), (1.8, 0.6, 0),
+                                   (0.7, 1.0, 5), (1.2, 0.8, 9)])
+def test_backward_finite_differences(T, p, k):
+    rng = np.random.default_rng(int(T * 10 + p * 100 + k))
     N, V, H = 3, 17, 8
     h = rng.normal(size=(N, H))
     W = rng.normal(0, 0.7, size=(V, H))
@@ -63,22 +64,24 @@ def test_backward_finite_differences(T, p):
     g_lp = rng.normal(size=N)
     g_H = rng.normal(size=N)
     for n in range(N):                       # keep away from a nucleus boundary
-        r = logprob.row(h[n] @ W.T, int(y[n]), T, p)
+        r = logprob.row(h[n] @ W.T, int(y[n]), T, p, k)
         assert r.flags & logprob.FLAG_BOUNDARY == 0
-    dh, dW = fused.backward(h, W, y, g_lp, g_H, T, p)
+        if k:                                # the top-k set is a strict subset
+            assert r.size <= k < V
+    dh, dW = fused.backward(h, W, y, g_lp, g_H, T, p, k)
     eps = 1e-6
     num_h = np.zeros_like(h)
     for idx in np.ndindex(h.shape):
         hp, hm = h.copy(), h.copy()
         hp[idx] += eps
         hm[idx] -= eps
-        num_h[idx] = (_loss(hp, W, y, g_lp, g_H, T, p) - _loss(hm, W, y, g_lp, g_H, T, p)) / (2 * eps)
+        num_h[idx] = (_loss(hp, W, y, g_lp, g_H, T, p, k) - _loss(hm, W, y, g_lp, g_H, T, p, k)) / (2 * eps)
     num_w = np.zeros_like(W)
     for idx in np.ndindex(W.shape):
         wp, wm = W.copy(), W.copy()
         wp[idx] += eps
         wm[idx] -= eps
-        num_w[idx] = (_loss(h, wp, y, g_lp, g_H, T, p) - _loss(h, wm, y, g_lp, g_H, T, p)) / (2 * eps)
+        num_w[idx] = (_loss(h, wp, y, g_lp, g_H, T, p, k) - _loss(h, wm, y, g_lp, g_H, T, p, k)) / (2 * eps)
     np.testing.assert_allclose(dh, num_h, rtol=1e-6, atol=1e-8)
     np.testing.assert_allclose(dW, num_w, rtol=1e-6, atol=1e-8)
 

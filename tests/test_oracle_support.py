@@ -132,3 +132,21 @@ def test_batch_and_csr():
     for n in range(5):
         lp, h, fl = support.row(z[n], 0, 0.7, np.flatnonzero(masks[n]))
         assert (out.lp[n], out.h[n], out.flags[n], out.size[n]) == (lp, h, fl, masks[n].sum())
+
+
+def test_top_k_check():
+    """The check against a top-k/top-p nucleus: the top-k nucleus itself
+    passes, the plain top-p nucleus (a different set here) is a mismatch."""
+    rng = np.random.default_rng(51)
+    z = rng.normal(0, 1.5, 300)
+    T, p, k = 0.8, 0.95, 10
+    keep_k, *_ = logprob.nucleus(z, T, p, top_k=k)
+    keep_p, *_ = logprob.nucleus(z, T, p)
+    assert keep_k.sum() <= k < keep_p.sum()
+    y = int(np.argmax(z))
+    _, _, f = support.row(z, y, T, np.flatnonzero(keep_k), check_p=p, check_k=k)
+    assert not f & support.FLAG_MISMATCH
+    _, _, f = support.row(z, y, T, np.flatnonzero(keep_p), check_p=p, check_k=k)
+    assert f & support.FLAG_MISMATCH
+    _, _, f = support.row(z, y, T, np.flatnonzero(keep_p), check_p=p)
+    assert not f & support.FLAG_MISMATCH

@@ -1,9 +1,10 @@
 """The no-allocation entry point (rlk_logprob_from_logits_noalloc) through the
 C ABI against rlk_logprob_from_logits on the same inputs: every output
 bitwise equal, on two calls in a row, the second with fewer rows. Its
-scratch (the bf16 row kernel's per-row hand-off flags) is a static array that
-keeps the last call's contents, so the rows handed on to the generic
-algorithm differ between the two calls: a stale flag would show."""
+scratch (the bf16 row kernel's per-row hand-off flags, and with top-k each
+row's floor) is a static array that keeps the last call's contents, so the
+rows handed on to the generic algorithm, and the top-k of each row, differ
+between the two calls: a stale flag or floor would show."""
 import ctypes
 
 import numpy as np
@@ -27,11 +28,12 @@ def _outs(n):
             "flags": torch.full((n,), 0xEE, device=DEV, dtype=torch.uint8)}
 
 
-def _call(L, x, dtype, y, T, p, noalloc):
+def _call(L, x, dtype, y, T, p, noalloc, top_k=0, k_row=None):
     n, V = x.shape
     o = _outs(n)
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
-    args = [ptr(x), dtype, n, V, x.stride(0), ptr(y), T, p, None, None, 0,
+    args = [ptr(x), dtype, n, V, x.stride(0), ptr(y), T, p, None, None, top_k,
+            None if k_row is None else ptr(k_row),
             ptr(o["lp_full"]), ptr(o["lp_trunc"]), ptr(o["entropy_trunc"]), ptr(o["entropy_full"]),
             ptr(o["nucleus_size"]), ptr(o["threshold"]), ptr(o["flags"])]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -83,3 +85,21 @@ def test_noalloc_matches_the_workspace_entry_point(T, p):
         want = _call(L, x, dtype, y, T, p, noalloc=False)
         for k in want:
             assert bits_equal(got[k], want[k]), (n, V, k)
+
+
+def test_noalloc_top_k_matches_the_workspace_entry_point():
+    """Top-k (per-row k in the first call, a scalar k in the second, smaller
+    one): the floors live in the static scratch too."""
+    L = _native.lib()
+    for n, handoff, seed, k_scalar in ((300, [3, 40, 200], 7, 0), (100, [1, 60], 900, 40)):
+        x, y = _bf16_rows(n, 151936, handoff, seed)
+        k_row = None
+        if k_scalar == 0:
+            k_row = torch.as_tensor(np.random.default_rng(seed).integers(0, 300, n),
+                                    dtype=torch.int32).to(DEV)
+        print(f"  rlk_logprob_from_logits_noalloc top-k N={n} k={k_scalar or 'per row'}",
+              flush=True)
+        got = _call(L, x, 1, y, 0.7, 0.95, True, k_scalar, k_row)
+        want = _call(L, x, 1, y, 0.7, 0.95, False, k_scalar, k_row)
+        for k in want:
+            assert bits_equal(got[k], want[k]), (n, k)
