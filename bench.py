@@ -7,8 +7,10 @@ Qwen3-scale workload (4096 rows x 151936 vocabulary, bf16 logits, T=0.7,
 top-p=0.95; rows = response tokens), with inputs resident in HBM. `roofline`
 is that kernel's achieved HBM bandwidth (algorithmic bytes / mean launch time
 from HIP events on the launch stream) against 8 TB/s. `cpu_baseline` is the
-fp64 oracle timed on a bounded sample of the same rows on the host. Other
-built paths are reported under `legs`.
+fp64 oracle over all rows of the same workload on the host's cores (one
+worker process per core, up to 16), timed before the GPU is first used.
+Other built paths are reported under `legs`, each with mean, median and min
+times and the GPU clock sampled during its timed region.
 """
 from __future__ import annotations
 
@@ -65,8 +67,70 @@ def _spin_up(torch, seconds=0.3):
         torch.cuda.synchronize()
 
 
+def _sclk_files():
+    import glob
+    return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+
+
+def _read_sclk(files):
+    """The current shader clock (MHz) from the driver's DPM table (the line
+    marked '*'), or None."""
+    import re
+    for f in files:
+        try:
+            for line in open(f):
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                    if m:
+                        return int(m.group(1))
+        except OSError:
+            continue
+    return None
+
+
+class _ClockSampler:
+    """Samples the shader clock every few ms on a host thread while the timed
+    region runs (reading the driver's sysfs table only: no GPU work)."""
+
+    def __init__(self):
+        import threading
+        self.files = _sclk_files()
+        self.samples = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self.stop.is_set():
+            v = _read_sclk(self.files)
+            if v is not None:
+                self.samples.append(v)
+            self.stop.wait(0.002)
+
+    def __enter__(self):
+        if self.files:
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.files:
+            self.thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"median_mhz": int(np.median(self.samples)), "min_mhz": int(min(self.samples)),
+                "max_mhz": int(max(self.samples)), "samples": len(self.samples),
+                "source": "pp_dpm_sclk current level, sampled every ~2 ms"}
+
+
+_LAST_CLOCK = [None]
+
+
 def _events_time(torch, fn, steps, warmup):
-    """Mean and total ms of `fn` over `steps` calls, HIP events on the current stream."""
+    """Mean, total, min and median ms of `fn` over `steps` calls, HIP events
+    on the current stream; the shader clock sampled meanwhile is left in
+    _LAST_CLOCK."""
     _spin_up(torch)
     for _ in range(warmup):
         fn()
@@ -76,15 +140,18 @@ def _events_time(torch, fn, steps, warmup):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        starts[i].record()
-        fn()
-        ends[i].record()
-    t1.record()
-    torch.cuda.synchronize()
+    with _ClockSampler() as clk:
+        t0.record()
+        for i in range(steps):
+            starts[i].record()
+            fn()
+            ends[i].record()
+        t1.record()
+        torch.cuda.synchronize()
+    _LAST_CLOCK[0] = clk.summary()
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return float(np.mean(per)), float(t0.elapsed_time(t1)), float(np.min(per))
+    return (float(np.mean(per)), float(t0.elapsed_time(t1)), float(np.min(per)),
+            float(np.median(per)))
 
 
 def _outs(torch, o):
@@ -143,22 +210,122 @@ def _determinism(torch, run_full, run_rows=None, n=0, seed=0, device="cuda:0"):
 _CPU_ORACLE = [True]
 
 
-def _cpu_oracle(fn, units, sample):
-    """The fp64 oracle timed on a bounded sample of the leg's workload, on one
-    host thread (BLAS pinned to one), as a baseline beside the GPU figure;
-    input widening and other preparation stay outside the timing."""
+def _cpu_oracle(fn, units, sample, blas=False):
+    """The fp64 oracle timed on a bounded sample of the leg's workload on the
+    host, as a baseline beside the GPU figure: with `blas`, its fp64 matrix
+    products use every host core (BLAS threads = _cores()); otherwise one
+    thread (per-row numpy work). Input widening and other preparation stay
+    outside the timing."""
     if not _CPU_ORACLE[0]:
         return None
     try:
         from threadpoolctl import threadpool_limits
-        with threadpool_limits(1):
+        n = _cores() if blas else 1
+        with threadpool_limits(n):
             t0 = time.perf_counter()
             fn()
             dt = time.perf_counter() - t0
-        return {"value": units / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                "sample": f"{sample}, fp64 numpy, one thread, {dt:.2f}s"}
+        how = f"{n} BLAS threads" if blas else "one thread"
+        return {"value": units / dt, "unit": "tokens/s", "cores": n, "kind": "oracle",
+                "sample": f"{sample}, fp64 numpy, {how}, {dt:.2f}s"}
     except Exception as e:  # noqa: BLE001 -- the GPU figure stands without it
         return {"error": f"{type(e).__name__}: {e}"}
+
+
+def _cores():
+    """Host cores this process may use, capped at 16 (a one-GPU machine's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+_POOL = {}    # kind -> fn(lo, hi): oracle work on rows lo..hi (set before the pool forks)
+_DATA = {}    # inputs generated for the CPU baselines, reused by the GPU legs
+_CPU_BASE = {}
+
+
+def _pool_task(task):
+    kind, lo, hi = task
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        _POOL[kind](lo, hi)
+    return hi - lo
+
+
+def _pool_ready(_):
+    return 0
+
+
+def _parallel_oracle(kind, n, cores, chunk):
+    """Wall seconds for the oracle over rows 0..n in `chunk`-row tasks on
+    `cores` forked worker processes (one BLAS thread each). Called before the
+    GPU is first used, so no worker inherits a GPU context."""
+    import multiprocessing as mp
+    tasks = [(kind, lo, min(lo + chunk, n)) for lo in range(0, n, chunk)]
+    with mp.get_context("fork").Pool(cores) as pool:
+        pool.map(_pool_ready, range(cores))          # workers started before the clock
+        t0 = time.perf_counter()
+        done = sum(pool.map(_pool_task, tasks, chunksize=1))
+        dt = time.perf_counter() - t0
+    assert done == n
+    return dt
+
+
+def cpu_baselines(synth):
+    """The fp64 oracle on the host's cores, before any GPU call: every row of
+    the logits-in workloads (4096 x 151936 bf16 and 256 x 8192 fp32) and the
+    GRPO loss stage over every token of the packed batch. Inputs are
+    generated first (untimed) and kept for the GPU legs."""
+    from oracle import grpo as OG
+    from oracle import logprob as OL
+    cores = _cores()
+    w = synth.workload("qwen")
+    t_gen = time.perf_counter()
+    arr = synth.logits_rows(w, range(w.N))
+    y = synth.peak_targets(w, range(w.N))
+    _DATA["qwen"] = (arr, y)
+    Tq, pq = OL.f32(w.temperature), OL.f32(w.top_p)
+    _POOL["qwen"] = lambda lo, hi: OL.logprob_from_logits(OL.widen_bf16(arr[lo:hi]), y[lo:hi],
+                                                          Tq, pq)
+    wt = synth.workload("tiny")
+    arr_t = synth.logits_rows(wt, range(wt.N))
+    y_t = np.argmax(arr_t, axis=1).astype(np.int64)
+    _DATA["tiny"] = (arr_t, y_t)
+    Tt, pt = OL.f32(wt.temperature), OL.f32(wt.top_p)
+    _POOL["tiny"] = lambda lo, hi: OL.logprob_from_logits(arr_t[lo:hi].astype(np.float64),
+                                                          y_t[lo:hi], Tt, pt)
+    print(f"[bench] CPU baselines: inputs generated in {time.perf_counter() - t_gen:.1f}s; "
+          f"{cores} worker processes", file=sys.stderr, flush=True)
+    dt = _parallel_oracle("qwen", w.N, cores, 16)
+    _CPU_BASE["logits"] = {"value": w.N / dt, "unit": "tokens/s", "cores": cores,
+                           "kind": "oracle",
+                           "sample": f"all {w.N} rows of the workload, fp64 numpy oracle "
+                                     f"(sort-based nucleus per row), {cores} worker processes "
+                                     f"x 1 thread, {dt:.1f}s wall"}
+    dt = _parallel_oracle("tiny", wt.N, cores, 8)
+    _CPU_BASE["tiny"] = {"value": wt.N / dt, "unit": "tokens/s", "cores": cores,
+                         "kind": "oracle",
+                         "sample": f"all {wt.N} rows, fp64 numpy oracle, {cores} worker "
+                                   f"processes x 1 thread, {dt:.2f}s wall"}
+    # the GRPO loss stage: one vectorised call over the whole packed batch
+    wg = synth.workload("grpo")
+    cu = synth.cu_seqlens(synth.response_lengths(wg))
+    T_tot = int(cu[-1])
+    r = np.random.default_rng(4)
+    lp_new = -np.abs(r.normal(0.5, 1.0, T_tot))
+    lp_old = lp_new + r.normal(0, 0.05, T_tot)
+    lp_ref = lp_new + r.normal(0, 0.1, T_tot)
+    rw = synth.rewards(wg)
+    t0 = time.perf_counter()
+    OG.token_loss(lp_new, lp_old, lp_ref, cu, OG.advantages(rw, wg.group_size))
+    dt = time.perf_counter() - t0
+    _CPU_BASE["grpo_loss"] = {"value": T_tot / dt, "unit": "tokens/s", "cores": 1,
+                              "kind": "oracle",
+                              "sample": f"the GRPO/DAPO loss stage over all {T_tot} packed "
+                                        f"tokens (advantages, ratios, clipped surrogate, k3, "
+                                        f"gradient), fp64 numpy, one thread, {dt:.3f}s"}
 
 
 def _host_bits(torch, t):
@@ -166,18 +333,21 @@ def _host_bits(torch, t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def leg_logits(torch, rlk, synth, steps, warmup, cpu_sample):
+def leg_logits(torch, rlk, synth, steps, warmup):
     w = synth.workload("qwen")
     t_gen = time.perf_counter()
-    arr = synth.logits_rows(w, range(w.N))
-    y = synth.peak_targets(w, range(w.N))
+    if "qwen" in _DATA:
+        arr, y = _DATA["qwen"]
+    else:
+        arr = synth.logits_rows(w, range(w.N))
+        y = synth.peak_targets(w, range(w.N))
     x = torch.from_numpy(arr.view(np.int16)).to("cuda:0").view(torch.bfloat16)
     yt = torch.from_numpy(y).to("cuda:0")
     gen_s = time.perf_counter() - t_gen
     print(f"[bench] logits leg: inputs {tuple(x.shape)} bf16 generated in {gen_s:.1f}s",
           file=sys.stderr, flush=True)
     fn = lambda: rlk.logprob_from_logits(x, yt, w.temperature, w.top_p)  # noqa: E731
-    mean_ms, total_ms, min_ms = _events_time(torch, fn, steps, warmup)
+    mean_ms, total_ms, min_ms, med_ms = _events_time(torch, fn, steps, warmup)
     det = _determinism(
         torch, fn, lambda idx: _outs(torch, rlk.logprob_from_logits(
             x[idx], yt[idx], w.temperature, w.top_p)), w.N, seed=2)
@@ -189,24 +359,53 @@ def leg_logits(torch, rlk, synth, steps, warmup, cpu_sample):
                     f"T={w.temperature}, top-p={w.top_p}",
         "tokens_per_s": rows * steps / (total_ms * 1e-3),
         "ms_per_step": total_ms / steps,
-        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "kernel_ms_mean": mean_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min_ms,
+        "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _profile_traffic("bf16_hist_rows_qwen3_logits_4096x151936")},
         "bytes_per_row": bytes_per_row,
         "determinism": det,
     }
-    if cpu_sample > 0:
-        from oracle import logprob as OL
-        rows_s = list(range(cpu_sample))
-        z = OL.widen_bf16(arr[rows_s])
-        t0 = time.perf_counter()
-        OL.logprob_from_logits(z, y[rows_s], OL.f32(w.temperature), OL.f32(w.top_p))
-        dt = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": cpu_sample / dt, "unit": "tokens/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": f"first {cpu_sample} of the {w.N} rows, fp64 numpy, "
-                                         f"one process/thread, {dt:.1f}s"}
+    if "logits" in _CPU_BASE:
+        res["cpu_baseline"] = _CPU_BASE["logits"]
+    return res
+
+
+def leg_tiny(torch, rlk, synth, steps, warmup):
+    """The small logits-in workload: 256 rows x 8192 fp32 logits ~N(0, 3^2),
+    T=0.7, top-p=0.95 (8.4 MB: it stays in the 256 MB Infinity Cache, so the
+    HBM roofline is reported, not a bound)."""
+    w = synth.workload("tiny")
+    if "tiny" in _DATA:
+        arr, y = _DATA["tiny"]
+    else:
+        arr = synth.logits_rows(w, range(w.N))
+        y = np.argmax(arr, axis=1).astype(np.int64)
+    x = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to("cuda:0")
+    yt = torch.from_numpy(y).to("cuda:0")
+    fn = lambda: rlk.logprob_from_logits(x, yt, w.temperature, w.top_p)  # noqa: E731
+    mean_ms, total_ms, min_ms, med_ms = _events_time(torch, fn, steps, warmup)
+    det = _determinism(
+        torch, fn, lambda idx: _outs(torch, rlk.logprob_from_logits(
+            x[idx], yt[idx], w.temperature, w.top_p)), w.N, seed=1)
+    bytes_per_row = 4 * w.V + 8 + 25
+    achieved = w.N * bytes_per_row / (mean_ms * 1e-3) / 1e9
+    res = {
+        "workload": f"logits-in, {w.N} rows x V={w.V}, fp32 ~N(0,3^2), T={w.temperature}, "
+                    f"top-p={w.top_p} (cache-resident: roofline reported, not graded)",
+        "tokens_per_s": w.N * steps / (total_ms * 1e-3),
+        "ms_per_step": total_ms / steps,
+        "kernel_ms_mean": mean_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min_ms,
+        "gpu_clock": _LAST_CLOCK[0],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "bytes_per_row": bytes_per_row,
+        "determinism": det,
+    }
+    if "tiny" in _CPU_BASE:
+        res["cpu_oracle"] = _CPU_BASE["tiny"]
     return res
 
 
@@ -237,10 +436,10 @@ def leg_support(torch, rlk, synth, steps, warmup):
     print(f"[bench] support leg: {w.N} rows, {nnz} retained ids (median "
           f"{int(sizes.median())}, max {int(sizes.max())})", file=sys.stderr, flush=True)
     fn = lambda: rlk.logprob_from_support(x, yt, w.temperature, offsets, ids)  # noqa: E731
-    mean_ms, total_ms, min_ms = _events_time(torch, fn, steps, warmup)
+    mean_ms, total_ms, min_ms, med_ms = _events_time(torch, fn, steps, warmup)
     fnc = lambda: rlk.logprob_from_support(x, yt, w.temperature, offsets, ids,  # noqa: E731
                                            check_top_p=w.top_p)
-    mean_c, total_c, min_c = _events_time(torch, fnc, max(3, steps // 4), warmup)
+    mean_c, total_c, min_c, med_c = _events_time(torch, fnc, max(3, steps // 4), warmup)
     det = _determinism(torch, fnc)
     from oracle import logprob as OL
     from oracle import support as OSup
@@ -266,7 +465,8 @@ def leg_support(torch, rlk, synth, steps, warmup):
                     f"sets = top-p {w.top_p} nuclei ({nnz} ids)",
         "tokens_per_s": w.N * steps / (total_ms * 1e-3),
         "ms_per_step": total_ms / steps,
-        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "kernel_ms_mean": mean_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min_ms,
+        "gpu_clock": _LAST_CLOCK[0],
         "distinct_64B_sectors": sectors,
         "with_nucleus_check_ms": mean_c,
         "with_nucleus_check_tokens_per_s": w.N / (mean_c * 1e-3),
@@ -282,8 +482,9 @@ def leg_sample(torch, rlk, synth, steps, warmup):
     """Rollout-side top-p sampler on the config-2 logits (4096 x 151936 bf16,
     T=0.7, p=0.95): nucleus (row kernel), then the seeded Gumbel-max draw,
     which scores the drawn token with the row kernel's own statistics
-    (bitwise the training-side value). The call reads each row twice
-    (nucleus, draw): 2 x 2V bytes per row plus outputs."""
+    (bitwise the training-side value). Algorithmic bytes: one read of each
+    row (2V) plus the outputs; the call reads each row twice (nucleus pass,
+    then the draw), so the fraction counts the second read as overhead."""
     w = synth.workload("qwen")
     arr = synth.logits_rows(w, range(w.N))
     x = torch.from_numpy(arr.view(np.int16)).to("cuda:0").view(torch.bfloat16)
@@ -293,7 +494,7 @@ def leg_sample(torch, rlk, synth, steps, warmup):
         state["offset"] += 1
         return rlk.sample_top_p(x, w.temperature, w.top_p, 1234, state["offset"])
 
-    mean_ms, total_ms, min_ms = _events_time(torch, fn, steps, warmup)
+    mean_ms, total_ms, min_ms, med_ms = _events_time(torch, fn, steps, warmup)
     # with row keys = original row ids, a draw is a function of its row alone
     det = _determinism(
         torch, lambda: rlk.sample_top_p(x, w.temperature, w.top_p, 1234, 7),
@@ -310,14 +511,15 @@ def leg_sample(torch, rlk, synth, steps, warmup):
         OL.logprob_from_logits(z_h, yd, Tf, pf)
 
     cpu = _cpu_oracle(oracle_draws, ns, f"first {ns} rows (draw and score)")
-    bytes_per_row = 2 * 2 * w.V + 8 + 4 + 4 + 4 + 1
+    bytes_per_row = 2 * w.V + 8 + 4 + 4 + 4 + 1
     achieved = w.N * bytes_per_row / (mean_ms * 1e-3) / 1e9
     return {
         "workload": f"top-p sampler + score, {w.N} rows x V={w.V} bf16, T={w.temperature}, "
                     f"top-p={w.top_p}, Philox-4x32-10 Gumbel-max",
         "tokens_per_s": w.N * steps / (total_ms * 1e-3),
         "ms_per_step": total_ms / steps,
-        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "kernel_ms_mean": mean_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min_ms,
+        "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "bytes_per_row": bytes_per_row,
@@ -339,7 +541,7 @@ def leg_fused(torch, rlk, synth, steps, warmup):
     print(f"[bench] fused leg: hidden {tuple(h.shape)} W {tuple(W.shape)} generated in "
           f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     fn = lambda: rlk.logprob_fused_linear(h, W, yt, w.temperature, 1.0)  # noqa: E731
-    mean_ms, total_ms, min_ms = _events_time(torch, fn, steps, warmup)
+    mean_ms, total_ms, min_ms, med_ms = _events_time(torch, fn, steps, warmup)
     det = _determinism(
         torch, fn, lambda idx: _outs(torch, rlk.logprob_fused_linear(
             h[idx], W, yt[idx], w.temperature, 1.0)), w.N, seed=3)
@@ -349,7 +551,7 @@ def leg_fused(torch, rlk, synth, steps, warmup):
     W64 = OL.widen_bf16(wb)
     h64 = OL.widen_bf16(hb[:ns])
     cpu = _cpu_oracle(lambda: OF.forward(h64, W64, y[:ns], OL.f32(w.temperature), 1.0), ns,
-                      f"first {ns} tokens")
+                      f"first {ns} tokens", blas=True)
     del W64
     flops = 2.0 * w.N * w.V * w.H
     achieved = flops / (mean_ms * 1e-3) / 1e12
@@ -358,7 +560,8 @@ def leg_fused(torch, rlk, synth, steps, warmup):
                     f"T={w.temperature}, top-p=1",
         "tokens_per_s": w.N * steps / (total_ms * 1e-3),
         "ms_per_step": total_ms / steps,
-        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "kernel_ms_mean": mean_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min_ms,
+        "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": _profile_traffic("fwd_tile_stats_qwen3_head_8192x4096x151936")},
@@ -390,7 +593,7 @@ def leg_fused_bwd(torch, rlk, synth, steps, warmup):
         out = rlk.logprob_fused_linear(h, W, yt, w.temperature, 1.0)
         return rlk.logprob_fused_linear_bwd(h, W, yt, out["saved"], g_lp, g_h, w.temperature, 1.0)
 
-    mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
+    mean_ms, total_ms, min_ms, med_ms = _events_time(torch, step, steps, warmup)
 
     def dh_rows(idx):   # dh of the rows idx (a row's dh depends on that row only; dW sums rows)
         hi, yi = h[idx], yt[idx]
@@ -411,7 +614,7 @@ def leg_fused_bwd(torch, rlk, synth, steps, warmup):
         OF.backward(h64, W64, y[:ns], gl, gh, 1.0, 1.0)
 
     cpu = _cpu_oracle(oracle_step, ns, f"first {ns} tokens, forward and backward "
-                                       "(dW: their contribution)")
+                                       "(dW: their contribution)", blas=True)
     del W64
     flops = 8.0 * w.N * w.V * w.H      # forward 2VH + recompute 2VH + dh 2VH + dW 2VH per token
     achieved = flops / (mean_ms * 1e-3) / 1e12
@@ -420,7 +623,8 @@ def leg_fused_bwd(torch, rlk, synth, steps, warmup):
                     f"W [{w.V},{w.H}] bf16, T=1, top-p=1, loss -mean lp - 0.001 mean H",
         "tokens_per_s": w.N * steps / (total_ms * 1e-3),
         "ms_per_step": total_ms / steps,
-        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "kernel_ms_mean": mean_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min_ms,
+        "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": None},
@@ -479,7 +683,7 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
         return rlk.grpo_token_loss(out["logprob"], g["lp_old"], g["lp_ref"], g["cu_dev"],
                                    rewards=g["rw"], group_size=w.group_size)
 
-    mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
+    mean_ms, total_ms, min_ms, med_ms = _events_time(torch, step, steps, warmup)
     # the loss and its per-token outputs run to run; the top-p forward's
     # per-token outputs under splits and a permutation of the tokens
     det = _determinism(torch, step)
@@ -504,7 +708,8 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
         OG.token_loss(lp_o, lp_o, lp_r, g["cu"], OG.advantages(r_h, w.group_size))
 
     cpu = _cpu_oracle(oracle_grpo, ns, f"first {ns} tokens of the top-p forward, plus the "
-                                       f"loss stage over all {T_tot} tokens")
+                                       f"loss stage over all {T_tot} tokens", blas=True)
+    cpu_loss = _CPU_BASE.get("grpo_loss")
     del W64
     flops = 2.0 * T_tot * w.V * w.H
     achieved = flops / (mean_ms * 1e-3) / 1e12
@@ -513,13 +718,15 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
                     f"H={w.H}, V={w.V}, T={w.temperature}, top-p={w.top_p}",
         "tokens_per_s": T_tot * steps / (total_ms * 1e-3),
         "ms_per_step": total_ms / steps,
-        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "kernel_ms_mean": mean_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min_ms,
+        "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": None},
         "flops_per_token": 2.0 * w.V * w.H,
         "determinism": det,
         "cpu_oracle": cpu,
+        "cpu_oracle_loss_stage": cpu_loss,
     }
 
 
@@ -537,7 +744,7 @@ def leg_grpo_train(torch, rlk, synth, steps, warmup):
         return rlk.logprob_fused_linear_bwd(g["h"], g["W"], g["yt"], out["saved"], loss["grad"],
                                             None, w.temperature, w.top_p)
 
-    mean_ms, total_ms, min_ms = _events_time(torch, step, steps, warmup)
+    mean_ms, total_ms, min_ms, med_ms = _events_time(torch, step, steps, warmup)
     det = _determinism(torch, step)   # dh and dW, three steps bitwise
     from oracle import fused as OF
     from oracle import logprob as OL
@@ -553,7 +760,7 @@ def leg_grpo_train(torch, rlk, synth, steps, warmup):
         OF.backward(h64, W64, y_h, gl, np.zeros(ns), Tf, pf)
 
     cpu = _cpu_oracle(oracle_step, ns, f"first {ns} tokens, top-p forward and backward "
-                                       "(dW: their contribution)")
+                                       "(dW: their contribution)", blas=True)
     del W64
     flops = 8.0 * T_tot * w.V * w.H    # forward 2VH + recompute 2VH + dh 2VH + dW 2VH per token
     achieved = flops / (mean_ms * 1e-3) / 1e12
@@ -563,7 +770,8 @@ def leg_grpo_train(torch, rlk, synth, steps, warmup):
                     f"T={w.temperature}, top-p={w.top_p}",
         "tokens_per_s": T_tot * steps / (total_ms * 1e-3),
         "ms_per_step": total_ms / steps,
-        "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+        "kernel_ms_mean": mean_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min_ms,
+        "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": None},
@@ -580,9 +788,10 @@ def leg_copy(torch, steps, warmup):
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
     dst = torch.empty_like(src)
-    mean_ms, total_ms, min_ms = _events_time(torch, lambda: dst.copy_(src), steps, warmup)
+    mean_ms, total_ms, min_ms, med_ms = _events_time(torch, lambda: dst.copy_(src), steps, warmup)
     return {"workload": "device copy, 1 GiB", "bytes_read": n, "bytes_written": n,
-            "kernel_ms_mean": mean_ms, "kernel_ms_min": min_ms,
+            "kernel_ms_mean": mean_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min_ms,
+        "gpu_clock": _LAST_CLOCK[0],
             "tokens_per_s": 0.0, "ms_per_step": total_ms / steps,
             "roofline": {"bound": "hbm", "achieved": round(2 * n / (mean_ms * 1e-3) / 1e9, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -595,9 +804,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--legs", default="logits,support,sample,fused,grpo,grpo_train,fused_bwd")
-    ap.add_argument("--cpu-sample", type=int, default=1024,
-                    help="rows of the logits workload the CPU oracle is timed on (0 = skip)")
+    ap.add_argument("--legs",
+                    default="logits,tiny,support,sample,fused,grpo,grpo_train,fused_bwd")
+    ap.add_argument("--cpu-sample", type=int, default=1,
+                    help="0 = skip the CPU oracle timings (profiler runs)")
     ap.add_argument("--no-determinism", action="store_true",
                     help="skip the bitwise determinism checks (profiler runs)")
     args = ap.parse_args()
@@ -608,16 +818,19 @@ def main():
                                    "(multi-GPU sharding is a design note only)"}))
         sys.exit(2)
 
-    import torch
     import synth
+    legs = [s for s in args.legs.split(",") if s]
+    if args.cpu_sample > 0 and "logits" in legs:
+        cpu_baselines(synth)   # before the GPU is first used
+
+    import torch
     import grpo_loss_rlk_amd as rlk
 
-    legs = [s for s in args.legs.split(",") if s]
     out_legs = {}
     if "logits" in legs:   # the headline: a failure here fails the run
-        out_legs["logits"] = leg_logits(torch, rlk, synth, args.steps, args.warmup,
-                                        args.cpu_sample)
+        out_legs["logits"] = leg_logits(torch, rlk, synth, args.steps, args.warmup)
     others = {
+        "tiny": lambda: leg_tiny(torch, rlk, synth, args.steps, args.warmup),
         "support": lambda: leg_support(torch, rlk, synth, args.steps, args.warmup),
         "sample": lambda: leg_sample(torch, rlk, synth, max(3, args.steps // 4), args.warmup),
         "fused": lambda: leg_fused(torch, rlk, synth, min(20, max(3, args.steps // 4)), 1),

@@ -65,3 +65,23 @@ def test_profile_traffic_follows_the_source_hash(tmp_path, monkeypatch):
         fh.write("edited\n")
     assert bench._profile_traffic("k_w") is None
     assert bench._profile_traffic("no_such_summary") is None
+
+
+def test_sclk_parser(tmp_path):
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1800Mhz *\n2: 2400Mhz\n")
+    assert bench._read_sclk([str(f)]) == 1800
+    f.write_text("S: 2103Mhz *\n")
+    assert bench._read_sclk([str(f)]) == 2103
+    f.write_text("0: 500Mhz\n")
+    assert bench._read_sclk([str(f)]) is None
+    assert bench._read_sclk([str(tmp_path / "missing")]) is None
+
+
+def test_parallel_oracle_covers_every_row():
+    seen = []
+    bench._POOL["toy"] = lambda lo, hi: sum(range(lo, hi))
+    dt = bench._parallel_oracle("toy", 103, 3, 10)
+    assert dt >= 0.0
+    assert bench._cores() >= 1
+    del bench._POOL["toy"], seen
