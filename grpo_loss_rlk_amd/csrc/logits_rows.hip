@@ -985,34 +985,41 @@ RLK_DEV int walk_bins(const uint64_t* bins, int nbins, uint64_t thr, uint64_t* a
 
 // Per-row constants of the fp32 kernel.
 struct F32Scale {
-  double m;      // row max
   double c;      // log2(e) / T
-  double invT;   // 1 / T
-  double cneg;   // -(bins per nat) / T: bin of s = z - m is floor(s * cneg)
+  double mc;     // m c, m the row max
+  double binc;   // -(bins per nat) ln 2: the bin of x is floor(x binc)
 };
 
-// exp((z - m)/T) in fp32 to about 1 ulp. s = z - m is exact in fp64 (two
-// fp32 values); the exponent x = s log2(e)/T is formed in fp64, rounded to
-// fp32 x_hi for the hardware exp2, and its residual restored to first order,
-// 2^x = 2^x_hi (1 + (x - x_hi) ln 2) (|x - x_hi| <= 2^-18 wherever the mass
-// is above 2^-64). Below 2^-126 a mass is far under the fixed-point unit and
-// the sums' resolution, whatever the denormal handling. *s receives z - m.
-RLK_DEV float f32_mass(float z, const F32Scale& k, double* s) {
-  const double sd = double(z) - k.m;
-  const double x = sd * k.c;
+// x = (z - m) log2(e) / T in fp64: one fma of z c - m c, monotone in z.
+RLK_DEV double f32_x(float z, const F32Scale& k) { return fma(double(z), k.c, -k.mc); }
+
+// exp((z - m)/T) = 2^x in fp32 to about 1 ulp: x rounded to fp32 x_hi for the
+// hardware exp2 and its residual restored to first order, 2^x = 2^x_hi (1 +
+// (x - x_hi) ln 2) (|x - x_hi| <= 2^-18 wherever the mass is above 2^-64).
+// Below 2^-126 a mass is far under the fixed-point unit and the sums'
+// resolution, whatever the denormal handling.
+RLK_DEV float f32_mass(double x) {
   const float xh = float(x);
   const float r = float(x - double(xh));
   const float e = __builtin_amdgcn_exp2f(xh);
-  *s = sd;
   return fmaf(e, r * 0.69314718f, e);
 }
 
-// round(e * 2^39) for e in [0, 1], ties to even: adding 2^52 in fp64 leaves
-// the integer in the low bits of the significand.
+// The d bin of x (64 bins per nat below the max, the last one open-ended): a
+// bin index never increases with z.
+RLK_DEV int f32_bin(double x, const F32Scale& k) {
+  const double u = x * k.binc;
+  return u < double(kFBins - 1) ? int(u) : kFBins - 1;
+}
+
+// round(e * 2^39) for e in [0, 1], ties to even: e 2^39 is exact, and adding
+// 2^52 in fp64 leaves the integer in the low bits of the significand.
 RLK_DEV uint64_t f32_fixed(double e) {
-  const double v = fma(e, 549755813888.0, 4503599627370496.0);
+#pragma clang fp contract(off)   // a multiply and an add: an fma costs two moves per element
+  const double v = e * 549755813888.0 + 4503599627370496.0;
   return uint64_t(__double_as_longlong(v)) - 0x4330000000000000ull;
 }
+constexpr double kFixUnit = 1.0 / 549755813888.0;   // 2^-39
 
 // Visit every element of a row, 16 bytes per lane per load with kF32Unroll
 // loads in flight per thread (the loads of a group are issued before any of
@@ -1131,96 +1138,114 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
   const double m = double(mx);
   const double invT = 1.0 / double(Tv);
   F32Scale ks;
-  ks.m = m;
   ks.c = 1.4426950408889634 * invT;
-  ks.invT = invT;
-  ks.cneg = -double(kFBinPerNat) * invT;
+  ks.mc = m * ks.c;
+  ks.binc = -double(kFBinPerNat) * 0.6931471805599453;
   // every element below this has zero mass at fp32 precision; clamping -inf
   // to it keeps the arithmetic free of inf - inf
   const float zfloor = float(m - 1e30);
   const bool cut_p = p < 1.f;
   const bool cut = cut_p || has_floor;
-  auto bin_of = [&](double s) {   // s = z - m <= 0
-    const double u = s * ks.cneg;
-    return u < double(kFBins - 1) ? int(u) : kFBins - 1;
-  };
+  // sum e d over the row is needed for the full entropy (when the caller
+  // asks for it) and at top-p 1 for the truncated one too
+  const bool need_s = a.ent_full != nullptr || !cut_p;
 
-  // ---- pass 2: Z, sum e d, histogram of fixed-point masses over d bins
-  //      (with top-k, of the values at or above its floor only) ----
+  // ---- pass 2: Z (fixed point), sum e d, histogram of fixed-point masses
+  //      over d bins (with top-k, of the values at or above its floor only) ----
   if (cut_p) {
     for (int i = tid; i < kFBins; i += kF32T) hist[i] = 0ull;
     if (tid == 0) ncand_s = 0;
     __syncthreads();
   }
-  // Per element without branches except the atomic; the top-p histogram and
-  // the top-k floor are compile-time variants.
-  double zt = 0.0, st = 0.0;
-  uint64_t wt = 0;
-  auto pass2 = [&](auto with_hist, auto with_floor) {
+  // Per element without branches except the atomic; the top-p histogram,
+  // the top-k floor and the entropy sum are compile-time variants.
+  // (wt: the cut's mass, at or above the top-k floor; wall: the whole row's,
+  // kept apart only when a floor makes the two differ)
+  double st = 0.0;
+  uint64_t wt = 0, wall = 0;
+  auto pass2 = [&](auto with_hist, auto with_floor, auto with_s) {
     for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
-      double dz;
-      const float e = f32_mass(fmaxf(z, zfloor), ks, &dz);
-      const double ed = double(e);
-      zt += ed;
-      st = fma(ed, dz * invT, st);
+      const double x = f32_x(fmaxf(z, zfloor), ks);
+      const double ed = double(f32_mass(x));
+      const uint64_t w = f32_fixed(ed);
+      if constexpr (decltype(with_s)::value) st = fma(ed, x * 0.6931471805599453, st);
       if constexpr (decltype(with_hist)::value) {
-        uint64_t w = f32_fixed(ed);
-        if constexpr (decltype(with_floor)::value) w = f32_key(z) >= fk ? w : 0ull;
+        uint64_t wk = w;
+        if constexpr (decltype(with_floor)::value) {
+          wall += w;
+          wk = f32_key(z) >= fk ? w : 0ull;
+        }
+        wt += wk;
+        if (wk)
+          atomicAdd(reinterpret_cast<unsigned long long*>(&hist[f32_bin(x, ks)]),
+                    (unsigned long long)wk);
+      } else {
         wt += w;
-        if (w)
-          atomicAdd(reinterpret_cast<unsigned long long*>(&hist[bin_of(dz)]),
-                    (unsigned long long)w);
       }
     });
   };
-  if (!cut_p) pass2(std::false_type{}, std::false_type{});
-  else if (has_floor) pass2(std::true_type{}, std::true_type{});
-  else pass2(std::true_type{}, std::false_type{});
-  const double Z = block_sum(zt, sd);
-  const double S = block_sum(st, sd);
+  constexpr std::true_type Y{};
+  constexpr std::false_type N{};
+  if (!cut_p) {
+    pass2(N, N, Y);
+  } else if (has_floor) {
+    pass2(Y, Y, N);
+    if (need_s)   // the full entropy with top-k and top-p: a pass of its own
+      for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {   // (one loop would spill)
+        const double x = f32_x(fmaxf(z, zfloor), ks);
+        st = fma(double(f32_mass(x)), x * 0.6931471805599453, st);
+      });
+  } else {
+    need_s ? pass2(Y, N, Y) : pass2(Y, N, N);
+  }
+  const uint64_t wt_sum = cut_p ? block_sum(wt, su64) : 0ull;
+  const uint64_t wall_sum = (cut_p && !has_floor) ? wt_sum : block_sum(cut_p ? wall : wt, su64);
+  const double Z = double(wall_sum) * kFixUnit;
+  const double S = need_s ? block_sum(st, sd) : 0.0;
 
   double Zs = Z, Ss = S;
   uint32_t tau_key = 0;
   uint32_t size = nfin;
   if (!cut_p && has_floor) {   // top-k at top-p 1: S is the top-k set
-    double zs = 0.0, ss = 0.0;
+    uint64_t zs = 0;
+    double ss = 0.0;
     uint32_t cnt = 0;
     for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
       const bool in = z > -INFINITY && f32_key(z) >= fk;
-      double dz;
-      const float e = f32_mass(fmaxf(z, zfloor), ks, &dz);
-      const double ed = in ? double(e) : 0.0;
-      zs += ed;
-      ss = fma(ed, dz * invT, ss);
+      const double x = f32_x(fmaxf(z, zfloor), ks);
+      const double ed = in ? double(f32_mass(x)) : 0.0;
+      zs += f32_fixed(ed);
+      ss = fma(ed, x * 0.6931471805599453, ss);
       cnt += in ? 1u : 0u;
     });
-    Zs = block_sum(zs, sd);
+    Zs = double(block_sum(zs, su64)) * kFixUnit;
     Ss = block_sum(ss, sd);
     size = uint32_t(block_sum(uint64_t(cnt), su64));
     tau_key = fk;
   }
   if (cut_p) {
-    const uint64_t W = block_sum(wt, su64);
+    const uint64_t W = wt_sum;
     const uint64_t thr = uint64_t(ceil(double(p) * double(W)));
     uint64_t above = 0;
     int bstar = walk_bins<kF32T>(hist, kFBins, thr, &above, su64, si, &bslot);
     if (bstar < 0) bstar = kFBins - 1;   // unreachable: the total mass reaches thr
 
-    // ---- pass 3: sums above the crossing bin; its elements' keys to LDS ----
-    // The sums take exp2 of the fp32-rounded exponent: about 2^-24 |x| ln 2
-    // relative per element, and weighted by mass |x| averages at most log2 of
-    // the element count (x = log2 of the element's mass relative to the max),
-    // so the sums are off by under 2e-6 relative. The cut never uses it.
-    double zs = 0.0, ss = 0.0;
+    // ---- pass 3: sum e d above the crossing bin; its elements' keys to LDS
+    // (Z_S itself is exact in fixed point: the mass above the crossing bin
+    // plus the crossing bin's kept masses). The sum takes exp2 of the
+    // fp32-rounded exponent: about 2^-24 |x| ln 2 relative per element, and
+    // weighted by mass |x| averages at most log2 of the element count (x =
+    // log2 of the element's mass relative to the max), so it is off by under
+    // 2e-6 relative. The cut never uses it.
+    double ss = 0.0;
     uint32_t cnt = 0;
     for_each_f32<kVec>(rowp, V, [&](float z, int64_t) {
-      const double dz = double(fmaxf(z, zfloor)) - m;
-      const int b = z > -INFINITY ? bin_of(dz) : kFBins;   // -inf: in no bin
+      const double x = f32_x(fmaxf(z, zfloor), ks);
+      const int b = z > -INFINITY ? f32_bin(x, ks) : kFBins;   // -inf: in no bin
       const bool in = b < bstar;
-      const float e = in ? __builtin_amdgcn_exp2f(float(dz * ks.c)) : 0.f;
-      const double ed = double(e);
-      zs += ed;
-      ss = fma(ed, dz * invT, ss);
+      const float xf = float(x);
+      const float e = in ? __builtin_amdgcn_exp2f(xf) : 0.f;
+      ss = fma(double(e), double(xf * 0.69314718f), ss);
       cnt += in ? 1u : 0u;
       if (b == bstar && f32_key(z) >= fk) {   // below the top-k floor: not a candidate
         const unsigned int slot = atomicAdd(&ncand_s, 1u);
@@ -1258,8 +1283,7 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
     int tau_idx = nc - 1;
     for (int base = 0; base < nc; base += kF32T) {
       const int i = base + tid;
-      double dz;
-      const uint64_t v = i < nc ? f32_fixed(double(f32_mass(key_f32(cand[i]), ks, &dz))) : 0ull;
+      const uint64_t v = i < nc ? f32_fixed(double(f32_mass(f32_x(key_f32(cand[i]), ks)))) : 0ull;
       uint64_t tot;
       const uint64_t incl = block_inclusive_scan(v, su64, &tot);
       const int c = (i < nc && carry + incl >= thr) ? tid : kF32T;
@@ -1276,19 +1300,18 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
     for (int i = tid; i < nc; i += kF32T) {
       const uint32_t k = cand[i];
       if (k < tau_key) continue;
-      double dz;
-      const double ed = double(f32_mass(key_f32(k), ks, &dz));
-      zs += ed;
-      ss = fma(ed, dz * invT, ss);
+      const double x = f32_x(key_f32(k), ks);
+      const double ed = double(f32_mass(x));
+      ss = fma(ed, x * 0.6931471805599453, ss);
       ++cnt;
       if (k > tau_key) mgt += f32_fixed(ed);
       else mat += f32_fixed(ed);
     }
-    Zs = block_sum(zs, sd);
     Ss = block_sum(ss, sd);
     size = uint32_t(block_sum(uint64_t(cnt), su64));
     mgt = above + block_sum(mgt, su64);
     mat = block_sum(mat, su64);
+    Zs = double(mgt + mat) * kFixUnit;
     if (tid == 0) {
       const double pp = double(p);
       if (fabs(double(mgt) / double(W) - pp) <= kBoundaryEps ||
@@ -1321,8 +1344,9 @@ __global__ __launch_bounds__(kF32T, kF32WavesPerSimd) void f32_rows(RowArgs a) {
       a.score_stats[2 * row] = m;
       a.score_stats[2 * row + 1] = logZs;
     }
-    store_row(a, row, lpf, lpt, float(logZ - S / Z), float(logZs - Ss / Zs), int32_t(size), tau,
-              flags, float(m * invT + logZs), float(m * invT + Ss / Zs));
+    const float h_full = need_s ? float(logZ - S / Z) : __builtin_nanf("");
+    store_row(a, row, lpf, lpt, h_full, float(logZs - Ss / Zs), int32_t(size), tau, flags,
+              float(m * invT + logZs), float(m * invT + Ss / Zs));
   }
 }
 
