@@ -73,33 +73,60 @@ RLK_DEV void copy_offsets(uint32_t (&off)[kLoads], int64_t row0, int64_t nrows, 
   }
 }
 
-// Copies of stages t and t+1 of one operand for one of this thread's slots
-// (the 64-byte halves of the same rows, back to back). The copy reads its
-// LDS destination from M0, which the statement sets and declares clobbered
-// (clang warns that M0 is reserved; declaring it is what keeps the compiler
-// from relying on an M0 value across the statement).
-struct CopyPlan {
-  uint4* lds_t[2];          // [A, B] stage t buffers
-  uint4* lds_t1[2];         // [A, B] stage t+1 buffers
-  const uint16_t* g_t[2];   // [A, B] global base of stage t
+// LDS addresses are 32-bit integers here. Everything a copy needs besides
+// the per-lane global offset is uniform over the wave (its LDS destination
+// goes to M0), so it is formed from scalar values only; formed from per-lane
+// values it costs a VALU chain and a v_readfirstlane per copy, which in-order
+// issue has to wait out between the MFMAs (about 8 % of the loop's time).
+// Fragment reads use one per-lane base per operand and k-step plus the
+// stage's offset, the rest as the instruction's immediate offset.
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
+
+struct TileCtx {
+  uint32_t lds;          // LDS byte address of the stage buffers
+  uint32_t wave_off;     // bytes: this wave's first copy slot inside an operand, w * kLoads * 1 KB
+  uint32_t frag[2][2];   // per lane, [A, B][k-step]: LDS byte address of its fragment row in stage 0
 };
 
+// Fragment rows 128 wm + 32 x + lane % 32: the swizzle hash depends on
+// row & 15 only, so a read's address is a per-lane part (one per k-step) plus
+// a uniform part.
+RLK_DEV TileCtx tile_ctx(Smem& smem) {
+  TileCtx c;
+  c.lds = uint32_t(reinterpret_cast<uintptr_t>((lds_char*)(&smem[0][0][0])));
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  c.wave_off = uint32_t(w * kLoads * 64 * 16);
+  const int lane = int(threadIdx.x) & 63, wid = int(threadIdx.x) >> 6;
+  const int wm = wid >> 1, wn = wid & 1, frow = lane & 31, fgrp = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const uint32_t lo = uint32_t(slot_of(frow, 2 * kk + fgrp)) * 16u;
+    c.frag[0][kk] = c.lds + uint32_t(128 * wm * kChunks * 16) + lo;
+    c.frag[1][kk] = c.lds + uint32_t(kOpSlots * 16 + 128 * wn * kChunks * 16) + lo;
+  }
+  return c;
+}
+
+// Copy unit u of a stage pair: operand u / kLoads, this thread's slot
+// j = u % kLoads, of stages t and t+1 (buffers bt and bt1, global base g0 of
+// stage t), the 64-byte halves of the same rows back to back. The copy reads
+// its LDS destination from M0, which the statement sets and declares
+// clobbered (clang warns that M0 is reserved; declaring it is what keeps the
+// compiler from relying on an M0 value across the statement).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-RLK_DEV void copy_unit(const CopyPlan& cp, int u, const uint32_t (&oa)[kLoads],
-                       const uint32_t (&ob)[kLoads]) {
+RLK_DEV void copy_unit(const TileCtx& c, int u, int bt, int bt1, const uint16_t* g0,
+                       const uint32_t (&oa)[kLoads], const uint32_t (&ob)[kLoads]) {
   const int op = u / kLoads, j = u % kLoads;
-  const int w = int(threadIdx.x) >> 6;
-  const uint32_t m0a = uint32_t(reinterpret_cast<uintptr_t>(cp.lds_t[op] + (w * kLoads + j) * 64));
-  const uint32_t m0b = uint32_t(reinterpret_cast<uintptr_t>(cp.lds_t1[op] + (w * kLoads + j) * 64));
-  const uint16_t* g0 = cp.g_t[op];
+  const uint32_t m0a = c.lds + uint32_t(((bt * 2 + op) * kOpSlots + j * 64) * 16) + c.wave_off;
+  const uint32_t m0b = c.lds + uint32_t(((bt1 * 2 + op) * kOpSlots + j * 64) * 16) + c.wave_off;
   const uint16_t* g1 = g0 + kStageK;
   asm volatile(
       "s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %4"
       :
-      : "s"(__builtin_amdgcn_readfirstlane(m0a)), "s"(__builtin_amdgcn_readfirstlane(m0b)),
-        "v"(op == 0 ? oa[j] : ob[j]), "s"(g0), "s"(g1)
+      : "s"(m0a), "s"(m0b), "v"(op == 0 ? oa[j] : ob[j]), "s"(g0), "s"(g1)
       : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -115,33 +142,17 @@ struct Frags {
   bf16x8 a[2][4], b[2][4];   // [k-step][32-row group]
 };
 
-// Fragment rows 128 wm + 32 x + lane % 32: the swizzle hash depends on
-// row & 15 only, so a read's address is a per-lane part (one per k-step) plus
-// a uniform part.
-struct FragAddr {
-  uint32_t lane_off[2];   // bytes, per k-step
-  uint32_t a_off, b_off;  // bytes: the wave's A rows and B rows inside a stage
-};
-
-RLK_DEV FragAddr frag_addr() {
-  const int lane = int(threadIdx.x) & 63, wid = int(threadIdx.x) >> 6;
-  const int wm = wid >> 1, wn = wid & 1, frow = lane & 31, fgrp = lane >> 5;
-  FragAddr f;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) f.lane_off[kk] = uint32_t(slot_of(frow, 2 * kk + fgrp)) * 16u;
-  f.a_off = uint32_t(128 * wm * kChunks * 16);
-  f.b_off = uint32_t(kOpSlots * 16 + 128 * wn * kChunks * 16);
-  return f;
-}
-
-RLK_DEV void read_frag(Frags& f, int r, const char* stage, const FragAddr& fa) {
+// Fragment read r of a stage at byte offset stage_off: k-step r / 8, row
+// group r % 8 (A for 0..3, B for 4..7).
+RLK_DEV void read_frag(Frags& f, int r, uint32_t stage_off, const TileCtx& c) {
   const int kk = r >> 3, x = r & 7;
-  if (x < 4)
-    f.a[kk][x] = *reinterpret_cast<const bf16x8*>(stage + fa.a_off + fa.lane_off[kk] +
-                                                  x * 32 * kChunks * 16);
-  else
-    f.b[kk][x - 4] = *reinterpret_cast<const bf16x8*>(stage + fa.b_off + fa.lane_off[kk] +
-                                                      (x - 4) * 32 * kChunks * 16);
+  if (x < 4) {
+    lds_frag* p = reinterpret_cast<lds_frag*>(uintptr_t(c.frag[0][kk] + stage_off));
+    f.a[kk][x] = p[x * 32 * kChunks];
+  } else {
+    lds_frag* p = reinterpret_cast<lds_frag*>(uintptr_t(c.frag[1][kk] + stage_off));
+    f.b[kk][x - 4] = p[(x - 4) * 32 * kChunks];
+  }
 }
 
 // Issue schedule inside a stage's 32 MFMAs (m = MFMA index): the 16
@@ -152,12 +163,13 @@ RLK_DEV void read_frag(Frags& f, int r, const char* stage, const FragAddr& fa) {
 constexpr int read_slot(int r) { return r; }
 constexpr int copy_slot(int u) { return 16 + 4 * u; }
 
-// The 32 MFMAs of one stage, the next stage's fragment reads and (with
-// kCopyOp = 0 or 1) the copy units of operand A or B of two later stages.
+// The 32 MFMAs of one stage, the next stage's fragment reads (at byte offset
+// next_off) and the copy units of operand kCopyOp (0 = A, 1 = B) of the
+// stage pair in buffers bt, bt1 from global bases ga (A) / gb (B).
 template <int kCopyOp>
-RLK_DEV void stage_mma(f32x16 (&acc)[4][4], const Frags& cur, Frags& nxt, const char* next_stage,
-                       const FragAddr& fa, const CopyPlan& cp, const uint32_t (&oa)[kLoads],
-                       const uint32_t (&ob)[kLoads]) {
+RLK_DEV void stage_mma(f32x16 (&acc)[4][4], const Frags& cur, Frags& nxt, uint32_t next_off,
+                       const TileCtx& c, int bt, int bt1, const uint16_t* ga, const uint16_t* gb,
+                       const uint32_t (&oa)[kLoads], const uint32_t (&ob)[kLoads]) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -169,12 +181,11 @@ RLK_DEV void stage_mma(f32x16 (&acc)[4][4], const Frags& cur, Frags& nxt, const 
         const int m = kk * 16 + i * 4 + j;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (read_slot(r) == m) read_frag(nxt, r, next_stage, fa);
-        if (kCopyOp >= 0) {
+          if (read_slot(r) == m) read_frag(nxt, r, next_off, c);
 #pragma unroll
-          for (int u = 0; u < kLoads; ++u)
-            if (copy_slot(u) == m) copy_unit(cp, kCopyOp * kLoads + u, oa, ob);
-        }
+        for (int u = 0; u < kLoads; ++u)
+          if (copy_slot(u) == m)
+            copy_unit(c, kCopyOp * kLoads + u, bt, bt1, kCopyOp ? gb : ga, oa, ob);
         // keep the issue order as written: the scheduler would otherwise
         // sink the reads to their uses in the next stage
         __builtin_amdgcn_sched_barrier(0);
@@ -194,37 +205,26 @@ RLK_DEV void gemm_nt_tile(f32x16 (&acc)[4][4], Smem& smem, const uint16_t* A, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const char* sbase = reinterpret_cast<const char*>(&smem[0][0][0]);
-  const FragAddr fa = frag_addr();
+  const TileCtx c = tile_ctx(smem);
   const int nk = int(K / kStageK);   // even
   uint32_t oa[kLoads], ob[kLoads];
   copy_offsets(oa, a_row0, a_rows, lda);
   copy_offsets(ob, b_row0, b_rows, ldb);
   const uint16_t* a_base = A + a_row0 * lda;
   const uint16_t* b_base = B + b_row0 * ldb;
-  // copies of stages t, t+1 (t even); past the end, a repeat of the last two
-  auto plan = [&](int t) __attribute__((always_inline)) {
-    const int64_t k0 = int64_t(t < nk ? t : nk - 2) * kStageK;
-    CopyPlan cp;
-    cp.lds_t[0] = smem[t % kStages][0];
-    cp.lds_t[1] = smem[t % kStages][1];
-    cp.lds_t1[0] = smem[(t + 1) % kStages][0];
-    cp.lds_t1[1] = smem[(t + 1) % kStages][1];
-    cp.g_t[0] = a_base + k0;
-    cp.g_t[1] = b_base + k0;
-    return cp;
+  // global K offset of the pair t, t+1 (t even); past the end, the last pair
+  auto kof = [&](int t) __attribute__((always_inline)) {
+    return int64_t(t < nk ? t : nk - 2) * kStageK;
   };
-  {
-    const CopyPlan c0 = plan(0), c2 = plan(2);
 #pragma unroll
-    for (int u = 0; u < 2 * kLoads; ++u) copy_unit(c0, u, oa, ob);
+  for (int t = 0; t < 4; t += 2)
 #pragma unroll
-    for (int u = 0; u < 2 * kLoads; ++u) copy_unit(c2, u, oa, ob);
-  }
+    for (int u = 0; u < 2 * kLoads; ++u)
+      copy_unit(c, u, t, t + 1, (u < kLoads ? a_base : b_base) + kof(t), oa, ob);
   vm_wait_barrier<2 * kVmPerStage>();   // stages 0 and 1 landed
   Frags f0, f1;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) read_frag(f0, r, sbase, fa);
+  for (int r = 0; r < 16; ++r) read_frag(f0, r, 0u, c);
 
   // Step s: stage s (fragments in registers) is multiplied while stage s+1
   // is read. Stages s+4 and s+5 are copied into the buffers of stages s-1
@@ -232,12 +232,19 @@ RLK_DEV void gemm_nt_tile(f32x16 (&acc)[4][4], Smem& smem, const uint16_t* A, in
   // during step s+1 (s even). Copies complete in issue order, so at the top
   // of an even step the wait leaves the last 16 copies (pair s+2, s+3) in
   // flight and at the top of an odd step the last 8 (A of pair s+4, s+5).
+  // b1, b2, b4: buffers of stages s+1, s+2, s+4.
+  int b1 = 1, b2 = 2, b4 = 4;
   for (int s = 0; s < nk; s += 2) {
     vm_wait_barrier<2 * kVmPerStage>();   // stage s+1 landed
-    const CopyPlan cp = plan(s + 4);
-    stage_mma<0>(acc, f0, f1, sbase + ((s + 1) % kStages) * kStageBytes, fa, cp, oa, ob);
+    const int b5 = b4 == kStages - 1 ? 0 : b4 + 1;
+    const uint16_t* ga = a_base + kof(s + 4);
+    const uint16_t* gb = b_base + kof(s + 4);
+    stage_mma<0>(acc, f0, f1, uint32_t(b1 * kStageBytes), c, b4, b5, ga, gb, oa, ob);
     vm_wait_barrier<kVmPerStage>();       // stage s+2 landed
-    stage_mma<1>(acc, f1, f0, sbase + ((s + 2) % kStages) * kStageBytes, fa, cp, oa, ob);
+    stage_mma<1>(acc, f1, f0, uint32_t(b2 * kStageBytes), c, b4, b5, ga, gb, oa, ob);
+    b1 = b1 + 2 >= kStages ? b1 + 2 - kStages : b1 + 2;
+    b2 = b2 + 2 >= kStages ? b2 + 2 - kStages : b2 + 2;
+    b4 = b4 + 2 >= kStages ? b4 + 2 - kStages : b4 + 2;
   }
   vm_wait_barrier<0>();
 }
