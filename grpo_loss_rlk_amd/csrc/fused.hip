@@ -60,35 +60,45 @@ RLK_DEV Part merge_part(Part p, Part q, float c2) {
 
 // This lane's 64 logits of token column j folded into (max, sum 2^x, sum 2^x x).
 // kFull: every vocabulary row of the tile exists; else rows from `rem` on
-// (relative to this lane's first row) are past the vocabulary. A NaN or
-// infinite logit makes the partial's max NaN, which every merge propagates.
+// (relative to this lane's first row) are past the vocabulary and are left
+// out. `rem` passes through an empty asm per column and per pass, so that the
+// 64 comparisons are made afresh each time rather than shared and kept live:
+// their masks would not fit the scalar registers. A NaN or
+// infinite logit makes the partial's max NaN, which every merge propagates;
+// it is detected by a sum of z * 0, which stays 0 for finite z. That sum
+// includes rows past the vocabulary: the GEMM loaded them as copies of the
+// last vocabulary row, which lies in the same tile, so they are non-finite
+// only where a real logit of this token is, and the token's merged result is
+// NaN either way.
 template <bool kFull>
 RLK_DEV Part fold_lane(const f32x16 (&acc)[4][4], int j, int rem, float c2) {
-  float mx = -INFINITY;
-  bool bad = false;
+  float mx = -INFINITY, chk = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (kFull || 32 * i + 8 * (r >> 2) + (r & 3) < rem) {
-        mx = fmaxf(mx, acc[i][j][r]);
-        bad |= !(fabsf(acc[i][j][r]) <= 3.402823466e38f);
-      }
-  if (bad) return Part{__builtin_nanf(""), 0.f, 0.f};
+    for (int r = 0; r < 16; ++r) {
+      const float z = acc[i][j][r];
+      chk = fmaf(z, 0.f, chk);
+      if (kFull || 32 * i + 8 * (r >> 2) + (r & 3) < rem) mx = fmaxf(mx, z);
+    }
+  if (!(chk == 0.f)) return Part{__builtin_nanf(""), 0.f, 0.f};
   float A = 0.f, B = 0.f;
   if (mx > -INFINITY) {
+    if (!kFull) asm volatile("" : "+v"(rem));   // fresh comparisons, as above
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (kFull || 32 * i + 8 * (r >> 2) + (r & 3) < rem) {
-          // x <= 0; below 2^-126 a term is far under the sum's resolution,
-          // whatever the denormal handling of the hardware exp2
-          const float x = (acc[i][j][r] - mx) * c2;
-          const float e = __builtin_amdgcn_exp2f(x);
-          A += e;
-          B = fmaf(e, x, B);
-        }
+      for (int r = 0; r < 16; ++r) {
+        // x <= 0; below 2^-126 a term is far under the sum's resolution,
+        // whatever the denormal handling of the hardware exp2. The clamp
+        // changes no term (exp2 of anything below -150 is 0 in fp32) and
+        // gives rows past the vocabulary a zero term.
+        float x = fmaxf((acc[i][j][r] - mx) * c2, -1024.f);
+        if (!kFull && !(32 * i + 8 * (r >> 2) + (r & 3) < rem)) x = -1024.f;
+        const float e = __builtin_amdgcn_exp2f(x);
+        A += e;
+        B = fmaf(e, x, B);
+      }
   }
   return Part{mx, A, B};
 }
@@ -110,7 +120,9 @@ RLK_DEV void tile_epilogue(const FusedFwdArgs& a, f32x16 (&acc)[4][4], int64_t v
   Part mine[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const Part p = full ? fold_lane<true>(acc, j, rem, c2) : fold_lane<false>(acc, j, rem, c2);
+    int remj = rem;
+    asm volatile("" : "+v"(remj));
+    const Part p = full ? fold_lane<true>(acc, j, remj, c2) : fold_lane<false>(acc, j, remj, c2);
     Part q;
     q.m = __shfl_xor(p.m, 32, 64);
     q.A = __shfl_xor(p.A, 32, 64);
@@ -124,15 +136,22 @@ RLK_DEV void tile_epilogue(const FusedFwdArgs& a, f32x16 (&acc)[4][4], int64_t v
     const int64_t rel = y - vbase;
     const bool hit = rel >= 0 && rel < 128 && ((rel >> 2) & 1) == fgrp;
     if (__any(hit)) {
-      const int ii = int(rel >> 5), ww = int(rel & 31);
-      const int rr = ((ww >> 3) << 2) | (ww & 3);
-      float val = 0.f;
+      // element (i, r) = (rel / 32, 4 (rel % 32 / 8) + rel % 4), picked by a
+      // select tree over the 6 bits of 16 i + r (6 masks, not 64)
+      const int ww = int(rel & 31);
+      const int idx = (int(rel >> 5) << 4) | ((ww >> 3) << 2) | (ww & 3);
+      float t[64];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (i == ii && r == rr) val = acc[i][j][r];
-      if (hit) a.zy[n] = val;
+        for (int r = 0; r < 16; ++r) t[16 * i + r] = acc[i][j][r];
+#pragma unroll
+      for (int b = 0; b < 6; ++b) {
+        const bool bit = (idx >> b) & 1;
+#pragma unroll
+        for (int k = 0; k < (32 >> b); ++k) t[k] = bit ? t[2 * k + 1] : t[2 * k];
+      }
+      if (hit) a.zy[n] = t[0];
     }
   }
 

@@ -127,6 +127,11 @@ RLK_DEV void g_epilogue(const FusedBwdArgs& a, const ChunkArgs& c, const f32x16 
   for (int j = 0; j < 4; ++j) {
     const int nl = gemm::acc_b_row(j);
     const int64_t n = n0 + nl;
+    // a fresh copy per column: the 64 row comparisons below are then made per
+    // column rather than shared and kept live (their masks would not fit the
+    // scalar registers)
+    int vremj = vrem;
+    if (!kFullV) asm volatile("" : "+v"(vremj));
     float lse2 = 1e30f, eq = 0.f, glp = 0.f, gh = 0.f, tau = -INFINITY;
     int ty = -1;   // target row relative to this lane's first row (-1: none here)
     if (n < a.N) {
@@ -156,7 +161,7 @@ RLK_DEV void g_epilogue(const FusedBwdArgs& a, const ChunkArgs& c, const f32x16 
           float g = fmaf(-q, fmaf(gh, fmaf(z, inv_t, -eq), glp), 0.f);   // +0 when q = 0
           if (k0 + e == ty) g += glp;
           g *= inv_t;
-          if (!kFullV && k0 + e >= vrem) g = 0.f;
+          if (!kFullV && k0 + e >= vremj) g = 0.f;
           g4[e] = g;
         }
         const bf16x2 lo = {(__bf16)g4[0], (__bf16)g4[1]};
