@@ -190,77 +190,70 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats(FusedFwdArgs a) {
   tile_epilogue(a, acc, v0, n0, vt, reinterpret_cast<float*>(&smem[0][0][0]));
 }
 
-// Logits of a row block: A = h (tokens), B = W (vocabulary). Each wave
-// passes its 128 x 128 block through LDS one 32-id slab at a time (16 KB per
-// wave) and writes each token's 32 logits (128 contiguous bytes of a scratch
-// row) as eight 16-byte stores, 4x fewer store instructions than writing the
-// accumulators lane by lane. From the same staged values, per token: the max
-// logit over the tile (as an order key, merged with atomicMax, which is
-// order-free) and whether a non-finite logit appeared, so that the row kernel
-// can skip its max pass; the max is folded in registers over the 16 values a
-// lane stores per token and then over the 8 lanes of that token, one atomic
-// per token and wave.
+// Logits of a row block: A = W (vocabulary), B = h (tokens), the
+// orientation (and XCD-aware tile order) of fwd_tile_stats, so that each XCD
+// streams its own range of W once. A lane's accumulators acc[i][j][4 s + e],
+// e = 0..3, are 4 consecutive ids of one token, so each goes to the scratch
+// row as one 16-byte store straight from registers (lanes l and l + 32 write
+// the two halves of 32 contiguous bytes; the 4 values of s complete a
+// token's 128-byte line). Per token: the max logit over the tile (as an order
+// key, merged with atomicMax, which is order-free) and whether a non-finite
+// logit appeared (a sum of z * 0 is NaN), so that the row kernel can skip its
+// max pass; one atomic per token and wave.
+template <bool kFullV>
+RLK_DEV void logits_epilogue(f32x16 (&acc)[4][4], int64_t v0, int64_t n0, int64_t V,
+                             int64_t rows, float* z, int64_t zs, uint32_t* zmax_key,
+                             uint32_t* zbad) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int lane = int(threadIdx.x) & 63;
+  const int64_t vb = v0 + gemm::acc_a_row(0, 0);   // this lane's first id
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + gemm::acc_b_row(j);
+    // a fresh copy per column: the 64 id comparisons are then made per column
+    // rather than shared and kept live (their masks would not fit the scalar
+    // registers)
+    int64_t vrem = V - vb;
+    if (!kFullV) asm volatile("" : "+v"(vrem));
+    float mx = -INFINITY, chk = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int k0 = 32 * i + 8 * s4;   // ids vb + k0 .. + 3
+        const f32x4 v = {acc[i][j][4 * s4], acc[i][j][4 * s4 + 1], acc[i][j][4 * s4 + 2],
+                         acc[i][j][4 * s4 + 3]};
+        // zs is a multiple of 4, so a chunk that starts inside the row ends inside it
+        if (n < rows && vb + k0 < zs) *reinterpret_cast<f32x4*>(z + n * zs + vb + k0) = v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          chk = fmaf(v[e], 0.f, chk);   // rows past V are copies of row V - 1
+          if (kFullV || k0 + e < vrem) mx = fmaxf(mx, v[e]);
+        }
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    chk = chk + __shfl_xor(chk, 32, 64);
+    if (lane < 32 && n < rows) {
+      if (mx > -INFINITY) atomicMax(&zmax_key[n], f32_key(mx));
+      if (!(chk == 0.f)) atomicOr(&zbad[n], 1u);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kT) void fwd_logits_tile(FusedFwdArgs a, int64_t r0, int64_t rows,
                                                       float* z, int64_t zs, uint32_t* zmax_key,
                                                       uint32_t* zbad) {
   __shared__ gemm::Smem smem;
-  const int nnt = int((rows + kBN - 1) / kBN), nvt = int((a.V + kBM - 1) / kBM);
-  int nt, vt;
-  gemm::tile_of_block(nnt, nvt, nt, vt);
-  const int64_t n0 = int64_t(nt) * kBN, v0 = int64_t(vt) * kBM;
+  const int nvt = int((a.V + kBM - 1) / kBM), nnt = int((rows + kBN - 1) / kBN);
+  int vt, nt;
+  gemm::tile_of_block(nvt, nnt, vt, nt);
+  const int64_t v0 = int64_t(vt) * kBM, n0 = int64_t(nt) * kBN;
   f32x16 acc[4][4];
-  gemm::gemm_nt_tile(acc, smem, a.h + r0 * a.hs, n0, rows, a.hs, a.w, v0, a.V, a.ws, a.H);
-
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  // the GEMM's LDS is free: this wave's [128 tokens][32 ids] fp32 slab
-  float* stg = reinterpret_cast<float*>(&smem[0][0][0]) + wid * (128 * 32);
-  float tmax[16];      // token 8 q + lane / 8 of this wave's 128
-  uint32_t badq = 0;   // bit q: a non-finite logit of that token
-#pragma unroll
-  for (int q = 0; q < 16; ++q) tmax[q] = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // acc[i][j][r] is token 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, id 32 j + lane % 32
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        stg[(32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * 32 + (lane & 31)] =
-            acc[i][j][r];
-    __syncthreads();
-    // lane: ids col .. col + 3 of tokens 8 q + lane / 8
-    const int64_t col = v0 + 128 * wn + 32 * j + 4 * (lane & 7);
-    const int64_t nv = a.V - col;   // ids of the chunk inside the vocabulary, if < 4
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int tl = 8 * q + (lane >> 3);
-      const int64_t n = n0 + 128 * wm + tl;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stg + tl * 32 + 4 * (lane & 7));
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (e < nv) {
-          tmax[q] = fmaxf(tmax[q], v[e]);
-          badq |= (fabsf(v[e]) <= 3.402823466e38f) ? 0u : (1u << q);
-        }
-      // zs is a multiple of 4, so a chunk that starts inside the row ends inside it
-      if (n < rows && col < zs) *reinterpret_cast<f32x4*>(z + n * zs + col) = v;
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int k = 1; k < 8; k <<= 1) badq |= __shfl_xor(badq, k, 64);
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-#pragma unroll
-    for (int k = 1; k < 8; k <<= 1) tmax[q] = fmaxf(tmax[q], __shfl_xor(tmax[q], k, 64));
-    const int64_t n = n0 + 128 * wm + 8 * q + (lane >> 3);
-    if ((lane & 7) == 0 && n < rows) {
-      if (tmax[q] > -INFINITY) atomicMax(&zmax_key[n], f32_key(tmax[q]));
-      if ((badq >> q) & 1u) atomicOr(&zbad[n], 1u);
-    }
-  }
+  gemm::gemm_nt_tile(acc, smem, a.w, v0, a.V, a.ws, a.h + r0 * a.hs, n0, rows, a.hs, a.H);
+  if (v0 + kBM <= a.V)
+    logits_epilogue<true>(acc, v0, n0, a.V, rows, z, zs, zmax_key, zbad);
+  else
+    logits_epilogue<false>(acc, v0, n0, a.V, rows, z, zs, zmax_key, zbad);
 }
 
 __global__ void clear_u32(uint32_t* p, int64_t n) {
