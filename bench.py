@@ -400,7 +400,7 @@ def leg_tiny(torch, rlk, synth, steps, warmup):
         "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": _profile_traffic("f32_rows_tiny_256x8192")},
         "bytes_per_row": bytes_per_row,
         "determinism": det,
     }
@@ -521,7 +521,8 @@ def leg_sample(torch, rlk, synth, steps, warmup):
         "kernel_ms_mean": mean_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min_ms,
         "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _profile_traffic("sampler_qwen3_logits_4096x151936")},
         "bytes_per_row": bytes_per_row,
         "determinism": det,
         "cpu_oracle": cpu,
@@ -627,7 +628,7 @@ def leg_fused_bwd(torch, rlk, synth, steps, warmup):
         "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": _profile_traffic("fused_fwd_bwd_llama70b_16384x8192x128256")},
         "flops_per_token_executed": 8.0 * w.V * w.H,
         "frac_useful_6vh": round(0.75 * achieved / BF16_PEAK_TFLOPS, 4),
         "determinism": det,
@@ -722,7 +723,7 @@ def leg_grpo(torch, rlk, synth, steps, warmup):
         "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": _profile_traffic("fused_topp_grpo_loss_109833_tokens")},
         "flops_per_token": 2.0 * w.V * w.H,
         "determinism": det,
         "cpu_oracle": cpu,
@@ -774,7 +775,7 @@ def leg_grpo_train(torch, rlk, synth, steps, warmup):
         "gpu_clock": _LAST_CLOCK[0],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": _profile_traffic("grpo_train_step_109833_tokens")},
         "flops_per_token_executed": 8.0 * w.V * w.H,
         "determinism": det,
         "cpu_oracle": cpu,
