@@ -54,17 +54,17 @@ def _profile_traffic(name):
         return None
 
 
-def _spin_up(torch, seconds=0.3):
-    """Keep the GPU busy for a moment with unrelated bf16 matmuls so that the
-    timed steps see the clocks of sustained load (as inside a training step),
-    not the ramp out of idle while inputs were generated on the host."""
-    a = torch.randn(4096, 4096, device="cuda:0", dtype=torch.bfloat16)
-    b = torch.randn(4096, 4096, device="cuda:0", dtype=torch.bfloat16)
+def _spin_up(torch, fn, seconds=0.3):
+    """Run the leg's own call for a moment (at least once) so that the timed
+    steps see the clocks the power manager settles on for this workload, not
+    the ramp out of idle while inputs were generated on the host nor the
+    state another workload left behind."""
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        for _ in range(20):
-            torch.matmul(a, b)
+    while True:
+        fn()
         torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
 
 
 def _sclk_files():
@@ -88,40 +88,64 @@ def _read_sclk(files):
     return None
 
 
+def _clock_child(conn):
+    """Sampler process: on "start", read the shader clock every ~2 ms until
+    "stop", then send the samples back; "exit" ends it."""
+    files = _sclk_files()
+    while True:
+        if conn.recv() == "exit":
+            return
+        samples = []
+        while not conn.poll(0.002):
+            v = _read_sclk(files)
+            if v is not None:
+                samples.append(v)
+        conn.recv()
+        conn.send(samples)
+
+
+_CLOCK_PROC = {}
+
+
+def start_clock_process():
+    """Fork the clock sampler before the GPU is first used: it only reads the
+    driver's sysfs table, and as a separate process it takes no time from the
+    thread that launches the timed calls (a sampling thread shares that
+    thread's interpreter lock)."""
+    import multiprocessing as mp
+    if _CLOCK_PROC or not _sclk_files():
+        return
+    ctx = mp.get_context("fork")
+    conn, child = ctx.Pipe()
+    proc = ctx.Process(target=_clock_child, args=(child,), daemon=True)
+    proc.start()
+    _CLOCK_PROC.update(conn=conn, proc=proc)
+
+
 class _ClockSampler:
-    """Samples the shader clock every few ms on a host thread while the timed
-    region runs (reading the driver's sysfs table only: no GPU work)."""
+    """Shader-clock samples taken by the sampler process while the timed
+    region runs (none when there is no such process)."""
 
     def __init__(self):
-        import threading
-        self.files = _sclk_files()
         self.samples = []
-        self.stop = threading.Event()
-        self.thread = threading.Thread(target=self._run, daemon=True)
-
-    def _run(self):
-        while not self.stop.is_set():
-            v = _read_sclk(self.files)
-            if v is not None:
-                self.samples.append(v)
-            self.stop.wait(0.002)
 
     def __enter__(self):
-        if self.files:
-            self.thread.start()
+        if _CLOCK_PROC:
+            _CLOCK_PROC["conn"].send("start")
         return self
 
     def __exit__(self, *exc):
-        self.stop.set()
-        if self.files:
-            self.thread.join()
+        if _CLOCK_PROC:
+            _CLOCK_PROC["conn"].send("stop")
+            self.samples = _CLOCK_PROC["conn"].recv()
 
     def summary(self):
         if not self.samples:
             return None
         return {"median_mhz": int(np.median(self.samples)), "min_mhz": int(min(self.samples)),
                 "max_mhz": int(max(self.samples)), "samples": len(self.samples),
-                "source": "pp_dpm_sclk current level, sampled every ~2 ms"}
+                "source": "pp_dpm_sclk current DPM level (the power manager's level, not a "
+                          "kernel clock), sampled every ~2 ms by a separate process"}
 
 
 _LAST_CLOCK = [None]
@@ -131,7 +155,7 @@ def _events_time(torch, fn, steps, warmup):
     """Mean, total, min and median ms of `fn` over `steps` calls, HIP events
     on the current stream; the shader clock sampled meanwhile is left in
     _LAST_CLOCK."""
-    _spin_up(torch)
+    _spin_up(torch, fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -823,6 +847,7 @@ def main():
     legs = [s for s in args.legs.split(",") if s]
     if args.cpu_sample > 0 and "logits" in legs:
         cpu_baselines(synth)   # before the GPU is first used
+    start_clock_process()      # likewise
 
     import torch
     import grpo_loss_rlk_amd as rlk

@@ -2,6 +2,7 @@
 must pass deterministic per-row functions and catch run-to-run noise and
 batch dependence) and the traffic figure read from a counter summary (null
 once the kernel's sources no longer hash to the recorded value)."""
+import time
 import pytest
 import torch
 
@@ -85,3 +86,20 @@ def test_parallel_oracle_covers_every_row():
     assert dt >= 0.0
     assert bench._cores() >= 1
     del bench._POOL["toy"], seen
+
+
+def test_clock_sampler_process(tmp_path, monkeypatch):
+    """The sampler runs in a forked process and reports the DPM level it read."""
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1500Mhz\n2: 2100Mhz *\n")
+    monkeypatch.setattr(bench, "_sclk_files", lambda: [str(f)])
+    monkeypatch.setattr(bench, "_CLOCK_PROC", {})
+    bench.start_clock_process()
+    try:
+        with bench._ClockSampler() as c:
+            time.sleep(0.05)
+        s = c.summary()
+        assert s is not None and s["median_mhz"] == 2100 and s["samples"] >= 1
+    finally:
+        bench._CLOCK_PROC["conn"].send("exit")
+        bench._CLOCK_PROC["proc"].join(5)
