@@ -117,6 +117,14 @@ RLK_DEV void tile_epilogue(const FusedFwdArgs& a, f32x16 (&acc)[4][4], int64_t v
   const bool full = v0 + kBM <= a.V;
   const int64_t rem64 = a.V - vbase - 4 * fgrp;
   const int rem = int(rem64 < 256 ? rem64 : 256);
+  // the four token columns' targets, loaded together so that one memory
+  // latency is exposed instead of a chain of four
+  int64_t yv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + 128 * wn + 32 * j + frow;
+    yv[j] = n < a.N ? a.targets[n] : -1;
+  }
   Part mine[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -132,7 +140,7 @@ RLK_DEV void tile_epilogue(const FusedFwdArgs& a, f32x16 (&acc)[4][4], int64_t v
 
     // target logit: the lane holding vocab row y of this token writes it
     const int64_t n = n0 + 128 * wn + 32 * j + frow;
-    const int64_t y = n < a.N ? a.targets[n] : -1;
+    const int64_t y = yv[j];
     const int64_t rel = y - vbase;
     const bool hit = rel >= 0 && rel < 128 && ((rel >> 2) & 1) == fgrp;
     if (__any(hit)) {
