@@ -91,56 +91,34 @@ def _read_sclk(files):
     return None
 
 
-def _clock_child(conn):
-    """Sampler process: on "start", read the shader clock every ~2 ms until
-    "stop", then send the samples back; "exit" ends it."""
-    files = _sclk_files()
-    while True:
-        if conn.recv() == "exit":
-            return
-        samples = []
-        while not conn.poll(0.002):
-            v = _read_sclk(files)
-            if v is not None:
-                samples.append(v)
-        conn.recv()
-        conn.send(samples)
-
-
-_CLOCK_PROC = {}
-
-
-def start_clock_process():
-    """Fork the clock sampler before the GPU is first used: it only reads the
-    driver's sysfs table, and as a separate process it takes no time from the
-    thread that launches the timed calls (a sampling thread shares that
-    thread's interpreter lock)."""
-    import multiprocessing as mp
-    if _CLOCK_PROC or not _sclk_files():
-        return
-    ctx = mp.get_context("fork")
-    conn, child = ctx.Pipe()
-    proc = ctx.Process(target=_clock_child, args=(child,), daemon=True)
-    proc.start()
-    _CLOCK_PROC.update(conn=conn, proc=proc)
-
-
 class _ClockSampler:
-    """Shader-clock samples taken by the sampler process while the timed
-    region runs (none when there is no such process)."""
+    """Samples the shader clock's DPM level every ~2 ms on a host thread while
+    the timed calls run (it reads the driver's sysfs table only: no GPU work;
+    the thread sleeps, and reads, without holding the interpreter lock)."""
 
     def __init__(self):
+        import threading
+        self.files = _sclk_files()
         self.samples = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self.stop.is_set():
+            v = _read_sclk(self.files)
+            if v is not None:
+                self.samples.append(v)
+            self.stop.wait(0.002)
 
     def __enter__(self):
-        if _CLOCK_PROC:
-            _CLOCK_PROC["conn"].send("start")
+        if self.files:
+            self.thread.start()
         return self
 
     def __exit__(self, *exc):
-        if _CLOCK_PROC:
-            _CLOCK_PROC["conn"].send("stop")
-            self.samples = _CLOCK_PROC["conn"].recv()
+        self.stop.set()
+        if self.files:
+            self.thread.join()
 
     def summary(self):
         if not self.samples:
@@ -148,7 +126,14 @@ class _ClockSampler:
         return {"median_mhz": int(np.median(self.samples)), "min_mhz": int(min(self.samples)),
                 "max_mhz": int(max(self.samples)), "samples": len(self.samples),
                 "source": "pp_dpm_sclk current DPM level (the power manager's level, not a "
-                          "kernel clock), sampled every ~2 ms by a separate process"}
+                          "kernel clock), sampled every ~2 ms"}
+
+
+def _profiler_attached():
+    """True under rocprofv3, whose preloaded library initialises the GPU before
+    this program starts: no worker process may then be forked."""
+    pre = os.environ.get("LD_PRELOAD", "")
+    return "rocprof" in pre or any(k.startswith("ROCPROF") for k in os.environ)
 
 
 _LAST_CLOCK = [None]
@@ -854,8 +839,12 @@ def main():
     import synth
     legs = [s for s in args.legs.split(",") if s]
     if args.cpu_sample > 0 and "logits" in legs:
-        cpu_baselines(synth)   # before the GPU is first used
-    start_clock_process()      # likewise
+        if _profiler_attached():
+            print("[bench] CPU baselines skipped: a profiler is attached (it initialises "
+                  "the GPU before this program starts, so no worker may be forked)",
+                  file=sys.stderr, flush=True)
+        else:
+            cpu_baselines(synth)   # before the GPU is first used
 
     import torch
     import grpo_loss_rlk_amd as rlk

@@ -88,18 +88,12 @@ def test_parallel_oracle_covers_every_row():
     del bench._POOL["toy"], seen
 
 
-def test_clock_sampler_process(tmp_path, monkeypatch):
-    """The sampler runs in a forked process and reports the DPM level it read."""
+def test_clock_sampler(tmp_path, monkeypatch):
+    """The sampler thread reports the DPM level it read."""
     f = tmp_path / "pp_dpm_sclk"
     f.write_text("0: 500Mhz\n1: 1500Mhz\n2: 2100Mhz *\n")
     monkeypatch.setattr(bench, "_sclk_files", lambda: [str(f)])
-    monkeypatch.setattr(bench, "_CLOCK_PROC", {})
-    bench.start_clock_process()
-    try:
-        with bench._ClockSampler() as c:
-            time.sleep(0.05)
-        s = c.summary()
-        assert s is not None and s["median_mhz"] == 2100 and s["samples"] >= 1
-    finally:
-        bench._CLOCK_PROC["conn"].send("exit")
-        bench._CLOCK_PROC["proc"].join(5)
+    with bench._ClockSampler() as c:
+        time.sleep(0.05)
+    s = c.summary()
+    assert s is not None and s["median_mhz"] == 2100 and s["samples"] >= 1
