@@ -893,6 +893,9 @@ def main():
         "config": {"workload": main_leg["workload"]},
         "roofline": main_leg["roofline"],
         "cpu_baseline": main_leg.get("cpu_baseline"),
+        # the metric's MFMA half: the fused LM-head forward at H = 4096, V = 151936
+        "roofline_mfma": (out_legs.get("fused") or {}).get("roofline"),
+        "tokens_per_s_fused": (out_legs.get("fused") or {}).get("tokens_per_s"),
         "legs": {k: {kk: vv for kk, vv in v.items() if kk != "cpu_baseline"}
                  for k, v in out_legs.items()},
     }
