@@ -81,15 +81,23 @@ __global__ __launch_bounds__(256) void fill_f32(float* p, int64_t n) {
     p[i] = 0.f;
 }
 
+// Row strides of the workspace matrices are 64 elements (128 bytes) past a
+// multiple of 64, so never a multiple of a large power of two: a GEMM stage
+// reads 256 rows at one k offset, and at a stride of 64 KB (a 32768-row chunk)
+// those rows' lines crowd onto a few memory channels (the dh product ran 4-6 %
+// slower at that stride than at 64 KB + 128 bytes).
+constexpr int64_t kLdPad = 64;
+
 struct ChunkArgs {
   int64_t c0, csz, cpad;   // chunk start, rows, rows padded to a multiple of 64
-  int64_t cap;             // row length of g_nc (chunk capacity, multiple of 64)
-  int64_t npad;            // tokens padded to a multiple of 64
+  int64_t cap;             // row stride of g_nc (chunk capacity + kLdPad)
+  int64_t npad;            // tokens padded to a multiple of 64 (the dW product's K)
+  int64_t nld;             // row stride of g_cn and h^T (npad + kLdPad)
   uint16_t* g_nc;          // bf16 [N, cap]    G_c, token rows
-  uint16_t* g_cn;          // bf16 [cap, npad] G_c^T, vocabulary rows
-  const uint16_t* wt;      // bf16 [H, vpad]   W^T
-  int64_t vpad;
-  const uint16_t* ht;      // bf16 [H, npad]   h^T
+  uint16_t* g_cn;          // bf16 [cap, nld]  G_c^T, vocabulary rows
+  const uint16_t* wt;      // bf16 [H, vld]    W^T
+  int64_t vld;             // row stride of W^T (V padded to 64, + kLdPad)
+  const uint16_t* ht;      // bf16 [H, nld]    h^T
   float* dh_acc;           // fp32 [N, H] partial sums over chunks (several chunks only)
 };
 
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(kT) void bwd_g_tile(FusedBwdArgs a, ChunkArgs c) {
     const int vl = q / kRowChunks, ch = q % kRowChunks;
     const int64_t v = v0 + vl, n = n0 + ch * 8;
     if (v < c.cpad && n < c.npad)
-      *reinterpret_cast<uint4*>(c.g_cn + v * c.npad + n) =
+      *reinterpret_cast<uint4*>(c.g_cn + v * c.nld + n) =
           *reinterpret_cast<const uint4*>(tg + vl * kTile + ch * 8);
   }
 }
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(kT) void bwd_dh_tile(FusedBwdArgs a, ChunkArgs c) {
   gemm::tile_of_block(nnt, nht, nt, ht);
   const int64_t n0 = int64_t(nt) * kTile, k0 = int64_t(ht) * kTile;
   f32x16 acc[4][4];
-  gemm::gemm_nt_tile(acc, smem, c.g_nc, n0, a.N, c.cap, c.wt + c.c0, k0, a.H, c.vpad, c.cpad);
+  gemm::gemm_nt_tile(acc, smem, c.g_nc, n0, a.N, c.cap, c.wt + c.c0, k0, a.H, c.vld, c.cpad);
 
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -294,7 +302,7 @@ __global__ __launch_bounds__(kT) void bwd_dw_tile(FusedBwdArgs a, ChunkArgs c) {
   gemm::tile_of_block(nvt, nht, vt, ht);
   const int64_t v0 = int64_t(vt) * kTile, k0 = int64_t(ht) * kTile;
   f32x16 acc[4][4];
-  gemm::gemm_nt_tile(acc, smem, c.g_cn, v0, c.csz, c.npad, c.ht, k0, a.H, c.npad, c.npad);
+  gemm::gemm_nt_tile(acc, smem, c.g_cn, v0, c.csz, c.nld, c.ht, k0, a.H, c.nld, c.npad);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t col = k0 + gemm::acc_b_row(j);
@@ -310,15 +318,17 @@ __global__ __launch_bounds__(kT) void bwd_dw_tile(FusedBwdArgs a, ChunkArgs c) {
 }
 
 struct BwdLayout {
-  int64_t npad, vpad, cap, nchunks;
+  int64_t npad, nld, vld, cap, nchunks;
   size_t off_wt, off_ht, off_gnc, off_gcn, off_acc, total;
 };
 
 BwdLayout bwd_layout(int64_t N, int64_t H, int64_t V) {
   BwdLayout L{};
   L.npad = round_up(N > 0 ? N : 1, 64);
-  L.vpad = round_up(V, 64);
-  L.cap = L.vpad < kBwdChunk ? L.vpad : kBwdChunk;
+  L.nld = L.npad + kLdPad;
+  const int64_t vpad = round_up(V, 64);
+  L.vld = vpad + kLdPad;
+  L.cap = (vpad < kBwdChunk ? vpad : kBwdChunk) + kLdPad;
   L.nchunks = (V + kBwdChunk - 1) / kBwdChunk;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -326,10 +336,10 @@ BwdLayout bwd_layout(int64_t N, int64_t H, int64_t V) {
     o += (bytes + 255) / 256 * 256;
     return at;
   };
-  L.off_wt = take(size_t(H) * size_t(L.vpad) * 2);
-  L.off_ht = take(size_t(H) * size_t(L.npad) * 2);
+  L.off_wt = take(size_t(H) * size_t(L.vld) * 2);
+  L.off_ht = take(size_t(H) * size_t(L.nld) * 2);
   L.off_gnc = take(size_t(N) * size_t(L.cap) * 2);
-  L.off_gcn = take(size_t(L.cap) * size_t(L.npad) * 2);
+  L.off_gcn = take(size_t(L.cap) * size_t(L.nld) * 2);
   L.off_acc = take(L.nchunks > 1 ? size_t(N) * size_t(H) * 4 : 0);
   L.total = o;
   return L;
@@ -351,7 +361,8 @@ hipError_t launch_fused_bwd(const FusedBwdArgs& a, void* workspace, hipStream_t 
   ChunkArgs c{};
   c.cap = L.cap;
   c.npad = L.npad;
-  c.vpad = L.vpad;
+  c.nld = L.nld;
+  c.vld = L.vld;
   c.g_nc = reinterpret_cast<uint16_t*>(ws + L.off_gnc);
   c.g_cn = reinterpret_cast<uint16_t*>(ws + L.off_gcn);
   uint16_t* wt = reinterpret_cast<uint16_t*>(ws + L.off_wt);
@@ -360,10 +371,10 @@ hipError_t launch_fused_bwd(const FusedBwdArgs& a, void* workspace, hipStream_t 
   c.ht = ht;
   c.dh_acc = reinterpret_cast<float*>(ws + L.off_acc);
 
-  hipLaunchKernelGGL(transpose_pad, dim3(unsigned(L.vpad / 64), unsigned(a.H / 64)), dim3(256), 0,
-                     stream, a.w, a.V, a.ws, wt, L.vpad);
-  hipLaunchKernelGGL(transpose_pad, dim3(unsigned(L.npad / 64), unsigned(a.H / 64)), dim3(256), 0,
-                     stream, a.h, a.N, a.hs, ht, L.npad);
+  hipLaunchKernelGGL(transpose_pad, dim3(unsigned(L.vld / 64), unsigned(a.H / 64)), dim3(256), 0,
+                     stream, a.w, a.V, a.ws, wt, L.vld);
+  hipLaunchKernelGGL(transpose_pad, dim3(unsigned(L.nld / 64), unsigned(a.H / 64)), dim3(256), 0,
+                     stream, a.h, a.N, a.hs, ht, L.nld);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
