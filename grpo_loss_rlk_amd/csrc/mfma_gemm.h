@@ -250,21 +250,39 @@ RLK_DEV void gemm_nt_tile(f32x16 (&acc)[4][4], Smem& smem, const uint16_t* A, in
 }
 
 constexpr int kXcds = 8;      // workgroups are dealt to the XCDs round-robin
-constexpr int kGroupA = 8;    // A tiles per group of the tile order
+constexpr int kSupA = 32;     // A tiles per super-tile
+constexpr int kSupB = 8;      // B tiles per super-tile
+constexpr int kSubA = 8;      // A tiles of one XCD's part of a super-tile
+constexpr int kSubB = 4;      // B tiles of one XCD's part
+static_assert((kSupA / kSubA) * (kSupB / kSubB) == kXcds && kSubA * kSubB * kXcds == kSupA * kSupB,
+              "a super-tile is one 8 x 4 part per XCD");
 
-// Tile (ta, tb) of this workgroup in an na x nb grid. Each XCD takes a
-// contiguous range of the tile order, so its L2 serves one region of A and
-// B; within the order, groups of kGroupA A-tiles sweep all B-tiles with the
-// A-tile fastest, so the 32 workgroups an XCD runs at once cover about 8
-// A-tiles and 4 B-tiles.
+// Tile (ta, tb) of this workgroup in an na x nb grid. The order runs over
+// super-tiles of 32 A-tiles x 8 B-tiles (256 tiles: one per CU), B fastest
+// within a band of 32 A-tiles. Inside a full super-tile, the 32 workgroups
+// that one XCD receives (every 8th) cover an 8 x 4 part of it. So the tiles
+// that run at one time read 32 A and 8 B panels between them, which the
+// memory-side cache holds, and each XCD's L2 serves 8 + 4 of them. A ragged
+// super-tile (the last band or the end of a band) is taken A-fastest.
+// The map is a bijection on [0, na nb) (checked on the host for many grids).
 RLK_DEV void tile_of_block(int na, int nb, int& ta, int& tb) {
-  const int T = na * nb, b = int(blockIdx.x);
-  const int x = b % kXcds, q = T / kXcds, r = T % kXcds;
-  const int lid = x * q + (x < r ? x : r) + b / kXcds;
-  const int grp = lid / (kGroupA * nb), rem = lid % (kGroupA * nb);
-  const int ga = kGroupA < na - grp * kGroupA ? kGroupA : na - grp * kGroupA;
-  ta = grp * kGroupA + rem % ga;
-  tb = rem / ga;
+  const int b = int(blockIdx.x);
+  const int band = b / (kSupA * nb), i = b % (kSupA * nb);
+  const int ga = kSupA < na - band * kSupA ? kSupA : na - band * kSupA;
+  const int blk = i / (ga * kSupB), j = i % (ga * kSupB);
+  const int gb = kSupB < nb - blk * kSupB ? kSupB : nb - blk * kSupB;
+  int a, c;
+  if (ga == kSupA && gb == kSupB) {
+    constexpr int kPartsA = kSupA / kSubA;
+    const int x = j % kXcds, s = j / kXcds;
+    a = (x % kPartsA) * kSubA + s % kSubA;
+    c = (x / kPartsA) * kSubB + s / kSubA;
+  } else {
+    a = j % ga;
+    c = j / ga;
+  }
+  ta = band * kSupA + a;
+  tb = blk * kSupB + c;
 }
 
 // Row of acc[i][j][r] inside the A and B halves of the tile (see the top).
