@@ -199,8 +199,8 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats(FusedFwdArgs a) {
 }
 
 // Logits of a row block: A = W (vocabulary), B = h (tokens), the
-// orientation (and XCD-aware tile order) of fwd_tile_stats, so that each XCD
-// streams its own range of W once. A lane's accumulators acc[i][j][4 s + e],
+// orientation (and tile order) of fwd_tile_stats, so that W is streamed once
+// per row block in bands of 32 vocabulary tiles. A lane's accumulators acc[i][j][4 s + e],
 // e = 0..3, are 4 consecutive ids of one token, so each goes to the scratch
 // row as one 16-byte store straight from registers (lanes l and l + 32 write
 // the two halves of 32 contiguous bytes; the 4 values of s complete a
