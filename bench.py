@@ -250,7 +250,7 @@ def _cpu_oracle(fn, units, sample, blas=False):
 
 
 def _cores():
-    """Host cores this process may use, capped at 16 (a one-GPU machine's share)."""
+    """Host cores this process may use, capped at 16 (one GPU's share of a 128-core, 8-GPU host)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
