@@ -832,8 +832,8 @@ def main():
     _CHECK_DETERMINISM[0] = not args.no_determinism
     _CPU_ORACLE[0] = args.cpu_sample > 0
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is a design note only)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 "
+                                   "(how the path would shard is described, not built)"}))
         sys.exit(2)
 
     import synth
