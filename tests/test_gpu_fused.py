@@ -61,7 +61,8 @@ def _check(out, hb, wb, y, T, rows=None):
 
 
 @pytest.mark.parametrize("N,H,V,T", [(300, 256, 1000, 1.0), (77, 128, 515, 0.7),
-                                     (513, 512, 2049, 1.8), (5, 64, 7, 1.0)])
+                                     (513, 512, 2049, 1.8), (5, 64, 7, 1.0),
+                                     (5, 64, 1, 1.0), (9, 64, 2, 0.7)])
 def test_ragged_small_shapes(N, H, V, T):
     w, hb, wb, y = _inputs("fused", N, H, V)
     out = _run(hb, wb, y, T)
@@ -156,3 +157,23 @@ def test_nonfinite_hidden_rows_are_flagged(p):
     torch.cuda.synchronize()
     assert np.all(host(out["flags"]) & rlk.FLAG_NONFINITE)
     assert np.all(np.isnan(host(out["logprob"])))
+
+
+def test_zero_rows():
+    """N = 0: empty outputs from the forward; the backward writes dW = 0."""
+    H, V = 64, 3001
+    w = synth.workload("fused", N=1, H=H, V=V)
+    W = bf16_to_device(synth.weight_rows(w, range(V)))
+    h = torch.empty(0, H, device=DEV, dtype=torch.bfloat16)
+    y = torch.empty(0, device=DEV, dtype=torch.int64)
+    for p in (1.0, 0.9):
+        print(f"  rlk_logprob_fused_linear N=0 H={H} V={V} p={p}", flush=True)
+        out = rlk.logprob_fused_linear(h, W, y, 0.7, p)
+        torch.cuda.synchronize()
+        assert out["logprob"].numel() == 0 and out["entropy"].numel() == 0
+        g = torch.empty(0, device=DEV, dtype=torch.float32)
+        print(f"  rlk_logprob_fused_linear_bwd N=0 H={H} V={V} p={p}", flush=True)
+        dh, dw = rlk.logprob_fused_linear_bwd(h, W, y, out["saved"], g, g, 0.7, p)
+        torch.cuda.synchronize()
+        assert dh.numel() == 0 and dw.shape == (V, H)
+        assert torch.count_nonzero(dw).item() == 0

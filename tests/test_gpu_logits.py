@@ -347,3 +347,34 @@ def test_bf16_row_as_last_and_middle_row_of_a_block(p):
                 assert host(v)[0].tobytes() == host(out[k])[c].tobytes(), (k, c)
     o = OL.logprob_from_logits(OL.widen_bf16(base), yb, OL.f32(0.7), OL.f32(p))
     check({k: (None if v is None else host(v)[:K]) for k, v in out.items()}, o, **BF16_TOL)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 9, 17])
+@pytest.mark.parametrize("T,p", [(1.0, 1.0), (0.7, 0.5), (0.3, 0.95)])
+def test_tiny_vocabularies(dtype, V, T, p):
+    """V below one 16-byte vector and just past it: a one-token vocabulary
+    (lp = 0, H = 0), ties across the whole row, a dominant token."""
+    r = np.random.default_rng(V)
+    rows = [r.normal(0, 2.0, V), np.full(V, 1.5), np.where(np.arange(V) == V - 1, 9.0, -1.0)]
+    arr = np.stack(rows).astype(np.float32)
+    if dtype == "bf16":
+        arr = synth.bf16_bits_from_f32(arr).reshape(arr.shape)
+    y = np.array([0, V // 2, V - 1], dtype=np.int64)
+    z = widen(arr, dtype)
+    o = OL.logprob_from_logits(z, y, OL.f32(T), OL.f32(p))
+    g = run(arr, dtype, y, T, p)
+    check(g, o, **(F32_TOL if dtype == "f32" else BF16_TOL))
+    if V == 1:   # (the entropy is a difference of fp64 terms: zero to rounding)
+        assert np.all(g["lp_full"] == 0) and np.all(g["lp_trunc"] == 0)
+        assert np.all(np.abs(g["entropy_full"]) <= 1e-12) and np.all(g["nucleus_size"] == 1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_rows(dtype):
+    V = 151936 if dtype == "bf16" else 8192
+    x = torch.empty(0, V, device=DEV, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    print(f"  rlk_logprob_from_logits N=0 V={V} {dtype}", flush=True)
+    out = rlk.logprob_from_logits(x, torch.empty(0, dtype=torch.int64), 0.7, 0.95)
+    torch.cuda.synchronize()
+    assert all(v is None or v.numel() == 0 for v in out.values())
