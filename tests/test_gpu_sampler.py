@@ -168,3 +168,26 @@ def test_qwen_logits_full_size_sampled_rows():
     for i, n in enumerate(rows):
         want = OS.sample_row(z[i], T, p, SEED, OFFSET, int(n))
         assert ids[n] == want or ids[n] in _acceptable(z[i], T, p, SEED, OFFSET, int(n)), n
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 2, 9])
+def test_tiny_vocabularies_and_zero_rows(dtype, V):
+    """V = 1 always draws token 0 with logprob 0; tiny rows agree with the
+    oracle's draw; a zero-row call returns empty outputs."""
+    r = np.random.default_rng(40 + V)
+    z = r.normal(0, 2, (16, V)).astype(np.float32)
+    z[1, :] = 0.5                                    # a tied row
+    if dtype == "bf16":
+        bits = synth.bf16_bits_from_f32(z).reshape(z.shape)
+        x, z64 = bf16_to_device(bits), OL.widen_bf16(bits)
+    else:
+        x, z64 = f32_to_device(z), z.astype(np.float64)
+    for T, p in ((1.0, 1.0), (0.7, 0.5)):
+        out = _draw(x, T, p)
+        _check_ids(out["samples"], z64, OL.f32(T), OL.f32(p))
+        if V == 1:
+            assert torch.all(out["samples"] == 0) and torch.all(out["logprob"] == 0)
+    empty = x[:0]
+    out = _draw(empty, 0.7, 0.95)
+    assert all(v is None or v.numel() == 0 for v in out.values())
