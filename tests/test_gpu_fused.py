@@ -177,3 +177,4 @@ def test_zero_rows():
         torch.cuda.synchronize()
         assert dh.numel() == 0 and dw.shape == (V, H)
         assert torch.count_nonzero(dw).item() == 0
+

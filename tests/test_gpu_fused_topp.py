@@ -220,3 +220,41 @@ def test_grpo_workload_full_size_sampled_rows():
     _check({k: v[rows] for k, v in g.items()}, o, z64, y[rows], w.temperature,
            hw=(OL.widen_bf16(hb[rows]), W64))
     assert np.all(g["nucleus_size"] >= 1) and np.all(g["nucleus_size"] <= w.V)
+
+
+class _WidenedRows:
+    """fp64 rows of a bf16 matrix, widened on demand (the near-tie rule reads
+    a few rows of W; all of W in fp64 would not fit at V = 2^24)."""
+
+    def __init__(self, bits):
+        self.bits = bits
+
+    def __getitem__(self, idx):
+        return OL.widen_bf16(self.bits[idx])
+
+
+@pytest.mark.parametrize("p", [0.9, 1.0])
+def test_maximum_vocabulary(p):
+    """V = 2^24, the largest vocabulary the boundary accepts (H = 64, two
+    tokens, so one 2^24-wide logits block), against the oracle, whose fp64
+    logits are formed chunk by chunk from the same bf16 operands."""
+    N, H, V = 2, 64, 1 << 24
+    r = np.random.default_rng(91)
+    wb = synth.bf16_bits_from_f32(r.standard_normal((V, H), dtype=np.float32) * np.float32(0.05))
+    wb = wb.reshape(V, H)
+    hb = synth.bf16_bits_from_f32(r.standard_normal((N, H), dtype=np.float32)).reshape(N, H)
+    y = np.array([3, V - 2], dtype=np.int64)
+    print(f"  oracle logits {N} x {V} (H={H})", flush=True)
+    h64 = OL.widen_bf16(hb)
+    z64 = np.empty((N, V))
+    for c in range(0, V, 1 << 20):
+        z64[:, c:c + (1 << 20)] = OF.logits(h64, OL.widen_bf16(wb[c:c + (1 << 20)]))
+    T = 0.7
+    o = OL.logprob_from_logits(z64, y, OL.f32(T), OL.f32(p))
+    g = _run(bf16_to_device(hb), bf16_to_device(wb), y, T, p)
+    if p < 1.0:
+        _check(g, o, z64, y, OL.f32(T), hw=(h64, _WidenedRows(wb)))
+    else:   # the p = 1 path (tile statistics and their merge): the full softmax
+        assert_close_rows(g["logprob"], o.lp_full, LP_TOL, what="logprob")
+        assert_close_rows(g["entropy"], o.h_full, H_ATOL, H_RTOL, what="entropy")
+        assert np.all(g["nucleus_size"] == V)

@@ -378,3 +378,22 @@ def test_zero_rows(dtype):
     out = rlk.logprob_from_logits(x, torch.empty(0, dtype=torch.int64), 0.7, 0.95)
     torch.cuda.synchronize()
     assert all(v is None or v.numel() == 0 for v in out.values())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_maximum_vocabulary(dtype):
+    """V = 2^24, the largest vocabulary the boundary accepts: a Gaussian row
+    and, in bf16, a constant row (one value held 2^24 times wraps its 16-bit
+    counter, so the row is handed to the generic kernel), in fp32 a row with
+    a dominant token."""
+    V = 1 << 24
+    r = np.random.default_rng(77)
+    second = (np.full(V, -1.25) if dtype == "bf16"
+              else np.where(np.arange(V) == 12345, 20.0, r.normal(0, 1.0, V)))
+    rows = np.stack([r.normal(0, 2.5, V), second]).astype(np.float32)
+    arr = synth.bf16_bits_from_f32(rows).reshape(rows.shape) if dtype == "bf16" else rows
+    y = np.array([7, 12345], dtype=np.int64)
+    print(f"  oracle on 2 x {V} ({dtype})", flush=True)
+    o = OL.logprob_from_logits(widen(arr, dtype), y, OL.f32(0.7), OL.f32(0.95))
+    g = run(arr, dtype, y, 0.7, 0.95)
+    check(g, o, **(F32_TOL if dtype == "f32" else BF16_TOL))
