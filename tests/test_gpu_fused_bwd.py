@@ -329,3 +329,52 @@ def test_bwd_grad_hidden_only_2_byte_aligned():
         assert bits_equal(dw, dw_ref)
         # nothing written outside [ptr, ptr + 2 N H)
         assert torch.isnan(buf[0].float()) and torch.isnan(buf[1 + N * H:].float()).all()
+
+
+@pytest.mark.parametrize("p", [1.0, 0.9])
+def test_maximum_rows(p):
+    """N = 2^23 - 1 tokens, the most the fused path accepts: 513 logits
+    blocks at top-p, and in the backward rows of h^T and G^T 2^23 + 64
+    elements long, at the edge of the tile GEMM's 32-bit copy offsets. The
+    upstream gradients are zero except on 64 sampled rows (block seams and
+    the last row among them), so the oracle's dW is the sum over those rows
+    alone; the forward and dh are compared there, and dh of every other row
+    must be exactly 0."""
+    N, H, V, T = (1 << 23) - 1, 64, 7, 0.7
+    r = np.random.default_rng(123)
+    hb = synth.bf16_bits_from_f32(r.standard_normal((N, H), dtype=np.float32)).reshape(N, H)
+    wb = synth.bf16_bits_from_f32(r.standard_normal((V, H), dtype=np.float32)
+                                  * np.float32(0.2)).reshape(V, H)
+    y = r.integers(0, V, N)
+    rows = np.unique(np.concatenate([[0, 16383, 16384, N - 16384, N - 1],
+                                     r.choice(N, 59, replace=False)]))
+    g_lp = np.zeros(N, np.float32)
+    g_h = np.zeros(N, np.float32)
+    g_lp[rows] = (r.standard_normal(len(rows)) / len(rows)).astype(np.float32)
+    g_h[rows] = (r.standard_normal(len(rows)) / len(rows)).astype(np.float32)
+    h, W, yt = bf16_to_device(hb), bf16_to_device(wb), torch.as_tensor(y).to(DEV)
+    print(f"  rlk fused fwd+bwd N={N} H={H} V={V} T={T} p={p}", flush=True)
+    fwd = rlk.logprob_fused_linear(h, W, yt, T, p)
+    dh, dw = rlk.logprob_fused_linear_bwd(h, W, yt, fwd["saved"], torch.as_tensor(g_lp).to(DEV),
+                                          torch.as_tensor(g_h).to(DEV), T, p)
+    torch.cuda.synchronize()
+    h64, w64 = OL.widen_bf16(hb[rows]), OL.widen_bf16(wb)
+    o = OF.forward(h64, w64, y[rows], OL.f32(T), OL.f32(p))
+    ok = (o.flags & OL.FLAG_BOUNDARY) == 0
+    lp = host(fwd["logprob"])[rows]
+    assert_close_rows(lp[ok], o.lp_trunc[ok], 2e-3, what="logprob")
+    assert_close_rows(host(fwd["entropy"])[rows][ok], o.h_trunc[ok], 1e-5, 1e-3, what="entropy")
+    lp_all = fwd["logprob"]
+    assert bool(torch.all((lp_all <= 0) | torch.isneginf(lp_all)))
+    dh_ref, dw_ref = OF.backward(h64, w64, y[rows], g_lp[rows].astype(np.float64),
+                                 g_h[rows].astype(np.float64), OL.f32(T), OL.f32(p))
+    idx = torch.as_tensor(rows).to(DEV)
+    dh_rows = host(dh.index_select(0, idx).float()).astype(np.float64)
+    assert _rel(dh_rows, dh_ref) <= NORM_TOL, ("dh", _rel(dh_rows, dh_ref))
+    _rows_ok(dh_rows, dh_ref, "dh rows")
+    others = torch.ones(N, dtype=torch.bool, device=DEV)
+    others[idx] = False
+    assert int(torch.count_nonzero(dh[others])) == 0
+    dw_got = host(dw).astype(np.float64)
+    assert _rel(dw_got, dw_ref) <= NORM_TOL, ("dW", _rel(dw_got, dw_ref))
+    _rows_ok(dw_got, dw_ref, "dW rows")
