@@ -197,3 +197,20 @@ def test_device_offsets_and_their_device_check():
     again = rlk.grpo_token_loss(*args, cu_dev, rewards=r, group_size=4)
     for k in good:
         assert torch.equal(good[k], again[k]), k
+
+
+def test_many_tokens():
+    """About 10^7 packed tokens (32 responses of 2^17..2^19 tokens): tens of
+    thousands of 256-token partials folded in one fixed order."""
+    rng = np.random.default_rng(31)
+    lengths = rng.integers(1 << 17, 1 << 19, 32)
+    cu, lp_new, lp_old, lp_ref = _inputs(8, lengths, sd_old=0.3, sd_ref=0.2)
+    r = rng.integers(0, 2, 32).astype(np.float32)
+    A = OG.advantages(r, 8)
+    print(f"  oracle loss T_tot={cu[-1]}", flush=True)
+    o = OG.token_loss(lp_new, lp_old, lp_ref, cu, A)
+    print(f"  rlk_grpo_token_loss T_tot={cu[-1]} B={len(lengths)}", flush=True)
+    out = rlk.grpo_token_loss(f32_to_device(lp_new), f32_to_device(lp_old), f32_to_device(lp_ref),
+                              cu, rewards=r, group_size=8)
+    torch.cuda.synchronize()
+    _compare(out, o, o.near_branch)
