@@ -87,6 +87,9 @@ __global__ __launch_bounds__(256) void fill_f32(float* p, int64_t n) {
 // those rows' lines crowd onto a few memory channels (the dh product ran 4-6 %
 // slower at that stride than at 64 KB + 128 bytes).
 constexpr int64_t kLdPad = 64;
+// rows and vocabularies below 2^23 (checked at the boundary) keep every
+// padded stride within the tile GEMM's limit
+static_assert((int64_t(1) << 23) + kLdPad <= gemm::kMaxLd, "padded strides fit the copy offsets");
 
 struct ChunkArgs {
   int64_t c0, csz, cpad;   // chunk start, rows, rows padded to a multiple of 64

@@ -45,7 +45,9 @@ constexpr int kLoads = kOpSlots / kThreads;   // copies per thread per operand p
 constexpr int kVmPerStage = 2 * kLoads;       // vmcnt of one stage (A and B)
 constexpr int kStageBytes = 2 * kOpSlots * 16;  // 32 KB: A then B
 constexpr int kKMultiple = 2 * kStageK;       // K must be a multiple of this
-constexpr int64_t kMaxLd = int64_t(1) << 23;  // 255 * ld * 2 bytes must fit 32 bits
+// largest row length (elements): a copy's per-lane byte offset, up to
+// (255 ld + 24) 2, is a 32-bit unsigned value
+constexpr int64_t kMaxLd = ((int64_t(1) << 32) - 48) / 510;
 
 // LDS of one block: [stage][A, B][slot].
 typedef uint4 Smem[kStages][2][kOpSlots];
