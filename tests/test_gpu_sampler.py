@@ -191,3 +191,15 @@ def test_tiny_vocabularies_and_zero_rows(dtype, V):
     empty = x[:0]
     out = _draw(empty, 0.7, 0.95)
     assert all(v is None or v.numel() == 0 for v in out.values())
+
+
+def test_maximum_vocabulary():
+    """A bf16 row of 2^24 - 3 tokens (the largest vocabulary the boundary
+    accepts, less a ragged tail inside the last 16-byte vector); the draw
+    against the oracle's."""
+    V = (1 << 24) - 3
+    r = np.random.default_rng(55)
+    bits = synth.bf16_bits_from_f32(r.normal(0, 2.5, (1, V)).astype(np.float32)).reshape(1, V)
+    out = _draw(bf16_to_device(bits), 0.7, 0.95)
+    print(f"  oracle draw over {V} tokens", flush=True)
+    _check_ids(out["samples"], OL.widen_bf16(bits), OL.f32(0.7), OL.f32(0.95))
