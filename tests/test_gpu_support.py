@@ -220,3 +220,23 @@ def test_qwen_logits_full_size_sampled_rows():
     o = OSup.logprob_from_support(z, y[rows], OL.f32(w.temperature), sub_off, sub_ids)
     _check({k: v[rows] for k, v in g.items()}, o)
     assert np.all(g["flags"] == 0) and np.all(np.isfinite(g["logprob"]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_maximum_vocabulary(dtype):
+    """Rows of 2^24 tokens, the largest vocabulary the boundary accepts: a
+    sparse set, the full vocabulary, and the nucleus check on a sparse set."""
+    V = 1 << 24
+    r = np.random.default_rng(66)
+    z32 = r.normal(0, 2.5, (2, V)).astype(np.float32)
+    arr = synth.bf16_bits_from_f32(z32).reshape(z32.shape) if dtype == "bf16" else z32
+    z = _widen(arr, dtype)
+    sparse = np.unique(np.concatenate([[0, V - 1], r.choice(V, 5000, replace=False)]))
+    ids = np.concatenate([sparse, np.arange(V)]).astype(np.int32)
+    offsets = np.array([0, len(sparse), len(sparse) + V], dtype=np.int64)
+    y = np.array([int(sparse[17]), V - 1], dtype=np.int64)
+    T = OL.f32(0.7)
+    print(f"  oracle support scoring over {V} tokens ({dtype})", flush=True)
+    o = OSup.logprob_from_support(z, y, T, offsets, ids)
+    g = _run(_dev(arr, dtype), y, 0.7, offsets, ids)
+    _check(g, o)
